@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the reductions.
+
+This module only draws numbers: it holds none of the reduction arithmetic, so
+both the GPU tests and the CPU oracle may take their inputs from it.  Every
+array is drawn on the host with ``torch.Generator("cpu").manual_seed(seed)``,
+so the oracle and the GPU see identical bytes.
+
+Arrays are column-major, as on the AcceleratedKernels.jl pages (Julia
+semantics): a column-major (d1, d2, d3) array is held as a flat buffer with
+element strides (1, d1, d1*d2).  ``cm_strides`` gives those strides.
+
+The shapes follow the pages' own benchmark rows: PR #139 ("Finish whole-array
+reductions on the device", section "Numbers") times Float32 sums of 10^4,
+10^6 and 10^8 elements; PR #176 (strided reductions along dims, section
+"Timings") times sum(x; dims=2) of 768x1024x8, 64x4096x32, 3072x2048 and
+8192x8192 arrays in BFloat16 and Float32.  The pages give no value
+distributions; the ones used here are listed with each workload.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+def _gen(seed: int) -> torch.Generator:
+    return torch.Generator("cpu").manual_seed(int(seed))
+
+
+def uniform(n: int, lo: float, hi: float, seed: int) -> torch.Tensor:
+    """n float32 values lo + (hi - lo) * U[0, 1)."""
+    u = torch.rand(int(n), generator=_gen(seed), dtype=torch.float32)
+    if lo == 0.0 and hi == 1.0:
+        return u
+    return u.mul_(hi - lo).add_(lo)
+
+
+def normal(n: int, seed: int, dtype=torch.float32) -> torch.Tensor:
+    """n standard normal values, drawn in float32 and rounded to dtype."""
+    z = torch.randn(int(n), generator=_gen(seed), dtype=torch.float32)
+    return z if dtype == torch.float32 else z.to(dtype)
+
+
+def randint(n: int, lo: int, hi: int, seed: int, dtype=torch.int32) -> torch.Tensor:
+    """n integers drawn uniformly from the inclusive range [lo, hi]."""
+    return torch.randint(int(lo), int(hi) + 1, (int(n),), generator=_gen(seed), dtype=dtype)
+
+
+def small_ints(n: int, lo: int, hi: int, seed: int, dtype=torch.float32) -> torch.Tensor:
+    """Integer values in [lo, hi] stored as a floating dtype (exact sums)."""
+    return randint(n, lo, hi, seed, torch.int64).to(dtype)
+
+
+def randperm(n: int, seed: int) -> torch.Tensor:
+    """A random permutation of 0..n-1 as int32."""
+    return torch.randperm(int(n), generator=_gen(seed)).to(torch.int32)
+
+
+def cm_strides(shape) -> tuple:
+    """Element strides of a contiguous column-major array of `shape`."""
+    st, acc = [], 1
+    for s in shape:
+        st.append(acc)
+        acc *= int(s)
+    return tuple(st)
+
+
+@dataclass
+class Array:
+    """A flat host buffer viewed as a column-major array."""
+    name: str
+    data: torch.Tensor          # flat, contiguous
+    shape: tuple                # column-major extents
+    recipe: str
+
+    @property
+    def strides(self) -> tuple:
+        return cm_strides(self.shape)
+
+    @property
+    def numel(self) -> int:
+        return int(math.prod(self.shape))
+
+
+# ----------------------------------------------------------------- workloads
+# Each function returns the arrays of one workload, drawn from seeds
+# 1000 * k + j (k = workload number, j = array number).
+
+def whole_small(n: int = 10_000) -> list:
+    """10^4 float32 U[-1,1); the same draw scaled to int32 in [-1000, 1000]."""
+    x = uniform(n, -1.0, 1.0, 1000)
+    xi = torch.round(x * 1000.0).to(torch.int32)
+    return [Array("f32_u[-1,1)", x, (n,), "U[-1,1) seed 1000"),
+            Array("i32_[-1000,1000]", xi, (n,), "round(1000*U[-1,1)) seed 1000")]
+
+
+def whole_large(n: int) -> list:
+    """n float32 U[0,1) and a random permutation of 0..n-1 as int32."""
+    j = 0 if n <= 10**6 else 2
+    x = uniform(n, 0.0, 1.0, 2000 + j)
+    p = randperm(n, 2001 + j)
+    return [Array("f32_u[0,1)", x, (n,), f"U[0,1) seed {2000 + j}"),
+            Array("i32_perm", p, (n,), f"randperm seed {2001 + j}")]
+
+
+def matrix_3072x2048() -> list:
+    """3072x2048 column-major N(0,1) in bfloat16 and float32."""
+    shape = (3072, 2048)
+    n = math.prod(shape)
+    return [Array("bf16_n01", normal(n, 3000, torch.bfloat16), shape, "N(0,1)->bf16 seed 3000"),
+            Array("f32_n01", normal(n, 3001), shape, "N(0,1) seed 3001")]
+
+
+def middle_dim_3d() -> list:
+    """(features, sequence, batch) arrays reduced over the middle dim."""
+    s1, s2 = (768, 1024, 8), (64, 4096, 32)
+    return [Array("bf16_768x1024x8", normal(math.prod(s1), 4000, torch.bfloat16), s1,
+                  "N(0,1)->bf16 seed 4000"),
+            Array("f32_768x1024x8", normal(math.prod(s1), 4001), s1, "N(0,1) seed 4001"),
+            Array("f32_64x4096x32", uniform(math.prod(s2), 0.0, 1.0, 4002), s2,
+                  "U[0,1) seed 4002")]
+
+
+def matrix_8192() -> list:
+    """8192x8192 float32 U[-1,1) and int32 in [-2^20, 2^20]."""
+    shape = (8192, 8192)
+    n = math.prod(shape)
+    return [Array("f32_u[-1,1)", uniform(n, -1.0, 1.0, 5000), shape, "U[-1,1) seed 5000"),
+            Array("i32_pm2^20", randint(n, -2**20, 2**20, 5001), shape,
+                  "U{-2^20..2^20} seed 5001")]
