@@ -1,0 +1,410 @@
+"""Benchmark of the device-wide mapreduce on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step runs every call of the hot path once over resident synthetic input:
+  whole array, 10^8 float32 U[0,1) (AcceleratedKernels.jl PR #139, "Numbers"):
+    1. sum -> host value                  (two launches + copy + host finish)
+    2. sum -> device scalar, init = 1.5   (overwrite)
+    3. sum -> fold into that scalar
+    4. max and 5. min of a permutation of 0..10^8-1 (int32)
+  8192x8192 column-major (PR #176, "Timings", last row):
+    6. float32 sum over dims=2   7. float32 sum over dims=1
+    8. float32 max over dims=2   9. float32 sum of squares of the whole array
+   10. int32 sum over dims=1 into int64
+Each call reads its own copy of the input, so no call finds its data in the
+256 MB Infinity Cache left behind by the previous one.
+
+Printed: one JSON line with the aggregate algorithmic bandwidth (bytes the
+method must move / time), the roofline of the dominant kernel (the float32
+sum first pass, timed per launch with HIP events on its stream), and the CPU
+oracle timed on the host over the same step as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for 1e8 fp32 sum and strided dims reductions"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+N_WHOLE = 10**8
+SIDE = 8192
+DOMINANT = "k_all_pass1<float, float, OpSum, MapIdentity>"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=30.0,
+                    help="seconds of oracle work allowed for the CPU baseline")
+    ap.add_argument("--per-call-reps", type=int, default=5,
+                    help="reps of the per-call table (0 skips it)")
+    return ap.parse_args()
+
+
+class Call:
+    """One rk_* call of the step with its marshalled arguments."""
+
+    def __init__(self, name, kind, bytes_alg, fn, timed=False, kernel=""):
+        self.name, self.kind, self.bytes_alg, self.fn = name, kind, bytes_alg, fn
+        self.timed, self.kernel = timed, kernel
+
+    def __call__(self):
+        rc = self.fn()
+        if rc != 0:
+            raise RuntimeError(f"{self.name}: rk status {rc}")
+
+
+def build_step(rk, torch, dev):
+    from reduction_primitives_amd import workloads as W
+
+    log("generating inputs ...")
+    t0 = time.time()
+    xf, perm = W.whole_large(N_WHOLE)
+    mf, mi = W.matrix_8192()
+    log(f"  inputs drawn in {time.time() - t0:.1f} s")
+
+    x = [xf.data.to(dev) for _ in range(3)]
+    p = [perm.data.to(dev) for _ in range(2)]
+    y = [mf.data.to(dev) for _ in range(4)]
+    z = mi.data.to(dev)
+    torch.cuda.synchronize()
+
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    shape, strides = (SIDE, SIDE), (1, SIDE)
+    ws_bytes = max(rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 1, [N_WHOLE], [1], 1),
+                   rk.rk_workspace_size(rk.RK_I32, rk.RK_I64, 1, [N_WHOLE], [1], 1),
+                   rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 2, shape, strides, 2),
+                   rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 2, shape, strides, 1),
+                   rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 2, shape, strides, 3),
+                   rk.rk_workspace_size(rk.RK_I32, rk.RK_I64, 2, shape, strides, 1))
+    ws_t = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = ws_t.data_ptr()
+    init15 = ctypes.c_float(1.5)
+    host_out = ctypes.c_float()
+    o_scalar = torch.empty(1, dtype=torch.float32, device=dev)
+    o_max = torch.empty(1, dtype=torch.int32, device=dev)
+    o_min = torch.empty(1, dtype=torch.int32, device=dev)
+    o_d2 = torch.empty(SIDE, dtype=torch.float32, device=dev)
+    o_d1 = torch.empty(SIDE, dtype=torch.float32, device=dev)
+    o_mx = torch.empty(SIDE, dtype=torch.float32, device=dev)
+    o_sq = torch.empty(1, dtype=torch.float32, device=dev)
+    o_i = torch.empty(SIDE, dtype=torch.int64, device=dev)
+    F32, I32, I64 = rk.RK_F32, rk.RK_I32, rk.RK_I64
+    SUM, MAX, MIN = rk.RK_OP_SUM, rk.RK_OP_MAX, rk.RK_OP_MIN
+    ID, SQ = rk.RK_MAP_IDENTITY, rk.RK_MAP_SQUARE
+    OW, FO, HO = rk.RK_MODE_OVERWRITE, rk.RK_MODE_FOLD, rk.RK_MODE_HOST
+    nb = N_WHOLE * 4
+    mb = SIDE * SIDE * 4
+    init_p = ctypes.byref(init15)
+    calls = [
+        Call("sum_1e8_f32_host", "all", nb + 4,
+             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[0].data_ptr(), N_WHOLE, None, HO,
+                                      ctypes.addressof(host_out), ws, st), True, DOMINANT),
+        Call("sum_1e8_f32_init1.5", "all", nb + 4,
+             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[1].data_ptr(), N_WHOLE, init_p, OW,
+                                      o_scalar.data_ptr(), ws, st), True, DOMINANT),
+        Call("sum_1e8_f32_fold", "all", nb + 8,
+             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[2].data_ptr(), N_WHOLE, None, FO,
+                                      o_scalar.data_ptr(), ws, st), True, DOMINANT),
+        Call("max_1e8_i32_perm", "all", nb + 4,
+             lambda: rk.rk_reduce_all(MAX, ID, I32, I32, I32, p[0].data_ptr(), N_WHOLE, None, OW,
+                                      o_max.data_ptr(), ws, st)),
+        Call("min_1e8_i32_perm", "all", nb + 4,
+             lambda: rk.rk_reduce_all(MIN, ID, I32, I32, I32, p[1].data_ptr(), N_WHOLE, None, OW,
+                                      o_min.data_ptr(), ws, st)),
+        Call("sum_8192sq_f32_dims2", "dims", mb + SIDE * 4,
+             lambda: rk.rk_reduce_dims(SUM, ID, F32, F32, F32, y[0].data_ptr(), 2, shape, strides, 2,
+                                       None, OW, o_d2.data_ptr(), ws, st)),
+        Call("sum_8192sq_f32_dims1", "dims", mb + SIDE * 4,
+             lambda: rk.rk_reduce_dims(SUM, ID, F32, F32, F32, y[1].data_ptr(), 2, shape, strides, 1,
+                                       None, OW, o_d1.data_ptr(), ws, st)),
+        Call("max_8192sq_f32_dims2", "dims", mb + SIDE * 4,
+             lambda: rk.rk_reduce_dims(MAX, ID, F32, F32, F32, y[2].data_ptr(), 2, shape, strides, 2,
+                                       None, OW, o_mx.data_ptr(), ws, st)),
+        Call("sumsq_8192sq_f32_all", "dims", mb + 4,
+             lambda: rk.rk_reduce_dims(SUM, SQ, F32, F32, F32, y[3].data_ptr(), 2, shape, strides, 3,
+                                       None, OW, o_sq.data_ptr(), ws, st)),
+        Call("sum_8192sq_i32_dims1_i64", "dims", mb + SIDE * 8,
+             lambda: rk.rk_reduce_dims(SUM, ID, I32, I64, I64, z.data_ptr(), 2, shape, strides, 1,
+                                       None, OW, o_i.data_ptr(), ws, st)),
+    ]
+    outs = dict(host=host_out, scalar=o_scalar, max=o_max, min=o_min, d2=o_d2, d1=o_d1, mx=o_mx,
+                sq=o_sq, i64=o_i)
+    inputs = dict(xf=xf, perm=perm, mf=mf, mi=mi)
+    keep = (x, p, y, z, ws_t)
+    return calls, outs, inputs, keep
+
+
+def plan_names(rk, torch):
+    """Kernel each call takes, from the library's planner."""
+    names = {}
+    for dims, key in ((2, "d2"), (1, "d1"), ((1, 2), "all")):
+        names[key] = rk.plan_dims(torch.float32, (SIDE, SIDE), (1, SIDE), dims)["kernel_name"]
+    names["i64"] = rk.plan_dims(torch.int32, (SIDE, SIDE), (1, SIDE), 1)["kernel_name"]
+    return names
+
+
+def cpu_leg(inputs, outs, budget_s, host_value):
+    import numpy as np
+
+    import oracle as O
+
+    xf = inputs["xf"].data.numpy()
+    perm = inputs["perm"].data.numpy()
+    mf = inputs["mf"].data.numpy()
+    mi = inputs["mi"].data.numpy()
+    shape, strides = (SIDE, SIDE), (1, SIDE)
+    plan = [
+        ("sum_1e8_f32_host", N_WHOLE * 4, lambda: O.reduce_all(O.SUM, O.IDENTITY, O.F32, O.F32, xf, 0.0)),
+        ("sum_1e8_f32_init1.5", N_WHOLE * 4, lambda: O.reduce_all(O.SUM, O.IDENTITY, O.F32, O.F32, xf, 1.5)),
+        ("max_1e8_i32_perm", N_WHOLE * 4, lambda: O.reduce_all(O.MAX, O.IDENTITY, O.I32, O.I32, perm, -2**31)),
+        ("min_1e8_i32_perm", N_WHOLE * 4, lambda: O.reduce_all(O.MIN, O.IDENTITY, O.I32, O.I32, perm, 2**31 - 1)),
+        ("sum_8192sq_f32_dims2", SIDE * SIDE * 4,
+         lambda: O.reduce_dims(O.SUM, O.IDENTITY, O.F32, O.F32, mf, shape, strides, 0b10, 0.0)),
+        ("sum_8192sq_f32_dims1", SIDE * SIDE * 4,
+         lambda: O.reduce_dims(O.SUM, O.IDENTITY, O.F32, O.F32, mf, shape, strides, 0b01, 0.0)),
+        ("max_8192sq_f32_dims2", SIDE * SIDE * 4,
+         lambda: O.reduce_dims(O.MAX, O.IDENTITY, O.F32, O.F32, mf, shape, strides, 0b10, -math.inf)),
+        ("sumsq_8192sq_f32_all", SIDE * SIDE * 4,
+         lambda: O.reduce_all(O.SUM, O.SQUARE, O.F32, O.F32, mf, 0.0)),
+        ("sum_8192sq_i32_dims1_i64", SIDE * SIDE * 4,
+         lambda: O.reduce_dims(O.SUM, O.IDENTITY, O.I32, O.I64, mi, shape, strides, 0b01, 0)),
+    ]
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+        pinned = True
+    except (AttributeError, OSError):
+        pinned = False
+    results, t_total, b_total = {}, 0.0, 0
+    for name, nbytes, fn in plan:
+        if t_total > budget_s:
+            break
+        t0 = time.perf_counter()
+        r = fn()
+        dt = time.perf_counter() - t0
+        results[name] = r
+        t_total += dt
+        b_total += nbytes
+        log(f"  oracle {name}: {dt * 1e3:.1f} ms ({nbytes / dt / 1e9:.2f} GB/s)")
+    # parity of the last GPU step against these oracle results
+    ok = True
+    notes = []
+
+    def near(g, r, s):
+        return abs(g - r) <= 1e-5 * s
+
+    S_x = float(np.abs(xf.astype(np.float64)).sum()) if "sum_1e8_f32_host" in results else None
+    if "sum_1e8_f32_host" in results:
+        ok &= near(host_value, results["sum_1e8_f32_host"], S_x)
+    if "sum_1e8_f32_init1.5" in results:
+        # after the fold the scalar holds (1.5 + sum) + sum
+        want = results["sum_1e8_f32_init1.5"] + results["sum_1e8_f32_host"]
+        ok &= near(float(outs["scalar"].item()), want, 1.5 + 2 * S_x)
+    if "max_1e8_i32_perm" in results:
+        ok &= int(outs["max"].item()) == results["max_1e8_i32_perm"] == N_WHOLE - 1
+    if "min_1e8_i32_perm" in results:
+        ok &= int(outs["min"].item()) == results["min_1e8_i32_perm"] == 0
+    absm = None
+    if "sum_8192sq_f32_dims2" in results:
+        absm = O.reduce_dims(O.SUM, O.ABS, O.F32, O.F32, mf, shape, strides, 0b10, 0.0)
+        ok &= bool(np.all(np.abs(outs["d2"].cpu().numpy() - results["sum_8192sq_f32_dims2"]) <= 1e-5 * absm))
+    if "sum_8192sq_f32_dims1" in results:
+        absm1 = O.reduce_dims(O.SUM, O.ABS, O.F32, O.F32, mf, shape, strides, 0b01, 0.0)
+        ok &= bool(np.all(np.abs(outs["d1"].cpu().numpy() - results["sum_8192sq_f32_dims1"]) <= 1e-5 * absm1))
+    if "max_8192sq_f32_dims2" in results:
+        ok &= bool(np.array_equal(outs["mx"].cpu().numpy().astype(np.float64), results["max_8192sq_f32_dims2"]))
+    if "sumsq_8192sq_f32_all" in results:
+        r = results["sumsq_8192sq_f32_all"]
+        ok &= near(float(outs["sq"].item()), r, r)
+    if "sum_8192sq_i32_dims1_i64" in results:
+        ok &= bool(np.array_equal(outs["i64"].cpu().numpy(), results["sum_8192sq_i32_dims1_i64"]))
+    sample = (", ".join(results) if len(results) < len(plan)
+              else "every call of one step except the fold, whose arithmetic is the overwrite's")
+    return dict(value=round(b_total / t_total / 1e9, 3), unit="GB/s", cores=1 if pinned else None,
+                kind="oracle", sample=f"{sample} (same inputs; {b_total / 1e9:.2f} GB in {t_total:.1f} s)",
+                host_cores_available=len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None), \
+        bool(ok)
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_all_pass1_f32_1e8.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        from reduction_primitives_amd.build import kernel_source_digest
+        if rec.get("kernel_source_digest") != kernel_source_digest():
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def per_call_table(calls, torch, reps, dev):
+    """Per call: warm (back to back) and cold (Infinity Cache flushed by a
+    512 MiB write first) times of the whole rk call, min and median."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    table = {}
+    for c in calls:
+        rows = {}
+        for mode in ("warm", "cold"):
+            ts = []
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.zero_()
+                torch.cuda.synchronize()
+                b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0 = time.perf_counter()
+                b.record()
+                c()
+                e.record()
+                e.synchronize()
+                wall = time.perf_counter() - t0
+                ts.append(wall * 1e6 if c.name.endswith("_host") else b.elapsed_time(e) * 1e3)
+            rows[mode] = dict(us_min=round(min(ts), 2), us_median=round(statistics.median(ts), 2),
+                              GBps=round(c.bytes_alg / (min(ts) * 1e-6) / 1e9, 1))
+        table[c.name] = rows
+        log(f"  {c.name:28s} warm {rows['warm']['us_min']:8.1f} us ({rows['warm']['GBps']:7.1f} GB/s)"
+            f"  cold {rows['cold']['us_min']:8.1f} us ({rows['cold']['GBps']:7.1f} GB/s)")
+    del flush
+    return table
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import reduction_primitives_amd as rk
+    rk.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs")
+
+    calls, outs, inputs, keep = build_step(rk, torch, dev)
+    kernels = plan_names(rk, torch)
+    bytes_step = sum(c.bytes_alg for c in calls)
+
+    def step(events=None):
+        for c in calls:
+            if events is not None and c.timed:
+                b, e = events.pop()
+                rk.rk_debug_set_launch_events(ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(e.cuda_event))
+                try:
+                    c()
+                finally:
+                    rk.rk_debug_set_launch_events(None, None)
+            else:
+                c()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    n_timed = sum(1 for c in calls if c.timed) * args.steps
+    pairs = []
+    for _ in range(n_timed):
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record(); e.record()          # creates the HIP events
+        pairs.append((b, e))
+    torch.cuda.synchronize()
+    pending = list(reversed(pairs))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(pending)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = bytes_step * args.steps / elapsed / 1e9
+    launch_ms = [b.elapsed_time(e) for b, e in pairs]
+    avg_launch_s = statistics.mean(launch_ms) * 1e-3
+    achieved = N_WHOLE * 4 / avg_launch_s / 1e9
+    log(f"step: {ms_per_step:.3f} ms, {value:.1f} GB/s aggregate ({value / PEAK_GBPS:.1%} of peak)")
+    log(f"dominant kernel {DOMINANT}: {avg_launch_s * 1e6:.1f} us per launch, {achieved:.1f} GB/s")
+
+    host_value = outs["host"].value
+    per_call = per_call_table(calls, torch, args.per_call_reps, dev) if args.per_call_reps > 0 else None
+
+    cpu, parity = None, None
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        cpu, parity = cpu_leg(inputs, outs, args.cpu_budget, host_value)
+
+    traffic = traffic_from_profile()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32,i32,i64",
+        "data": "synthetic (seeded torch CPU generator, copied to HBM before timing)",
+        "config": {
+            "workload": "1e8 fp32 whole-array sum (host; device init=1.5; fold) + 1e8 int32 "
+                        "permutation max and min + 8192x8192 fp32 column-major sum dims=2, sum "
+                        "dims=1, max dims=2, whole-array sum of squares + 8192x8192 int32 sum "
+                        "dims=1 into int64",
+            "calls_per_step": len(calls),
+            "algorithmic_bytes_per_step": bytes_step,
+            "value_frac_of_peak": round(value / PEAK_GBPS, 4),
+            "kernels_8192": kernels,
+            "device": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": DOMINANT,
+            "algorithmic_bytes_per_launch": N_WHOLE * 4,
+            "avg_launch_us": round(avg_launch_s * 1e6, 2),
+            "launches_timed": len(launch_ms),
+        },
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "per_call": per_call,
+    }
+    del keep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

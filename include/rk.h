@@ -1,0 +1,200 @@
+/*
+ * rk.h -- device-wide mapreduce for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  It computes the mapped reductions
+ * described on the AcceleratedKernels.jl pull-request pages:
+ *
+ *   - PR #139, "Finish whole-array reductions on the device": a whole array
+ *     is reduced in at most two launches (a grid-capped first pass whose
+ *     blocks stride over tiles, then a one-block second pass); the last pass
+ *     applies `init`, or folds into the output's previous value, or leaves a
+ *     bare partial that the host finishes (sections "What changes" and
+ *     "Compatibility").
+ *   - PR #176, strided reductions along dims: one selector picks among one
+ *     thread per output, a tiled 2-d block and a split columns kernel, and
+ *     the columns kernel also takes runs of contiguous outputs such as the
+ *     middle dim of a 3-d array (section "This PR").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Arrays are column-major (Julia semantics).  `shape[d]` is the extent of
+ * dim d and `strides[d]` its stride in ELEMENTS (>= 0); a contiguous
+ * (d1, d2, d3) array has strides (1, d1, d1*d2).  Bit d of `reduce_mask`
+ * marks dim d (0-based) as reduced, so Julia's `dims=k` is bit k-1.  The
+ * outputs are the kept dims, stored contiguously in column-major order (the
+ * reduced dims behave as extent 1).
+ *
+ * The result for each output is  R = s (+) f(x_0) (+) f(x_1) (+) ...  where
+ * (+) is the op, f the map applied after widening an element to the
+ * accumulator type, and s the starting value chosen by the mode:
+ *   RK_MODE_OVERWRITE  s = *init (the op's identity when init is NULL); the
+ *                      result is stored into the device array `out`;
+ *   RK_MODE_FOLD       s = the previous value of out[o], read back into the
+ *                      accumulator type; `init` is ignored, so an init that
+ *                      was applied by an earlier call is not applied again;
+ *   RK_MODE_HOST       s = *init (or identity); the GPU leaves a bare
+ *                      accumulator-typed partial in the workspace, which is
+ *                      copied back and finished on the host; `out` is a
+ *                      HOST pointer and the call returns after the stream has
+ *                      drained.  Valid only when there is a single output.
+ * `init` is applied exactly once.  Partial results keep the accumulator type
+ * until the final store, which converts once to the output type (round to
+ * nearest even for floating point, two's-complement wrap for integers).  The
+ * output is never used to hold intermediate values.  The association order
+ * is the library's own, so floating-point results may differ from a
+ * sequential loop by rounding.  Identities: 0 for sum, -inf / the
+ * accumulator's minimum integer for max, +inf / its maximum for min.  max
+ * and min propagate NaN.
+ *
+ * Dtype combinations: the input and accumulator are both floating point or
+ * both integer, and the accumulator is at least as wide as the input
+ * (f32 -> f32|f64, bf16 -> f32|f64, f16 -> f32|f64, f64 -> f64,
+ * i32 -> i32|i64, i64 -> i64).  The output has the accumulator's kind and any
+ * width of that kind; it may be narrower than the accumulator.
+ *
+ * Ownership: the caller owns every buffer (`ptr`, `out`, `workspace`).  The
+ * library allocates and frees no device memory.  Kernels are enqueued on
+ * `stream` (a hipStream_t; NULL is the null stream) of the current device.
+ * OVERWRITE and FOLD calls are asynchronous: buffers must stay alive until
+ * the stream's work has completed.  The library keeps no state between calls
+ * other than cached device properties, so calls from several host threads
+ * are safe (two calls that share a workspace must be ordered by the caller).
+ *
+ * Errors: every argument is validated before any launch; a rejected call
+ * returns a non-zero rk_status and writes nothing.  A HIP launch failure is
+ * reported as RK_ERR_HIP.  The library prints nothing unless the environment
+ * variable RK_DEBUG is set.
+ */
+#ifndef RK_H
+#define RK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RK_OK = 0,
+    RK_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, shape, mask, mode or alignment */
+    RK_ERR_UNSUPPORTED = 2,      /* dtype combination outside the table above */
+    RK_ERR_HIP = 3               /* the HIP runtime reported an error */
+} rk_status;
+
+typedef enum { RK_OP_SUM = 0, RK_OP_MAX = 1, RK_OP_MIN = 2 } rk_op;
+
+/* Element map f, applied after widening to the accumulator type (the `f` of
+ * mapreduce(f, op, A); PR #139, opening section).  Integer maps wrap in the
+ * accumulator type. */
+typedef enum { RK_MAP_IDENTITY = 0, RK_MAP_SQUARE = 1, RK_MAP_ABS = 2 } rk_map;
+
+typedef enum {
+    RK_F32 = 0, RK_BF16 = 1, RK_F16 = 2, RK_F64 = 3, RK_I32 = 4, RK_I64 = 5
+} rk_dtype;
+
+typedef enum { RK_MODE_OVERWRITE = 0, RK_MODE_FOLD = 1, RK_MODE_HOST = 2 } rk_mode;
+
+/*
+ * Bytes of device workspace that rk_reduce_all (ndim = 1, reduce_mask = 1,
+ * strides[0] = 1, shape[0] = n) or rk_reduce_dims needs for this layout on the
+ * current device.  For a whole array this is one accumulator per first-pass
+ * block plus one for the bare final partial (PR #139, "What changes": the
+ * workspace holds target_blocks + 1 partial results), rounded up to 256
+ * bytes; for a dims reduction split across blocks it is split * n_out
+ * accumulators; otherwise 0.  The contents need not be initialised and the
+ * same workspace may be reused by later calls of any shape and type.
+ * Returns 0 for invalid arguments as well.
+ */
+size_t rk_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64_t *shape,
+                         const int64_t *strides, uint32_t reduce_mask);
+
+/*
+ * Whole-array mapped reduction of n contiguous elements at `ptr` (device
+ * pointer, aligned to its element size; it need not be 16-byte aligned, so
+ * offset views work).  PR #139, "What changes": at most two launches, one
+ * launch when the input fits one block.
+ *   init      host pointer to one accumulator-typed value, or NULL.
+ *   mode      RK_MODE_OVERWRITE / RK_MODE_FOLD: `out` is a device pointer to
+ *             one out-typed element; RK_MODE_HOST: `out` is a host pointer to
+ *             one out-typed element, written before the call returns.
+ *   workspace device pointer to >= rk_workspace_size bytes, aligned to 8
+ *             bytes (may be NULL only if that size is 0).
+ *   stream    hipStream_t or NULL.
+ * n = 0 gives the starting value s.  Returns an rk_status.
+ */
+int rk_reduce_all(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
+                  const void *ptr, int64_t n, const void *init, int mode, void *out,
+                  void *workspace, void *stream);
+
+/*
+ * Mapped reduction along the dims in `reduce_mask` of a strided column-major
+ * view with 1 <= ndim <= 4 dims (PR #176, section "This PR"; a single output
+ * with a contiguous source takes the whole-array path, PR #139 "What
+ * changes").  `ptr` is the device address of element (0,...,0), aligned to
+ * its element size; `out` holds prod(kept extents) out-typed elements,
+ * contiguous, column-major over the kept dims (device pointer; a host pointer
+ * to one element in RK_MODE_HOST, which requires a single output).  `out`
+ * must not alias the input.  Other arguments as for rk_reduce_all.
+ */
+int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
+                   const void *ptr, int ndim, const int64_t *shape, const int64_t *strides,
+                   uint32_t reduce_mask, const void *init, int mode, void *out,
+                   void *workspace, void *stream);
+
+/* Static, human-readable name of an rk_status value. */
+const char *rk_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.  They launch nothing; tests and benchmarks use them to see
+ * which kernel a call takes and to time its first pass.
+ * ---------------------------------------------------------------------- */
+
+/* Kernels a call can take.  The dims selector (PR #176, "This PR" item 1)
+ * chooses among THREAD, TILED and COLUMNS for a strided reduced dim with
+ * contiguous runs of outputs; ROW serves a contiguous reduced dim, GENERIC
+ * any other layout, and a single output takes the whole-array path. */
+typedef enum {
+    RK_KERNEL_NONE = 0,         /* nothing to compute (no outputs) */
+    RK_KERNEL_ALL = 1,          /* whole-array first pass (+ one-block second pass) */
+    RK_KERNEL_ALL_STRIDED = 2,  /* whole-array passes over a non-contiguous single-output view */
+    RK_KERNEL_THREAD = 3,       /* one thread per output (or per 16-byte group of outputs) */
+    RK_KERNEL_TILED = 4,        /* 2-d block over a narrow tile of outputs, one pass */
+    RK_KERNEL_COLUMNS = 5,      /* 2-d block over a wide tile of outputs, split along the reduced dim */
+    RK_KERNEL_ROW = 6,          /* one wave per output over a contiguous reduced dim */
+    RK_KERNEL_GENERIC = 7       /* one block per output, any layout */
+} rk_kernel;
+
+typedef struct {
+    int kernel;               /* rk_kernel */
+    int launches;             /* kernel launches the call makes: 0, 1 or 2 */
+    int64_t grid;             /* blocks of the first launch */
+    int block;                /* threads per block of the first launch */
+    int split;                /* blocks sharing one output's reduction (1 = no second pass) */
+    int vec;                  /* elements per load in the first launch */
+    int tile_outputs;         /* outputs per block tile (tile kernels) */
+    int64_t n_out;            /* number of outputs */
+    int64_t reduce_len;       /* elements folded into each output */
+    size_t workspace_bytes;   /* what rk_workspace_size returns for this layout */
+} rk_plan_info;
+
+/* Plan of rk_reduce_all / rk_reduce_dims for `num_cus` compute units (0 =
+ * the current device), without launching.  `ptr` only matters through its
+ * alignment.  Returns an rk_status. */
+int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num_cus,
+                rk_plan_info *info);
+int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const int64_t *shape,
+                 const int64_t *strides, uint32_t reduce_mask, int num_cus,
+                 rk_plan_info *info);
+
+/* Benchmark hook: while both are non-NULL, every later rk_reduce_* call made
+ * by this host thread records hipEvent_t `begin` immediately before its first
+ * kernel launch and `end` immediately after it, on the call's stream.  Pass
+ * NULLs to stop.  Returns an rk_status. */
+int rk_debug_set_launch_events(void *begin, void *end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RK_H */

@@ -1,0 +1,186 @@
+"""Device-wide mapreduce for AMD Instinct MI355X (gfx950).
+
+Python face of librk.so.  ``rk_reduce_all``, ``rk_reduce_dims``,
+``rk_workspace_size`` and the plan/diagnostic calls keep the C ABI's names
+(see include/rk.h); ``reduce_all`` and ``reduce_dims`` below only marshal torch
+tensors into those calls -- pick dtype codes, allocate the output and the
+workspace with torch, pass the current HIP stream.  All arithmetic happens
+in the library's kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._native import (  # noqa: F401
+    EXPORTS, KERNEL_NAMES, LIB_PATH, RK_BF16, RK_ERR_HIP, RK_ERR_INVALID_ARGUMENT,
+    RK_ERR_UNSUPPORTED, RK_F16, RK_F32, RK_F64, RK_I32, RK_I64, RK_KERNEL_ALL,
+    RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE, RK_KERNEL_ROW,
+    RK_KERNEL_THREAD, RK_KERNEL_TILED, RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
+    RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,
+    RkError, load, rk_debug_set_launch_events, rk_plan_all, rk_plan_dims, rk_plan_info,
+    rk_reduce_all, rk_reduce_dims, rk_workspace_size, status_string)
+
+OPS = {"sum": RK_OP_SUM, "max": RK_OP_MAX, "min": RK_OP_MIN}
+MAPS = {"identity": RK_MAP_IDENTITY, "square": RK_MAP_SQUARE, "abs": RK_MAP_ABS}
+MODES = {"overwrite": RK_MODE_OVERWRITE, "fold": RK_MODE_FOLD, "host": RK_MODE_HOST}
+DTYPE_SIZE = {RK_F32: 4, RK_BF16: 2, RK_F16: 2, RK_F64: 8, RK_I32: 4, RK_I64: 8}
+_CTYPE = {RK_F32: ctypes.c_float, RK_F64: ctypes.c_double, RK_I32: ctypes.c_int32,
+          RK_I64: ctypes.c_int64, RK_BF16: ctypes.c_uint16, RK_F16: ctypes.c_uint16}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    """rk dtype code of a torch dtype (or pass an int code through)."""
+    if isinstance(dt, int):
+        return dt
+    torch = _torch()
+    table = {torch.float32: RK_F32, torch.bfloat16: RK_BF16, torch.float16: RK_F16,
+             torch.float64: RK_F64, torch.int32: RK_I32, torch.int64: RK_I64}
+    return table[dt]
+
+
+def torch_dtype(code: int):
+    torch = _torch()
+    return {RK_F32: torch.float32, RK_BF16: torch.bfloat16, RK_F16: torch.float16,
+            RK_F64: torch.float64, RK_I32: torch.int32, RK_I64: torch.int64}[code]
+
+
+def default_acc(in_code: int) -> int:
+    """f32 for floating inputs up to 4 bytes, f64 for f64, i64 for integers."""
+    if in_code in (RK_F32, RK_BF16, RK_F16):
+        return RK_F32
+    if in_code == RK_F64:
+        return RK_F64
+    return RK_I64
+
+
+def _code(table, v):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def init_arg(acc_code: int, init):
+    """Host buffer holding `init` in the accumulator type (None -> NULL)."""
+    if init is None:
+        return None
+    ct = _CTYPE[acc_code]
+    return ctypes.byref(ct(init if acc_code in (RK_F32, RK_F64) else int(init)))
+
+
+def decode_host_out(buf, out_code: int):
+    """Python value of a host-mode output buffer."""
+    v = buf.value
+    if out_code == RK_BF16:
+        return ctypes.c_float.from_buffer_copy(ctypes.c_uint32(v << 16)).value
+    if out_code == RK_F16:
+        import numpy as np
+        return float(np.array([v], np.uint16).view(np.float16)[0])
+    return v
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_for(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _check(rc, what):
+    if rc != RK_OK:
+        raise RkError(rc, what)
+
+
+def reduce_all(x, op="sum", map="identity", acc=None, out_dtype=None, init=None,
+               mode="overwrite", out=None, workspace=None, stream=None):
+    """Whole-array reduction of a contiguous device tensor (views with a
+    storage offset are fine).  Returns `out` (device modes) or a Python value
+    (host mode)."""
+    torch = _torch()
+    if not x.is_contiguous():
+        raise ValueError("reduce_all takes a contiguous tensor; use reduce_dims for views")
+    in_code = dtype_code(x.dtype)
+    acc_code = default_acc(in_code) if acc is None else dtype_code(acc)
+    out_code = in_code if out_dtype is None else dtype_code(out_dtype)
+    if out_code in (RK_I32, RK_I64) and in_code in (RK_I32, RK_I64) and out_dtype is None:
+        out_code = acc_code
+    op_c, map_c, mode_c = _code(OPS, op), _code(MAPS, map), _code(MODES, mode)
+    n = x.numel()
+    if workspace is None:
+        workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), x.device)
+    st = _stream_handle(stream)
+    if mode_c == RK_MODE_HOST:
+        buf = _CTYPE[out_code]()
+        rc = rk_reduce_all(op_c, map_c, in_code, acc_code, out_code, x.data_ptr(), n,
+                           init_arg(acc_code, init), mode_c, ctypes.addressof(buf),
+                           workspace.data_ptr(), st)
+        _check(rc, "rk_reduce_all")
+        return decode_host_out(buf, out_code)
+    if out is None:
+        out = torch.empty(1, dtype=torch_dtype(out_code), device=x.device)
+    rc = rk_reduce_all(op_c, map_c, in_code, acc_code, out_code, x.data_ptr(), n,
+                       init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
+    _check(rc, "rk_reduce_all")
+    return out
+
+
+def reduce_dims(x, shape, strides, dims, op="sum", map="identity", acc=None, out_dtype=None,
+                init=None, mode="overwrite", out=None, workspace=None, stream=None, offset=0):
+    """Reduction along `dims` (1-based, Julia style) of the column-major view
+    (shape, strides in elements) of device tensor x's storage, starting
+    `offset` elements into x.  Returns `out` (flat, column-major over the
+    kept dims) or, in host mode, a Python value."""
+    torch = _torch()
+    in_code = dtype_code(x.dtype)
+    acc_code = default_acc(in_code) if acc is None else dtype_code(acc)
+    out_code = in_code if out_dtype is None else dtype_code(out_dtype)
+    if out_code in (RK_I32, RK_I64) and in_code in (RK_I32, RK_I64) and out_dtype is None:
+        out_code = acc_code
+    if isinstance(dims, int):
+        dims = (dims,)
+    mask = 0
+    for d in dims:
+        mask |= 1 << (int(d) - 1)
+    op_c, map_c, mode_c = _code(OPS, op), _code(MAPS, map), _code(MODES, mode)
+    ndim = len(shape)
+    n_out = math.prod(int(s) for i, s in enumerate(shape) if not (mask >> i) & 1)
+    ptr = x.data_ptr() + int(offset) * x.element_size()
+    if workspace is None:
+        workspace = workspace_for(rk_workspace_size(in_code, acc_code, ndim, shape, strides, mask),
+                                  x.device)
+    st = _stream_handle(stream)
+    if mode_c == RK_MODE_HOST:
+        buf = _CTYPE[out_code]()
+        rc = rk_reduce_dims(op_c, map_c, in_code, acc_code, out_code, ptr, ndim, shape, strides,
+                            mask, init_arg(acc_code, init), mode_c, ctypes.addressof(buf),
+                            workspace.data_ptr(), st)
+        _check(rc, "rk_reduce_dims")
+        return decode_host_out(buf, out_code)
+    if out is None:
+        out = torch.empty(max(n_out, 1), dtype=torch_dtype(out_code), device=x.device)
+    rc = rk_reduce_dims(op_c, map_c, in_code, acc_code, out_code, ptr, ndim, shape, strides, mask,
+                        init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
+    _check(rc, "rk_reduce_dims")
+    return out
+
+
+def plan_dims(dtype, shape, strides, dims, acc=None, ptr=0, num_cus=0) -> dict:
+    """The plan rk_reduce_dims would use, as a dict (no launch)."""
+    in_code = dtype_code(dtype)
+    acc_code = default_acc(in_code) if acc is None else dtype_code(acc)
+    if isinstance(dims, int):
+        dims = (dims,)
+    mask = 0
+    for d in dims:
+        mask |= 1 << (int(d) - 1)
+    info = rk_plan_dims(in_code, acc_code, ptr, len(shape), shape, strides, mask, num_cus)
+    d = {f: getattr(info, f) for f, _ in rk_plan_info._fields_}
+    d["kernel_name"] = KERNEL_NAMES[info.kernel]
+    return d

@@ -1,0 +1,492 @@
+// rk_api.cpp -- the C ABI declared in include/rk.h.
+//
+// Validates every argument before launching anything, plans the call
+// (rk_plan.cpp), hands the plan to the kernel translation unit of the input
+// dtype, and, in host mode, finishes the bare partial on the host
+// (AcceleratedKernels.jl PR #139, "What changes": when a host value is wanted
+// the last pass stores the bare partial, which is copied back and finished
+// with init on the host).
+#include "rk.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+
+#include "rk_launch.hpp"
+#include "rk_plan.hpp"
+
+namespace {
+
+using namespace rk;
+
+thread_local void *t_ev_begin = nullptr;
+thread_local void *t_ev_end = nullptr;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+// Compute units of the current device (0 when there is no usable device).
+int device_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < kMaxDevices)
+        g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+bool debug_enabled()
+{
+    static const bool on = std::getenv("RK_DEBUG") != nullptr;
+    return on;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool op_ok(int op) { return op >= 0 && op <= 2; }
+bool map_ok(int map) { return map >= 0 && map <= 2; }
+bool mode_ok(int mode) { return mode >= RK_MODE_OVERWRITE && mode <= RK_MODE_HOST; }
+
+int check_types(int op, int map, int in, int acc, int out, int mode)
+{
+    if (!op_ok(op) || !map_ok(map) || !mode_ok(mode))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (!dtype_known(in) || !dtype_known(acc) || !dtype_known(out))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (!dtype_combo_ok(in, acc, out))
+        return RK_ERR_UNSUPPORTED;
+    return RK_OK;
+}
+
+// ------------------------------------------------------ host-side values
+
+template <class T> uint64_t to_bits(T v)
+{
+    uint64_t b = 0;
+    std::memcpy(&b, &v, sizeof v);
+    return b;
+}
+
+uint64_t identity_bits(int op, int acc)
+{
+    switch (acc) {
+    case F32:
+        return to_bits(op == RK_OP_SUM ? 0.0f : op == RK_OP_MAX ? -INFINITY : INFINITY);
+    case F64:
+        return to_bits(op == RK_OP_SUM ? 0.0 : op == RK_OP_MAX ? -(double)INFINITY : (double)INFINITY);
+    case I32:
+        return to_bits(op == RK_OP_SUM ? int32_t(0)
+                                       : op == RK_OP_MAX ? std::numeric_limits<int32_t>::min()
+                                                         : std::numeric_limits<int32_t>::max());
+    case I64:
+        return to_bits(op == RK_OP_SUM ? int64_t(0)
+                                       : op == RK_OP_MAX ? std::numeric_limits<int64_t>::min()
+                                                         : std::numeric_limits<int64_t>::max());
+    }
+    return 0;
+}
+
+uint64_t start_bits(int op, int acc, const void *init)
+{
+    if (!init)
+        return identity_bits(op, acc);
+    uint64_t b = 0;
+    std::memcpy(&b, init, dtype_size(acc));
+    return b;
+}
+
+template <class T> T host_apply(int op, T a, T b)
+{
+    if constexpr (std::is_integral_v<T>) {
+        using U = std::make_unsigned_t<T>;
+        if (op == RK_OP_SUM) return (T)((U)a + (U)b);
+        if (op == RK_OP_MAX) return a > b ? a : b;
+        return a < b ? a : b;
+    } else {
+        if (op == RK_OP_SUM) return a + b;
+        if (a != a || b != b) return a + b;
+        if (op == RK_OP_MAX) return a > b ? a : b;
+        return a < b ? a : b;
+    }
+}
+
+uint16_t host_f32_to_bf16(float f)
+{
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// double -> float rounded to odd (see the device version in rk_device.hpp)
+float host_f64_to_f32_odd(double d)
+{
+    float f = (float)d;
+    if (d != d)
+        return f;
+    if (std::isinf(f) && !std::isinf(d))
+        return d > 0 ? std::numeric_limits<float>::max() : -std::numeric_limits<float>::max();
+    const double back = (double)f;
+    if (back != d) {
+        uint32_t b;
+        std::memcpy(&b, &f, 4);
+        if (std::fabs(back) > std::fabs(d))
+            b -= 1;
+        b |= 1u;
+        std::memcpy(&f, &b, 4);
+    }
+    return f;
+}
+
+template <class Acc> void host_store(void *out, int out_dtype, Acc v)
+{
+    if constexpr (std::is_floating_point_v<Acc>) {
+        float f32v = std::is_same_v<Acc, double> ? host_f64_to_f32_odd((double)v) : (float)v;
+        switch (out_dtype) {
+        case F32: { float r = (float)v; std::memcpy(out, &r, 4); break; }
+        case F64: { double r = (double)v; std::memcpy(out, &r, 8); break; }
+        case BF16: { uint16_t r = host_f32_to_bf16(f32v); std::memcpy(out, &r, 2); break; }
+        case F16: { _Float16 h = (_Float16)f32v; std::memcpy(out, &h, 2); break; }
+        }
+    } else {
+        if (out_dtype == I32) {
+            int32_t r = (int32_t)(uint32_t)(uint64_t)v;
+            std::memcpy(out, &r, 4);
+        } else {
+            int64_t r = (int64_t)v;
+            std::memcpy(out, &r, 8);
+        }
+    }
+}
+
+template <class Acc> void host_finish_typed(int op, uint64_t init_bits, const void *partial, int have_partial,
+                                            void *out, int out_dtype)
+{
+    Acc s, v;
+    std::memcpy(&s, &init_bits, sizeof(Acc));
+    Acc r = s;
+    if (have_partial) {
+        std::memcpy(&v, partial, sizeof(Acc));
+        r = host_apply<Acc>(op, s, v);
+    }
+    host_store<Acc>(out, out_dtype, r);
+}
+
+void host_finish(int op, int acc, uint64_t init_bits, const void *partial, int have_partial, void *out,
+                 int out_dtype)
+{
+    switch (acc) {
+    case F32: host_finish_typed<float>(op, init_bits, partial, have_partial, out, out_dtype); break;
+    case F64: host_finish_typed<double>(op, init_bits, partial, have_partial, out, out_dtype); break;
+    case I32: host_finish_typed<int32_t>(op, init_bits, partial, have_partial, out, out_dtype); break;
+    case I64: host_finish_typed<int64_t>(op, init_bits, partial, have_partial, out, out_dtype); break;
+    }
+}
+
+int dispatch(int in_dtype, const Launch &L)
+{
+    switch (in_dtype) {
+    case F32: return launch_in_f32(L);
+    case BF16: return launch_in_bf16(L);
+    case F16: return launch_in_f16(L);
+    case F64: return launch_in_f64(L);
+    case I32: return launch_in_i32(L);
+    case I64: return launch_in_i64(L);
+    }
+    return RK_ERR_INVALID_ARGUMENT;
+}
+
+const char *kernel_name(int k)
+{
+    static const char *names[] = {"none", "all", "all_strided", "thread", "tiled", "columns", "row", "generic"};
+    return (k >= 0 && k <= 7) ? names[k] : "?";
+}
+
+// Copy the bare partial back and finish it on the host.
+int finish_on_host(int op, int acc, uint64_t init_bits, const void *ws, int grid, void *out, int out_dtype,
+                   hipStream_t st)
+{
+    const int asz = dtype_size(acc);
+    unsigned char partial[8];
+    const unsigned char *src = static_cast<const unsigned char *>(ws) + size_t(grid) * asz;
+    if (hipMemcpyAsync(partial, src, asz, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return RK_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess)
+        return RK_ERR_HIP;
+    host_finish(op, acc, init_bits, partial, 1, out, out_dtype);
+    return RK_OK;
+}
+
+Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, void *out)
+{
+    Finish f;
+    f.out = mode == RK_MODE_HOST ? nullptr : out;
+    f.out_dtype = out_dtype;
+    f.mode = mode;
+    f.init_bits = start_bits(op, acc, init);
+    return f;
+}
+
+int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, const AllPlan &a,
+              int kernel, const Layout *red, const void *init, int mode, void *out, void *ws,
+              hipStream_t st)
+{
+    Launch L;
+    std::memset(&L, 0, sizeof L);
+    L.kernel = kernel;
+    L.acc = acc;
+    L.op = op;
+    L.map = map;
+    L.vec = a.vec;
+    L.lanes = 1;
+    L.grid = a.grid;
+    L.block = a.block;
+    L.all.x = ptr;
+    L.all.n = a.n;
+    L.all.head = a.head;
+    L.all.nvec = a.nvec;
+    L.all.tail = a.tail;
+    if (red) {
+        L.all.nd = red->nd;
+        for (int i = 0; i < red->nd; ++i) {
+            L.all.ext[i] = red->ext[i];
+            L.all.str[i] = red->str[i];
+        }
+    }
+    L.all.ws = ws;
+    L.all.grid = a.grid;
+    L.all.fin = make_finish(op, acc, out_dtype, mode, init, out);
+    L.stream = st;
+    L.ev_begin = t_ev_begin;
+    L.ev_end = t_ev_end;
+    int rc = dispatch(in, L);
+    if (rc != RK_OK)
+        return rc;
+    if (mode == RK_MODE_HOST)
+        return finish_on_host(op, acc, L.all.fin.init_bits, ws, a.grid, out, out_dtype, st);
+    return RK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rk_status_string(int status)
+{
+    switch (status) {
+    case RK_OK: return "ok";
+    case RK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RK_ERR_UNSUPPORTED: return "unsupported dtype combination";
+    case RK_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int rk_debug_set_launch_events(void *begin, void *end)
+{
+    if ((begin == nullptr) != (end == nullptr))
+        return RK_ERR_INVALID_ARGUMENT;
+    t_ev_begin = begin;
+    t_ev_end = end;
+    return RK_OK;
+}
+
+int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num_cus, rk_plan_info *info)
+{
+    if (!info || !dtype_known(in_dtype) || !dtype_known(acc_dtype) || n < 0)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (num_cus <= 0)
+        num_cus = device_cus();
+    AllPlan a;
+    int rc = plan_all(in_dtype, acc_dtype, reinterpret_cast<uintptr_t>(ptr), n, num_cus, &a);
+    if (rc)
+        return rc;
+    std::memset(info, 0, sizeof *info);
+    info->kernel = RK_KERNEL_ALL;
+    info->launches = a.launches;
+    info->grid = a.grid;
+    info->block = a.block;
+    info->split = 1;
+    info->vec = a.vec;
+    info->tile_outputs = 1;
+    info->n_out = 1;
+    info->reduce_len = n;
+    info->workspace_bytes = a.ws_bytes;
+    return RK_OK;
+}
+
+int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const int64_t *shape,
+                 const int64_t *strides, uint32_t reduce_mask, int num_cus, rk_plan_info *info)
+{
+    if (!info)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (num_cus <= 0)
+        num_cus = device_cus();
+    DimsPlan d;
+    int rc = plan_dims(in_dtype, acc_dtype, reinterpret_cast<uintptr_t>(ptr), ndim, shape, strides,
+                       reduce_mask, num_cus, &d);
+    if (rc)
+        return rc;
+    std::memset(info, 0, sizeof *info);
+    info->kernel = d.kernel;
+    info->launches = d.launches;
+    info->grid = d.grid;
+    info->block = d.block;
+    info->split = d.split;
+    info->vec = d.vec;
+    info->tile_outputs = d.tile_outputs;
+    info->n_out = d.n_out;
+    info->reduce_len = d.m;
+    info->workspace_bytes = d.ws_bytes;
+    return RK_OK;
+}
+
+size_t rk_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64_t *shape, const int64_t *strides,
+                         uint32_t reduce_mask)
+{
+    const int cus = device_cus();
+    DimsPlan d;
+    if (plan_dims(in_dtype, acc_dtype, 0, ndim, shape, strides, reduce_mask, cus, &d) != ST_OK)
+        return 0;
+    return d.ws_bytes;
+}
+
+int rk_reduce_all(int op, int map, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int64_t n,
+                  const void *init, int mode, void *out, void *workspace, void *stream)
+{
+    int rc = check_types(op, map, in_dtype, acc_dtype, out_dtype, mode);
+    if (rc)
+        return rc;
+    if (n < 0 || (n > 0 && !ptr) || !out || !workspace)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (!aligned(ptr, dtype_size(in_dtype)) || !aligned(out, dtype_size(out_dtype)) ||
+        !aligned(workspace, 8))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (mode != RK_MODE_HOST && out == ptr)
+        return RK_ERR_INVALID_ARGUMENT;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mode == RK_MODE_HOST && n == 0) {          // nothing to reduce: s itself
+        host_finish(op, acc_dtype, start_bits(op, acc_dtype, init), nullptr, 0, out, out_dtype);
+        return RK_OK;
+    }
+    AllPlan a;
+    rc = plan_all(in_dtype, acc_dtype, reinterpret_cast<uintptr_t>(ptr), n, device_cus(), &a);
+    if (rc)
+        return rc;
+    if (debug_enabled())
+        std::fprintf(stderr, "rk_reduce_all: n=%lld grid=%d block=%d head=%lld nvec=%lld tail=%lld launches=%d\n",
+                     (long long)n, a.grid, a.block, (long long)a.head, (long long)a.nvec, (long long)a.tail,
+                     a.launches);
+    return run_whole(op, map, in_dtype, acc_dtype, out_dtype, ptr, a, K_ALL, nullptr, init, mode, out, workspace,
+                     st);
+}
+
+int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,
+                   const int64_t *shape, const int64_t *strides, uint32_t reduce_mask, const void *init, int mode,
+                   void *out, void *workspace, void *stream)
+{
+    int rc = check_types(op, map, in_dtype, acc_dtype, out_dtype, mode);
+    if (rc)
+        return rc;
+    if (!shape || !strides || ndim < 1 || ndim > kMaxDims || !out)
+        return RK_ERR_INVALID_ARGUMENT;
+    DimsPlan d;
+    rc = plan_dims(in_dtype, acc_dtype, reinterpret_cast<uintptr_t>(ptr), ndim, shape, strides, reduce_mask,
+                   device_cus(), &d);
+    if (rc)
+        return rc;
+    const int64_t total = d.n_out * d.m;
+    if ((total > 0 && !ptr) || (ptr && !aligned(ptr, dtype_size(in_dtype))))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (!aligned(out, dtype_size(out_dtype)))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (mode == RK_MODE_HOST && d.n_out != 1)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (mode != RK_MODE_HOST && out == ptr)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (d.ws_bytes > 0 && (!workspace || !aligned(workspace, 8)))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (d.grid > std::numeric_limits<int32_t>::max())
+        return RK_ERR_UNSUPPORTED;
+    if (debug_enabled())
+        std::fprintf(stderr,
+                     "rk_reduce_dims: kernel=%s n_out=%lld m=%lld grid=%lld block=%d split=%d vec=%d tile=%d "
+                     "ws=%zu\n",
+                     kernel_name(d.kernel), (long long)d.n_out, (long long)d.m, (long long)d.grid, d.block,
+                     d.split, d.vec, d.tile_outputs, d.ws_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (d.kernel == K_NONE)
+        return RK_OK;
+    if (mode == RK_MODE_HOST && d.m == 0) {
+        host_finish(op, acc_dtype, start_bits(op, acc_dtype, init), nullptr, 0, out, out_dtype);
+        return RK_OK;
+    }
+    if (d.kernel == K_ALL)
+        return run_whole(op, map, in_dtype, acc_dtype, out_dtype, ptr, d.all, K_ALL, nullptr, init, mode, out,
+                         workspace, st);
+    if (d.kernel == K_ALL_STRIDED)
+        return run_whole(op, map, in_dtype, acc_dtype, out_dtype, ptr, d.all, K_ALL_STRIDED, &d.red, init, mode,
+                         out, workspace, st);
+    if (mode == RK_MODE_HOST)
+        return RK_ERR_INVALID_ARGUMENT;   // single outputs always take a whole-array path above
+
+    Launch L;
+    std::memset(&L, 0, sizeof L);
+    L.kernel = d.kernel;
+    L.acc = acc_dtype;
+    L.op = op;
+    L.map = map;
+    L.vec = d.vec;
+    L.lanes = d.lanes;
+    L.grid = d.grid;
+    L.block = d.block;
+    DimsArgs &a = L.dims;
+    a.x = ptr;
+    a.ws = workspace;
+    a.n_out = d.n_out;
+    a.m = d.m;
+    a.s_red = d.s_red;
+    a.run_len = d.run_len;
+    a.tiles_per_run = d.tiles_per_run;
+    a.tiles = d.tiles;
+    a.rows_per_split = d.rows_per_split;
+    a.split = d.split;
+    a.outer_nd = d.outer.nd;
+    for (int i = 0; i < d.outer.nd && i < 3; ++i) {
+        a.outer_ext[i] = d.outer.ext[i];
+        a.outer_str[i] = d.outer.str[i];
+    }
+    a.kept_nd = d.kept.nd;
+    for (int i = 0; i < d.kept.nd; ++i) {
+        a.kept_ext[i] = d.kept.ext[i];
+        a.kept_str[i] = d.kept.str[i];
+    }
+    a.red_nd = d.red.nd;
+    for (int i = 0; i < d.red.nd; ++i) {
+        a.red_ext[i] = d.red.ext[i];
+        a.red_str[i] = d.red.str[i];
+    }
+    a.fin = make_finish(op, acc_dtype, out_dtype, mode, init, out);
+    L.stream = st;
+    L.ev_begin = t_ev_begin;
+    L.ev_end = t_ev_end;
+    return dispatch(in_dtype, L);
+}
+
+}  // extern "C"

@@ -1,0 +1,470 @@
+// rk_device.hpp -- gfx950 (CDNA4) device primitives for the reductions.
+//
+// Element decoding from 16-byte loads, the ops and maps, wave64 reductions
+// built from DPP and ds_swizzle lane moves, block reductions through LDS, the
+// XCD-aware block order, and the finishing store that every last pass uses
+// (AcceleratedKernels.jl PR #139, "What changes": each pass stores through
+// one finishing step that applies init, or folds into the output's previous
+// value, or leaves a bare partial; "Compatibility": partials keep the
+// accumulator type until that single final conversion).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <limits>
+#include <type_traits>
+
+#include "rk_launch.hpp"
+#include "rk_plan.hpp"
+
+namespace rk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class To, class From>
+__device__ __forceinline__ To bitcast(From v)
+{
+    static_assert(sizeof(To) == sizeof(From), "size mismatch");
+    return __builtin_bit_cast(To, v);
+}
+
+// ------------------------------------------------------------ input types
+
+struct bf16_in {};   // tag: bfloat16 input, stored as uint16_t
+struct f16_in {};    // tag: IEEE half input, stored as uint16_t
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return bitcast<float>(h16 << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h16)
+{
+    return (float)bitcast<_Float16>((uint16_t)h16);
+}
+
+// InTraits<In>: storage type, elements per 16-byte vector, and widening of
+// one element / one vector to the accumulator type.
+template <class In> struct InTraits;
+
+template <> struct InTraits<float> {
+    using S = float;
+    static constexpr int vec = 4;
+    template <class Acc> __device__ static Acc one(S v) { return (Acc)v; }
+    template <class Acc> __device__ static void decode(u32x4 w, Acc *e)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            e[i] = (Acc)bitcast<float>(w[i]);
+    }
+};
+
+template <> struct InTraits<bf16_in> {
+    using S = uint16_t;
+    static constexpr int vec = 8;
+    template <class Acc> __device__ static Acc one(S v) { return (Acc)bf16_bits_to_f32(v); }
+    template <class Acc> __device__ static void decode(u32x4 w, Acc *e)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e[2 * i] = (Acc)bitcast<float>(w[i] << 16);
+            e[2 * i + 1] = (Acc)bitcast<float>(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+template <> struct InTraits<f16_in> {
+    using S = uint16_t;
+    static constexpr int vec = 8;
+    template <class Acc> __device__ static Acc one(S v) { return (Acc)f16_bits_to_f32(v); }
+    template <class Acc> __device__ static void decode(u32x4 w, Acc *e)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e[2 * i] = (Acc)f16_bits_to_f32(w[i] & 0xffffu);
+            e[2 * i + 1] = (Acc)f16_bits_to_f32(w[i] >> 16);
+        }
+    }
+};
+
+template <> struct InTraits<double> {
+    using S = double;
+    static constexpr int vec = 2;
+    template <class Acc> __device__ static Acc one(S v) { return (Acc)v; }
+    template <class Acc> __device__ static void decode(u32x4 w, Acc *e)
+    {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            e[i] = (Acc)bitcast<double>(((uint64_t)w[2 * i + 1] << 32) | w[2 * i]);
+    }
+};
+
+template <> struct InTraits<int32_t> {
+    using S = int32_t;
+    static constexpr int vec = 4;
+    template <class Acc> __device__ static Acc one(S v) { return (Acc)v; }
+    template <class Acc> __device__ static void decode(u32x4 w, Acc *e)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            e[i] = (Acc)(int32_t)w[i];
+    }
+};
+
+template <> struct InTraits<int64_t> {
+    using S = int64_t;
+    static constexpr int vec = 2;
+    template <class Acc> __device__ static Acc one(S v) { return (Acc)v; }
+    template <class Acc> __device__ static void decode(u32x4 w, Acc *e)
+    {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            e[i] = (Acc)(int64_t)(((uint64_t)w[2 * i + 1] << 32) | w[2 * i]);
+    }
+};
+
+// -------------------------------------------------------------- maps, ops
+// Integer maps and sums wrap (two's complement) in the accumulator type.
+
+struct MapIdentity {
+    template <class T> __device__ __forceinline__ static T apply(T v) { return v; }
+};
+
+struct MapSquare {
+    template <class T> __device__ __forceinline__ static T apply(T v)
+    {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            return (T)((U)v * (U)v);
+        } else {
+            return v * v;     // built with -ffp-contract=off: never fused into the fold
+        }
+    }
+};
+
+struct MapAbs {
+    template <class T> __device__ __forceinline__ static T apply(T v)
+    {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            return v < 0 ? (T)((U)0 - (U)v) : v;
+        } else {
+            return __builtin_fabs(v);
+        }
+    }
+};
+
+struct OpSum {
+    template <class T> __device__ __forceinline__ static T identity() { return T(0); }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b)
+    {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            return (T)((U)a + (U)b);
+        } else {
+            return a + b;
+        }
+    }
+};
+
+// max/min propagate NaN: the result is NaN when either operand is.
+struct OpMax {
+    template <class T> __device__ __forceinline__ static T identity()
+    {
+        if constexpr (std::is_integral_v<T>)
+            return std::numeric_limits<T>::min();
+        else
+            return -std::numeric_limits<T>::infinity();
+    }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b)
+    {
+        if constexpr (std::is_integral_v<T>)
+            return a > b ? a : b;
+        else
+            return (a != a || b != b) ? a + b : (a > b ? a : b);
+    }
+};
+
+struct OpMin {
+    template <class T> __device__ __forceinline__ static T identity()
+    {
+        if constexpr (std::is_integral_v<T>)
+            return std::numeric_limits<T>::max();
+        else
+            return std::numeric_limits<T>::infinity();
+    }
+    template <class T> __device__ __forceinline__ static T apply(T a, T b)
+    {
+        if constexpr (std::is_integral_v<T>)
+            return a < b ? a : b;
+        else
+            return (a != a || b != b) ? a + b : (a < b ? a : b);
+    }
+};
+
+// ------------------------------------------------------------ lane moves
+// wave64 cross-lane moves: DPP within a 16-lane row (quad permutes and
+// mirrors), ds_swizzle (bit-mask mode) within 32 lanes, ds_bpermute across
+// the halves.  64-bit values move as two 32-bit halves.
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+template <int PATTERN>
+__device__ __forceinline__ uint32_t swizzle32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, PATTERN);
+}
+
+__device__ __forceinline__ uint32_t bpermute32(uint32_t v, int src_lane)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
+}
+
+template <class T, class F>
+__device__ __forceinline__ T move_words(T v, F &&f)
+{
+    if constexpr (sizeof(T) == 4) {
+        return bitcast<T>(f(bitcast<uint32_t>(v)));
+    } else {
+        static_assert(sizeof(T) == 8, "4- or 8-byte values");
+        const uint64_t u = bitcast<uint64_t>(v);
+        const uint32_t lo = f((uint32_t)u), hi = f((uint32_t)(u >> 32));
+        return bitcast<T>(((uint64_t)hi << 32) | lo);
+    }
+}
+
+// DPP controls (GFX9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_move(T v)
+{
+    return move_words(v, [](uint32_t w) { return dpp32<CTRL>(w); });
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// value of lane (this lane ^ X)
+template <int X, class T>
+__device__ __forceinline__ T lane_xor(T v)
+{
+    if constexpr (X == 1) {
+        return dpp_move<kDppQuadXor1>(v);
+    } else if constexpr (X == 2) {
+        return dpp_move<kDppQuadXor2>(v);
+    } else if constexpr (X < 32) {
+        // ds_swizzle bit-mask mode: lane' = ((lane & 0x1f) | 0) ^ X within 32 lanes
+        return move_words(v, [](uint32_t w) { return swizzle32<(X << 10) | 0x1f>(w); });
+    } else {
+        const int src = lane_id() ^ X;
+        return move_words(v, [src](uint32_t w) { return bpermute32(w, src); });
+    }
+}
+
+template <class T>
+__device__ __forceinline__ T read_lane(T v, int lane)
+{
+    return move_words(v, [lane](uint32_t w) {
+        return (uint32_t)__builtin_amdgcn_readlane((int)w, lane);
+    });
+}
+
+// Reduce over all 64 lanes; every lane gets the (wave-uniform) result.
+// All 64 lanes must be active.
+template <class Op, class T>
+__device__ __forceinline__ T wave_reduce(T v)
+{
+    v = Op::apply(v, dpp_move<kDppQuadXor1>(v));
+    v = Op::apply(v, dpp_move<kDppQuadXor2>(v));
+    v = Op::apply(v, dpp_move<kDppRowHalfMirror>(v));   // the two quads of a half-row
+    v = Op::apply(v, dpp_move<kDppRowMirror>(v));       // the two halves of a row
+    // every lane of a 16-lane row now holds that row's result
+    return Op::apply(Op::apply(read_lane(v, 0), read_lane(v, 16)),
+                     Op::apply(read_lane(v, 32), read_lane(v, 48)));
+}
+
+// Reduce over the lanes that share (lane % CL), i.e. the 64/CL rows of a
+// wave that hold the same tile column; every lane gets its column's result.
+template <int CL, class Op, class T>
+__device__ __forceinline__ T wave_reduce_columns(T v)
+{
+    if constexpr (CL <= 1) v = Op::apply(v, lane_xor<1>(v));
+    if constexpr (CL <= 2) v = Op::apply(v, lane_xor<2>(v));
+    if constexpr (CL <= 4) v = Op::apply(v, lane_xor<4>(v));
+    if constexpr (CL <= 8) v = Op::apply(v, lane_xor<8>(v));
+    if constexpr (CL <= 16) v = Op::apply(v, lane_xor<16>(v));
+    if constexpr (CL <= 32) v = Op::apply(v, lane_xor<32>(v));
+    return v;
+}
+
+// Whole-block reduction; the result is valid in wave 0 (thread 0 stores it).
+// Uses LDS: a caller that reduces again must __syncthreads() first.
+template <class Op, int BLOCK, class T>
+__device__ __forceinline__ T block_reduce(T v)
+{
+    constexpr int NW = BLOCK / 64;
+    static_assert(BLOCK % 64 == 0, "blocks are whole waves");
+    v = wave_reduce<Op>(v);
+    if constexpr (NW == 1) {
+        return v;
+    } else {
+        __shared__ T part[NW];
+        const int w = (int)(threadIdx.x >> 6);
+        if (lane_id() == 0)
+            part[w] = v;
+        __syncthreads();
+        T r = Op::template identity<T>();
+        if (w == 0) {
+            r = lane_id() < NW ? part[lane_id()] : r;
+            r = wave_reduce<Op>(r);
+        }
+        return r;
+    }
+}
+
+// ------------------------------------------------------- XCD block order
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
+// with a private L2.  This permutation gives every XCD one contiguous range
+// of logical block ids, so neighbouring tiles that share cache lines are
+// served by the same L2.  It is a bijection for any grid size.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_block(uint32_t bid, uint32_t nblocks)
+{
+    const uint32_t q = nblocks / kXcds, r = nblocks % kXcds;
+    const uint32_t xcd = bid % kXcds, local = bid / kXcds;
+    return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+// ----------------------------------------------------------- conversions
+
+// float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = bitcast<uint32_t>(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// double -> float rounded to odd: truncate, then set the last bit when the
+// conversion was inexact.  Rounding that float once more to a format of at
+// most 22 significant bits gives the correctly rounded double result
+// (rounding to odd as an intermediate step, Boldo and Melquiond 2008).
+__device__ __forceinline__ float f64_to_f32_odd(double d)
+{
+    float f = (float)d;
+    if (d != d)
+        return f;
+    if (__builtin_isinf(f) && !__builtin_isinf(d))
+        return d > 0 ? 3.40282347e38f : -3.40282347e38f;
+    const double back = (double)f;
+    if (back != d) {
+        uint32_t b = bitcast<uint32_t>(f);
+        if (__builtin_fabs(back) > __builtin_fabs(d))
+            b -= 1;                    // one step toward zero
+        f = bitcast<float>(b | 1u);
+    }
+    return f;
+}
+
+template <class Acc>
+__device__ __forceinline__ void store_out(void *out, int64_t o, int out_dtype, Acc v)
+{
+    if constexpr (std::is_floating_point_v<Acc>) {
+        switch (out_dtype) {
+        case F32: static_cast<float *>(out)[o] = (float)v; break;
+        case F64: static_cast<double *>(out)[o] = (double)v; break;
+        case BF16:
+            if constexpr (std::is_same_v<Acc, double>)
+                static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(f64_to_f32_odd(v));
+            else
+                static_cast<uint16_t *>(out)[o] = f32_to_bf16_rne(v);
+            break;
+        case F16: {
+            float f;
+            if constexpr (std::is_same_v<Acc, double>)
+                f = f64_to_f32_odd(v);
+            else
+                f = v;
+            static_cast<uint16_t *>(out)[o] = bitcast<uint16_t>((_Float16)f);
+            break;
+        }
+        default: break;
+        }
+    } else {
+        switch (out_dtype) {
+        case I32: static_cast<int32_t *>(out)[o] = (int32_t)(uint32_t)(uint64_t)v; break;
+        case I64: static_cast<int64_t *>(out)[o] = (int64_t)v; break;
+        default: break;
+        }
+    }
+}
+
+// Previous output value, read back into the accumulator type (fold mode).
+template <class Acc>
+__device__ __forceinline__ Acc load_out(const void *out, int64_t o, int out_dtype)
+{
+    if constexpr (std::is_floating_point_v<Acc>) {
+        switch (out_dtype) {
+        case F32: return (Acc) static_cast<const float *>(out)[o];
+        case F64: return (Acc) static_cast<const double *>(out)[o];
+        case BF16: return (Acc)bf16_bits_to_f32(static_cast<const uint16_t *>(out)[o]);
+        case F16: return (Acc)f16_bits_to_f32(static_cast<const uint16_t *>(out)[o]);
+        default: return Acc(0);
+        }
+    } else {
+        switch (out_dtype) {
+        case I32: return (Acc) static_cast<const int32_t *>(out)[o];
+        case I64: return (Acc) static_cast<const int64_t *>(out)[o];
+        default: return Acc(0);
+        }
+    }
+}
+
+template <class Acc>
+__device__ __forceinline__ Acc from_bits(uint64_t b)
+{
+    if constexpr (sizeof(Acc) == 4)
+        return bitcast<Acc>((uint32_t)b);
+    else
+        return bitcast<Acc>(b);
+}
+
+// The one finishing step of every last pass, for output o.
+//   OVERWRITE: out[o] = convert(op(init, v))
+//   FOLD:      out[o] = convert(op(widen(out[o]), v))
+// (HOST and PARTIAL store bare accumulators; the callers do that.)
+template <class Op, class Acc>
+__device__ __forceinline__ void finish_store(const Finish &f, int64_t o, Acc v)
+{
+    Acc s = f.mode == FIN_FOLD ? load_out<Acc>(f.out, o, f.out_dtype) : from_bits<Acc>(f.init_bits);
+    store_out<Acc>(f.out, o, f.out_dtype, Op::apply(s, v));
+}
+
+// ------------------------------------------------------------------ misc
+
+// Offset of linear index idx in a column-major layout of nd <= 4 dims.
+__device__ __forceinline__ int64_t layout_offset(int nd, const int64_t *ext, const int64_t *str,
+                                                 int64_t idx)
+{
+    int64_t off = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        if (d < nd) {
+            const int64_t q = idx / ext[d];
+            off += (idx - q * ext[d]) * str[d];
+            idx = q;
+        }
+    }
+    return off;
+}
+
+__device__ __forceinline__ u32x4 load16(const u32x4 *p) { return *p; }
+
+}  // namespace rk

@@ -1,0 +1,523 @@
+// rk_kernels.hpp -- the HIP kernels and their typed launchers (gfx950).
+//
+// Whole array (AcceleratedKernels.jl PR #139, "What changes"): a first pass
+// of at most a grid cap of blocks, each striding over tiles of the input with
+// several 16-byte loads in flight per thread, then a one-block second pass;
+// an input that fits one block finishes in the first pass.
+//
+// Strided dims (PR #176, "This PR"): one tile kernel serves the selector's
+// three shapes -- one thread per output (a tile one row tall), the narrow
+// tiled block (8 outputs, one pass) and the wide columns block (32 outputs,
+// split along the reduced dim, then a second pass) -- over runs of contiguous
+// outputs placed by the other kept dims (the middle dim of 3-d arrays).  A
+// contiguous reduced dim takes the row kernel (one wave per output); any
+// other layout the generic kernel (one block per output).
+//
+// Every last pass stores through finish_store().  No kernel reads workspace
+// it did not write in the same call, so a workspace is reusable as is.
+#pragma once
+
+#include "rk_device.hpp"
+
+namespace rk {
+
+template <class Acc, class Op, int V>
+__device__ __forceinline__ void set_identity(Acc (&a)[V])
+{
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        a[i] = Op::template identity<Acc>();
+}
+
+template <class In, class Acc, class Op, class Map, int V>
+__device__ __forceinline__ void fold_vec(Acc (&a)[V], u32x4 w)
+{
+    Acc e[V];
+    InTraits<In>::template decode<Acc>(w, e);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        a[i] = Op::apply(a[i], Map::apply(e[i]));
+}
+
+template <class Acc, class Op, int V>
+__device__ __forceinline__ Acc fold_all(const Acc (&a)[V])
+{
+    // pairwise, so the per-thread tree stays shallow
+    Acc t[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        t[i] = a[i];
+#pragma unroll
+    for (int w = V / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i)
+            t[i] = Op::apply(t[i], t[i + w]);
+    return t[0];
+}
+
+// ================================================================ whole array
+
+template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
+{
+    using S = typename InTraits<In>::S;
+    constexpr int V = InTraits<In>::vec;
+    const S *x = static_cast<const S *>(a.x);
+    const u32x4 *body = reinterpret_cast<const u32x4 *>(x + a.head);
+
+    Acc acc0[V], acc1[V];
+    set_identity<Acc, Op>(acc0);
+    set_identity<Acc, Op>(acc1);
+
+    // Full tiles of BLOCK * UNROLL vectors; block b takes tiles b, b + G, ...
+    // One wave instruction reads 64 * 16 = 1 KiB of consecutive bytes.
+    constexpr int64_t kTile = int64_t(BLOCK) * UNROLL;
+    const int64_t full = a.nvec / kTile;
+    for (int64_t t = blockIdx.x; t < full; t += gridDim.x) {
+        const u32x4 *p = body + t * kTile + threadIdx.x;
+        u32x4 w[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            w[u] = load16(p + u * BLOCK);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (u & 1)
+                fold_vec<In, Acc, Op, Map, V>(acc1, w[u]);
+            else
+                fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+        }
+    }
+    // the last, partial tile is spread over the whole grid
+    const int64_t gtid = int64_t(blockIdx.x) * BLOCK + threadIdx.x;
+    const int64_t gthreads = int64_t(gridDim.x) * BLOCK;
+    for (int64_t i = full * kTile + gtid; i < a.nvec; i += gthreads)
+        fold_vec<In, Acc, Op, Map, V>(acc0, load16(body + i));
+    // scalars before the first 16-byte boundary and after the last vector
+    Acc s = Op::template identity<Acc>();
+    if (gtid < a.head)
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(x[gtid])));
+    if (gtid < a.tail)
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(x[a.head + a.nvec * V + gtid])));
+
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        acc0[i] = Op::apply(acc0[i], acc1[i]);
+    Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
+    v = block_reduce<Op, BLOCK>(v);
+    if (threadIdx.x == 0) {
+        Acc *ws = static_cast<Acc *>(a.ws);
+        if (a.grid > 1)
+            ws[blockIdx.x] = v;                 // bare partial for the second pass
+        else if (a.fin.mode == FIN_HOST)
+            ws[a.grid] = v;                     // bare result for the host to finish
+        else
+            finish_store<Op>(a.fin, 0, v);
+    }
+}
+
+// Single output over a non-contiguous view: element i lives at
+// layout_offset(i); scalar loads, several in flight per thread.
+template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
+{
+    using S = typename InTraits<In>::S;
+    const S *x = static_cast<const S *>(a.x);
+    Acc acc[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+        acc[u] = Op::template identity<Acc>();
+    const int64_t step = int64_t(gridDim.x) * BLOCK * UNROLL;
+    for (int64_t base = int64_t(blockIdx.x) * BLOCK * UNROLL + threadIdx.x; base < a.n; base += step) {
+        S w[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t i = base + int64_t(u) * BLOCK;
+            if (i < a.n)
+                w[u] = x[layout_offset(a.nd, a.ext, a.str, i)];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t i = base + int64_t(u) * BLOCK;
+            if (i < a.n)
+                acc[u] = Op::apply(acc[u], Map::apply(InTraits<In>::template one<Acc>(w[u])));
+        }
+    }
+    Acc v = fold_all<Acc, Op, UNROLL>(acc);
+    v = block_reduce<Op, BLOCK>(v);
+    if (threadIdx.x == 0) {
+        Acc *ws = static_cast<Acc *>(a.ws);
+        if (a.grid > 1)
+            ws[blockIdx.x] = v;
+        else if (a.fin.mode == FIN_HOST)
+            ws[a.grid] = v;
+        else
+            finish_store<Op>(a.fin, 0, v);
+    }
+}
+
+template <class Acc, class Op, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_all_pass2(Acc *ws, int grid, Finish fin)
+{
+    Acc v = Op::template identity<Acc>();
+    for (int i = threadIdx.x; i < grid; i += BLOCK)
+        v = Op::apply(v, ws[i]);
+    v = block_reduce<Op, BLOCK>(v);
+    if (threadIdx.x == 0) {
+        if (fin.mode == FIN_HOST)
+            ws[grid] = v;
+        else
+            finish_store<Op>(fin, 0, v);
+    }
+}
+
+// ======================================================================= dims
+
+// Tile kernel.  A block covers W = CL * V contiguous outputs of one run and
+// RG = BLOCK / CL row groups; lane c of a row group loads V outputs' worth of
+// one row (one 16-byte load when V > 1), so a wave reads 64 / CL rows of
+// W * sizeof(In) bytes per instruction.  Row groups stride over the reduced
+// dim with UNROLL loads in flight, then fold together (in-wave lane moves,
+// then LDS across waves).  CL == BLOCK is the thread-per-output shape.
+template <class In, class Acc, class Op, class Map, bool VECTOR, int CL, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
+{
+    using S = typename InTraits<In>::S;
+    constexpr int V = VECTOR ? InTraits<In>::vec : 1;
+    constexpr int W = CL * V;
+    constexpr int RG = BLOCK / CL;
+    constexpr int NW = BLOCK / 64;
+    static_assert(CL == BLOCK || CL <= 64, "a row group is within one wave, or the whole block");
+
+    const int c = (int)(threadIdx.x % CL);
+    const int rg = (int)(threadIdx.x / CL);
+    const uint32_t b = xcd_block(blockIdx.x, gridDim.x);
+    const int64_t tile = int64_t(b % (uint64_t)a.tiles);
+    const int sp = (int)(b / (uint64_t)a.tiles);
+    const int64_t run = tile / a.tiles_per_run;
+    const int64_t col0 = (tile - run * a.tiles_per_run) * W;
+    const int64_t col = col0 + int64_t(c) * V;
+    const bool active = col < a.run_len;       // vector loads: run_len % V == 0
+    const int64_t in_base = layout_offset(a.outer_nd, a.outer_ext, a.outer_str, run) + col;
+    const int64_t j0 = int64_t(sp) * a.rows_per_split;
+    const int64_t j1 = j0 + a.rows_per_split < a.m ? j0 + a.rows_per_split : a.m;
+    const S *x = static_cast<const S *>(a.x) + in_base;
+    const int64_t s = a.s_red;
+
+    Acc acc0[V], acc1[V];
+    set_identity<Acc, Op>(acc0);
+    set_identity<Acc, Op>(acc1);
+    if (active) {
+        int64_t j = j0 + rg;
+        for (; j + int64_t(UNROLL - 1) * RG < j1; j += int64_t(UNROLL) * RG) {
+            if constexpr (VECTOR) {
+                u32x4 w[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    w[u] = load16(reinterpret_cast<const u32x4 *>(x + (j + int64_t(u) * RG) * s));
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    if (u & 1)
+                        fold_vec<In, Acc, Op, Map, V>(acc1, w[u]);
+                    else
+                        fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+                }
+            } else {
+                S w[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    w[u] = x[(j + int64_t(u) * RG) * s];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    Acc e = Map::apply(InTraits<In>::template one<Acc>(w[u]));
+                    if (u & 1)
+                        acc1[0] = Op::apply(acc1[0], e);
+                    else
+                        acc0[0] = Op::apply(acc0[0], e);
+                }
+            }
+        }
+        for (; j < j1; j += RG) {
+            if constexpr (VECTOR)
+                fold_vec<In, Acc, Op, Map, V>(acc0, load16(reinterpret_cast<const u32x4 *>(x + j * s)));
+            else
+                acc0[0] = Op::apply(acc0[0], Map::apply(InTraits<In>::template one<Acc>(x[j * s])));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        acc0[i] = Op::apply(acc0[i], acc1[i]);
+
+    const int64_t o_tile = run * a.run_len + col0;     // output index of the tile's first column
+    const int64_t outs_left = a.run_len - col0;        // outputs of this tile inside the run
+    Acc *ws = static_cast<Acc *>(a.ws);
+
+    if constexpr (CL == BLOCK) {
+        // one row group: this thread owns its V outputs
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int64_t o = o_tile + int64_t(c) * V + i;
+                if (a.split > 1)
+                    ws[int64_t(sp) * a.n_out + o] = acc0[i];
+                else
+                    finish_store<Op>(a.fin, o, acc0[i]);
+            }
+        }
+    } else {
+        // fold the 64 / CL row groups of each wave, then the NW waves
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            acc0[i] = wave_reduce_columns<CL, Op>(acc0[i]);
+        __shared__ Acc part[NW][W];
+        const int w = (int)(threadIdx.x >> 6);
+        if (lane_id() < CL) {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                part[w][lane_id() * V + i] = acc0[i];
+        }
+        __syncthreads();
+        if (threadIdx.x < W && int64_t(threadIdx.x) < outs_left) {
+            Acc v = part[0][threadIdx.x];
+#pragma unroll
+            for (int k = 1; k < NW; ++k)
+                v = Op::apply(v, part[k][threadIdx.x]);
+            const int64_t o = o_tile + threadIdx.x;
+            if (a.split > 1)
+                ws[int64_t(sp) * a.n_out + o] = v;
+            else
+                finish_store<Op>(a.fin, o, v);
+        }
+    }
+}
+
+// Row kernel: one wave per (output, chunk) over a contiguous reduced dim.
+template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
+{
+    using S = typename InTraits<In>::S;
+    constexpr int V = InTraits<In>::vec;
+    const int lane = lane_id();
+    const int64_t unit = int64_t(blockIdx.x) * (BLOCK / 64) + (threadIdx.x >> 6);
+    if (unit >= a.n_out * a.split)
+        return;                                 // whole wave; no block barrier below
+    const int64_t o = unit / a.split;
+    const int sp = (int)(unit - o * a.split);
+    const int64_t j0 = int64_t(sp) * a.rows_per_split;
+    const int64_t len = a.m - j0 < a.rows_per_split ? a.m - j0 : a.rows_per_split;
+    const S *row = static_cast<const S *>(a.x) +
+                   layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o) + j0;
+
+    // scalar head up to the first 16-byte boundary, vector body, scalar tail
+    int64_t head = (int64_t)(((16u - ((uintptr_t)row & 15u)) & 15u) / sizeof(S));
+    head = head < len ? head : len;
+    const int64_t nv = (len - head) / V;
+    const int64_t tail = len - head - nv * V;
+    const u32x4 *body = reinterpret_cast<const u32x4 *>(row + head);
+
+    Acc acc0[V], acc1[V];
+    set_identity<Acc, Op>(acc0);
+    set_identity<Acc, Op>(acc1);
+    int64_t i = lane;
+    for (; i + int64_t(UNROLL - 1) * 64 < nv; i += int64_t(UNROLL) * 64) {
+        u32x4 w[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            w[u] = load16(body + i + u * 64);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (u & 1)
+                fold_vec<In, Acc, Op, Map, V>(acc1, w[u]);
+            else
+                fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+        }
+    }
+    for (; i < nv; i += 64)
+        fold_vec<In, Acc, Op, Map, V>(acc0, load16(body + i));
+    Acc s = Op::template identity<Acc>();
+    if (lane < head)
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(row[lane])));
+    if (lane < tail)
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(row[head + nv * V + lane])));
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        acc0[k] = Op::apply(acc0[k], acc1[k]);
+    Acc v = wave_reduce<Op>(Op::apply(fold_all<Acc, Op, V>(acc0), s));
+    if (lane == 0) {
+        if (a.split > 1)
+            static_cast<Acc *>(a.ws)[int64_t(sp) * a.n_out + o] = v;
+        else
+            finish_store<Op>(a.fin, o, v);
+    }
+}
+
+// Generic kernel: one block per output (grid-stride over outputs); the
+// block's threads share the output's elements, addressed through the
+// reduced layout.  Serves any layout the fast kernels do not take.
+template <class In, class Acc, class Op, class Map, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
+{
+    using S = typename InTraits<In>::S;
+    const S *x = static_cast<const S *>(a.x);
+    for (int64_t o = blockIdx.x; o < a.n_out; o += gridDim.x) {
+        const int64_t base = layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o);
+        Acc v = Op::template identity<Acc>();
+        for (int64_t j = threadIdx.x; j < a.m; j += BLOCK)
+            v = Op::apply(v, Map::apply(InTraits<In>::template one<Acc>(
+                                 x[base + layout_offset(a.red_nd, a.red_ext, a.red_str, j)])));
+        v = block_reduce<Op, BLOCK>(v);
+        if (threadIdx.x == 0)
+            finish_store<Op>(a.fin, o, v);
+        __syncthreads();                        // LDS of block_reduce is reused next output
+    }
+}
+
+// Second pass of a split dims reduction: fold split partials per output.
+template <class Acc, class Op, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_split_finish(const Acc *ws, int64_t n_out, int split, Finish fin)
+{
+    const int64_t o = int64_t(blockIdx.x) * BLOCK + threadIdx.x;
+    if (o >= n_out)
+        return;
+    Acc v = ws[o];
+    for (int k = 1; k < split; ++k)
+        v = Op::apply(v, ws[int64_t(k) * n_out + o]);
+    finish_store<Op>(fin, o, v);
+}
+
+// ================================================================== launchers
+
+// Run the call's kernels for one (In, Acc, Op, Map).
+template <class In, class Acc, class Op, class Map>
+int run_typed(const Launch &L)
+{
+    constexpr int V = InTraits<In>::vec;
+    hipStream_t st = static_cast<hipStream_t>(L.stream);
+    hipEvent_t evb = static_cast<hipEvent_t>(L.ev_begin), eve = static_cast<hipEvent_t>(L.ev_end);
+    const dim3 grid((unsigned)L.grid), block((unsigned)L.block);
+    if (evb && eve && hipEventRecord(evb, st) != hipSuccess)
+        return ST_HIP;
+
+    int split = 1;
+    switch (L.kernel) {
+    case K_ALL:
+        hipLaunchKernelGGL((k_all_pass1<In, Acc, Op, Map, tune::kAllBlock, tune::kAllUnroll>), grid,
+                           dim3(tune::kAllBlock), 0, st, L.all);
+        break;
+    case K_ALL_STRIDED:
+        hipLaunchKernelGGL((k_all_pass1_strided<In, Acc, Op, Map, tune::kAllBlock, tune::kAllUnroll>),
+                           grid, dim3(tune::kAllBlock), 0, st, L.all);
+        break;
+    case K_THREAD: case K_TILED: case K_COLUMNS: {
+        constexpr int B = tune::kDimsBlock, U = tune::kDimsUnroll;
+        const bool vec = L.vec > 1;
+        int want;
+        if (L.kernel == K_THREAD)
+            want = B;
+        else if (L.kernel == K_TILED)
+            want = vec ? tune::kTiledOutputs / V : tune::kTiledOutputs;
+        else
+            want = vec ? tune::kColumnsOutputs / V : tune::kColumnsOutputs;
+        if (L.lanes != want || (vec && L.vec != V))
+            return ST_INVALID;
+        if (L.kernel == K_THREAD) {
+            if (vec)
+                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, true, B, B, U>), grid, block, 0, st, L.dims);
+            else
+                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, false, B, B, U>), grid, block, 0, st, L.dims);
+        } else if (L.kernel == K_TILED) {
+            if (vec)
+                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, true, tune::kTiledOutputs / V, B, U>),
+                                   grid, block, 0, st, L.dims);
+            else
+                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, false, tune::kTiledOutputs, B, U>),
+                                   grid, block, 0, st, L.dims);
+        } else {
+            if (vec)
+                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, true, tune::kColumnsOutputs / V, B, U>),
+                                   grid, block, 0, st, L.dims);
+            else
+                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, false, tune::kColumnsOutputs, B, U>),
+                                   grid, block, 0, st, L.dims);
+        }
+        split = L.dims.split;
+        break;
+    }
+    case K_ROW:
+        hipLaunchKernelGGL((k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, tune::kDimsUnroll>), grid,
+                           block, 0, st, L.dims);
+        split = L.dims.split;
+        break;
+    case K_GENERIC:
+        hipLaunchKernelGGL((k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock>), grid, block, 0, st, L.dims);
+        break;
+    default:
+        return ST_INVALID;
+    }
+    if (hipGetLastError() != hipSuccess)
+        return ST_HIP;
+    if (evb && eve && hipEventRecord(eve, st) != hipSuccess)
+        return ST_HIP;
+
+    // second launches
+    if ((L.kernel == K_ALL || L.kernel == K_ALL_STRIDED) && L.all.grid > 1) {
+        hipLaunchKernelGGL((k_all_pass2<Acc, Op, tune::kPass2Block>), dim3(1), dim3(tune::kPass2Block), 0,
+                           st, static_cast<Acc *>(L.all.ws), L.all.grid, L.all.fin);
+    } else if (split > 1) {
+        constexpr int B = 256;
+        const unsigned g = (unsigned)((L.dims.n_out + B - 1) / B);
+        hipLaunchKernelGGL((k_split_finish<Acc, Op, B>), dim3(g), dim3(B), 0, st,
+                           static_cast<const Acc *>(L.dims.ws), L.dims.n_out, split, L.dims.fin);
+    } else {
+        return ST_OK;
+    }
+    return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
+}
+
+template <class In, class Acc>
+int run_acc(const Launch &L)
+{
+    switch (L.op) {
+    case 0:
+        switch (L.map) {
+        case 0: return run_typed<In, Acc, OpSum, MapIdentity>(L);
+        case 1: return run_typed<In, Acc, OpSum, MapSquare>(L);
+        case 2: return run_typed<In, Acc, OpSum, MapAbs>(L);
+        }
+        break;
+    case 1:
+        switch (L.map) {
+        case 0: return run_typed<In, Acc, OpMax, MapIdentity>(L);
+        case 1: return run_typed<In, Acc, OpMax, MapSquare>(L);
+        case 2: return run_typed<In, Acc, OpMax, MapAbs>(L);
+        }
+        break;
+    case 2:
+        switch (L.map) {
+        case 0: return run_typed<In, Acc, OpMin, MapIdentity>(L);
+        case 1: return run_typed<In, Acc, OpMin, MapSquare>(L);
+        case 2: return run_typed<In, Acc, OpMin, MapAbs>(L);
+        }
+        break;
+    }
+    return ST_INVALID;
+}
+
+// Accumulators a given input type may use (the public dtype table).
+template <class In>
+int run_in(const Launch &L)
+{
+    if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
+        if (L.acc == F32) return run_acc<In, float>(L);
+        if (L.acc == F64) return run_acc<In, double>(L);
+    } else if constexpr (std::is_same_v<In, double>) {
+        if (L.acc == F64) return run_acc<In, double>(L);
+    } else if constexpr (std::is_same_v<In, int32_t>) {
+        if (L.acc == I32) return run_acc<In, int32_t>(L);
+        if (L.acc == I64) return run_acc<In, int64_t>(L);
+    } else if constexpr (std::is_same_v<In, int64_t>) {
+        if (L.acc == I64) return run_acc<In, int64_t>(L);
+    }
+    return ST_UNSUPPORTED;
+}
+
+}  // namespace rk

@@ -1,0 +1,81 @@
+// rk_launch.hpp -- what the C ABI hands to the kernel translation units.
+//
+// Plain structs passed by value as kernel arguments, plus one launcher entry
+// per input dtype (each lives in its own .hip file so they compile in
+// parallel).  No HIP types appear here.
+#pragma once
+
+#include <cstdint>
+
+namespace rk {
+
+// Finishing modes of the last pass: the three public modes plus PARTIAL,
+// which stores a bare accumulator per block for a following pass.
+enum FinishMode { FIN_OVERWRITE = 0, FIN_FOLD = 1, FIN_HOST = 2, FIN_PARTIAL = 3 };
+
+struct Finish {
+    void *out;            // device output (OVERWRITE / FOLD)
+    int out_dtype;
+    int mode;             // FinishMode
+    uint64_t init_bits;   // starting value, accumulator bits (identity when no init)
+};
+
+struct AllArgs {
+    const void *x;        // first element
+    int64_t n;            // elements
+    int64_t head;         // scalars before the 16-byte-aligned body
+    int64_t nvec;         // 16-byte vectors in the body (strided variant: elements)
+    int64_t tail;         // scalars after the body
+    int nd;               // strided variant: element i sits at sum_d ((i / prod ext[<d]) % ext[d]) * str[d]
+    int64_t ext[4];
+    int64_t str[4];
+    void *ws;             // grid + 1 accumulators
+    int grid;
+    Finish fin;
+};
+
+struct DimsArgs {
+    const void *x;        // element (0, ..., 0)
+    void *ws;             // split * n_out accumulators when split > 1
+    int64_t n_out;
+    int64_t m;            // elements per output
+    int64_t s_red;        // reduced stride (tile kernels)
+    int64_t run_len;      // contiguous outputs per run (tile kernels)
+    int64_t tiles_per_run;
+    int64_t tiles;
+    int64_t rows_per_split;
+    int split;
+    int outer_nd;         // kept dims after the first (tile kernels): run offsets
+    int64_t outer_ext[3];
+    int64_t outer_str[3];
+    int kept_nd;          // all kept dims (row and generic kernels)
+    int64_t kept_ext[4];
+    int64_t kept_str[4];
+    int red_nd;           // reduced dims (generic kernel)
+    int64_t red_ext[4];
+    int64_t red_str[4];
+    Finish fin;
+};
+
+struct Launch {
+    int kernel;           // rk::Kernel
+    int acc, op, map;     // accumulator dtype, op and map codes
+    int vec;              // elements per load of the first launch
+    int lanes;            // tile kernels: lanes across a tile row
+    int64_t grid;
+    int block;
+    AllArgs all;          // K_ALL, K_ALL_STRIDED
+    DimsArgs dims;        // other kernels
+    void *stream;         // hipStream_t
+    void *ev_begin;       // optional hipEvent_t pair around the first launch
+    void *ev_end;
+};
+
+int launch_in_f32(const Launch &L);
+int launch_in_bf16(const Launch &L);
+int launch_in_f16(const Launch &L);
+int launch_in_f64(const Launch &L);
+int launch_in_i32(const Launch &L);
+int launch_in_i64(const Launch &L);
+
+}  // namespace rk

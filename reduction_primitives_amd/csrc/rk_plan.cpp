@@ -1,0 +1,273 @@
+// rk_plan.cpp -- host-side planning (no HIP; unit-tested on the CPU).
+#include "rk_plan.hpp"
+
+#include <algorithm>
+
+namespace rk {
+
+int dtype_size(int d)
+{
+    switch (d) {
+    case F32: case I32: return 4;
+    case BF16: case F16: return 2;
+    case F64: case I64: return 8;
+    }
+    return 0;
+}
+
+bool dtype_known(int d) { return dtype_size(d) != 0; }
+bool dtype_is_fp(int d) { return d == F32 || d == BF16 || d == F16 || d == F64; }
+
+bool dtype_combo_ok(int in, int acc, int out)
+{
+    if (!dtype_known(in) || !dtype_known(acc) || !dtype_known(out))
+        return false;
+    if (dtype_is_fp(in) != dtype_is_fp(acc) || dtype_is_fp(acc) != dtype_is_fp(out))
+        return false;
+    if (acc == BF16 || acc == F16)          // accumulators are f32, f64, i32 or i64
+        return false;
+    return dtype_size(acc) >= dtype_size(in);
+}
+
+size_t round_up_256(size_t b) { return (b + 255) & ~size_t(255); }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus, AllPlan *p)
+{
+    if (!p || n < 0 || !dtype_known(in_dtype) || !dtype_known(acc_dtype))
+        return ST_INVALID;
+    if (num_cus <= 0)
+        num_cus = tune::kDefaultCus;
+    const int isz = dtype_size(in_dtype);
+    AllPlan a;
+    a.n = n;
+    a.vec = 16 / isz;
+    // Peel scalars up to the first 16-byte boundary so the body can use
+    // dwordx4 loads (offset views need not be aligned).
+    const uintptr_t mis = addr & 15;
+    a.head = mis ? std::min<int64_t>(n, int64_t((16 - mis) / isz)) : 0;
+    const int64_t body = n - a.head;
+    a.nvec = body / a.vec;
+    a.tail = body - a.nvec * a.vec;
+    const int64_t tile_vecs = int64_t(tune::kAllBlock) * tune::kAllUnroll;
+    a.tiles = ceil_div(a.nvec, tile_vecs);
+    a.block = tune::kAllBlock;
+    if (a.tiles <= tune::kAllSingleLaunchTiles) {
+        a.grid = 1;                         // fits one block: one launch
+    } else {
+        a.grid = int(std::min<int64_t>(a.tiles, int64_t(num_cus) * tune::kAllBlocksPerCu));
+    }
+    a.launches = a.grid == 1 ? 1 : 2;
+    // pass-1 partials plus one slot for the bare final partial
+    a.ws_bytes = round_up_256(size_t(a.grid + 1) * dtype_size(acc_dtype));
+    *p = a;
+    return ST_OK;
+}
+
+int select_strided_kernel(int64_t run_len, int64_t n_out, int64_t m, int in_size, int num_cus)
+{
+    // Rule 1: one thread per output when a row of outputs is already wide
+    // enough to keep the device busy, or when the reduction is too short to
+    // be worth sharing among threads.
+    if (run_len * in_size >= tune::kThreadRowBytes || m < tune::kMinReduceLen)
+        return K_THREAD;
+    // Rule 2: the narrow one-pass tile when there are at least as many
+    // outputs as elements per output and wide tiles would not fill the GPU.
+    const int64_t wide_tiles = ceil_div(n_out, tune::kColumnsOutputs);
+    if (n_out >= m && wide_tiles < int64_t(num_cus) * tune::kFillTilesPerCu)
+        return K_TILED;
+    // Rule 3: wide tiles, split along the reduced dim when they are too few.
+    return K_COLUMNS;
+}
+
+// Drop extent-1 dims and merge neighbouring dims of the same class (both
+// kept or both reduced) whose strides chain, keeping column-major order.
+static void push_dim(Layout &l, int64_t e, int64_t s)
+{
+    if (l.nd > 0) {
+        const int i = l.nd - 1;
+        if (s == l.str[i] * l.ext[i]) {
+            l.ext[i] *= e;
+            return;
+        }
+    }
+    l.ext[l.nd] = e;
+    l.str[l.nd] = s;
+    ++l.nd;
+}
+
+int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64_t *shape,
+              const int64_t *strides, uint32_t mask, int num_cus, DimsPlan *p)
+{
+    if (!p || !shape || !strides || ndim < 1 || ndim > kMaxDims)
+        return ST_INVALID;
+    if (!dtype_known(in_dtype) || !dtype_known(acc_dtype))
+        return ST_INVALID;
+    if (mask >> ndim)
+        return ST_INVALID;
+    if (num_cus <= 0)
+        num_cus = tune::kDefaultCus;
+    const int isz = dtype_size(in_dtype);
+    const int asz = dtype_size(acc_dtype);
+
+    DimsPlan d;
+    int64_t n_out = 1, m = 1;
+    for (int i = 0; i < ndim; ++i) {
+        if (shape[i] < 0 || strides[i] < 0)
+            return ST_INVALID;
+        if ((mask >> i) & 1)
+            m *= shape[i];
+        else
+            n_out *= shape[i];
+    }
+    d.n_out = n_out;
+    d.m = m;
+    if (n_out == 0) {                   // nothing to store
+        d.kernel = K_NONE;
+        *p = d;
+        return ST_OK;
+    }
+    if (m == 0) {
+        // Every output is its starting value: a zero-length generic fold.
+        for (int i = 0; i < ndim; ++i)
+            if (!((mask >> i) & 1) && shape[i] != 1)
+                push_dim(d.kept, shape[i], strides[i]);
+        d.red = Layout();
+        d.kernel = K_GENERIC;
+    } else {
+        for (int i = 0; i < ndim; ++i) {
+            if (shape[i] == 1)
+                continue;
+            if ((mask >> i) & 1)
+                push_dim(d.red, shape[i], strides[i]);
+            else
+                push_dim(d.kept, shape[i], strides[i]);
+        }
+        if (d.kept.nd == 0) {
+            // A single output.  A contiguous source takes the whole-array
+            // path (PR #139, "What changes", last paragraph).
+            if (d.red.nd == 0 || (d.red.nd == 1 && d.red.str[0] == 1))
+                d.kernel = K_ALL;
+            else
+                d.kernel = K_ALL_STRIDED;
+        } else if (d.red.nd == 0) {
+            d.kernel = K_GENERIC;           // nothing to reduce: f applied per element
+        } else if (d.red.nd == 1 && d.red.str[0] == 1) {
+            d.kernel = K_ROW;
+        } else if (d.red.nd == 1 && d.kept.str[0] == 1) {
+            d.kernel = select_strided_kernel(d.kept.ext[0], n_out, m, isz, num_cus);
+        } else {
+            d.kernel = K_GENERIC;
+        }
+    }
+
+    switch (d.kernel) {
+    case K_ALL: {
+        int rc = plan_all(in_dtype, acc_dtype, addr, m, num_cus, &d.all);
+        if (rc)
+            return rc;
+        d.launches = d.all.launches;
+        d.grid = d.all.grid;
+        d.block = d.all.block;
+        d.vec = d.all.vec;
+        d.ws_bytes = d.all.ws_bytes;
+        break;
+    }
+    case K_ALL_STRIDED: {
+        AllPlan a;
+        a.n = m;
+        a.vec = 1;
+        a.nvec = m;                         // scalar "vectors", addressed through `red`
+        const int64_t tile = int64_t(tune::kAllBlock) * tune::kAllUnroll;
+        a.tiles = ceil_div(m, tile);
+        a.grid = a.tiles <= tune::kAllSingleLaunchTiles
+                     ? 1
+                     : int(std::min<int64_t>(a.tiles, int64_t(num_cus) * tune::kAllBlocksPerCu));
+        a.launches = a.grid == 1 ? 1 : 2;
+        a.ws_bytes = round_up_256(size_t(a.grid + 1) * asz);
+        d.all = a;
+        d.launches = a.launches;
+        d.grid = a.grid;
+        d.block = a.block;
+        d.ws_bytes = a.ws_bytes;
+        break;
+    }
+    case K_THREAD: case K_TILED: case K_COLUMNS: {
+        d.run_len = d.kept.ext[0];
+        d.runs = n_out / d.run_len;
+        d.s_red = d.red.str[0];
+        d.outer = Layout();
+        for (int i = 1; i < d.kept.nd; ++i) {
+            d.outer.ext[d.outer.nd] = d.kept.ext[i];
+            d.outer.str[d.outer.nd] = d.kept.str[i];
+            ++d.outer.nd;
+        }
+        // 16-byte loads when every row of every run starts 16-byte aligned
+        const int v = 16 / isz;
+        bool vec_ok = (addr % 16) == 0 && d.run_len % v == 0 && (d.s_red * isz) % 16 == 0;
+        for (int i = 0; i < d.outer.nd; ++i)
+            vec_ok = vec_ok && (d.outer.str[i] * isz) % 16 == 0;
+        d.vec = vec_ok ? v : 1;
+        const int block = tune::kDimsBlock;
+        if (d.kernel == K_THREAD)
+            d.tile_outputs = block * d.vec;
+        else if (d.kernel == K_TILED)
+            d.tile_outputs = tune::kTiledOutputs;
+        else
+            d.tile_outputs = tune::kColumnsOutputs;
+        if (d.tile_outputs % d.vec)             // keep whole vectors per lane
+            d.tile_outputs = d.vec;
+        d.lanes = d.tile_outputs / d.vec;
+        d.tiles_per_run = ceil_div(d.run_len, d.tile_outputs);
+        d.tiles = d.runs * d.tiles_per_run;
+        d.split = 1;
+        if (d.kernel == K_COLUMNS) {
+            const int64_t target = int64_t(num_cus) * tune::kColumnsBlocksPerCu;
+            int64_t s = std::max<int64_t>(1, ceil_div(target, d.tiles));
+            s = std::min<int64_t>(s, std::max<int64_t>(1, m / tune::kColumnsMinRows));
+            d.rows_per_split = ceil_div(m, s);
+            d.split = int(ceil_div(m, d.rows_per_split));
+        } else {
+            d.rows_per_split = m;
+        }
+        d.grid = d.tiles * d.split;
+        d.block = block;
+        d.launches = d.split > 1 ? 2 : 1;
+        d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
+        break;
+    }
+    case K_ROW: {
+        d.vec = 16 / isz;
+        const int64_t waves_target = int64_t(num_cus) * tune::kRowWavesPerCu;
+        int64_t s = 1;
+        if (n_out < waves_target)
+            s = std::min<int64_t>(ceil_div(waves_target, n_out),
+                                  std::max<int64_t>(1, m / tune::kRowMinChunk));
+        int64_t rows = ceil_div(m, s);
+        rows = ceil_div(rows, d.vec) * d.vec;   // chunks keep the row's 16-byte phase
+        d.rows_per_split = rows;
+        d.split = int(ceil_div(m, rows));
+        const int waves_per_block = tune::kDimsBlock / 64;
+        d.block = tune::kDimsBlock;
+        d.grid = ceil_div(n_out * d.split, waves_per_block);
+        d.launches = d.split > 1 ? 2 : 1;
+        d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
+        break;
+    }
+    case K_GENERIC: {
+        d.vec = 1;
+        d.block = tune::kDimsBlock;
+        d.grid = std::min<int64_t>(n_out, int64_t(num_cus) * tune::kGenericBlocksPerCu);
+        d.launches = 1;
+        d.ws_bytes = 0;
+        break;
+    }
+    default:
+        break;
+    }
+    *p = d;
+    return ST_OK;
+}
+
+}  // namespace rk

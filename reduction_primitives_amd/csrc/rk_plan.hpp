@@ -1,0 +1,121 @@
+// rk_plan.hpp -- host-side planning of whole-array and dims reductions.
+//
+// Pure C++ (no HIP): it turns a call's dtypes, shape, strides and alignment
+// into a launch plan -- which kernel, grid, split and workspace -- so the
+// same decisions can be unit-tested on a machine without a GPU.  All tuning
+// values live in the one table below; the dims kernel choice is made in one
+// place, select_strided_kernel() (AcceleratedKernels.jl PR #176, section
+// "This PR" item 1).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace rk {
+
+enum Dtype { F32 = 0, BF16 = 1, F16 = 2, F64 = 3, I32 = 4, I64 = 5 };
+enum Mode { OVERWRITE = 0, FOLD = 1, HOST = 2 };
+enum Kernel {
+    K_NONE = 0, K_ALL = 1, K_ALL_STRIDED = 2, K_THREAD = 3, K_TILED = 4,
+    K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7
+};
+
+int dtype_size(int d);            // bytes per element, 0 for an unknown code
+bool dtype_is_fp(int d);
+bool dtype_known(int d);
+// input/accumulator/output combination of the public dtype table
+bool dtype_combo_ok(int in, int acc, int out);
+
+// ---------------------------------------------------------------- tuning
+// gfx950 values.  The pages' own numbers (256 target blocks, 64 bytes of
+// accumulator per thread, 8- and 32-output tiles, a 64 KiB row threshold, a
+// reduction-length floor of 32) were tuned for other GPUs; the defaults here
+// are set from MI355X's 256 CUs and measured on it.
+namespace tune {
+// whole-array first pass
+constexpr int kAllBlock = 256;            // threads per block
+constexpr int kAllUnroll = 8;             // 16-byte loads in flight per thread
+constexpr int kAllBlocksPerCu = 4;        // grid cap = CUs * this
+constexpr int kAllSingleLaunchTiles = 2;  // <= this many tiles: one launch
+constexpr int kPass2Block = 256;          // threads of the one-block second pass
+// dims
+constexpr int kDimsBlock = 256;
+constexpr int kDimsUnroll = 8;
+constexpr int64_t kThreadRowBytes = 64 * 1024;  // rule 1: row of outputs this wide -> thread kernel
+constexpr int64_t kMinReduceLen = 32;           // rule 1: shorter reductions -> thread kernel
+constexpr int kTiledOutputs = 8;                // tiled kernel: outputs per block
+constexpr int kColumnsOutputs = 32;             // columns kernel: outputs per block
+constexpr int kFillTilesPerCu = 1;              // rule 2: 32-output tiles that "fill" the device
+constexpr int kColumnsBlocksPerCu = 4;          // columns split target
+constexpr int64_t kColumnsMinRows = 128;        // rows per split chunk, at least
+constexpr int kRowWavesPerCu = 16;              // row kernel split target
+constexpr int64_t kRowMinChunk = 2048;          // elements per row chunk, at least
+constexpr int kGenericBlocksPerCu = 8;
+constexpr int kDefaultCus = 256;                // MI355X
+}  // namespace tune
+
+constexpr int kMaxDims = 4;
+
+struct Layout {                   // column-major dims, innermost first
+    int nd = 0;
+    int64_t ext[kMaxDims] = {0, 0, 0, 0};
+    int64_t str[kMaxDims] = {0, 0, 0, 0};
+};
+
+struct AllPlan {
+    int64_t n = 0;
+    int vec = 1;            // elements per 16-byte load
+    int64_t head = 0;       // scalar elements before the first 16-byte boundary
+    int64_t nvec = 0;       // 16-byte vectors of the aligned body
+    int64_t tail = 0;       // scalar elements after the body
+    int64_t tiles = 0;      // tiles of block * unroll vectors
+    int grid = 1;           // first-pass blocks
+    int block = tune::kAllBlock;
+    int launches = 1;
+    size_t ws_bytes = 0;
+};
+
+struct DimsPlan {
+    int kernel = K_NONE;
+    int launches = 0;
+    int64_t n_out = 0;      // outputs
+    int64_t m = 0;          // elements folded into each output
+    Layout kept;            // normalised kept dims (output order)
+    Layout red;             // normalised reduced dims
+    AllPlan all;            // K_ALL / K_ALL_STRIDED
+    // tile kernels (THREAD / TILED / COLUMNS): outputs come in runs of
+    // run_len contiguous elements (kept.ext[0], stride 1); the other kept
+    // dims (`outer`) place the runs.
+    int64_t run_len = 0;
+    int64_t runs = 0;
+    int64_t s_red = 0;      // stride of the single reduced dim
+    Layout outer;
+    int vec = 1;            // elements per load
+    int lanes = 1;          // lanes across one row of a tile
+    int tile_outputs = 1;
+    int64_t tiles_per_run = 0;
+    int64_t tiles = 0;
+    int split = 1;          // blocks (tile kernels) or waves (row) per output
+    int64_t rows_per_split = 0;
+    int64_t grid = 0;
+    int block = tune::kDimsBlock;
+    size_t ws_bytes = 0;
+};
+
+// Status codes as in the public header.
+enum { ST_OK = 0, ST_INVALID = 1, ST_UNSUPPORTED = 2, ST_HIP = 3 };
+
+// Whole-array plan: n elements at address `addr`.
+int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus, AllPlan *p);
+
+// Dims plan: validates the layout (1..4 dims, non-negative extents and
+// strides, mask within ndim) and normalises it before choosing a kernel.
+int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64_t *shape,
+              const int64_t *strides, uint32_t mask, int num_cus, DimsPlan *p);
+
+// The selector for a strided reduced dim with contiguous runs of outputs.
+int select_strided_kernel(int64_t run_len, int64_t n_out, int64_t m, int in_size, int num_cus);
+
+size_t round_up_256(size_t b);
+
+}  // namespace rk

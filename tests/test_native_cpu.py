@@ -1,0 +1,191 @@
+"""Host-side checks of librk.so that need no GPU: exports, plans, validation.
+
+Nothing here launches a kernel: plans are computed for an explicit CU count,
+and every rk_reduce_* call made here is rejected by validation before any
+launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _rk():
+    import reduction_primitives_amd as rk
+    rk.load()
+    return rk
+
+
+def test_library_exports_every_declared_function():
+    rk = _rk()
+    with open(os.path.join(ROOT, "include", "rk.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(rk_[a-z_]+)\s*\(", header))
+    assert declared == set(rk.EXPORTS)
+    lib = ctypes.CDLL(rk.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    rk = _rk()
+    assert rk.status_string(0) == "ok"
+    assert "invalid" in rk.status_string(1)
+    assert "unsupported" in rk.status_string(2)
+    assert "HIP" in rk.status_string(3)
+    assert rk.status_string(99) == "unknown status"
+
+
+# ------------------------------------------------------------------- plans
+
+def plan(dtype, shape, dims, strides=None, cus=256, ptr=0):
+    import reduction_primitives_amd as rk
+    from reduction_primitives_amd.workloads import cm_strides
+    return rk.plan_dims(dtype, shape, strides or cm_strides(shape), dims, ptr=ptr, num_cus=cus)
+
+
+def test_whole_array_plan():
+    rk = _rk()
+    info = rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**8, 256)
+    assert info.kernel == rk.RK_KERNEL_ALL and info.launches == 2
+    assert info.grid == 1024 and info.block == 256 and info.vec == 4
+    assert info.workspace_bytes == 4352          # (1024 + 1) * 4 rounded to 256
+    small = rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**4, 256)
+    assert small.grid == 1 and small.launches == 1
+    # the grid cap follows the CU count
+    assert rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**8, 80).grid == 320
+    # workspace: one accumulator per first-pass block plus the final slot
+    d = rk.rk_plan_all(rk.RK_I32, rk.RK_I64, 0, 10**8, 256)
+    assert d.workspace_bytes == ((1024 + 1) * 8 + 255) // 256 * 256
+
+
+def test_config_shapes_take_the_expected_kernels():
+    import torch
+    assert plan(torch.bfloat16, (3072, 2048), 2)["kernel_name"] == "tiled"
+    assert plan(torch.float32, (3072, 2048), 2)["kernel_name"] == "tiled"
+    assert plan(torch.float32, (3072, 2048), 1)["kernel_name"] == "row"
+    assert plan(torch.bfloat16, (768, 1024, 8), 2)["kernel_name"] == "tiled"
+    assert plan(torch.float32, (768, 1024, 8), 2)["kernel_name"] == "tiled"
+    p = plan(torch.float32, (64, 4096, 32), 2)
+    assert p["kernel_name"] == "columns" and p["split"] > 1 and p["launches"] == 2
+    p = plan(torch.float32, (8192, 8192), 2)
+    assert p["kernel_name"] == "columns"
+    assert plan(torch.float32, (8192, 8192), 1)["kernel_name"] == "row"
+    assert plan(torch.int32, (8192, 8192), 1)["kernel_name"] == "row"
+    p = plan(torch.float32, (8192, 8192), (1, 2))
+    assert p["kernel_name"] == "all" and p["n_out"] == 1 and p["reduce_len"] == 8192 * 8192
+
+
+def test_selector_rules():
+    import torch
+    # rule 1: a row of outputs of at least 64 KiB, or a reduction shorter than 32
+    assert plan(torch.float32, (16384, 100), 2)["kernel_name"] == "thread"
+    assert plan(torch.bfloat16, (32768, 100), 2)["kernel_name"] == "thread"
+    assert plan(torch.bfloat16, (32767, 100), 2)["kernel_name"] == "columns"   # 1024 wide tiles
+    assert plan(torch.bfloat16, (8000, 100), 2)["kernel_name"] == "tiled"
+    assert plan(torch.float32, (1000, 31), 2)["kernel_name"] == "thread"
+    # rule 2: outputs >= elements per output and few wide tiles -> tiled
+    assert plan(torch.float32, (1000, 1000), 2)["kernel_name"] == "tiled"
+    assert plan(torch.float32, (999, 1000), 2)["kernel_name"] == "columns"
+    # "fill the device" scales with the CU count
+    assert plan(torch.float32, (8192, 8192), 2, cus=512)["kernel_name"] == "tiled"
+    # rule 3 splits along the reduced dim only when tiles are few
+    p = plan(torch.float32, (64, 100000), 2)
+    assert p["kernel_name"] == "columns" and p["split"] > 1
+    p = plan(torch.float32, (1 << 16, 1 << 15), 2)   # 256 KiB row of outputs: rule 1
+    assert p["kernel_name"] == "thread" and p["split"] == 1
+
+
+def test_normalisation_drops_unit_dims_and_merges():
+    import torch
+    # (768, 1024, 8) reduced over dims 1 and 2 merges into one contiguous run per batch
+    p = plan(torch.float32, (768, 1024, 8), (1, 2))
+    assert p["kernel_name"] == "row" and p["n_out"] == 8 and p["reduce_len"] == 768 * 1024
+    # unit dims vanish
+    assert plan(torch.float32, (1, 3072, 1, 2048), 4, strides=(1, 1, 3072, 3072))["kernel_name"] == "tiled"
+    # every dim reduced, contiguous: the whole-array path
+    assert plan(torch.float32, (100, 7, 3), (1, 2, 3))["kernel_name"] == "all"
+    # kept dims split by a reduced dim: runs of outputs (middle dim)
+    p = plan(torch.float32, (768, 1024, 8), 2)
+    assert p["n_out"] == 768 * 8 and p["reduce_len"] == 1024
+
+
+def test_vector_loads_need_alignment():
+    import torch
+    assert plan(torch.float32, (3072, 2048), 2)["vec"] == 4
+    assert plan(torch.float32, (3072, 2048), 2, ptr=4)["vec"] == 1          # misaligned base
+    assert plan(torch.float32, (3070, 2048), 2)["vec"] == 1                 # odd run / stride
+    assert plan(torch.bfloat16, (3072, 2048), 2)["vec"] == 8
+
+
+def test_workspace_sizes():
+    rk = _rk()
+    from reduction_primitives_amd.workloads import cm_strides
+    assert rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 2, (3072, 2048), cm_strides((3072, 2048)), 2) == 0
+    ws = rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 3, (64, 4096, 32), cm_strides((64, 4096, 32)), 2)
+    p = plan(__import__("torch").float32, (64, 4096, 32), 2)
+    assert ws == (p["split"] * 2048 * 4 + 255) // 256 * 256
+    assert rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 1, (10**8,), (1,), 1) > 0
+    # invalid layouts give 0
+    assert rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 5, (1,) * 5, (1,) * 5, 1) == 0
+    assert rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, 2, (3, 4), (1, 3), 4) == 0
+
+
+def test_plan_rejects_bad_layouts():
+    rk = _rk()
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, 0, (), (), 0)
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, 2, (3, -1), (1, 3), 1)
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, 2, (3, 4), (1, -3), 1)
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, 2, (3, 4), (1, 3), 0b100)
+
+
+# -------------------------------------------------------------- validation
+
+FAKE = 0x10000          # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(op=3), 1), (dict(map_=3), 1), (dict(mode=3), 1), (dict(in_dtype=9), 1),
+    (dict(acc=1), 2),                       # bf16 accumulator
+    (dict(acc=4), 2),                       # integer accumulator for float input
+    (dict(in_dtype=3, acc=0), 2),           # accumulator narrower than the input
+    (dict(out=4), 2),                       # int output of a float reduction
+    (dict(n=-1), 1), (dict(ptr=None), 1), (dict(ptr=FAKE + 2), 1), (dict(out_ptr=None), 1),
+    (dict(ws=None), 1), (dict(ws=FAKE + 4), 1), (dict(out_ptr=FAKE), 1),
+])
+def test_reduce_all_validation(args, code):
+    rk = _rk()
+    rc = rk.rk_reduce_all(args.get("op", 0), args.get("map_", 0), args.get("in_dtype", 0),
+                          args.get("acc", 0), args.get("out", 0), args.get("ptr", FAKE),
+                          args.get("n", 100), None, args.get("mode", 0),
+                          args.get("out_ptr", FAKE + 4096), args.get("ws", FAKE + 8192), None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(ndim=0), 1), (dict(ndim=5), 1), (dict(mask=0b100), 1), (dict(shape=(3, -4)), 1),
+    (dict(strides=(1, -3)), 1), (dict(mode=2), 1),          # host mode with 4 outputs
+    (dict(ptr=FAKE + 1), 1), (dict(out_ptr=FAKE), 1), (dict(acc=5), 2),
+])
+def test_reduce_dims_validation(args, code):
+    rk = _rk()
+    ndim = args.get("ndim", 2)
+    shape = args.get("shape", (3, 4))[:max(ndim, 0)] if ndim <= 2 else (1,) * ndim
+    strides = args.get("strides", (1, 3))[:max(ndim, 0)] if ndim <= 2 else (1,) * ndim
+    rc = rk.rk_reduce_dims(0, 0, 0, args.get("acc", 0), 0, args.get("ptr", FAKE), ndim, shape,
+                           strides, args.get("mask", 0b10), None, args.get("mode", 0),
+                           args.get("out_ptr", FAKE + 4096), FAKE + 8192, None)
+    assert rc == code
+
+
+def test_launch_event_hook_pairs():
+    rk = _rk()
+    assert rk.rk_debug_set_launch_events(FAKE, None) == rk.RK_ERR_INVALID_ARGUMENT
+    assert rk.rk_debug_set_launch_events(None, None) == rk.RK_OK
