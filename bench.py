@@ -3,15 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step runs every call of the hot path once over resident synthetic input:
-  whole array, 10^8 float32 U[0,1) (AcceleratedKernels.jl PR #139, "Numbers"):
-    1. sum -> host value                  (two launches + copy + host finish)
-    2. sum -> device scalar, init = 1.5   (overwrite)
-    3. sum -> fold into that scalar
-    4. max and 5. min of a permutation of 0..10^8-1 (int32)
+  whole array, 10^8 elements (AcceleratedKernels.jl PR #139, "Numbers"):
+    max and min of a permutation of 0..10^8-1 (int32), then float32 U[0,1)
+    sums: into a device scalar with init = 1.5 (overwrite), folded into that
+    scalar, and to a host value (two launches + copy + host finish)
   8192x8192 column-major (PR #176, "Timings", last row):
-    6. float32 sum over dims=2   7. float32 sum over dims=1
-    8. float32 max over dims=2   9. float32 sum of squares of the whole array
-   10. int32 sum over dims=1 into int64
+    float32 sum over dims=2, sum over dims=1, max over dims=2, sum of
+    squares of the whole array; int32 sum over dims=1 into int64
 Each call reads its own copy of the input, so no call finds its data in the
 256 MB Infinity Cache left behind by the previous one.
 
@@ -56,6 +54,11 @@ def parse():
                     help="seconds of oracle work allowed for the CPU baseline")
     ap.add_argument("--per-call-reps", type=int, default=5,
                     help="reps of the per-call table (0 skips it)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time every configuration's calls one by one (cold and warm)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run one plain elementwise copy (torch.neg) of 10^8 float32, "
+                         "400 MB read + 400 MB written, to scale HBM byte counters against")
     return ap.parse_args()
 
 
@@ -114,16 +117,10 @@ def build_step(rk, torch, dev):
     nb = N_WHOLE * 4
     mb = SIDE * SIDE * 4
     init_p = ctypes.byref(init15)
+    # The three timed float32 sums come last, behind seven queued calls, so
+    # their launch events never wait on an idle GPU; the host call, which
+    # drains the stream, closes the step.
     calls = [
-        Call("sum_1e8_f32_host", "all", nb + 4,
-             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[0].data_ptr(), N_WHOLE, None, HO,
-                                      ctypes.addressof(host_out), ws, st), True, DOMINANT),
-        Call("sum_1e8_f32_init1.5", "all", nb + 4,
-             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[1].data_ptr(), N_WHOLE, init_p, OW,
-                                      o_scalar.data_ptr(), ws, st), True, DOMINANT),
-        Call("sum_1e8_f32_fold", "all", nb + 8,
-             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[2].data_ptr(), N_WHOLE, None, FO,
-                                      o_scalar.data_ptr(), ws, st), True, DOMINANT),
         Call("max_1e8_i32_perm", "all", nb + 4,
              lambda: rk.rk_reduce_all(MAX, ID, I32, I32, I32, p[0].data_ptr(), N_WHOLE, None, OW,
                                       o_max.data_ptr(), ws, st)),
@@ -145,6 +142,15 @@ def build_step(rk, torch, dev):
         Call("sum_8192sq_i32_dims1_i64", "dims", mb + SIDE * 8,
              lambda: rk.rk_reduce_dims(SUM, ID, I32, I64, I64, z.data_ptr(), 2, shape, strides, 1,
                                        None, OW, o_i.data_ptr(), ws, st)),
+        Call("sum_1e8_f32_init1.5", "all", nb + 4,
+             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[1].data_ptr(), N_WHOLE, init_p, OW,
+                                      o_scalar.data_ptr(), ws, st), True, DOMINANT),
+        Call("sum_1e8_f32_fold", "all", nb + 8,
+             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[2].data_ptr(), N_WHOLE, None, FO,
+                                      o_scalar.data_ptr(), ws, st), True, DOMINANT),
+        Call("sum_1e8_f32_host", "all", nb + 4,
+             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[0].data_ptr(), N_WHOLE, None, HO,
+                                      ctypes.addressof(host_out), ws, st), True, DOMINANT),
     ]
     outs = dict(host=host_out, scalar=o_scalar, max=o_max, min=o_min, d2=o_d2, d1=o_d1, mx=o_mx,
                 sq=o_sq, i64=o_i)
@@ -188,11 +194,13 @@ def cpu_leg(inputs, outs, budget_s, host_value):
         ("sum_8192sq_i32_dims1_i64", SIDE * SIDE * 4,
          lambda: O.reduce_dims(O.SUM, O.IDENTITY, O.I32, O.I64, mi, shape, strides, 0b01, 0)),
     ]
+    cores_available = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     try:
-        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+        saved_affinity = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {sorted(saved_affinity)[0]})
         pinned = True
     except (AttributeError, OSError):
-        pinned = False
+        saved_affinity, pinned = None, False
     results, t_total, b_total = {}, 0.0, 0
     for name, nbytes, fn in plan:
         if t_total > budget_s:
@@ -204,6 +212,8 @@ def cpu_leg(inputs, outs, budget_s, host_value):
         t_total += dt
         b_total += nbytes
         log(f"  oracle {name}: {dt * 1e3:.1f} ms ({nbytes / dt / 1e9:.2f} GB/s)")
+    if saved_affinity is not None:
+        os.sched_setaffinity(0, saved_affinity)
     # parity of the last GPU step against these oracle results
     ok = True
     notes = []
@@ -225,22 +235,22 @@ def cpu_leg(inputs, outs, budget_s, host_value):
     absm = None
     if "sum_8192sq_f32_dims2" in results:
         absm = O.reduce_dims(O.SUM, O.ABS, O.F32, O.F32, mf, shape, strides, 0b10, 0.0)
-        ok &= bool(np.all(np.abs(outs["d2"].cpu().numpy() - results["sum_8192sq_f32_dims2"]) <= 1e-5 * absm))
+        ok &= bool(np.all(np.abs(outs["d2"].numpy() - results["sum_8192sq_f32_dims2"]) <= 1e-5 * absm))
     if "sum_8192sq_f32_dims1" in results:
         absm1 = O.reduce_dims(O.SUM, O.ABS, O.F32, O.F32, mf, shape, strides, 0b01, 0.0)
-        ok &= bool(np.all(np.abs(outs["d1"].cpu().numpy() - results["sum_8192sq_f32_dims1"]) <= 1e-5 * absm1))
+        ok &= bool(np.all(np.abs(outs["d1"].numpy() - results["sum_8192sq_f32_dims1"]) <= 1e-5 * absm1))
     if "max_8192sq_f32_dims2" in results:
-        ok &= bool(np.array_equal(outs["mx"].cpu().numpy().astype(np.float64), results["max_8192sq_f32_dims2"]))
+        ok &= bool(np.array_equal(outs["mx"].numpy().astype(np.float64), results["max_8192sq_f32_dims2"]))
     if "sumsq_8192sq_f32_all" in results:
         r = results["sumsq_8192sq_f32_all"]
         ok &= near(float(outs["sq"].item()), r, r)
     if "sum_8192sq_i32_dims1_i64" in results:
-        ok &= bool(np.array_equal(outs["i64"].cpu().numpy(), results["sum_8192sq_i32_dims1_i64"]))
+        ok &= bool(np.array_equal(outs["i64"].numpy(), results["sum_8192sq_i32_dims1_i64"]))
     sample = (", ".join(results) if len(results) < len(plan)
               else "every call of one step except the fold, whose arithmetic is the overwrite's")
     return dict(value=round(b_total / t_total / 1e9, 3), unit="GB/s", cores=1 if pinned else None,
                 kind="oracle", sample=f"{sample} (same inputs; {b_total / 1e9:.2f} GB in {t_total:.1f} s)",
-                host_cores_available=len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None), \
+                host_cores_available=cores_available), \
         bool(ok)
 
 
@@ -262,18 +272,25 @@ def traffic_from_profile():
 
 
 def per_call_table(calls, torch, reps, dev):
-    """Per call: warm (back to back) and cold (Infinity Cache flushed by a
-    512 MiB write first) times of the whole rk call, min and median."""
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    """Per call: warm (the same input again, back to back) and cold (the
+    Infinity Cache first filled with other, clean lines by reading a 1 GiB
+    buffer) times of the whole rk call, min and median."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     table = {}
     for c in calls:
         rows = {}
         for mode in ("warm", "cold"):
             ts = []
             for _ in range(reps):
+                host = c.name.endswith("_host")
                 if mode == "cold":
-                    flush.zero_()
+                    flush.sum()
                 torch.cuda.synchronize()
+                # queue work ahead of a device-mode call, so its start event
+                # does not wait on the host's launch latency; a host-mode call
+                # drains the stream itself and is timed by the wall clock
+                if not host:
+                    torch.cuda._sleep(200_000)
                 b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 t0 = time.perf_counter()
                 b.record()
@@ -281,7 +298,7 @@ def per_call_table(calls, torch, reps, dev):
                 e.record()
                 e.synchronize()
                 wall = time.perf_counter() - t0
-                ts.append(wall * 1e6 if c.name.endswith("_host") else b.elapsed_time(e) * 1e3)
+                ts.append(wall * 1e6 if host else b.elapsed_time(e) * 1e3)
             rows[mode] = dict(us_min=round(min(ts), 2), us_median=round(statistics.median(ts), 2),
                               GBps=round(c.bytes_alg / (min(ts) * 1e-6) / 1e9, 1))
         table[c.name] = rows
@@ -289,6 +306,92 @@ def per_call_table(calls, torch, reps, dev):
             f"  cold {rows['cold']['us_min']:8.1f} us ({rows['cold']['GBps']:7.1f} GB/s)")
     del flush
     return table
+
+
+def configs_table(rk, torch, dev, reps):
+    """Every configuration's calls timed one by one: warm (input just read)
+    and cold (Infinity Cache refilled with other clean lines first), each
+    queued behind GPU work so the events measure the GPU alone."""
+    from reduction_primitives_amd import workloads as W
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    rows = []
+
+    def timed(name, fn, nbytes, kernel, is_host=False):
+        res = {}
+        for mode in ("warm", "cold"):
+            ts = []
+            for _ in range(reps):
+                if mode == "cold":
+                    flush.sum()
+                torch.cuda.synchronize()
+                if not is_host:
+                    torch.cuda._sleep(1_000_000)
+                b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0 = time.perf_counter()
+                b.record()
+                host = fn()
+                e.record()
+                e.synchronize()
+                ts.append((time.perf_counter() - t0) * 1e6 if host else b.elapsed_time(e) * 1e3)
+            res[mode] = dict(us_min=round(min(ts), 2), us_median=round(statistics.median(ts), 2),
+                             GBps=round(nbytes / (min(ts) * 1e-6) / 1e9, 1))
+        rows.append(dict(call=name, kernel=kernel, bytes=nbytes, **res))
+        log(f"  {name:40s} {kernel:8s} warm {res['warm']['us_min']:8.2f} us ({res['warm']['GBps']:7.1f} GB/s)"
+            f"  cold {res['cold']['us_min']:8.2f} us ({res['cold']['GBps']:7.1f} GB/s)")
+
+    def whole(name, x, **kw):
+        host = kw.get("mode") == "host"
+        in_c = rk.dtype_code(x.dtype)
+        acc_c = rk.dtype_code(kw["acc"]) if "acc" in kw else rk.default_acc(in_c)
+        ws = rk.workspace_for(rk.rk_workspace_size(in_c, acc_c, 1, [x.numel()], [1], 1), dev)
+        out = None if host else torch.zeros(1, dtype=kw.get("out_dtype", x.dtype), device=dev)
+
+        def fn():
+            rk.reduce_all(x, workspace=ws, out=out, **kw)
+            return host
+        timed(name, fn, x.numel() * x.element_size(), "all", is_host=host)
+
+    def dims(name, arr, xd, d, **kw):
+        plan = rk.plan_dims(xd.dtype, arr.shape, arr.strides, d)
+        ws = rk.workspace_for(plan["workspace_bytes"], dev)
+        out_dt = kw.get("out_dtype", xd.dtype)
+        out = torch.zeros(max(1, plan["n_out"]), dtype=out_dt, device=dev)
+
+        def fn():
+            rk.reduce_dims(xd, arr.shape, arr.strides, d, workspace=ws, out=out, **kw)
+            return False
+        timed(name, fn, xd.numel() * xd.element_size(), plan["kernel_name"])
+
+    xf, xi = W.whole_small()
+    whole("1e4 f32 sum -> host", xf.data.to(dev), mode="host")
+    whole("1e4 i32 sum -> int64 host", xi.data.to(dev), acc=torch.int64, out_dtype=torch.int64, mode="host")
+    for n in (10**6, 10**8):
+        xf, perm = W.whole_large(n)
+        xd, pd = xf.data.to(dev), perm.data.to(dev)
+        whole(f"{n:.0e} f32 sum -> host", xd, mode="host")
+        whole(f"{n:.0e} f32 sum init 1.5 -> device", xd, init=1.5)
+        whole(f"{n:.0e} f32 sum fold -> device", xd, mode="fold")
+        whole(f"{n:.0e} i32 perm max", pd, op="max", acc=torch.int32, out_dtype=torch.int32)
+        whole(f"{n:.0e} i32 perm min", pd, op="min", acc=torch.int32, out_dtype=torch.int32)
+        del xd, pd
+    bf, f32 = W.matrix_3072x2048()
+    bd, fd = bf.data.to(dev), f32.data.to(dev)
+    dims("3072x2048 bf16 dims=2 -> bf16", bf, bd, 2)
+    dims("3072x2048 f32 dims=2", f32, fd, 2)
+    dims("3072x2048 f32 dims=1", f32, fd, 1)
+    dims("3072x2048 bf16 dims=1 -> bf16", bf, bd, 1)
+    for arr in W.middle_dim_3d():
+        dims(f"{'x'.join(map(str, arr.shape))} {arr.name.split('_')[0]} dims=2", arr, arr.data.to(dev), 2)
+    mf, mi = W.matrix_8192()
+    md, mid = mf.data.to(dev), mi.data.to(dev)
+    dims("8192x8192 f32 sum dims=2", mf, md, 2)
+    dims("8192x8192 f32 sum dims=1", mf, md, 1)
+    dims("8192x8192 f32 max dims=2", mf, md, 2, op="max")
+    dims("8192x8192 f32 sum of squares (all)", mf, md, (1, 2), map="square", init=0.0)
+    dims("8192x8192 i32 sum dims=1 -> int64", mi, mid, 1, acc=torch.int64, out_dtype=torch.int64)
+    del flush
+    return rows
 
 
 def main():
@@ -309,6 +412,12 @@ def main():
     log(f"device: {props.name}, {props.multi_processor_count} CUs")
 
     calls, outs, inputs, keep = build_step(rk, torch, dev)
+    if args.calibration_copy:
+        src = keep[0][0]
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del dst
     kernels = plan_names(rk, torch)
     bytes_step = sum(c.bytes_alg for c in calls)
 
@@ -353,12 +462,15 @@ def main():
     log(f"dominant kernel {DOMINANT}: {avg_launch_s * 1e6:.1f} us per launch, {achieved:.1f} GB/s")
 
     host_value = outs["host"].value
+    snap = {k: (v.detach().cpu().clone() if hasattr(v, "detach") else v) for k, v in outs.items()}
     per_call = per_call_table(calls, torch, args.per_call_reps, dev) if args.per_call_reps > 0 else None
+
+    configs = configs_table(rk, torch, dev, max(3, args.per_call_reps)) if args.all_configs else None
 
     cpu, parity = None, None
     if not args.no_cpu:
         log("CPU oracle baseline ...")
-        cpu, parity = cpu_leg(inputs, outs, args.cpu_budget, host_value)
+        cpu, parity = cpu_leg(inputs, snap, args.cpu_budget, host_value)
 
     traffic = traffic_from_profile()
     line = {
@@ -401,6 +513,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "per_call": per_call,
+        "configs": configs,
     }
     del keep
     print(json.dumps(line), flush=True)

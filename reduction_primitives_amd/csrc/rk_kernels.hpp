@@ -17,6 +17,8 @@
 // it did not write in the same call, so a workspace is reusable as is.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "rk_device.hpp"
 
 namespace rk {
@@ -95,9 +97,9 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
     // scalars before the first 16-byte boundary and after the last vector
     Acc s = Op::template identity<Acc>();
     if (gtid < a.head)
-        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(x[gtid])));
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(x + gtid))));
     if (gtid < a.tail)
-        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(x[a.head + a.nvec * V + gtid])));
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(x + a.head + a.nvec * V + gtid))));
 
 #pragma unroll
     for (int i = 0; i < V; ++i)
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t i = base + int64_t(u) * BLOCK;
             if (i < a.n)
-                w[u] = x[layout_offset(a.nd, a.ext, a.str, i)];
+                w[u] = load1(x + layout_offset(a.nd, a.ext, a.str, i));
         }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass2(Acc *ws, int grid, Finish f
 // W * sizeof(In) bytes per instruction.  Row groups stride over the reduced
 // dim with UNROLL loads in flight, then fold together (in-wave lane moves,
 // then LDS across waves).  CL == BLOCK is the thread-per-output shape.
-template <class In, class Acc, class Op, class Map, bool VECTOR, int CL, int BLOCK, int UNROLL>
+template <class In, class Acc, class Op, class Map, bool VECTOR, int CL, int BLOCK, int UNROLL, bool NT>
 __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 {
     using S = typename InTraits<In>::S;
@@ -208,12 +210,13 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
     set_identity<Acc, Op>(acc1);
     if (active) {
         int64_t j = j0 + rg;
+        // full groups of UNROLL rows per thread, every load issued first
         for (; j + int64_t(UNROLL - 1) * RG < j1; j += int64_t(UNROLL) * RG) {
             if constexpr (VECTOR) {
                 u32x4 w[UNROLL];
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
-                    w[u] = load16(reinterpret_cast<const u32x4 *>(x + (j + int64_t(u) * RG) * s));
+                    w[u] = load16<NT>(reinterpret_cast<const u32x4 *>(x + (j + int64_t(u) * RG) * s));
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u) {
                     if (u & 1)
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
                 S w[UNROLL];
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
-                    w[u] = x[(j + int64_t(u) * RG) * s];
+                    w[u] = load1<NT>(x + (j + int64_t(u) * RG) * s);
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u) {
                     Acc e = Map::apply(InTraits<In>::template one<Acc>(w[u]));
@@ -236,11 +239,30 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
                 }
             }
         }
-        for (; j < j1; j += RG) {
-            if constexpr (VECTOR)
-                fold_vec<In, Acc, Op, Map, V>(acc0, load16(reinterpret_cast<const u32x4 *>(x + j * s)));
-            else
-                acc0[0] = Op::apply(acc0[0], Map::apply(InTraits<In>::template one<Acc>(x[j * s])));
+        // the last, partial group (fewer than UNROLL rows left per thread),
+        // still with all of its loads in flight together
+        if (j < j1) {
+            if constexpr (VECTOR) {
+                u32x4 w[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (j + int64_t(u) * RG < j1)
+                        w[u] = load16<NT>(reinterpret_cast<const u32x4 *>(x + (j + int64_t(u) * RG) * s));
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (j + int64_t(u) * RG < j1)
+                        fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+            } else {
+                S w[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (j + int64_t(u) * RG < j1)
+                        w[u] = load1<NT>(x + (j + int64_t(u) * RG) * s);
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (j + int64_t(u) * RG < j1)
+                        acc0[0] = Op::apply(acc0[0], Map::apply(InTraits<In>::template one<Acc>(w[u])));
+            }
         }
     }
 #pragma unroll
@@ -331,13 +353,22 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
                 fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
         }
     }
-    for (; i < nv; i += 64)
-        fold_vec<In, Acc, Op, Map, V>(acc0, load16(body + i));
+    if (i < nv) {                               // last, partial group, loads together
+        u32x4 w[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            if (i + u * 64 < nv)
+                w[u] = load16(body + i + u * 64);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            if (i + u * 64 < nv)
+                fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+    }
     Acc s = Op::template identity<Acc>();
     if (lane < head)
-        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(row[lane])));
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(row + lane))));
     if (lane < tail)
-        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(row[head + nv * V + lane])));
+        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(row + head + nv * V + lane))));
 #pragma unroll
     for (int k = 0; k < V; ++k)
         acc0[k] = Op::apply(acc0[k], acc1[k]);
@@ -363,7 +394,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
         Acc v = Op::template identity<Acc>();
         for (int64_t j = threadIdx.x; j < a.m; j += BLOCK)
             v = Op::apply(v, Map::apply(InTraits<In>::template one<Acc>(
-                                 x[base + layout_offset(a.red_nd, a.red_ext, a.red_str, j)])));
+                                 load1(x + base + layout_offset(a.red_nd, a.red_ext, a.red_str, j)))));
         v = block_reduce<Op, BLOCK>(v);
         if (threadIdx.x == 0)
             finish_store<Op>(a.fin, o, v);
@@ -386,76 +417,107 @@ __global__ __launch_bounds__(BLOCK) void k_split_finish(const Acc *ws, int64_t n
 
 // ================================================================== launchers
 
+// Launch a call's first kernel.  With a timing event pair the events ride
+// on the kernel's own dispatch packet (hipExtLaunchKernel), so they bracket
+// exactly that kernel and add no packets of their own to the stream.
+template <class... KArgs, class... Args>
+void launch_first(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, const Launch &L,
+                  Args... args)
+{
+    hipEvent_t b = static_cast<hipEvent_t>(L.ev_begin), e = static_cast<hipEvent_t>(L.ev_end);
+    if (b && e)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, b, e, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
+// Launch the tile kernel shape the planner chose (kernel, vector width,
+// lanes per tile row).  Returns false for a shape that has no instantiation.
+template <class In, class Acc, class Op, class Map>
+bool launch_tile(const Launch &L, dim3 grid, hipStream_t st)
+{
+    constexpr int V = InTraits<In>::vec;
+    constexpr int U = tune::kDimsUnroll;
+    const bool vec = L.vec > 1;
+    if (vec && L.vec != V)
+        return false;
+    const DimsArgs &a = L.dims;
+#define RK_TILE(VECTOR, CL, B, NT) \
+    launch_first(&k_dims_tile<In, Acc, Op, Map, VECTOR, CL, B, U, NT>, grid, dim3(B), st, L, a)
+    if (L.kernel == K_THREAD) {
+        constexpr int B = tune::kThreadBlock;
+        if (L.lanes != B || L.block != B)
+            return false;
+        if (vec)
+            RK_TILE(true, B, B, true);
+        else
+            RK_TILE(false, B, B, true);
+        return true;
+    }
+    if (L.kernel == K_TILED) {
+        constexpr int B = tune::kTiledBlock;
+        constexpr int CLV = tune::kTiledOutputs / V, CLS = tune::kTiledOutputs;
+        if (L.block != B || L.lanes != (vec ? CLV : CLS))
+            return false;
+        if (vec)
+            RK_TILE(true, CLV, B, false);
+        else
+            RK_TILE(false, CLS, B, false);
+        return true;
+    }
+    constexpr int B = tune::kColumnsBlock;
+    if (L.block != B)
+        return false;
+    if (!vec) {
+        if (L.lanes != tune::kColumnsScalarLanes)
+            return false;
+        RK_TILE(false, tune::kColumnsScalarLanes, B, true);
+        return true;
+    }
+    switch (L.lanes) {          // tile rows of 16 * lanes bytes
+    case 8: RK_TILE(true, 8, B, true); return true;
+    case 16: RK_TILE(true, 16, B, true); return true;
+    case 32: RK_TILE(true, 32, B, true); return true;
+    }
+#undef RK_TILE
+    return false;
+}
+
 // Run the call's kernels for one (In, Acc, Op, Map).
 template <class In, class Acc, class Op, class Map>
 int run_typed(const Launch &L)
 {
-    constexpr int V = InTraits<In>::vec;
     hipStream_t st = static_cast<hipStream_t>(L.stream);
-    hipEvent_t evb = static_cast<hipEvent_t>(L.ev_begin), eve = static_cast<hipEvent_t>(L.ev_end);
     const dim3 grid((unsigned)L.grid), block((unsigned)L.block);
-    if (evb && eve && hipEventRecord(evb, st) != hipSuccess)
-        return ST_HIP;
 
     int split = 1;
     switch (L.kernel) {
     case K_ALL:
-        hipLaunchKernelGGL((k_all_pass1<In, Acc, Op, Map, tune::kAllBlock, tune::kAllUnroll>), grid,
-                           dim3(tune::kAllBlock), 0, st, L.all);
+        launch_first(&k_all_pass1<In, Acc, Op, Map, tune::kAllBlock, tune::kAllUnroll>, grid,
+                     dim3(tune::kAllBlock), st, L, L.all);
         break;
     case K_ALL_STRIDED:
-        hipLaunchKernelGGL((k_all_pass1_strided<In, Acc, Op, Map, tune::kAllBlock, tune::kAllUnroll>),
-                           grid, dim3(tune::kAllBlock), 0, st, L.all);
+        launch_first(&k_all_pass1_strided<In, Acc, Op, Map, tune::kAllBlock, tune::kAllUnroll>, grid,
+                     dim3(tune::kAllBlock), st, L, L.all);
         break;
     case K_THREAD: case K_TILED: case K_COLUMNS: {
-        constexpr int B = tune::kDimsBlock, U = tune::kDimsUnroll;
-        const bool vec = L.vec > 1;
-        int want;
-        if (L.kernel == K_THREAD)
-            want = B;
-        else if (L.kernel == K_TILED)
-            want = vec ? tune::kTiledOutputs / V : tune::kTiledOutputs;
-        else
-            want = vec ? tune::kColumnsOutputs / V : tune::kColumnsOutputs;
-        if (L.lanes != want || (vec && L.vec != V))
+        if (!launch_tile<In, Acc, Op, Map>(L, grid, st))
             return ST_INVALID;
-        if (L.kernel == K_THREAD) {
-            if (vec)
-                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, true, B, B, U>), grid, block, 0, st, L.dims);
-            else
-                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, false, B, B, U>), grid, block, 0, st, L.dims);
-        } else if (L.kernel == K_TILED) {
-            if (vec)
-                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, true, tune::kTiledOutputs / V, B, U>),
-                                   grid, block, 0, st, L.dims);
-            else
-                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, false, tune::kTiledOutputs, B, U>),
-                                   grid, block, 0, st, L.dims);
-        } else {
-            if (vec)
-                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, true, tune::kColumnsOutputs / V, B, U>),
-                                   grid, block, 0, st, L.dims);
-            else
-                hipLaunchKernelGGL((k_dims_tile<In, Acc, Op, Map, false, tune::kColumnsOutputs, B, U>),
-                                   grid, block, 0, st, L.dims);
-        }
         split = L.dims.split;
         break;
     }
     case K_ROW:
-        hipLaunchKernelGGL((k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, tune::kDimsUnroll>), grid,
-                           block, 0, st, L.dims);
+        launch_first(&k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, tune::kDimsUnroll>, grid, block, st, L,
+                     L.dims);
         split = L.dims.split;
         break;
     case K_GENERIC:
-        hipLaunchKernelGGL((k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock>), grid, block, 0, st, L.dims);
+        launch_first(&k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock>, grid, block, st, L, L.dims);
         break;
     default:
         return ST_INVALID;
     }
     if (hipGetLastError() != hipSuccess)
-        return ST_HIP;
-    if (evb && eve && hipEventRecord(eve, st) != hipSuccess)
         return ST_HIP;
 
     // second launches

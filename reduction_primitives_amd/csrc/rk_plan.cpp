@@ -73,9 +73,10 @@ int select_strided_kernel(int64_t run_len, int64_t n_out, int64_t m, int in_size
     if (run_len * in_size >= tune::kThreadRowBytes || m < tune::kMinReduceLen)
         return K_THREAD;
     // Rule 2: the narrow one-pass tile when there are at least as many
-    // outputs as elements per output and wide tiles would not fill the GPU.
-    const int64_t wide_tiles = ceil_div(n_out, tune::kColumnsOutputs);
-    if (n_out >= m && wide_tiles < int64_t(num_cus) * tune::kFillTilesPerCu)
+    // outputs as elements per output and its tiles would not fill the GPU
+    // (so wide tiles would need a split and a second launch).
+    const int64_t narrow_tiles = ceil_div(n_out, tune::kTiledOutputs);
+    if (n_out >= m && narrow_tiles < int64_t(num_cus) * tune::kFillTilesPerCu)
         return K_TILED;
     // Rule 3: wide tiles, split along the reduced dim when they are too few.
     return K_COLUMNS;
@@ -209,16 +210,25 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         for (int i = 0; i < d.outer.nd; ++i)
             vec_ok = vec_ok && (d.outer.str[i] * isz) % 16 == 0;
         d.vec = vec_ok ? v : 1;
-        const int block = tune::kDimsBlock;
-        if (d.kernel == K_THREAD)
-            d.tile_outputs = block * d.vec;
-        else if (d.kernel == K_TILED)
-            d.tile_outputs = tune::kTiledOutputs;
-        else
-            d.tile_outputs = tune::kColumnsOutputs;
-        if (d.tile_outputs % d.vec)             // keep whole vectors per lane
-            d.tile_outputs = d.vec;
-        d.lanes = d.tile_outputs / d.vec;
+        if (d.kernel == K_THREAD) {
+            d.block = tune::kThreadBlock;
+            d.lanes = d.block;
+        } else if (d.kernel == K_TILED) {
+            d.block = tune::kTiledBlock;
+            d.lanes = tune::kTiledOutputs / d.vec;
+        } else {
+            d.block = tune::kColumnsBlock;
+            if (d.vec > 1) {
+                // widest row of 128, 256 or 512 bytes the runs can fill
+                int bytes = tune::kColumnsRowBytes;
+                while (bytes > tune::kColumnsMinRowBytes && d.run_len * isz <= bytes / 2)
+                    bytes /= 2;
+                d.lanes = bytes / 16;
+            } else {
+                d.lanes = tune::kColumnsScalarLanes;
+            }
+        }
+        d.tile_outputs = d.lanes * d.vec;
         d.tiles_per_run = ceil_div(d.run_len, d.tile_outputs);
         d.tiles = d.runs * d.tiles_per_run;
         d.split = 1;
@@ -232,7 +242,6 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
             d.rows_per_split = m;
         }
         d.grid = d.tiles * d.split;
-        d.block = block;
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
         break;

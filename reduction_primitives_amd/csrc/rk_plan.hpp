@@ -27,10 +27,18 @@ bool dtype_known(int d);
 bool dtype_combo_ok(int in, int acc, int out);
 
 // ---------------------------------------------------------------- tuning
-// gfx950 values.  The pages' own numbers (256 target blocks, 64 bytes of
-// accumulator per thread, 8- and 32-output tiles, a 64 KiB row threshold, a
-// reduction-length floor of 32) were tuned for other GPUs; the defaults here
-// are set from MI355X's 256 CUs and measured on it.
+// gfx950 values, set from measurements on MI355X (256 CUs, 8 XCDs, 128-byte
+// L2 lines).  The pages' own numbers -- 256 target blocks, 64 bytes of
+// accumulator per thread, 8-output tiled blocks, 32-output column tiles, a
+// 64 KiB row threshold -- were tuned for other GPUs and are not used as is:
+//  * an 8-output tile reads 32-byte row pieces and wastes most of each
+//    128-byte line (1.5-2.7x slower than the best shape on every shape
+//    measured), so the one-pass tiled kernel takes 32 outputs per block;
+//  * a split tile streams best with 512-byte rows and about one block per
+//    CU, so the columns kernel takes 512 bytes of outputs (256 or 128 bytes
+//    when a run of outputs is shorter);
+//  * one thread per output keeps only a few bytes in flight per thread, so it
+//    needs a row of outputs of 4 MiB before it can keep HBM busy.
 namespace tune {
 // whole-array first pass
 constexpr int kAllBlock = 256;            // threads per block
@@ -39,19 +47,24 @@ constexpr int kAllBlocksPerCu = 4;        // grid cap = CUs * this
 constexpr int kAllSingleLaunchTiles = 2;  // <= this many tiles: one launch
 constexpr int kPass2Block = 256;          // threads of the one-block second pass
 // dims
-constexpr int kDimsBlock = 256;
-constexpr int kDimsUnroll = 8;
-constexpr int64_t kThreadRowBytes = 64 * 1024;  // rule 1: row of outputs this wide -> thread kernel
-constexpr int64_t kMinReduceLen = 32;           // rule 1: shorter reductions -> thread kernel
-constexpr int kTiledOutputs = 8;                // tiled kernel: outputs per block
-constexpr int kColumnsOutputs = 32;             // columns kernel: outputs per block
-constexpr int kFillTilesPerCu = 1;              // rule 2: 32-output tiles that "fill" the device
-constexpr int kColumnsBlocksPerCu = 4;          // columns split target
-constexpr int64_t kColumnsMinRows = 128;        // rows per split chunk, at least
-constexpr int kRowWavesPerCu = 16;              // row kernel split target
-constexpr int64_t kRowMinChunk = 2048;          // elements per row chunk, at least
+constexpr int kDimsBlock = 256;           // row and generic kernels
+constexpr int kDimsUnroll = 8;            // loads in flight per thread
+constexpr int kThreadBlock = 256;         // thread-per-output kernel
+constexpr int kTiledBlock = 1024;         // one-pass tiled kernel: 16 waves share a tile
+constexpr int kColumnsBlock = 256;        // split columns kernel
+constexpr int64_t kThreadRowBytes = 4 * 1024 * 1024;  // rule 1: row of outputs this wide -> thread kernel
+constexpr int64_t kMinReduceLen = 32;                 // rule 1: shorter reductions -> thread kernel
+constexpr int kTiledOutputs = 32;                     // tiled kernel: outputs per block
+constexpr int kColumnsRowBytes = 512;                 // columns kernel: bytes of outputs per block (max)
+constexpr int kColumnsMinRowBytes = 128;              //   ... and the narrowest it goes for short runs
+constexpr int kColumnsScalarLanes = 64;               // columns tile without 16-byte loads: 64 outputs
+constexpr int kFillTilesPerCu = 1;        // rule 2: tiled while its tiles number fewer than CUs * this
+constexpr int kColumnsBlocksPerCu = 1;    // columns split target: CUs * this blocks
+constexpr int64_t kColumnsMinRows = 128;  // rows per split chunk, at least
+constexpr int kRowWavesPerCu = 16;        // row kernel split target
+constexpr int64_t kRowMinChunk = 2048;    // elements per row chunk, at least
 constexpr int kGenericBlocksPerCu = 8;
-constexpr int kDefaultCus = 256;                // MI355X
+constexpr int kDefaultCus = 256;          // MI355X
 }  // namespace tune
 
 constexpr int kMaxDims = 4;

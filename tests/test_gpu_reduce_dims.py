@@ -160,16 +160,18 @@ def test_selector_kernels(case):
 
 
 def test_selector_rules_from_tuning():
-    """The selector's three rules, checked on plans only (no launch)."""
+    """The selector's three rules on the device's own CU count, with the
+    thresholds of the tuning table (no launch)."""
+    from tests import tuning
     rk = _rk()
-    p = rk.plan_dims(torch.float32, (16384, 100), (1, 16384), 2, num_cus=256)   # 64 KiB row
-    assert p["kernel_name"] == "thread"
-    p = rk.plan_dims(torch.float32, (8000, 100), (1, 8000), 2, num_cus=256)
-    assert p["kernel_name"] == "tiled"
-    p = rk.plan_dims(torch.float32, (512, 31), (1, 512), 2, num_cus=256)
-    assert p["kernel_name"] == "thread"
-    p = rk.plan_dims(torch.float32, (512, 32), (1, 512), 2, num_cus=256)
-    assert p["kernel_name"] == "tiled"
+    t = tuning.values()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    row = t["kThreadRowBytes"] // 4
+    assert rk.plan_dims(torch.float32, (row, 100), (1, row), 2)["kernel_name"] == "thread"
+    n = cus * t["kTiledOutputs"] - t["kTiledOutputs"]
+    assert rk.plan_dims(torch.float32, (n, 100), (1, n), 2)["kernel_name"] == "tiled"
+    assert rk.plan_dims(torch.float32, (512, 31), (1, 512), 2)["kernel_name"] == "thread"
+    assert rk.plan_dims(torch.float32, (512, 32), (1, 512), 2)["kernel_name"] == "tiled"
 
 
 @pytest.mark.parametrize("case", SELECTOR_CASES[:7], ids=lambda c: c[4].replace(" ", "_"))

@@ -80,23 +80,42 @@ def test_config_shapes_take_the_expected_kernels():
 
 
 def test_selector_rules():
+    """The three rules of the selector, with thresholds read from the tuning
+    table (so the test follows the table, not hard-coded numbers)."""
     import torch
-    # rule 1: a row of outputs of at least 64 KiB, or a reduction shorter than 32
-    assert plan(torch.float32, (16384, 100), 2)["kernel_name"] == "thread"
-    assert plan(torch.bfloat16, (32768, 100), 2)["kernel_name"] == "thread"
-    assert plan(torch.bfloat16, (32767, 100), 2)["kernel_name"] == "columns"   # 1024 wide tiles
-    assert plan(torch.bfloat16, (8000, 100), 2)["kernel_name"] == "tiled"
-    assert plan(torch.float32, (1000, 31), 2)["kernel_name"] == "thread"
-    # rule 2: outputs >= elements per output and few wide tiles -> tiled
-    assert plan(torch.float32, (1000, 1000), 2)["kernel_name"] == "tiled"
-    assert plan(torch.float32, (999, 1000), 2)["kernel_name"] == "columns"
+    from tests import tuning
+    t = tuning.values()
+    cus = 256
+    row_f32 = t["kThreadRowBytes"] // 4           # outputs in a threshold-wide f32 row
+    # rule 1: a row of outputs at least kThreadRowBytes wide, or a short reduction
+    assert plan(torch.float32, (row_f32, 100), 2)["kernel_name"] == "thread"
+    assert plan(torch.float32, (row_f32 - 4, 100), 2)["kernel_name"] != "thread"
+    assert plan(torch.bfloat16, (2 * row_f32, 100), 2)["kernel_name"] == "thread"
+    m_short = t["kMinReduceLen"]
+    assert plan(torch.float32, (1000, m_short - 1), 2)["kernel_name"] == "thread"
+    assert plan(torch.float32, (1000, m_short), 2)["kernel_name"] == "tiled"
+    # rule 2: outputs >= elements per output and fewer narrow tiles than CUs -> tiled
+    w = t["kTiledOutputs"]
+    n_fill = cus * t["kFillTilesPerCu"] * w       # outputs whose narrow tiles fill the device
+    assert plan(torch.float32, (n_fill - w, 1000), 2)["kernel_name"] == "tiled"
+    assert plan(torch.float32, (n_fill, 1000), 2)["kernel_name"] == "columns"
+    assert plan(torch.float32, (999, 1000), 2)["kernel_name"] == "columns"   # outputs < elements
     # "fill the device" scales with the CU count
-    assert plan(torch.float32, (8192, 8192), 2, cus=512)["kernel_name"] == "tiled"
-    # rule 3 splits along the reduced dim only when tiles are few
+    assert plan(torch.float32, (8192, 8192), 2, cus=cus)["kernel_name"] == "columns"
+    assert plan(torch.float32, (8192, 8192), 2, cus=2 * cus)["kernel_name"] == "tiled"
+    # rule 3 splits along the reduced dim to reach the block target
     p = plan(torch.float32, (64, 100000), 2)
     assert p["kernel_name"] == "columns" and p["split"] > 1
-    p = plan(torch.float32, (1 << 16, 1 << 15), 2)   # 256 KiB row of outputs: rule 1
-    assert p["kernel_name"] == "thread" and p["split"] == 1
+    assert p["grid"] <= cus * t["kColumnsBlocksPerCu"] * 2
+    p = plan(torch.float32, (8192, 8192), 2)
+    assert p["tile_outputs"] == t["kColumnsRowBytes"] // 4
+    assert p["grid"] == cus * t["kColumnsBlocksPerCu"]
+    # short runs narrow the columns tile (but never below kColumnsMinRowBytes)
+    assert plan(torch.float32, (64, 4096, 32), 2)["tile_outputs"] == 64
+    assert plan(torch.float32, (16, 4096, 32), 2)["tile_outputs"] == t["kColumnsMinRowBytes"] // 4
+    # tile shapes: tiled tiles are kTiledOutputs wide, thread tiles one block of vectors
+    assert plan(torch.bfloat16, (3072, 2048), 2)["tile_outputs"] == w
+    assert plan(torch.float32, (row_f32, 100), 2)["tile_outputs"] == t["kThreadBlock"] * 4
 
 
 def test_normalisation_drops_unit_dims_and_merges():
