@@ -56,9 +56,12 @@
  * library allocates and frees no device memory.  Kernels are enqueued on
  * `stream` (a hipStream_t; NULL is the null stream) of the current device.
  * OVERWRITE and FOLD calls are asynchronous: buffers must stay alive until
- * the stream's work has completed.  The library keeps no state between calls
- * other than cached device properties, so calls from several host threads
- * are safe (two calls that share a workspace must be ordered by the caller).
+ * the stream's work has completed.  Between calls the library keeps only
+ * cached device properties and, per (device, stream), a slot of arrival
+ * counters in its own device memory: a reduction split across blocks is
+ * finished by the last block to arrive instead of a second launch, and its
+ * counters return to zero by themselves.  Calls from several host threads are
+ * safe; two calls that share a workspace must be ordered by the caller.
  *
  * Errors: every argument is validated before any launch; a rejected call
  * returns a non-zero rk_status and writes nothing.  A HIP launch failure is
@@ -113,7 +116,9 @@ size_t rk_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64_t *s
  * Whole-array mapped reduction of n contiguous elements at `ptr` (device
  * pointer, aligned to its element size; it need not be 16-byte aligned, so
  * offset views work).  PR #139, "What changes": at most two launches, one
- * launch when the input fits one block.
+ * launch when the input fits one block.  Here a larger input also takes one
+ * launch: the last first-pass block to arrive folds the partials (it falls
+ * back to the one-block second launch when its stream has no counter slot).
  *   init      host pointer to one accumulator-typed value, or NULL.
  *   mode      RK_MODE_OVERWRITE / RK_MODE_FOLD: `out` is a device pointer to
  *             one out-typed element; RK_MODE_HOST: `out` is a host pointer to
@@ -167,7 +172,8 @@ typedef enum {
 
 typedef struct {
     int kernel;               /* rk_kernel */
-    int launches;             /* kernel launches the call makes: 0, 1 or 2 */
+    int launches;             /* kernel launches the call makes: 0, 1 or 2 (1 when a split
+                                 reduction finishes in its last block to arrive) */
     int64_t grid;             /* blocks of the first launch */
     int block;                /* threads per block of the first launch */
     int split;                /* blocks sharing one output's reduction (1 = no second pass) */
@@ -186,6 +192,12 @@ int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num
 int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const int64_t *shape,
                  const int64_t *strides, uint32_t reduce_mask, int num_cus,
                  rk_plan_info *info);
+
+/* Whether a split reduction may finish in the last block to arrive (one
+ * launch; the default) instead of a second launch.  Both give the same
+ * results; tests switch it off to cover the second-launch path.  Process-
+ * wide.  Returns the previous setting (1 or 0). */
+int rk_debug_set_fused_finish(int enable);
 
 /* Benchmark hook: while both are non-NULL, every later rk_reduce_* call made
  * by this host thread records hipEvent_t `begin` immediately before its first

@@ -18,7 +18,7 @@ from ._native import (  # noqa: F401
     RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE, RK_KERNEL_ROW,
     RK_KERNEL_THREAD, RK_KERNEL_TILED, RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
     RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,
-    RkError, load, rk_debug_set_launch_events, rk_plan_all, rk_plan_dims, rk_plan_info,
+    RkError, load, rk_debug_set_fused_finish, rk_debug_set_launch_events, rk_plan_all, rk_plan_dims, rk_plan_info,
     rk_reduce_all, rk_reduce_dims, rk_workspace_size, status_string)
 
 OPS = {"sum": RK_OP_SUM, "max": RK_OP_MAX, "min": RK_OP_MIN}

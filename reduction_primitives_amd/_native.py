@@ -25,7 +25,7 @@ KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 
 
 # every function include/rk.h declares
 EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_dims", "rk_status_string",
-           "rk_plan_all", "rk_plan_dims", "rk_debug_set_launch_events")
+           "rk_plan_all", "rk_plan_dims", "rk_debug_set_fused_finish", "rk_debug_set_launch_events")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.rk_plan_all.restype = i32
     lib.rk_plan_dims.argtypes = [i32, i32, vp, i32, p64, p64, u32, i32, ctypes.POINTER(rk_plan_info)]
     lib.rk_plan_dims.restype = i32
+    lib.rk_debug_set_fused_finish.argtypes = [i32]
+    lib.rk_debug_set_fused_finish.restype = i32
     lib.rk_debug_set_launch_events.argtypes = [vp, vp]
     lib.rk_debug_set_launch_events.restype = i32
     _lib = lib
@@ -121,6 +123,10 @@ def rk_plan_dims(in_dtype, acc_dtype, ptr, ndim, shape, strides, reduce_mask, nu
     if rc:
         raise RkError(rc, "rk_plan_dims")
     return info
+
+
+def rk_debug_set_fused_finish(enable: int) -> int:
+    return int(load().rk_debug_set_fused_finish(int(enable)))
 
 
 def rk_debug_set_launch_events(begin, end) -> int:

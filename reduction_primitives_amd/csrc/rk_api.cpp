@@ -12,6 +12,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -47,6 +48,35 @@ int device_cus()
     if (dev < kMaxDevices)
         g_cus[dev].store(cus, std::memory_order_relaxed);
     return cus;
+}
+
+// ---- arrival-counter slots: one per (device, stream), so calls that may
+// run concurrently never share a counter.  Calls on one stream are ordered,
+// so they share their slot safely.  hipStreamPerThread names a different
+// stream on each host thread and never gets a slot.
+std::atomic<bool> g_fused_finish{true};
+std::mutex g_slot_mu;
+struct SlotKey { int dev; void *stream; bool used; };
+SlotKey g_slots[kArriveSlots];
+
+int arrive_slot(hipStream_t st)
+{
+    if (!g_fused_finish.load(std::memory_order_relaxed) || st == hipStreamPerThread)
+        return -1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    for (int i = 0; i < kArriveSlots; ++i)
+        if (g_slots[i].used && g_slots[i].dev == dev && g_slots[i].stream == (void *)st)
+            return i;
+    for (int i = 0; i < kArriveSlots; ++i) {
+        if (!g_slots[i].used) {
+            g_slots[i] = SlotKey{dev, (void *)st, true};
+            return i;
+        }
+    }
+    return -1;                                  // all slots taken: two launches
 }
 
 bool debug_enabled()
@@ -271,6 +301,7 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     }
     L.all.ws = ws;
     L.all.grid = a.grid;
+    L.all.arrive_slot = a.grid > 1 ? arrive_slot(st) : -1;
     L.all.fin = make_finish(op, acc, out_dtype, mode, init, out);
     L.stream = st;
     L.ev_begin = t_ev_begin;
@@ -298,6 +329,11 @@ const char *rk_status_string(int status)
     return "unknown status";
 }
 
+int rk_debug_set_fused_finish(int enable)
+{
+    return g_fused_finish.exchange(enable != 0) ? 1 : 0;
+}
+
 int rk_debug_set_launch_events(void *begin, void *end)
 {
     if ((begin == nullptr) != (end == nullptr))
@@ -319,7 +355,7 @@ int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num
         return rc;
     std::memset(info, 0, sizeof *info);
     info->kernel = RK_KERNEL_ALL;
-    info->launches = a.launches;
+    info->launches = (a.grid > 1 && g_fused_finish.load()) ? 1 : a.launches;
     info->grid = a.grid;
     info->block = a.block;
     info->split = 1;
@@ -345,7 +381,7 @@ int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const i
         return rc;
     std::memset(info, 0, sizeof *info);
     info->kernel = d.kernel;
-    info->launches = d.launches;
+    info->launches = (d.fused_ok && g_fused_finish.load()) ? 1 : d.launches;
     info->grid = d.grid;
     info->block = d.block;
     info->split = d.split;
@@ -483,6 +519,7 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
         a.red_str[i] = d.red.str[i];
     }
     a.fin = make_finish(op, acc_dtype, out_dtype, mode, init, out);
+    a.arrive_slot = d.fused_ok ? arrive_slot(st) : -1;
     L.stream = st;
     L.ev_begin = t_ev_begin;
     L.ev_end = t_ev_end;

@@ -447,6 +447,60 @@ __device__ __forceinline__ void finish_store(const Finish &f, int64_t o, Acc v)
     store_out<Acc>(f.out, o, f.out_dtype, Op::apply(s, v));
 }
 
+// ------------------------------------------------- finishing in one launch
+// The blocks that share an output store their partials, and the last one to
+// arrive folds them and finishes: one launch instead of a second pass.  The
+// counters belong to the library, are zero when the code object loads, and
+// atomicInc's wrap-around (n - 1 -> 0) leaves each one at zero again after
+// its n arrivals, so nothing has to be cleared between calls.  Each stream
+// gets its own slot of counters, so calls that may overlap never share one.
+static __device__ uint32_t g_arrive[kArriveSlots * kArriveCapacity];
+
+// Partials cross XCDs, each with a private L2.  They are written with
+// device-scope atomic stores, which write through to the device's point of
+// coherence (`sc1` stores on gfx950), and read with device-scope atomic
+// loads, which do not hit a stale L2 line (`sc1` loads).  So handing them
+// over needs no L2 writeback or invalidation -- which is what a device-scope
+// release/acquire fence would add (buffer_wbl2 / buffer_inv), at a cost of
+// tens of microseconds over a 1024-block grid -- only that each store has
+// completed before its block's arrival is counted (wait_stores).
+template <class T>
+__device__ __forceinline__ void store_partial(T *p, T v)
+{
+    if constexpr (sizeof(T) == 4)
+        __hip_atomic_store(reinterpret_cast<uint32_t *>(p), bitcast<uint32_t>(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(p), bitcast<uint64_t>(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class T>
+__device__ __forceinline__ T load_partial(const T *p)
+{
+    if constexpr (sizeof(T) == 4)
+        return bitcast<T>(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT));
+    else
+        return bitcast<T>(__hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Wait until this thread's outstanding memory operations have completed
+// (s_waitcnt with every counter at zero).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Count one arrival on counter idx of a slot; true for the n-th (last) one.
+// Every thread that stored a partial must have called wait_stores() and met
+// the caller at a barrier first.
+__device__ __forceinline__ bool arrive_last(int slot, int64_t idx, uint32_t n)
+{
+    wait_stores();
+    const uint32_t prev = __builtin_amdgcn_atomic_inc32(&g_arrive[int64_t(slot) * kArriveCapacity + idx], n - 1,
+                                                        __ATOMIC_RELAXED, "agent");
+    return prev == n - 1;
+}
+
 // ------------------------------------------------------------------ misc
 
 // Offset of linear index idx in a column-major layout of nd <= 4 dims.

@@ -59,6 +59,74 @@ __device__ __forceinline__ Acc fold_all(const Acc (&a)[V])
 
 // ================================================================ whole array
 
+// Fold a whole-array call's `grid` block partials and finish: store into
+// the output, or leave the bare result in ws[grid] for the host.  Run by one
+// block (the second launch, or the last block to arrive).
+// Fold `count` partials p[first + k * stride], k < count, issuing up to 8
+// loads at a time: the partials come from memory, and one round trip per
+// partial would dominate the finishing step.
+template <class Acc, class Op>
+__device__ __forceinline__ Acc fold_partials(const Acc *p, int64_t first, int64_t count, int64_t stride)
+{
+    constexpr int P = 8;
+    Acc v = Op::template identity<Acc>();
+    for (int64_t k0 = 0; k0 < count; k0 += P) {
+        Acc w[P];
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+            w[u] = k0 + u < count ? load_partial(p + first + (k0 + u) * stride) : Op::template identity<Acc>();
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+            v = Op::apply(v, w[u]);
+    }
+    return v;
+}
+
+template <class Acc, class Op, int BLOCK>
+__device__ __forceinline__ void fold_partials_and_finish(Acc *ws, int grid, const Finish &fin)
+{
+    // thread t folds partials t, t + BLOCK, ...
+    const int64_t mine = threadIdx.x < grid ? (grid - 1 - threadIdx.x) / BLOCK + 1 : 0;
+    Acc v = fold_partials<Acc, Op>(ws, threadIdx.x, mine, BLOCK);
+    v = block_reduce<Op, BLOCK>(v);
+    if (threadIdx.x == 0) {
+        if (fin.mode == FIN_HOST)
+            ws[grid] = v;
+        else
+            finish_store<Op>(fin, 0, v);
+    }
+}
+
+// End of a first-pass block holding its reduced value v (valid in thread 0).
+template <class Acc, class Op, int BLOCK>
+__device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v)
+{
+    Acc *ws = static_cast<Acc *>(a.ws);
+    if (a.grid == 1) {                          // the whole input in one block
+        if (threadIdx.x == 0) {
+            if (a.fin.mode == FIN_HOST)
+                ws[1] = v;                      // bare result for the host to finish
+            else
+                finish_store<Op>(a.fin, 0, v);
+        }
+        return;
+    }
+    if (a.arrive_slot < 0) {                    // a second launch folds the partials
+        if (threadIdx.x == 0)
+            ws[blockIdx.x] = v;
+        return;
+    }
+    __shared__ int last;
+    if (threadIdx.x == 0) {
+        store_partial(ws + blockIdx.x, v);
+        last = arrive_last(a.arrive_slot, 0, (uint32_t)a.grid);
+    }
+    __syncthreads();
+    if (!last)
+        return;
+    fold_partials_and_finish<Acc, Op, BLOCK>(ws, a.grid, a.fin);
+}
+
 template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
 {
@@ -106,15 +174,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
         acc0[i] = Op::apply(acc0[i], acc1[i]);
     Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
     v = block_reduce<Op, BLOCK>(v);
-    if (threadIdx.x == 0) {
-        Acc *ws = static_cast<Acc *>(a.ws);
-        if (a.grid > 1)
-            ws[blockIdx.x] = v;                 // bare partial for the second pass
-        else if (a.fin.mode == FIN_HOST)
-            ws[a.grid] = v;                     // bare result for the host to finish
-        else
-            finish_store<Op>(a.fin, 0, v);
-    }
+    whole_epilogue<Acc, Op, BLOCK>(a, v);
 }
 
 // Single output over a non-contiguous view: element i lives at
@@ -146,30 +206,13 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
     }
     Acc v = fold_all<Acc, Op, UNROLL>(acc);
     v = block_reduce<Op, BLOCK>(v);
-    if (threadIdx.x == 0) {
-        Acc *ws = static_cast<Acc *>(a.ws);
-        if (a.grid > 1)
-            ws[blockIdx.x] = v;
-        else if (a.fin.mode == FIN_HOST)
-            ws[a.grid] = v;
-        else
-            finish_store<Op>(a.fin, 0, v);
-    }
+    whole_epilogue<Acc, Op, BLOCK>(a, v);
 }
 
 template <class Acc, class Op, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_all_pass2(Acc *ws, int grid, Finish fin)
 {
-    Acc v = Op::template identity<Acc>();
-    for (int i = threadIdx.x; i < grid; i += BLOCK)
-        v = Op::apply(v, ws[i]);
-    v = block_reduce<Op, BLOCK>(v);
-    if (threadIdx.x == 0) {
-        if (fin.mode == FIN_HOST)
-            ws[grid] = v;
-        else
-            finish_store<Op>(fin, 0, v);
-    }
+    fold_partials_and_finish<Acc, Op, BLOCK>(ws, grid, fin);
 }
 
 // ======================================================================= dims
@@ -298,17 +341,39 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
                 part[w][lane_id() * V + i] = acc0[i];
         }
         __syncthreads();
-        if (threadIdx.x < W && int64_t(threadIdx.x) < outs_left) {
-            Acc v = part[0][threadIdx.x];
+        const bool mine = threadIdx.x < W && int64_t(threadIdx.x) < outs_left;
+        const int64_t o = o_tile + threadIdx.x;
+        Acc v = Op::template identity<Acc>();
+        if (mine) {
+            v = part[0][threadIdx.x];
 #pragma unroll
             for (int k = 1; k < NW; ++k)
                 v = Op::apply(v, part[k][threadIdx.x]);
-            const int64_t o = o_tile + threadIdx.x;
-            if (a.split > 1)
-                ws[int64_t(sp) * a.n_out + o] = v;
-            else
-                finish_store<Op>(a.fin, o, v);
         }
+        if (a.split == 1) {
+            if (mine)
+                finish_store<Op>(a.fin, o, v);
+            return;
+        }
+        if (a.arrive_slot < 0) {                // a second launch folds the splits
+            if (mine)
+                ws[int64_t(sp) * a.n_out + o] = v;
+            return;
+        }
+        // the last of the tile's `split` blocks to arrive folds and finishes
+        if (mine) {
+            store_partial(ws + int64_t(sp) * a.n_out + o, v);
+            wait_stores();
+        }
+        __shared__ int last;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            last = arrive_last(a.arrive_slot, tile, (uint32_t)a.split);
+        __syncthreads();
+        if (!last)
+            return;
+        if (mine)
+            finish_store<Op>(a.fin, o, fold_partials<Acc, Op>(ws, o, a.split, a.n_out));
     }
 }
 
@@ -373,12 +438,32 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
     for (int k = 0; k < V; ++k)
         acc0[k] = Op::apply(acc0[k], acc1[k]);
     Acc v = wave_reduce<Op>(Op::apply(fold_all<Acc, Op, V>(acc0), s));
-    if (lane == 0) {
-        if (a.split > 1)
-            static_cast<Acc *>(a.ws)[int64_t(sp) * a.n_out + o] = v;
-        else
+    Acc *ws = static_cast<Acc *>(a.ws);
+    if (a.split == 1) {
+        if (lane == 0)
             finish_store<Op>(a.fin, o, v);
+        return;
     }
+    if (a.arrive_slot < 0) {                    // a second launch folds the chunks
+        if (lane == 0)
+            ws[int64_t(sp) * a.n_out + o] = v;
+        return;
+    }
+    // the last of the output's `split` waves to arrive folds and finishes
+    int last = 0;
+    if (lane == 0) {
+        store_partial(ws + int64_t(sp) * a.n_out + o, v);
+        last = arrive_last(a.arrive_slot, o, (uint32_t)a.split);
+    }
+    last = __builtin_amdgcn_readfirstlane(last);
+    if (!last)
+        return;
+    Acc r = Op::template identity<Acc>();
+    for (int k = lane; k < a.split; k += 64)
+        r = Op::apply(r, load_partial(ws + int64_t(k) * a.n_out + o));
+    r = wave_reduce<Op>(r);
+    if (lane == 0)
+        finish_store<Op>(a.fin, o, r);
 }
 
 // Generic kernel: one block per output (grid-stride over outputs); the
@@ -520,11 +605,11 @@ int run_typed(const Launch &L)
     if (hipGetLastError() != hipSuccess)
         return ST_HIP;
 
-    // second launches
-    if ((L.kernel == K_ALL || L.kernel == K_ALL_STRIDED) && L.all.grid > 1) {
+    // second launches, unless the last block to arrive finished the call
+    if ((L.kernel == K_ALL || L.kernel == K_ALL_STRIDED) && L.all.grid > 1 && L.all.arrive_slot < 0) {
         hipLaunchKernelGGL((k_all_pass2<Acc, Op, tune::kPass2Block>), dim3(1), dim3(tune::kPass2Block), 0,
                            st, static_cast<Acc *>(L.all.ws), L.all.grid, L.all.fin);
-    } else if (split > 1) {
+    } else if (split > 1 && L.dims.arrive_slot < 0) {
         constexpr int B = 256;
         const unsigned g = (unsigned)((L.dims.n_out + B - 1) / B);
         hipLaunchKernelGGL((k_split_finish<Acc, Op, B>), dim3(g), dim3(B), 0, st,

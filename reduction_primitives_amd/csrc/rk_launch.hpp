@@ -13,6 +13,12 @@ namespace rk {
 // which stores a bare accumulator per block for a following pass.
 enum FinishMode { FIN_OVERWRITE = 0, FIN_FOLD = 1, FIN_HOST = 2, FIN_PARTIAL = 3 };
 
+// Arrival counters for finishing in the last block to arrive (no second
+// launch).  Each stream slot owns kArriveCapacity counters; a plan whose
+// counters would not fit takes the two-launch path.
+constexpr int kArriveSlots = 32;
+constexpr int kArriveCapacity = 4096;
+
 struct Finish {
     void *out;            // device output (OVERWRITE / FOLD)
     int out_dtype;
@@ -31,6 +37,7 @@ struct AllArgs {
     int64_t str[4];
     void *ws;             // grid + 1 accumulators
     int grid;
+    int arrive_slot;      // >= 0: the last block to arrive finishes (one launch)
     Finish fin;
 };
 
@@ -54,6 +61,7 @@ struct DimsArgs {
     int red_nd;           // reduced dims (generic kernel)
     int64_t red_ext[4];
     int64_t red_str[4];
+    int arrive_slot;      // >= 0 with split > 1: the last block (or wave) of each output finishes
     Finish fin;
 };
 

@@ -173,6 +173,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.block = d.all.block;
         d.vec = d.all.vec;
         d.ws_bytes = d.all.ws_bytes;
+        d.fused_ok = d.all.grid > 1;
         break;
     }
     case K_ALL_STRIDED: {
@@ -192,6 +193,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.grid = a.grid;
         d.block = a.block;
         d.ws_bytes = a.ws_bytes;
+        d.fused_ok = a.grid > 1;
         break;
     }
     case K_THREAD: case K_TILED: case K_COLUMNS: {
@@ -244,6 +246,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.grid = d.tiles * d.split;
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
+        d.fused_ok = d.split > 1 && d.tiles <= kArriveCapacity;   // one counter per tile
         break;
     }
     case K_ROW: {
@@ -262,6 +265,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.grid = ceil_div(n_out * d.split, waves_per_block);
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
+        d.fused_ok = d.split > 1 && n_out <= kArriveCapacity;      // one counter per output
         break;
     }
     case K_GENERIC: {

@@ -11,6 +11,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "rk_launch.hpp"
+
 namespace rk {
 
 enum Dtype { F32 = 0, BF16 = 1, F16 = 2, F64 = 3, I32 = 4, I64 = 5 };
@@ -84,7 +86,7 @@ struct AllPlan {
     int64_t tiles = 0;      // tiles of block * unroll vectors
     int grid = 1;           // first-pass blocks
     int block = tune::kAllBlock;
-    int launches = 1;
+    int launches = 1;       // with a second pass; 1 when the last block finishes
     size_t ws_bytes = 0;
 };
 
@@ -113,6 +115,9 @@ struct DimsPlan {
     int64_t grid = 0;
     int block = tune::kDimsBlock;
     size_t ws_bytes = 0;
+    // split reductions can finish in the last block to arrive when their
+    // arrival counters fit one slot (see rk_launch.hpp)
+    bool fused_ok = false;
 };
 
 // Status codes as in the public header.

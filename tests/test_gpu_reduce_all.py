@@ -109,7 +109,7 @@ def _boundary_sizes():
 def test_tile_constant_matches_plan():
     tile = 256 * 8 * 4
     assert _plan(2 * tile).grid == 1 and _plan(2 * tile).launches == 1
-    assert _plan(2 * tile + 4).launches == 2
+    assert _plan(2 * tile + 4).grid > 1
 
 
 @pytest.mark.parametrize("n", _boundary_sizes())

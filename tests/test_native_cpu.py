@@ -49,8 +49,10 @@ def plan(dtype, shape, dims, strides=None, cus=256, ptr=0):
 
 def test_whole_array_plan():
     rk = _rk()
+    assert rk.rk_debug_set_fused_finish(1) in (0, 1)
     info = rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**8, 256)
-    assert info.kernel == rk.RK_KERNEL_ALL and info.launches == 2
+    # one launch: the last first-pass block to arrive folds the partials
+    assert info.kernel == rk.RK_KERNEL_ALL and info.launches == 1
     assert info.grid == 1024 and info.block == 256 and info.vec == 4
     assert info.workspace_bytes == 4352          # (1024 + 1) * 4 rounded to 256
     small = rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**4, 256)
@@ -70,7 +72,7 @@ def test_config_shapes_take_the_expected_kernels():
     assert plan(torch.bfloat16, (768, 1024, 8), 2)["kernel_name"] == "tiled"
     assert plan(torch.float32, (768, 1024, 8), 2)["kernel_name"] == "tiled"
     p = plan(torch.float32, (64, 4096, 32), 2)
-    assert p["kernel_name"] == "columns" and p["split"] > 1 and p["launches"] == 2
+    assert p["kernel_name"] == "columns" and p["split"] > 1 and p["launches"] == 1
     p = plan(torch.float32, (8192, 8192), 2)
     assert p["kernel_name"] == "columns"
     assert plan(torch.float32, (8192, 8192), 1)["kernel_name"] == "row"
@@ -202,6 +204,17 @@ def test_reduce_dims_validation(args, code):
                            strides, args.get("mask", 0b10), None, args.get("mode", 0),
                            args.get("out_ptr", FAKE + 4096), FAKE + 8192, None)
     assert rc == code
+
+
+def test_fused_finish_switch_changes_launch_count():
+    rk = _rk()
+    prev = rk.rk_debug_set_fused_finish(0)
+    try:
+        assert rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**8, 256).launches == 2
+        assert plan(__import__("torch").float32, (64, 4096, 32), 2)["launches"] == 2
+    finally:
+        rk.rk_debug_set_fused_finish(prev)
+    assert rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 10**8, 256).launches == (1 if prev else 2)
 
 
 def test_launch_event_hook_pairs():
