@@ -33,10 +33,14 @@
  *                      accumulator type; `init` is ignored, so an init that
  *                      was applied by an earlier call is not applied again;
  *   RK_MODE_HOST       s = *init (or identity); the GPU leaves a bare
- *                      accumulator-typed partial in the workspace, which is
- *                      copied back and finished on the host; `out` is a
- *                      HOST pointer and the call returns after the stream has
- *                      drained.  Valid only when there is a single output.
+ *                      accumulator-typed partial in a small pinned host
+ *                      buffer the library keeps per host thread (or, without
+ *                      one, in the workspace, copied back), and the host
+ *                      finishes it; `out` is a HOST pointer and the call
+ *                      returns after the stream has drained.  Valid only when
+ *                      there is a single output.  Setting the environment
+ *                      variable RK_HOST_COPY before the first host-mode call
+ *                      of a thread selects the copy.
  * `init` is applied exactly once.  Partial results keep the accumulator type
  * until the final store, which converts once to the output type (round to
  * nearest even for floating point, two's-complement wrap for integers).  The

@@ -248,17 +248,44 @@ const char *kernel_name(int k)
     return (k >= 0 && k <= 7) ? names[k] : "?";
 }
 
-// Copy the bare partial back and finish it on the host.
-int finish_on_host(int op, int acc, uint64_t init_bits, const void *ws, int grid, void *out, int out_dtype,
-                   hipStream_t st)
+// Host mode: a small pinned host buffer per host thread, which the last
+// pass writes the bare result into, so no copy has to be launched.  A
+// host-mode call returns only after its stream drained, so one buffer per
+// thread is never shared by two calls in flight.  Allocated once, kept for
+// the thread's lifetime; NULL (copy back from the workspace) if pinned
+// memory is unavailable.
+void *pinned_result()
+{
+    thread_local void *buf = nullptr;
+    thread_local bool tried = false;
+    if (!tried) {
+        tried = true;
+        // RK_HOST_COPY set: always copy back from the workspace (tests use it)
+        if (std::getenv("RK_HOST_COPY") != nullptr ||
+            hipHostMalloc(&buf, 64, hipHostMallocPortable) != hipSuccess)
+            buf = nullptr;
+    }
+    return buf;
+}
+
+// Wait for the bare partial, then finish it on the host: read it from the
+// pinned buffer the kernel wrote, or copy it back from ws[grid].
+int finish_on_host(int op, int acc, uint64_t init_bits, const Finish &fin, const void *ws, int grid, void *out,
+                   int out_dtype, hipStream_t st)
 {
     const int asz = dtype_size(acc);
     unsigned char partial[8];
-    const unsigned char *src = static_cast<const unsigned char *>(ws) + size_t(grid) * asz;
-    if (hipMemcpyAsync(partial, src, asz, hipMemcpyDeviceToHost, st) != hipSuccess)
-        return RK_ERR_HIP;
-    if (hipStreamSynchronize(st) != hipSuccess)
-        return RK_ERR_HIP;
+    if (fin.out) {
+        if (hipStreamSynchronize(st) != hipSuccess)
+            return RK_ERR_HIP;
+        std::memcpy(partial, fin.out, asz);
+    } else {
+        const unsigned char *src = static_cast<const unsigned char *>(ws) + size_t(grid) * asz;
+        if (hipMemcpyAsync(partial, src, asz, hipMemcpyDeviceToHost, st) != hipSuccess)
+            return RK_ERR_HIP;
+        if (hipStreamSynchronize(st) != hipSuccess)
+            return RK_ERR_HIP;
+    }
     host_finish(op, acc, init_bits, partial, 1, out, out_dtype);
     return RK_OK;
 }
@@ -266,7 +293,7 @@ int finish_on_host(int op, int acc, uint64_t init_bits, const void *ws, int grid
 Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, void *out)
 {
     Finish f;
-    f.out = mode == RK_MODE_HOST ? nullptr : out;
+    f.out = mode == RK_MODE_HOST ? pinned_result() : out;
     f.out_dtype = out_dtype;
     f.mode = mode;
     f.init_bits = start_bits(op, acc, init);
@@ -310,7 +337,7 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     if (rc != RK_OK)
         return rc;
     if (mode == RK_MODE_HOST)
-        return finish_on_host(op, acc, L.all.fin.init_bits, ws, a.grid, out, out_dtype, st);
+        return finish_on_host(op, acc, L.all.fin.init_bits, L.all.fin, ws, a.grid, out, out_dtype, st);
     return RK_OK;
 }
 

@@ -436,6 +436,24 @@ __device__ __forceinline__ Acc from_bits(uint64_t b)
         return bitcast<Acc>(b);
 }
 
+// Host mode: the bare result goes straight to the caller-side pinned host
+// buffer (f.out) with a system-scope store, or, when the library has no such
+// buffer, into the workspace slot ws[grid] for a copy back.
+template <class Acc>
+__device__ __forceinline__ void store_host_result(const Finish &f, Acc *ws, int grid, Acc v)
+{
+    if (f.out) {
+        if constexpr (sizeof(Acc) == 4)
+            __hip_atomic_store(static_cast<uint32_t *>(f.out), bitcast<uint32_t>(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        else
+            __hip_atomic_store(static_cast<uint64_t *>(f.out), bitcast<uint64_t>(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+    } else {
+        ws[grid] = v;
+    }
+}
+
 // The one finishing step of every last pass, for output o.
 //   OVERWRITE: out[o] = convert(op(init, v))
 //   FOLD:      out[o] = convert(op(widen(out[o]), v))
@@ -485,6 +503,11 @@ __device__ __forceinline__ T load_partial(const T *p)
         return bitcast<T>(__hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT));
 }
+
+// Keep every load of an unrolled group ahead of the arithmetic that consumes
+// it: without this the scheduler may interleave a wait (and cut the loads in
+// flight) to pair loads up for v_max3 and the like.
+__device__ __forceinline__ void issue_barrier() { __builtin_amdgcn_sched_barrier(0); }
 
 // Wait until this thread's outstanding memory operations have completed
 // (s_waitcnt with every counter at zero).

@@ -91,7 +91,7 @@ __device__ __forceinline__ void fold_partials_and_finish(Acc *ws, int grid, cons
     v = block_reduce<Op, BLOCK>(v);
     if (threadIdx.x == 0) {
         if (fin.mode == FIN_HOST)
-            ws[grid] = v;
+            store_host_result(fin, ws, grid, v);
         else
             finish_store<Op>(fin, 0, v);
     }
@@ -105,7 +105,7 @@ __device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v)
     if (a.grid == 1) {                          // the whole input in one block
         if (threadIdx.x == 0) {
             if (a.fin.mode == FIN_HOST)
-                ws[1] = v;                      // bare result for the host to finish
+                store_host_result(a.fin, ws, 1, v);   // bare result for the host to finish
             else
                 finish_store<Op>(a.fin, 0, v);
         }
@@ -149,6 +149,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
             w[u] = load16(p + u * BLOCK);
+        issue_barrier();
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             if (u & 1)
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
             if (i < a.n)
                 w[u] = load1(x + layout_offset(a.nd, a.ext, a.str, i));
         }
+        issue_barrier();
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t i = base + int64_t(u) * BLOCK;
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
                     w[u] = load16<NT>(reinterpret_cast<const u32x4 *>(x + (j + int64_t(u) * RG) * s));
+                issue_barrier();
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u) {
                     if (u & 1)
@@ -272,6 +275,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
                     w[u] = load1<NT>(x + (j + int64_t(u) * RG) * s);
+                issue_barrier();
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u) {
                     Acc e = Map::apply(InTraits<In>::template one<Acc>(w[u]));
@@ -410,6 +414,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
             w[u] = load16(body + i + u * 64);
+        issue_barrier();
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             if (u & 1)

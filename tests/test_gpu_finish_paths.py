@@ -148,3 +148,37 @@ def test_host_mode_and_fold_with_one_launch():
         torch.cuda.synchronize()
     assert abs(v - R) <= 1e-5 * R
     assert abs(float(out.item()) - (2 * R - 0.25)) <= 2e-5 * R
+
+
+def test_host_mode_copy_back_path():
+    """With RK_HOST_COPY set the bare partial is copied back from the
+    workspace instead of written to pinned host memory; same results."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import torch, reduction_primitives_amd as rk\n"
+        "from reduction_primitives_amd import workloads as W\n"
+        "x = W.uniform(5 * 10**6 + 3, -1.0, 1.0, 9500).cuda()\n"
+        "xi = W.randint(1000, -50, 50, 9501).cuda()\n"
+        "print(repr(rk.reduce_all(x, mode='host', init=0.5)))\n"
+        "print(repr(rk.reduce_all(xi, mode='host', acc=torch.int64, out_dtype=torch.int64)))\n"
+    ) % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = {}
+    for copy in (True, False):
+        env = dict(os.environ)
+        env.pop("RK_HOST_COPY", None)
+        if copy:
+            env["RK_HOST_COPY"] = "1"
+        proc = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                              timeout=240)
+        assert proc.returncode == 0, proc.stderr[-2000:]
+        res[copy] = proc.stdout.split()
+    assert res[True] == res[False]
+    x = W.uniform(5 * 10**6 + 3, -1.0, 1.0, 9500)
+    R = O.reduce_all(O.SUM, O.IDENTITY, O.F32, O.F32, raw_np(x), 0.5)
+    S = 0.5 + O.reduce_all(O.SUM, O.ABS, O.F32, O.F32, raw_np(x), 0.0)
+    assert abs(float(res[True][0]) - R) <= 1e-5 * S
+    xi = W.randint(1000, -50, 50, 9501)
+    assert int(res[True][1]) == int(xi.long().sum())
