@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <mutex>
 #include <cstdio>
@@ -264,20 +265,51 @@ void *pinned_result()
         if (std::getenv("RK_HOST_COPY") != nullptr ||
             hipHostMalloc(&buf, 64, hipHostMallocPortable) != hipSuccess)
             buf = nullptr;
+        else
+            std::memset(buf, 0, 64);            // sequence numbers start at 1
     }
     return buf;
 }
 
-// Wait for the bare partial, then finish it on the host: read it from the
-// pinned buffer the kernel wrote, or copy it back from ws[grid].
+// Wait for the bare partial, then finish it on the host.  With the pinned
+// buffer the kernel stores the result and then this call's sequence number;
+// spinning on that number returns as soon as the result has landed, without
+// the wake-up latency of a blocking stream wait.  The spin checks the stream
+// for errors and gives way to a blocking wait after kSpinMicros.  Without the
+// buffer the partial is copied back from ws[grid].
+constexpr int64_t kSpinMicros = 200;
+
 int finish_on_host(int op, int acc, uint64_t init_bits, const Finish &fin, const void *ws, int grid, void *out,
                    int out_dtype, hipStream_t st)
 {
     const int asz = dtype_size(acc);
     unsigned char partial[8];
     if (fin.out) {
-        if (hipStreamSynchronize(st) != hipSuccess)
-            return RK_ERR_HIP;
+        const volatile uint32_t *seq = reinterpret_cast<const volatile uint32_t *>(
+            static_cast<const char *>(fin.out) + 8);
+        const auto t0 = std::chrono::steady_clock::now();
+        bool arrived = false;
+        for (uint32_t i = 1; !arrived; ++i) {
+            if (*seq == fin.host_seq) {
+                arrived = true;
+                break;
+            }
+            if ((i & 255) == 0) {
+                const hipError_t q = hipStreamQuery(st);
+                if (q != hipSuccess && q != hipErrorNotReady)
+                    return RK_ERR_HIP;
+                if (q == hipSuccess || std::chrono::steady_clock::now() - t0 >
+                                           std::chrono::microseconds(kSpinMicros))
+                    break;
+            }
+        }
+        if (!arrived) {
+            if (hipStreamSynchronize(st) != hipSuccess)
+                return RK_ERR_HIP;
+            if (*seq != fin.host_seq)
+                return RK_ERR_HIP;                 // the kernel finished without a result
+        }
+        std::atomic_thread_fence(std::memory_order_acquire);
         std::memcpy(partial, fin.out, asz);
     } else {
         const unsigned char *src = static_cast<const unsigned char *>(ws) + size_t(grid) * asz;
@@ -294,6 +326,13 @@ Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, v
 {
     Finish f;
     f.out = mode == RK_MODE_HOST ? pinned_result() : out;
+    f.host_seq = 0;
+    if (mode == RK_MODE_HOST && f.out) {
+        // a fresh sequence number per host-mode call of this thread
+        thread_local uint32_t seq = 0;
+        seq = seq + 1 == 0 ? 1 : seq + 1;
+        f.host_seq = seq;
+    }
     f.out_dtype = out_dtype;
     f.mode = mode;
     f.init_bits = start_bits(op, acc, init);

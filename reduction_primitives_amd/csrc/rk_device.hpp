@@ -436,9 +436,10 @@ __device__ __forceinline__ Acc from_bits(uint64_t b)
         return bitcast<Acc>(b);
 }
 
-// Host mode: the bare result goes straight to the caller-side pinned host
-// buffer (f.out) with a system-scope store, or, when the library has no such
-// buffer, into the workspace slot ws[grid] for a copy back.
+// Host mode: the bare result goes straight to the library's pinned host
+// buffer (f.out) with a system-scope store, followed -- once that store has
+// completed -- by the call's sequence number at byte 8, which the host waits
+// for.  Without such a buffer the result goes to ws[grid] for a copy back.
 template <class Acc>
 __device__ __forceinline__ void store_host_result(const Finish &f, Acc *ws, int grid, Acc v)
 {
@@ -449,6 +450,9 @@ __device__ __forceinline__ void store_host_result(const Finish &f, Acc *ws, int 
         else
             __hip_atomic_store(static_cast<uint64_t *>(f.out), bitcast<uint64_t>(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_SYSTEM);
+        __builtin_amdgcn_s_waitcnt(0);
+        __hip_atomic_store(reinterpret_cast<uint32_t *>(static_cast<char *>(f.out) + 8), f.host_seq,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     } else {
         ws[grid] = v;
     }

@@ -597,7 +597,7 @@ int run_typed(const Launch &L)
         break;
     }
     case K_ROW:
-        launch_first(&k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, tune::kDimsUnroll>, grid, block, st, L,
+        launch_first(&k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, tune::kRowUnroll>, grid, block, st, L,
                      L.dims);
         split = L.dims.split;
         break;

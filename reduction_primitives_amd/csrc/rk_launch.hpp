@@ -20,10 +20,11 @@ constexpr int kArriveSlots = 32;
 constexpr int kArriveCapacity = 4096;
 
 struct Finish {
-    void *out;            // device output (OVERWRITE / FOLD)
+    void *out;            // device output (OVERWRITE / FOLD); HOST: pinned host result buffer or NULL
     int out_dtype;
     int mode;             // FinishMode
     uint64_t init_bits;   // starting value, accumulator bits (identity when no init)
+    uint32_t host_seq;    // HOST with a result buffer: stored after the result, at byte 8
 };
 
 struct AllArgs {

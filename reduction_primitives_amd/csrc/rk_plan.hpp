@@ -50,7 +50,8 @@ constexpr int kAllSingleLaunchTiles = 2;  // <= this many tiles: one launch
 constexpr int kPass2Block = 256;          // threads of the one-block second pass
 // dims
 constexpr int kDimsBlock = 256;           // row and generic kernels
-constexpr int kDimsUnroll = 8;            // loads in flight per thread
+constexpr int kDimsUnroll = 8;            // loads in flight per thread (tile kernels)
+constexpr int kRowUnroll = 16;            // loads in flight per lane (row kernel)
 constexpr int kThreadBlock = 256;         // thread-per-output kernel
 constexpr int kTiledBlock = 1024;         // one-pass tiled kernel: 16 waves share a tile
 constexpr int kColumnsBlock = 256;        // split columns kernel
