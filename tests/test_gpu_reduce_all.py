@@ -325,3 +325,26 @@ def test_invalid_arguments_rejected_without_writing():
         assert rc in (rk.RK_ERR_INVALID_ARGUMENT, rk.RK_ERR_UNSUPPORTED), b
     torch.cuda.synchronize()
     assert out.item() == 7.0
+
+
+def test_beyond_2_31_elements():
+    """Inputs of more than 2^31 elements (8.6 GB of int32 ones): 64-bit
+    indexing in the whole-array, row and columns kernels.  Totals are closed
+    forms, so every result is exact."""
+    rk = _rk()
+    n = 2**31 + 5
+    ones = torch.ones(n, dtype=torch.int32, device=DEV)
+    total = rk.reduce_all(ones, acc=torch.int64, out_dtype=torch.int64)
+    assert int(total.item()) == n
+    v = rk.reduce_all(ones[3:], acc=torch.int64, out_dtype=torch.int64, mode="host")
+    assert v == n - 3
+    # dims=1 over three long rows (row kernel, offsets beyond 2^31 elements)
+    m = (n - 2) // 3
+    rows = rk.reduce_dims(ones, (m, 3), (1, m), 1, acc=torch.int64, out_dtype=torch.int64)
+    assert rows.cpu().tolist() == [m, m, m]
+    # dims=2 over a strided dim whose last rows sit past 2^31 elements (columns kernel)
+    L, k = 1 << 16, (n // (1 << 16))
+    cols = rk.reduce_dims(ones, (L, k), (1, L), 2, acc=torch.int64, out_dtype=torch.int64)
+    assert bool((cols == k).all().item())
+    del ones
+    torch.cuda.empty_cache()
