@@ -27,6 +27,7 @@ import numpy as np
 
 SUM, MAX, MIN = 0, 1, 2
 IDENTITY, SQUARE, ABS = 0, 1, 2
+MUL, SQDIFF, ABSDIFF = 0, 1, 2          # two-input maps f(a, b)
 F32, BF16, F16, F64, I32, I64 = 0, 1, 2, 3, 4, 5
 OVERWRITE, FOLD, HOST = 0, 1, 2
 
@@ -71,13 +72,15 @@ def _load():
     lib.rko_identity_int.argtypes, lib.rko_identity_int.restype = [i32, i32], i64
     lib.rko_all_fp.argtypes = [i32, i32, i32, vp, i64, dbl, vp]
     lib.rko_all_int.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp]
+    lib.rko_all2_fp.argtypes = [i32, i32, i32, vp, vp, i64, dbl, vp]
+    lib.rko_all2_int.argtypes = [i32, i32, i32, i32, vp, vp, i64, i64, vp]
     lib.rko_dims_fp.argtypes = [i32, i32, i32, vp, i32, vp, vp, u32, vp, vp]
     lib.rko_dims_int.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, u32, vp, vp]
     lib.rko_cast_fp.argtypes = [i32, vp, i64, vp]
     lib.rko_cast_int.argtypes = [i32, vp, i64, vp]
     lib.rko_widen_fp.argtypes = [i32, vp, i64, vp]
     lib.rko_widen_int.argtypes = [i32, vp, i64, vp]
-    for name in ("rko_all_fp", "rko_all_int", "rko_dims_fp", "rko_dims_int",
+    for name in ("rko_all_fp", "rko_all_int", "rko_all2_fp", "rko_all2_int", "rko_dims_fp", "rko_dims_int",
                  "rko_cast_fp", "rko_cast_int", "rko_widen_fp", "rko_widen_int"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -136,6 +139,39 @@ def reduce_all(op: int, map_: int, in_dtype: int, acc_dtype: int,
     if rc:
         raise ValueError("oracle rejected arguments")
     return int(out[0])
+
+
+def reduce_all2(op: int, map2: int, in_dtype: int, acc_dtype: int, a: np.ndarray,
+                b: np.ndarray, start):
+    """Sequential fold of f(a_i, b_i) over two contiguous 1-d arrays."""
+    lib = _load()
+    a = np.ascontiguousarray(_raw(a, in_dtype)).reshape(-1)
+    b = np.ascontiguousarray(_raw(b, in_dtype)).reshape(-1)
+    if a.size != b.size:
+        raise ValueError("inputs differ in length")
+    if is_fp(in_dtype):
+        out = np.zeros(1, np.float64)
+        rc = lib.rko_all2_fp(op, map2, in_dtype, _ptr(a), _ptr(b), a.size, float(start), _ptr(out))
+        if rc:
+            raise ValueError("oracle rejected arguments")
+        return float(out[0])
+    out = np.zeros(1, np.int64)
+    rc = lib.rko_all2_int(op, map2, in_dtype, acc_dtype, _ptr(a), _ptr(b), a.size,
+                          wrap_int(int(start), I64), _ptr(out))
+    if rc:
+        raise ValueError("oracle rejected arguments")
+    return int(out[0])
+
+
+def expected_all2(op, map2, in_dtype, acc_dtype, out_dtype, a, b, mode, init=None, prev=None):
+    """(wide result, raw stored output) of a two-input whole-array reduction."""
+    s = start_value(op, acc_dtype, out_dtype, mode, init, prev)
+    if mode == FOLD:
+        s = s[0]
+    r = reduce_all2(op, map2, in_dtype, acc_dtype, a, b, s)
+    if not is_fp(acc_dtype):
+        r = wrap_int(r, acc_dtype)
+    return r, cast(out_dtype, [r])
 
 
 def reduce_dims(op: int, map_: int, in_dtype: int, acc_dtype: int,

@@ -15,6 +15,9 @@
  *   - PR #176 (strided reductions along dims), section "This PR": the same
  *     fold for each output of a reduction along one or more dimensions of a
  *     column-major array.
+ *   - PR #139, "What changes" and the test list under "Compatibility": the
+ *     source may be a lazy broadcast, here of two arrays, f(a_i, b_i), folded
+ *     the same way (rko_all2_*).
  * The GPU path reaches the same exact value by re-associating the fold; the
  * pages state that only rounding may differ when the reduction tree changes
  * (PR #139, "Compatibility").  So this file is the definition written out:
@@ -188,6 +191,72 @@ int rko_all_int(int op, int map, int in_dtype, int acc_dtype, const void *x,
     int64_t acc = start;
     for (int64_t i = 0; i < n; ++i)
         acc = op_int(op, acc, map_int(map, acc_dtype, load_int(in_dtype, x, i)));
+    *result = wrap_to(acc_dtype, acc);
+    return 0;
+}
+
+/* ------------------------------------------------- two-input (fused) source */
+
+/*
+ * Whole-array reduction of a fused two-input source, f(a_i, b_i): the
+ * broadcast of two arrays that AcceleratedKernels.jl PR #139 ("What
+ * changes", last paragraph, and its test list) routes to the whole-array
+ * path.  f is a*b, (a-b)^2 or |a-b|, evaluated after widening both
+ * elements: in double for floating point, in the accumulator type (with
+ * wrap-around) for integers.  Same left-to-right fold as rko_all_*.
+ */
+enum { M2_MUL = 0, M2_SQDIFF = 1, M2_ABSDIFF = 2 };
+
+static double map2_fp(int map2, double a, double b)
+{
+    switch (map2) {
+    case M2_MUL: return a * b;
+    case M2_SQDIFF: return (a - b) * (a - b);
+    case M2_ABSDIFF: return fabs(a - b);
+    }
+    return NAN;
+}
+
+static int64_t map2_int(int map2, int acc_dtype, int64_t a, int64_t b)
+{
+    uint64_t ua = (uint64_t)wrap_to(acc_dtype, a), ub = (uint64_t)wrap_to(acc_dtype, b), r = 0;
+    int64_t d;
+    switch (map2) {
+    case M2_MUL: r = ua * ub; break;
+    case M2_SQDIFF:
+        d = wrap_to(acc_dtype, (int64_t)(ua - ub));
+        r = (uint64_t)d * (uint64_t)d;
+        break;
+    case M2_ABSDIFF:
+        d = wrap_to(acc_dtype, (int64_t)(ua - ub));
+        r = d < 0 ? (uint64_t)0 - (uint64_t)d : (uint64_t)d;
+        break;
+    }
+    return wrap_to(acc_dtype, (int64_t)r);
+}
+
+int rko_all2_fp(int op, int map2, int in_dtype, const void *a, const void *b, int64_t n,
+                double start, double *result)
+{
+    if (!is_fp_dtype(in_dtype) || n < 0 || (n > 0 && (!a || !b)) || !result)
+        return -1;
+    double acc = start;
+    for (int64_t i = 0; i < n; ++i)
+        acc = op_fp(op, acc, map2_fp(map2, load_fp(in_dtype, a, i), load_fp(in_dtype, b, i)));
+    *result = acc;
+    return 0;
+}
+
+int rko_all2_int(int op, int map2, int in_dtype, int acc_dtype, const void *a, const void *b,
+                 int64_t n, int64_t start, int64_t *result)
+{
+    if (!is_int_dtype(in_dtype) || !is_int_dtype(acc_dtype) || n < 0 ||
+        (n > 0 && (!a || !b)) || !result)
+        return -1;
+    int64_t acc = start;
+    for (int64_t i = 0; i < n; ++i)
+        acc = op_int(op, acc, map2_int(map2, acc_dtype, load_int(in_dtype, a, i),
+                                       load_int(in_dtype, b, i)));
     *result = wrap_to(acc_dtype, acc);
     return 0;
 }

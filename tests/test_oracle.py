@@ -419,3 +419,72 @@ def test_golden(case):
         assert got == c["expected"]
         if "expected_bits" in c:
             assert int(raw.view(np.uint16)[0]) == c["expected_bits"]
+
+
+# ------------------------------------------------- two-input fused sources
+
+def test_two_input_closed_forms():
+    o = _o()
+    n = 2000
+    a = np.arange(1, n + 1, dtype=np.int32)
+    b = np.arange(2, n + 2, dtype=np.int32)
+    assert o.reduce_all2(o.SUM, o.MUL, o.I32, o.I64, a, a, 0) == n * (n + 1) * (2 * n + 1) // 6
+    assert o.reduce_all2(o.SUM, o.SQDIFF, o.I32, o.I64, a, b, 0) == n
+    assert o.reduce_all2(o.SUM, o.ABSDIFF, o.I32, o.I64, b, a, 7) == n + 7
+    c = (n - a).astype(np.int32)                      # sum i (n - i) = n * n(n+1)/2 - n(n+1)(2n+1)/6
+    assert o.reduce_all2(o.SUM, o.MUL, o.I32, o.I64, a, c, 0) == \
+        n * n * (n + 1) // 2 - n * (n + 1) * (2 * n + 1) // 6
+    af = a.astype(np.float32)
+    assert o.reduce_all2(o.SUM, o.MUL, o.F32, o.F32, af, af, 0.0) == float(n * (n + 1) * (2 * n + 1) // 6)
+    p = _rng(40).permutation(n).astype(np.int32)
+    ones = np.ones(n, np.int32)
+    assert o.reduce_all2(o.MAX, o.MUL, o.I32, o.I32, p, ones, o.identity(o.MAX, o.I32)) == n - 1
+    assert o.reduce_all2(o.MIN, o.MUL, o.I32, o.I32, p, ones, o.identity(o.MIN, o.I32)) == 0
+
+
+def test_two_input_dot_against_numpy():
+    o = _o()
+    rng = _rng(41)
+    a = rng.standard_normal(50_000).astype(np.float32)
+    b = rng.standard_normal(50_000).astype(np.float32)
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    r = o.reduce_all2(o.SUM, o.MUL, o.F32, o.F32, a, b, 0.0)
+    S = float(np.abs(a64 * b64).sum())
+    assert abs(r - float(np.dot(a64, b64))) <= 2 * a.size * U53 * S
+    ai = rng.integers(-2**20, 2**20, 50_000).astype(np.int32)
+    bi = rng.integers(-2**20, 2**20, 50_000).astype(np.int32)
+    assert o.reduce_all2(o.SUM, o.MUL, o.I32, o.I64, ai, bi, 0) == int(np.dot(ai.astype(np.int64), bi.astype(np.int64)))
+
+
+def test_two_input_identities_exact():
+    """(a-b)^2 = a^2 - 2ab + b^2 and, for a >= b, |a-b| = a - b, checked
+    against exact rational sums of other oracle paths and of the data."""
+    o = _o()
+    rng = _rng(42)
+    a = rng.uniform(-1, 1, 500).astype(np.float32)
+    b = rng.uniform(-1, 1, 500).astype(np.float32)
+    fa = [Fraction(float(v)) for v in a]
+    fb = [Fraction(float(v)) for v in b]
+    exact_sq = sum(x * x for x in fa) - 2 * sum(x * y for x, y in zip(fa, fb)) + sum(y * y for y in fb)
+    r = o.reduce_all2(o.SUM, o.SQDIFF, o.F32, o.F32, a, b, 0.0)
+    S = float(sum((x - y) * (x - y) for x, y in zip(fa, fb)))
+    assert abs(Fraction(r) - exact_sq) <= Fraction(4 * a.size * U53 * S)
+    hi, lo = np.maximum(a, b), np.minimum(a, b)
+    r = o.reduce_all2(o.SUM, o.ABSDIFF, o.F32, o.F32, hi, lo, 0.0)
+    exact = sum(Fraction(float(v)) for v in hi) - sum(Fraction(float(v)) for v in lo)
+    assert abs(Fraction(r) - exact) <= Fraction(4 * a.size * U53 * float(exact))
+    # |a - 0| folds like the one-input abs map
+    z = np.zeros_like(a)
+    assert o.reduce_all2(o.SUM, o.ABSDIFF, o.F32, o.F32, a, z, 0.0) == \
+        o.reduce_all(o.SUM, o.ABS, o.F32, o.F32, a, 0.0)
+
+
+def test_two_input_maps_wrap_in_int32():
+    o = _o()
+    a = np.array([65536, 3], np.int32)
+    assert o.reduce_all2(o.SUM, o.MUL, o.I32, o.I32, a, a, 0) == 9          # 2^32 wraps to 0
+    assert o.reduce_all2(o.SUM, o.MUL, o.I32, o.I64, a, a, 0) == 2**32 + 9
+    a = np.array([2**31 - 1], np.int32)
+    b = np.array([-1], np.int32)
+    assert o.reduce_all2(o.SUM, o.ABSDIFF, o.I32, o.I32, a, b, 0) == -2**31   # 2^31 wraps
+    assert o.reduce_all2(o.SUM, o.ABSDIFF, o.I32, o.I64, a, b, 0) == 2**31

@@ -40,6 +40,11 @@ MUTANTS = [
     ("dims_out_index", "out_stride[d] = no;\n            no *= shape[d];",
      "no *= shape[d];\n            out_stride[d] = no - 1;"),
     ("dims_int_no_wrap", "result[o] = wrap_to(acc_dtype, result[o]);", "(void)0;"),
+    ("map2_mul_is_add", "case M2_MUL: return a * b;", "case M2_MUL: return a + b;"),
+    ("map2_sqdiff_sign", "case M2_SQDIFF: return (a - b) * (a - b);", "case M2_SQDIFF: return (a + b) * (a - b);"),
+    ("map2_absdiff_no_abs", "case M2_ABSDIFF: return fabs(a - b);", "case M2_ABSDIFF: return a - b;"),
+    ("map2_int_mul", "case M2_MUL: r = ua * ub; break;", "case M2_MUL: r = ua * ua; break;"),
+    ("all2_second_operand", "load_fp(in_dtype, b, i)));", "load_fp(in_dtype, a, i)));"),
 ]
 
 
