@@ -363,6 +363,18 @@ def configs_table(rk, torch, dev, reps):
             return False
         timed(name, fn, xd.numel() * xd.element_size(), plan["kernel_name"])
 
+    def pair(name, a, b, map2, **kw):
+        ws = rk.workspace_for(rk.rk_workspace_size(rk.dtype_code(a.dtype), rk.default_acc(rk.dtype_code(a.dtype)),
+                                                   1, [a.numel()], [1], 1), dev)
+        out = torch.zeros(1, dtype=a.dtype, device=dev)
+        plan = rk.rk_plan_all2(rk.dtype_code(a.dtype), rk.default_acc(rk.dtype_code(a.dtype)),
+                               a.data_ptr(), b.data_ptr(), a.numel())
+
+        def fn():
+            rk.reduce_all2(a, b, map2, workspace=ws, out=out, **kw)
+            return False
+        timed(name, fn, 2 * a.numel() * a.element_size(), "all2" if plan.vec > 1 else "all2/elt")
+
     xf, xi = W.whole_small()
     whole("1e4 f32 sum -> host", xf.data.to(dev), mode="host")
     whole("1e4 i32 sum -> int64 host", xi.data.to(dev), acc=torch.int64, out_dtype=torch.int64, mode="host")
@@ -375,6 +387,13 @@ def configs_table(rk, torch, dev, reps):
         whole(f"{n:.0e} i32 perm max", pd, op="max", acc=torch.int32, out_dtype=torch.int32)
         whole(f"{n:.0e} i32 perm min", pd, op="min", acc=torch.int32, out_dtype=torch.int32)
         del xd, pd
+    for n in (10**6, 10**8):
+        a, b = W.vector_pair(n)
+        ad, bd = a.data.to(dev), b.data.to(dev)
+        pair(f"{n:.0e} f32 dot (a*b)", ad, bd, "mul")
+        pair(f"{n:.0e} f32 squared distance", ad, bd, "sqdiff")
+        pair(f"{n:.0e} f32 dot, offsets 1 and 2", ad[1:n - 1], bd[2:], "mul")
+        del ad, bd
     bf, f32 = W.matrix_3072x2048()
     bd, fd = bf.data.to(dev), f32.data.to(dev)
     dims("3072x2048 bf16 dims=2 -> bf16", bf, bd, 2)

@@ -96,6 +96,11 @@ typedef enum { RK_OP_SUM = 0, RK_OP_MAX = 1, RK_OP_MIN = 2 } rk_op;
  * accumulator type. */
 typedef enum { RK_MAP_IDENTITY = 0, RK_MAP_SQUARE = 1, RK_MAP_ABS = 2 } rk_map;
 
+/* Two-input map f(a, b) of a fused source (rk_reduce_all2), applied after
+ * widening both elements to the accumulator type; integer forms wrap in the
+ * accumulator type. */
+typedef enum { RK_MAP2_MUL = 0, RK_MAP2_SQDIFF = 1, RK_MAP2_ABSDIFF = 2 } rk_map2;
+
 typedef enum {
     RK_F32 = 0, RK_BF16 = 1, RK_F16 = 2, RK_F64 = 3, RK_I32 = 4, RK_I64 = 5
 } rk_dtype;
@@ -137,6 +142,27 @@ int rk_reduce_all(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
                   void *workspace, void *stream);
 
 /*
+ * Whole-array reduction of a fused two-input source: R = s (+) f(a_0, b_0)
+ * (+) f(a_1, b_1) (+) ..., f one of rk_map2 -- a dot product, a squared or an
+ * absolute distance.  PR #139, "What changes": the whole-array path takes a
+ * lazy broadcast as its source, and the page's test list covers fused
+ * sources; this is the broadcast of two arrays through f, read in one pass
+ * with nothing materialised.
+ *   a, b      device pointers to n contiguous in_dtype elements each, aligned
+ *             to the element size; they may be the same array.  When both sit
+ *             at the same offset from a 16-byte boundary the pass uses 16-byte
+ *             loads, otherwise element loads (slower; rk_plan_all2 reports
+ *             vec = 1).
+ *   workspace >= rk_workspace_size(in_dtype, acc_dtype, 1, &n, &one, 1) bytes
+ *             (the one-input whole-array size for n elements), aligned to 8.
+ * op, dtypes, init, mode, out and stream as for rk_reduce_all; `out` must not
+ * alias a or b.  n = 0 gives s.  Returns an rk_status.
+ */
+int rk_reduce_all2(int op, int map2, int in_dtype, int acc_dtype, int out_dtype,
+                   const void *a, const void *b, int64_t n, const void *init, int mode,
+                   void *out, void *workspace, void *stream);
+
+/*
  * Mapped reduction along the dims in `reduce_mask` of a strided column-major
  * view with 1 <= ndim <= 4 dims (PR #176, section "This PR"; a single output
  * with a contiguous source takes the whole-array path, PR #139 "What
@@ -171,7 +197,8 @@ typedef enum {
     RK_KERNEL_TILED = 4,        /* 2-d block over a narrow tile of outputs, one pass */
     RK_KERNEL_COLUMNS = 5,      /* 2-d block over a wide tile of outputs, split along the reduced dim */
     RK_KERNEL_ROW = 6,          /* one wave per output over a contiguous reduced dim */
-    RK_KERNEL_GENERIC = 7       /* one block per output, any layout */
+    RK_KERNEL_GENERIC = 7,      /* one block per output, any layout */
+    RK_KERNEL_ALL2 = 8          /* whole-array passes over a two-input source (rk_reduce_all2) */
 } rk_kernel;
 
 typedef struct {
@@ -188,11 +215,13 @@ typedef struct {
     size_t workspace_bytes;   /* what rk_workspace_size returns for this layout */
 } rk_plan_info;
 
-/* Plan of rk_reduce_all / rk_reduce_dims for `num_cus` compute units (0 =
+/* Plan of rk_reduce_all / rk_reduce_all2 / rk_reduce_dims for `num_cus` compute units (0 =
  * the current device), without launching.  `ptr` only matters through its
  * alignment.  Returns an rk_status. */
 int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num_cus,
                 rk_plan_info *info);
+int rk_plan_all2(int in_dtype, int acc_dtype, const void *a, const void *b, int64_t n, int num_cus,
+                 rk_plan_info *info);
 int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const int64_t *shape,
                  const int64_t *strides, uint32_t reduce_mask, int num_cus,
                  rk_plan_info *info);

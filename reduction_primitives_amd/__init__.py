@@ -1,9 +1,9 @@
 """Device-wide mapreduce for AMD Instinct MI355X (gfx950).
 
-Python face of librk.so.  ``rk_reduce_all``, ``rk_reduce_dims``,
+Python face of librk.so.  ``rk_reduce_all``, ``rk_reduce_all2``, ``rk_reduce_dims``,
 ``rk_workspace_size`` and the plan/diagnostic calls keep the C ABI's names
 (see include/rk.h); ``reduce_all`` and ``reduce_dims`` below only marshal torch
-tensors into those calls -- pick dtype codes, allocate the output and the
+tensors into those calls (``reduce_all2`` for a two-input source) -- pick dtype codes, allocate the output and the
 workspace with torch, pass the current HIP stream.  All arithmetic happens
 in the library's kernels; there is no fallback path.
 """
@@ -15,14 +15,16 @@ import math
 from ._native import (  # noqa: F401
     EXPORTS, KERNEL_NAMES, LIB_PATH, RK_BF16, RK_ERR_HIP, RK_ERR_INVALID_ARGUMENT,
     RK_ERR_UNSUPPORTED, RK_F16, RK_F32, RK_F64, RK_I32, RK_I64, RK_KERNEL_ALL,
-    RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE, RK_KERNEL_ROW,
-    RK_KERNEL_THREAD, RK_KERNEL_TILED, RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
+    RK_KERNEL_ALL2, RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE,
+    RK_KERNEL_ROW, RK_KERNEL_THREAD, RK_KERNEL_TILED, RK_MAP2_ABSDIFF, RK_MAP2_MUL, RK_MAP2_SQDIFF,
+    RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
     RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,
-    RkError, load, rk_debug_set_fused_finish, rk_debug_set_launch_events, rk_plan_all, rk_plan_dims, rk_plan_info,
-    rk_reduce_all, rk_reduce_dims, rk_workspace_size, status_string)
+    RkError, load, rk_debug_set_fused_finish, rk_debug_set_launch_events, rk_plan_all, rk_plan_all2, rk_plan_dims,
+    rk_plan_info, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_workspace_size, status_string)
 
 OPS = {"sum": RK_OP_SUM, "max": RK_OP_MAX, "min": RK_OP_MIN}
 MAPS = {"identity": RK_MAP_IDENTITY, "square": RK_MAP_SQUARE, "abs": RK_MAP_ABS}
+MAPS2 = {"mul": RK_MAP2_MUL, "sqdiff": RK_MAP2_SQDIFF, "absdiff": RK_MAP2_ABSDIFF}
 MODES = {"overwrite": RK_MODE_OVERWRITE, "fold": RK_MODE_FOLD, "host": RK_MODE_HOST}
 DTYPE_SIZE = {RK_F32: 4, RK_BF16: 2, RK_F16: 2, RK_F64: 8, RK_I32: 4, RK_I64: 8}
 _CTYPE = {RK_F32: ctypes.c_float, RK_F64: ctypes.c_double, RK_I32: ctypes.c_int32,
@@ -128,6 +130,41 @@ def reduce_all(x, op="sum", map="identity", acc=None, out_dtype=None, init=None,
     rc = rk_reduce_all(op_c, map_c, in_code, acc_code, out_code, x.data_ptr(), n,
                        init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
     _check(rc, "rk_reduce_all")
+    return out
+
+
+def reduce_all2(a, b, map2="mul", op="sum", acc=None, out_dtype=None, init=None,
+                mode="overwrite", out=None, workspace=None, stream=None):
+    """Whole-array reduction of f(a_i, b_i) over two contiguous device
+    tensors of one dtype and size (map2: "mul", "sqdiff" or "absdiff").
+    Returns `out` (device modes) or a Python value (host mode)."""
+    torch = _torch()
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("reduce_all2 takes contiguous tensors")
+    if a.dtype != b.dtype or a.numel() != b.numel():
+        raise ValueError("reduce_all2 takes two tensors of one dtype and size")
+    in_code = dtype_code(a.dtype)
+    acc_code = default_acc(in_code) if acc is None else dtype_code(acc)
+    out_code = in_code if out_dtype is None else dtype_code(out_dtype)
+    if out_code in (RK_I32, RK_I64) and in_code in (RK_I32, RK_I64) and out_dtype is None:
+        out_code = acc_code
+    op_c, map_c, mode_c = _code(OPS, op), _code(MAPS2, map2), _code(MODES, mode)
+    n = a.numel()
+    if workspace is None:
+        workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), a.device)
+    st = _stream_handle(stream)
+    if mode_c == RK_MODE_HOST:
+        buf = _CTYPE[out_code]()
+        rc = rk_reduce_all2(op_c, map_c, in_code, acc_code, out_code, a.data_ptr(), b.data_ptr(), n,
+                            init_arg(acc_code, init), mode_c, ctypes.addressof(buf),
+                            workspace.data_ptr(), st)
+        _check(rc, "rk_reduce_all2")
+        return decode_host_out(buf, out_code)
+    if out is None:
+        out = torch.empty(1, dtype=torch_dtype(out_code), device=a.device)
+    rc = rk_reduce_all2(op_c, map_c, in_code, acc_code, out_code, a.data_ptr(), b.data_ptr(), n,
+                        init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
+    _check(rc, "rk_reduce_all2")
     return out
 
 

@@ -16,16 +16,18 @@ LIB_PATH = os.path.join(_HERE, "librk.so")
 RK_OK, RK_ERR_INVALID_ARGUMENT, RK_ERR_UNSUPPORTED, RK_ERR_HIP = 0, 1, 2, 3
 RK_OP_SUM, RK_OP_MAX, RK_OP_MIN = 0, 1, 2
 RK_MAP_IDENTITY, RK_MAP_SQUARE, RK_MAP_ABS = 0, 1, 2
+RK_MAP2_MUL, RK_MAP2_SQDIFF, RK_MAP2_ABSDIFF = 0, 1, 2
 RK_F32, RK_BF16, RK_F16, RK_F64, RK_I32, RK_I64 = 0, 1, 2, 3, 4, 5
 RK_MODE_OVERWRITE, RK_MODE_FOLD, RK_MODE_HOST = 0, 1, 2
 (RK_KERNEL_NONE, RK_KERNEL_ALL, RK_KERNEL_ALL_STRIDED, RK_KERNEL_THREAD, RK_KERNEL_TILED,
- RK_KERNEL_COLUMNS, RK_KERNEL_ROW, RK_KERNEL_GENERIC) = range(8)
+ RK_KERNEL_COLUMNS, RK_KERNEL_ROW, RK_KERNEL_GENERIC, RK_KERNEL_ALL2) = range(9)
 KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 5: "columns",
-                6: "row", 7: "generic"}
+                6: "row", 7: "generic", 8: "all2"}
 
 # every function include/rk.h declares
-EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_dims", "rk_status_string",
-           "rk_plan_all", "rk_plan_dims", "rk_debug_set_fused_finish", "rk_debug_set_launch_events")
+EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_dims", "rk_status_string",
+           "rk_plan_all", "rk_plan_all2", "rk_plan_dims", "rk_debug_set_fused_finish",
+           "rk_debug_set_launch_events")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -64,12 +66,16 @@ def load() -> ctypes.CDLL:
     lib.rk_workspace_size.restype = sz
     lib.rk_reduce_all.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, i32, vp, vp, vp]
     lib.rk_reduce_all.restype = i32
+    lib.rk_reduce_all2.argtypes = [i32, i32, i32, i32, i32, vp, vp, i64, vp, i32, vp, vp, vp]
+    lib.rk_reduce_all2.restype = i32
     lib.rk_reduce_dims.argtypes = [i32, i32, i32, i32, i32, vp, i32, p64, p64, u32, vp, i32, vp, vp, vp]
     lib.rk_reduce_dims.restype = i32
     lib.rk_status_string.argtypes = [i32]
     lib.rk_status_string.restype = ctypes.c_char_p
     lib.rk_plan_all.argtypes = [i32, i32, vp, i64, i32, ctypes.POINTER(rk_plan_info)]
     lib.rk_plan_all.restype = i32
+    lib.rk_plan_all2.argtypes = [i32, i32, vp, vp, i64, i32, ctypes.POINTER(rk_plan_info)]
+    lib.rk_plan_all2.restype = i32
     lib.rk_plan_dims.argtypes = [i32, i32, vp, i32, p64, p64, u32, i32, ctypes.POINTER(rk_plan_info)]
     lib.rk_plan_dims.restype = i32
     lib.rk_debug_set_fused_finish.argtypes = [i32]
@@ -101,6 +107,12 @@ def rk_reduce_all(op, map_, in_dtype, acc_dtype, out_dtype, ptr, n, init, mode, 
                                     out, workspace, stream))
 
 
+def rk_reduce_all2(op, map2, in_dtype, acc_dtype, out_dtype, a, b, n, init, mode, out, workspace,
+                   stream) -> int:
+    return int(load().rk_reduce_all2(op, map2, in_dtype, acc_dtype, out_dtype, a, b, n, init, mode,
+                                     out, workspace, stream))
+
+
 def rk_reduce_dims(op, map_, in_dtype, acc_dtype, out_dtype, ptr, ndim, shape, strides,
                    reduce_mask, init, mode, out, workspace, stream) -> int:
     return int(load().rk_reduce_dims(op, map_, in_dtype, acc_dtype, out_dtype, ptr, ndim,
@@ -113,6 +125,14 @@ def rk_plan_all(in_dtype, acc_dtype, ptr, n, num_cus=0) -> rk_plan_info:
     rc = load().rk_plan_all(in_dtype, acc_dtype, ptr, n, num_cus, ctypes.byref(info))
     if rc:
         raise RkError(rc, "rk_plan_all")
+    return info
+
+
+def rk_plan_all2(in_dtype, acc_dtype, a, b, n, num_cus=0) -> rk_plan_info:
+    info = rk_plan_info()
+    rc = load().rk_plan_all2(in_dtype, acc_dtype, a, b, n, num_cus, ctypes.byref(info))
+    if rc:
+        raise RkError(rc, "rk_plan_all2")
     return info
 
 

@@ -245,8 +245,9 @@ int dispatch(int in_dtype, const Launch &L)
 
 const char *kernel_name(int k)
 {
-    static const char *names[] = {"none", "all", "all_strided", "thread", "tiled", "columns", "row", "generic"};
-    return (k >= 0 && k <= 7) ? names[k] : "?";
+    static const char *names[] = {"none", "all", "all_strided", "thread", "tiled", "columns", "row", "generic",
+                                  "all2"};
+    return (k >= 0 && k <= 8) ? names[k] : "?";
 }
 
 // Host mode: a small pinned host buffer per host thread, which the last
@@ -341,7 +342,7 @@ Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, v
 
 int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, const AllPlan &a,
               int kernel, const Layout *red, const void *init, int mode, void *out, void *ws,
-              hipStream_t st)
+              hipStream_t st, const void *ptr2 = nullptr)
 {
     Launch L;
     std::memset(&L, 0, sizeof L);
@@ -354,6 +355,7 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     L.grid = a.grid;
     L.block = a.block;
     L.all.x = ptr;
+    L.all.y = ptr2;
     L.all.n = a.n;
     L.all.head = a.head;
     L.all.nvec = a.nvec;
@@ -433,6 +435,32 @@ int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num
     return RK_OK;
 }
 
+int rk_plan_all2(int in_dtype, int acc_dtype, const void *a, const void *b, int64_t n, int num_cus,
+                 rk_plan_info *info)
+{
+    if (!info || !dtype_known(in_dtype) || !dtype_known(acc_dtype) || n < 0)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (num_cus <= 0)
+        num_cus = device_cus();
+    AllPlan p;
+    int rc = plan_all2(in_dtype, acc_dtype, reinterpret_cast<uintptr_t>(a), reinterpret_cast<uintptr_t>(b), n,
+                       num_cus, &p);
+    if (rc)
+        return rc;
+    std::memset(info, 0, sizeof *info);
+    info->kernel = RK_KERNEL_ALL2;
+    info->launches = (p.grid > 1 && g_fused_finish.load()) ? 1 : p.launches;
+    info->grid = p.grid;
+    info->block = p.block;
+    info->split = 1;
+    info->vec = p.vec;
+    info->tile_outputs = 1;
+    info->n_out = 1;
+    info->reduce_len = n;
+    info->workspace_bytes = p.ws_bytes;
+    return RK_OK;
+}
+
 int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const int64_t *shape,
                  const int64_t *strides, uint32_t reduce_mask, int num_cus, rk_plan_info *info)
 {
@@ -497,6 +525,36 @@ int rk_reduce_all(int op, int map, int in_dtype, int acc_dtype, int out_dtype, c
                      a.launches);
     return run_whole(op, map, in_dtype, acc_dtype, out_dtype, ptr, a, K_ALL, nullptr, init, mode, out, workspace,
                      st);
+}
+
+int rk_reduce_all2(int op, int map2, int in_dtype, int acc_dtype, int out_dtype, const void *a, const void *b,
+                   int64_t n, const void *init, int mode, void *out, void *workspace, void *stream)
+{
+    int rc = check_types(op, map2, in_dtype, acc_dtype, out_dtype, mode);
+    if (rc)
+        return rc;
+    if (n < 0 || (n > 0 && (!a || !b)) || !out || !workspace)
+        return RK_ERR_INVALID_ARGUMENT;
+    const size_t isz = dtype_size(in_dtype);
+    if (!aligned(a, isz) || !aligned(b, isz) || !aligned(out, dtype_size(out_dtype)) || !aligned(workspace, 8))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (mode != RK_MODE_HOST && (out == a || out == b))
+        return RK_ERR_INVALID_ARGUMENT;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mode == RK_MODE_HOST && n == 0) {
+        host_finish(op, acc_dtype, start_bits(op, acc_dtype, init), nullptr, 0, out, out_dtype);
+        return RK_OK;
+    }
+    AllPlan p;
+    rc = plan_all2(in_dtype, acc_dtype, reinterpret_cast<uintptr_t>(a), reinterpret_cast<uintptr_t>(b), n,
+                   device_cus(), &p);
+    if (rc)
+        return rc;
+    if (debug_enabled())
+        std::fprintf(stderr, "rk_reduce_all2: n=%lld grid=%d block=%d vec=%d head=%lld nvec=%lld tail=%lld\n",
+                     (long long)n, p.grid, p.block, p.vec, (long long)p.head, (long long)p.nvec, (long long)p.tail);
+    return run_whole(op, map2, in_dtype, acc_dtype, out_dtype, a, p, K_ALL2, nullptr, init, mode, out, workspace,
+                     st, b);
 }
 
 int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,

@@ -151,6 +151,47 @@ struct MapAbs {
     }
 };
 
+// Two-input maps f(a, b) of a fused source, evaluated after widening both
+// elements to the accumulator type; integer forms wrap in that type.
+struct Map2Mul {
+    template <class T> __device__ __forceinline__ static T apply(T a, T b)
+    {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            return (T)((U)a * (U)b);
+        } else {
+            return a * b;
+        }
+    }
+};
+
+struct Map2SqDiff {
+    template <class T> __device__ __forceinline__ static T apply(T a, T b)
+    {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            const U d = (U)a - (U)b;
+            return (T)(d * d);
+        } else {
+            const T d = a - b;
+            return d * d;
+        }
+    }
+};
+
+struct Map2AbsDiff {
+    template <class T> __device__ __forceinline__ static T apply(T a, T b)
+    {
+        if constexpr (std::is_integral_v<T>) {
+            using U = std::make_unsigned_t<T>;
+            const T d = (T)((U)a - (U)b);
+            return d < 0 ? (T)((U)0 - (U)d) : d;
+        } else {
+            return __builtin_fabs(a - b);
+        }
+    }
+};
+
 struct OpSum {
     template <class T> __device__ __forceinline__ static T identity() { return T(0); }
     template <class T> __device__ __forceinline__ static T apply(T a, T b)

@@ -3,12 +3,13 @@
 // Whole array (AcceleratedKernels.jl PR #139, "What changes"): a first pass
 // of at most a grid cap of blocks, each striding over tiles of the input with
 // several 16-byte loads in flight per thread, then a one-block second pass;
-// an input that fits one block finishes in the first pass.
+// an input that fits one block finishes in the first pass.  A fused
+// two-input source f(x_i, y_i) takes the same passes with two loads per step.
 //
 // Strided dims (PR #176, "This PR"): one tile kernel serves the selector's
 // three shapes -- one thread per output (a tile one row tall), the narrow
-// tiled block (8 outputs, one pass) and the wide columns block (32 outputs,
-// split along the reduced dim, then a second pass) -- over runs of contiguous
+// tiled block (one pass) and the wide columns block (split along the reduced
+// dim, finished by the last block to arrive or a second pass) -- over runs of contiguous
 // outputs placed by the other kept dims (the middle dim of 3-d arrays).  A
 // contiguous reduced dim takes the row kernel (one wave per output); any
 // other layout the generic kernel (one block per output).
@@ -215,6 +216,112 @@ template <class Acc, class Op, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void k_all_pass2(Acc *ws, int grid, Finish fin)
 {
     fold_partials_and_finish<Acc, Op, BLOCK>(ws, grid, fin);
+}
+
+// ========================================================= two-input source
+
+template <class In, class Acc, class Op, class Map2, int V>
+__device__ __forceinline__ void fold_vec2(Acc (&acc)[V], u32x4 wa, u32x4 wb)
+{
+    Acc ea[V], eb[V];
+    InTraits<In>::template decode<Acc>(wa, ea);
+    InTraits<In>::template decode<Acc>(wb, eb);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        acc[i] = Op::apply(acc[i], Map2::apply(ea[i], eb[i]));
+}
+
+template <class In, class Acc, class Map2>
+__device__ __forceinline__ Acc map2_one(typename InTraits<In>::S a, typename InTraits<In>::S b)
+{
+    return Map2::apply(InTraits<In>::template one<Acc>(a), InTraits<In>::template one<Acc>(b));
+}
+
+// First pass over a fused two-input source f(x_i, y_i) (PR #139: the source
+// may be a lazy broadcast).  VECTOR: x and y share their offset from a
+// 16-byte boundary, so both bodies take the one-input kernel's tiles with
+// UNROLL 16-byte loads of each input in flight.  Otherwise every element is
+// loaded on its own, 2 * UNROLL per input in flight, each wave instruction
+// still reading consecutive elements.  Same grid, epilogue and workspace as
+// the one-input pass.
+template <class In, class Acc, class Op, class Map2, int BLOCK, int UNROLL, bool VECTOR>
+__global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
+{
+    using S = typename InTraits<In>::S;
+    constexpr int V = VECTOR ? InTraits<In>::vec : 1;
+    const S *x = static_cast<const S *>(a.x);
+    const S *y = static_cast<const S *>(a.y);
+
+    Acc acc0[V], acc1[V];
+    set_identity<Acc, Op>(acc0);
+    set_identity<Acc, Op>(acc1);
+    Acc s = Op::template identity<Acc>();
+    const int64_t gtid = int64_t(blockIdx.x) * BLOCK + threadIdx.x;
+    const int64_t gthreads = int64_t(gridDim.x) * BLOCK;
+
+    if constexpr (VECTOR) {
+        const u32x4 *bx = reinterpret_cast<const u32x4 *>(x + a.head);
+        const u32x4 *by = reinterpret_cast<const u32x4 *>(y + a.head);
+        constexpr int64_t kTile = int64_t(BLOCK) * UNROLL;
+        const int64_t full = a.nvec / kTile;
+        for (int64_t t = blockIdx.x; t < full; t += gridDim.x) {
+            const int64_t off = t * kTile + threadIdx.x;
+            u32x4 wx[UNROLL], wy[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                wx[u] = load16(bx + off + u * BLOCK);
+                wy[u] = load16(by + off + u * BLOCK);
+            }
+            issue_barrier();
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (u & 1)
+                    fold_vec2<In, Acc, Op, Map2, V>(acc1, wx[u], wy[u]);
+                else
+                    fold_vec2<In, Acc, Op, Map2, V>(acc0, wx[u], wy[u]);
+            }
+        }
+        for (int64_t i = full * kTile + gtid; i < a.nvec; i += gthreads)
+            fold_vec2<In, Acc, Op, Map2, V>(acc0, load16(bx + i), load16(by + i));
+        if (gtid < a.head)
+            s = Op::apply(s, map2_one<In, Acc, Map2>(load1(x + gtid), load1(y + gtid)));
+        const int64_t t0 = a.head + a.nvec * InTraits<In>::vec;
+        if (gtid < a.tail)
+            s = Op::apply(s, map2_one<In, Acc, Map2>(load1(x + t0 + gtid), load1(y + t0 + gtid)));
+    } else {
+        constexpr int U = 2 * UNROLL;
+        const int64_t step = gthreads * U;
+        for (int64_t base = int64_t(blockIdx.x) * BLOCK * U + threadIdx.x; base < a.n; base += step) {
+            S wx[U], wy[U];
+            const bool whole = base + int64_t(U - 1) * BLOCK < a.n;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + int64_t(u) * BLOCK;
+                if (whole || i < a.n) {
+                    wx[u] = load1(x + i);
+                    wy[u] = load1(y + i);
+                }
+            }
+            issue_barrier();
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + int64_t(u) * BLOCK;
+                if (whole || i < a.n) {
+                    const Acc e = map2_one<In, Acc, Map2>(wx[u], wy[u]);
+                    if (u & 1)
+                        acc1[0] = Op::apply(acc1[0], e);
+                    else
+                        acc0[0] = Op::apply(acc0[0], e);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        acc0[i] = Op::apply(acc0[i], acc1[i]);
+    Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
+    v = block_reduce<Op, BLOCK>(v);
+    whole_epilogue<Acc, Op, BLOCK>(a, v);
 }
 
 // ======================================================================= dims
@@ -625,9 +732,51 @@ int run_typed(const Launch &L)
     return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
 }
 
+// Run a two-input call for one (In, Acc, Op, Map2).
+template <class In, class Acc, class Op, class Map2>
+int run_typed2(const Launch &L)
+{
+    hipStream_t st = static_cast<hipStream_t>(L.stream);
+    const dim3 grid((unsigned)L.grid), block(tune::kAllBlock);
+    if (L.vec > 1)
+        launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, true>, grid, block,
+                     st, L, L.all);
+    else
+        launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, false>, grid, block,
+                     st, L, L.all);
+    if (hipGetLastError() != hipSuccess)
+        return ST_HIP;
+    if (L.all.grid > 1 && L.all.arrive_slot < 0) {
+        hipLaunchKernelGGL((k_all_pass2<Acc, Op, tune::kPass2Block>), dim3(1), dim3(tune::kPass2Block), 0, st,
+                           static_cast<Acc *>(L.all.ws), L.all.grid, L.all.fin);
+        if (hipGetLastError() != hipSuccess)
+            return ST_HIP;
+    }
+    return ST_OK;
+}
+
+template <class In, class Acc, class Op>
+int run_op2(const Launch &L)
+{
+    switch (L.map) {
+    case 0: return run_typed2<In, Acc, Op, Map2Mul>(L);
+    case 1: return run_typed2<In, Acc, Op, Map2SqDiff>(L);
+    case 2: return run_typed2<In, Acc, Op, Map2AbsDiff>(L);
+    }
+    return ST_INVALID;
+}
+
 template <class In, class Acc>
 int run_acc(const Launch &L)
 {
+    if (L.kernel == K_ALL2) {
+        switch (L.op) {
+        case 0: return run_op2<In, Acc, OpSum>(L);
+        case 1: return run_op2<In, Acc, OpMax>(L);
+        case 2: return run_op2<In, Acc, OpMin>(L);
+        }
+        return ST_INVALID;
+    }
     switch (L.op) {
     case 0:
         switch (L.map) {

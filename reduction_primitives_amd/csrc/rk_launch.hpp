@@ -29,6 +29,7 @@ struct Finish {
 
 struct AllArgs {
     const void *x;        // first element
+    const void *y;        // two-input source: first element of the second input
     int64_t n;            // elements
     int64_t head;         // scalars before the 16-byte-aligned body
     int64_t nvec;         // 16-byte vectors in the body (strided variant: elements)
@@ -68,12 +69,12 @@ struct DimsArgs {
 
 struct Launch {
     int kernel;           // rk::Kernel
-    int acc, op, map;     // accumulator dtype, op and map codes
+    int acc, op, map;     // accumulator dtype, op and map codes (K_ALL2: the two-input map)
     int vec;              // elements per load of the first launch
     int lanes;            // tile kernels: lanes across a tile row
     int64_t grid;
     int block;
-    AllArgs all;          // K_ALL, K_ALL_STRIDED
+    AllArgs all;          // K_ALL, K_ALL_STRIDED, K_ALL2
     DimsArgs dims;        // other kernels
     void *stream;         // hipStream_t
     void *ev_begin;       // optional hipEvent_t pair around the first launch

@@ -65,6 +65,23 @@ int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus
     return ST_OK;
 }
 
+int plan_all2(int in_dtype, int acc_dtype, uintptr_t addr_a, uintptr_t addr_b, int64_t n, int num_cus,
+              AllPlan *p)
+{
+    AllPlan a;
+    const int rc = plan_all(in_dtype, acc_dtype, addr_a, n, num_cus, &a);
+    if (rc)
+        return rc;
+    if (((addr_a ^ addr_b) & 15) != 0) {
+        a.vec = 1;
+        a.head = 0;
+        a.nvec = n;
+        a.tail = 0;
+    }
+    *p = a;
+    return ST_OK;
+}
+
 int select_strided_kernel(int64_t run_len, int64_t n_out, int64_t m, int in_size, int num_cus)
 {
     // Rule 1: one thread per output when a row of outputs is already wide

@@ -19,7 +19,7 @@ enum Dtype { F32 = 0, BF16 = 1, F16 = 2, F64 = 3, I32 = 4, I64 = 5 };
 enum Mode { OVERWRITE = 0, FOLD = 1, HOST = 2 };
 enum Kernel {
     K_NONE = 0, K_ALL = 1, K_ALL_STRIDED = 2, K_THREAD = 3, K_TILED = 4,
-    K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7
+    K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7, K_ALL2 = 8
 };
 
 int dtype_size(int d);            // bytes per element, 0 for an unknown code
@@ -126,6 +126,14 @@ enum { ST_OK = 0, ST_INVALID = 1, ST_UNSUPPORTED = 2, ST_HIP = 3 };
 
 // Whole-array plan: n elements at address `addr`.
 int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus, AllPlan *p);
+
+// Whole-array plan of a two-input source: n elements at addr_a and at
+// addr_b.  The grid and workspace are those of plan_all() for the first
+// input.  When the two inputs sit at the same offset from a 16-byte
+// boundary both use 16-byte loads with the same head; otherwise the plan
+// takes element loads (vec = 1, no head or tail).
+int plan_all2(int in_dtype, int acc_dtype, uintptr_t addr_a, uintptr_t addr_b, int64_t n, int num_cus,
+              AllPlan *p);
 
 // Dims plan: validates the layout (1..4 dims, non-negative extents and
 // strides, mask within ndim) and normalises it before choosing a kernel.

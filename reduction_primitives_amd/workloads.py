@@ -129,3 +129,13 @@ def matrix_8192() -> list:
     return [Array("f32_u[-1,1)", uniform(n, -1.0, 1.0, 5000), shape, "U[-1,1) seed 5000"),
             Array("i32_pm2^20", randint(n, -2**20, 2**20, 5001), shape,
                   "U{-2^20..2^20} seed 5001")]
+
+
+def vector_pair(n: int) -> list:
+    """Two float32 N(0,1) vectors of n elements, the two inputs of a fused
+    source (dot product, squared and absolute distance).  PR #139 names fused
+    sources without sizes; the whole-array sizes of its "Numbers" table are
+    used (10^6, 10^8)."""
+    j = 0 if n <= 10**6 else 2
+    return [Array("f32_n01_a", normal(n, 6000 + j), (n,), f"N(0,1) seed {6000 + j}"),
+            Array("f32_n01_b", normal(n, 6001 + j), (n,), f"N(0,1) seed {6001 + j}")]

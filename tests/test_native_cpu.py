@@ -23,7 +23,7 @@ def test_library_exports_every_declared_function():
     rk = _rk()
     with open(os.path.join(ROOT, "include", "rk.h")) as f:
         header = f.read()
-    declared = set(re.findall(r"\b(rk_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(rk_[a-z0-9_]+)\s*\(", header))
     assert declared == set(rk.EXPORTS)
     lib = ctypes.CDLL(rk.LIB_PATH)
     for name in declared:
@@ -62,6 +62,20 @@ def test_whole_array_plan():
     # workspace: one accumulator per first-pass block plus the final slot
     d = rk.rk_plan_all(rk.RK_I32, rk.RK_I64, 0, 10**8, 256)
     assert d.workspace_bytes == ((1024 + 1) * 8 + 255) // 256 * 256
+
+
+def test_two_input_plan_matches_one_input_plan():
+    """Same grid and workspace as the one-input pass; 16-byte loads exactly
+    when the two inputs share their offset from a 16-byte boundary."""
+    rk = _rk()
+    for n in (0, 1, 10**4, 10**6 + 3, 10**8):
+        one = rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, n, 256)
+        two = rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 0, 0, n, 256)
+        assert (two.grid, two.workspace_bytes, two.vec) == (one.grid, one.workspace_bytes, 4)
+        assert two.kernel == rk.RK_KERNEL_ALL2
+        assert rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 16, 4, n, 256).vec == 1
+        assert rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 20, 36, n, 256).vec == 4
+        assert rk.rk_plan_all2(rk.RK_BF16, rk.RK_F32, 2, 4, n, 256).vec == 1
 
 
 def test_config_shapes_take_the_expected_kernels():
@@ -187,6 +201,22 @@ def test_reduce_all_validation(args, code):
                           args.get("acc", 0), args.get("out", 0), args.get("ptr", FAKE),
                           args.get("n", 100), None, args.get("mode", 0),
                           args.get("out_ptr", FAKE + 4096), args.get("ws", FAKE + 8192), None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(op=3), 1), (dict(map2=3), 1), (dict(mode=3), 1), (dict(in_dtype=9), 1),
+    (dict(acc=4), 2), (dict(in_dtype=4, acc=0), 2),
+    (dict(n=-1), 1), (dict(a=None), 1), (dict(b=None), 1), (dict(b=FAKE + 2), 1),
+    (dict(out_ptr=None), 1), (dict(ws=None), 1), (dict(ws=FAKE + 4), 1),
+    (dict(out_ptr=FAKE), 1), (dict(out_ptr=FAKE + 1024), 1),        # out aliases a or b
+])
+def test_reduce_all2_validation(args, code):
+    rk = _rk()
+    rc = rk.rk_reduce_all2(args.get("op", 0), args.get("map2", 0), args.get("in_dtype", 0),
+                           args.get("acc", 0), args.get("out", 0), args.get("a", FAKE),
+                           args.get("b", FAKE + 1024), args.get("n", 100), None, args.get("mode", 0),
+                           args.get("out_ptr", FAKE + 4096), args.get("ws", FAKE + 8192), None)
     assert rc == code
 
 
