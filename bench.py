@@ -402,6 +402,20 @@ def configs_table(rk, torch, dev, reps):
     dims("3072x2048 bf16 dims=1 -> bf16", bf, bd, 1)
     for arr in W.middle_dim_3d():
         dims(f"{'x'.join(map(str, arr.shape))} {arr.name.split('_')[0]} dims=2", arr, arr.data.to(dev), 2)
+    def view(name, xd, shape, strides, d):
+        plan = rk.plan_dims(xd.dtype, shape, strides, d)
+        ws = rk.workspace_for(plan["workspace_bytes"], dev)
+        out = torch.zeros(max(1, plan["n_out"]), dtype=xd.dtype, device=dev)
+
+        def fn():
+            rk.reduce_dims(xd, shape, strides, d, workspace=ws, out=out)
+            return False
+        timed(name, fn, math.prod(shape) * xd.element_size(), plan["kernel_name"])
+
+    for arr in W.general_layouts():
+        xd = arr.data.to(dev)
+        view(arr.name, xd, arr.shape, arr.view_strides, arr.dims)
+        del xd
     mf, mi = W.matrix_8192()
     md, mid = mf.data.to(dev), mi.data.to(dev)
     dims("8192x8192 f32 sum dims=2", mf, md, 2)

@@ -622,6 +622,15 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
     a.n_out = d.n_out;
     a.m = d.m;
     a.s_red = d.s_red;
+    a.row_len = d.row_len;
+    a.seg_nd = d.seg.nd;
+    for (int i = 0; i < d.seg.nd && i < 3; ++i) {
+        a.seg_ext[i] = d.seg.ext[i];
+        a.seg_str[i] = d.seg.str[i];
+    }
+    a.segs = d.segs;
+    a.segs_per_split = d.segs_per_split;
+    a.splits_per_seg = d.splits_per_seg;
     a.run_len = d.run_len;
     a.tiles_per_run = d.tiles_per_run;
     a.tiles = d.tiles;

@@ -587,6 +587,60 @@ __device__ __forceinline__ int64_t layout_offset(int nd, const int64_t *ext, con
     return off;
 }
 
+// A position in a column-major layout of nd <= 4 dims that moves forward by
+// a fixed number of elements without dividing: the position is kept as
+// mixed-radix digits, and a step adds the step's own digits with carries.
+// Set up once per thread (one division per dim), then advance() costs a few
+// adds and compares per dim.
+struct Walk {
+    int64_t idx[4];     // digits of the current linear index
+    int64_t off;        // its element offset
+    int64_t dig[4];     // digits of the step
+    int64_t step_off;   // offset change of the step without carries
+    int64_t wrap[4];    // offset change when digit d wraps: str[d+1] - ext[d] * str[d]
+
+    __device__ __forceinline__ void init(int nd, const int64_t *ext, const int64_t *str, int64_t first,
+                                         int64_t step)
+    {
+        off = 0;
+        step_off = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            idx[d] = 0;
+            dig[d] = 0;
+            wrap[d] = 0;
+            if (d < nd) {
+                const int64_t q = first / ext[d];
+                idx[d] = first - q * ext[d];
+                first = q;
+                off += idx[d] * str[d];
+                const int64_t qs = step / ext[d];
+                dig[d] = step - qs * ext[d];
+                step = qs;
+                step_off += dig[d] * str[d];
+                wrap[d] = (d + 1 < nd ? str[d + 1] : 0) - ext[d] * str[d];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void advance(int nd, const int64_t *ext)
+    {
+        off += step_off;
+        int64_t carry = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            if (d < nd) {
+                idx[d] += dig[d] + carry;
+                carry = idx[d] >= ext[d];
+                if (carry) {
+                    idx[d] -= ext[d];
+                    off += wrap[d];
+                }
+            }
+        }
+    }
+};
+
 // Loads.  Streaming kernels read every input byte exactly once and pass
 // NT = true: the non-temporal hint keeps the lines from displacing useful
 // cache contents, and on MI355X lifts a streaming read from about 6.1 to

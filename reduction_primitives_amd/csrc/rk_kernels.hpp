@@ -352,15 +352,28 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
     const int64_t col = col0 + int64_t(c) * V;
     const bool active = col < a.run_len;       // vector loads: run_len % V == 0
     const int64_t in_base = layout_offset(a.outer_nd, a.outer_ext, a.outer_str, run) + col;
-    const int64_t j0 = int64_t(sp) * a.rows_per_split;
-    const int64_t j1 = j0 + a.rows_per_split < a.m ? j0 + a.rows_per_split : a.m;
-    const S *x = static_cast<const S *>(a.x) + in_base;
+    // this block's share of the reduced dims: segments [k0, k1) and, in
+    // each, rows [j0, j1) of the row dim
+    int64_t k0, k1, j0, j1;
+    if (a.splits_per_seg > 1) {
+        k0 = sp / a.splits_per_seg;
+        k1 = k0 + 1;
+        j0 = (sp - k0 * a.splits_per_seg) * a.rows_per_split;
+        j1 = j0 + a.rows_per_split < a.row_len ? j0 + a.rows_per_split : a.row_len;
+    } else {
+        k0 = int64_t(sp) * a.segs_per_split;
+        k1 = k0 + a.segs_per_split < a.segs ? k0 + a.segs_per_split : a.segs;
+        j0 = 0;
+        j1 = a.row_len;
+    }
+    const S *xt = static_cast<const S *>(a.x) + in_base;
     const int64_t s = a.s_red;
 
     Acc acc0[V], acc1[V];
     set_identity<Acc, Op>(acc0);
     set_identity<Acc, Op>(acc1);
-    if (active) {
+    for (int64_t k = k0; active && k < k1; ++k) {
+        const S *x = xt + layout_offset(a.seg_nd, a.seg_ext, a.seg_str, k);
         int64_t j = j0 + rg;
         // full groups of UNROLL rows per thread, every load issued first
         for (; j + int64_t(UNROLL - 1) * RG < j1; j += int64_t(UNROLL) * RG) {
@@ -578,24 +591,63 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
         finish_store<Op>(a.fin, o, r);
 }
 
-// Generic kernel: one block per output (grid-stride over outputs); the
-// block's threads share the output's elements, addressed through the
-// reduced layout.  Serves any layout the fast kernels do not take.
-template <class In, class Acc, class Op, class Map, int BLOCK>
+// Generic kernel: any layout.  A unit is (output, chunk of its reduced
+// elements); blocks take units grid-stride.  The block's threads share the
+// chunk, element j at layout offset walked from j - BLOCK without a
+// division, UNROLL loads in flight per thread.  A split output is finished
+// by the last of its chunks to arrive, or by a second launch.
+template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
 {
     using S = typename InTraits<In>::S;
     const S *x = static_cast<const S *>(a.x);
-    for (int64_t o = blockIdx.x; o < a.n_out; o += gridDim.x) {
-        const int64_t base = layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o);
-        Acc v = Op::template identity<Acc>();
-        for (int64_t j = threadIdx.x; j < a.m; j += BLOCK)
-            v = Op::apply(v, Map::apply(InTraits<In>::template one<Acc>(
-                                 load1(x + base + layout_offset(a.red_nd, a.red_ext, a.red_str, j)))));
-        v = block_reduce<Op, BLOCK>(v);
-        if (threadIdx.x == 0)
-            finish_store<Op>(a.fin, o, v);
-        __syncthreads();                        // LDS of block_reduce is reused next output
+    Acc *ws = static_cast<Acc *>(a.ws);
+    const int64_t units = a.n_out * a.split;
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t o = unit / a.split;
+        const int sp = (int)(unit - o * a.split);
+        const int64_t j0 = int64_t(sp) * a.rows_per_split;
+        const int64_t j1 = j0 + a.rows_per_split < a.m ? j0 + a.rows_per_split : a.m;
+        const S *xo = x + layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o);
+        Acc acc[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            acc[u] = Op::template identity<Acc>();
+        Walk w;
+        w.init(a.red_nd, a.red_ext, a.red_str, j0 + threadIdx.x, BLOCK);
+        for (int64_t j = j0 + threadIdx.x; j < j1; j += int64_t(BLOCK) * UNROLL) {
+            S v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (j + int64_t(u) * BLOCK < j1)
+                    v[u] = load1(xo + w.off);
+                w.advance(a.red_nd, a.red_ext);
+            }
+            issue_barrier();
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (j + int64_t(u) * BLOCK < j1)
+                    acc[u] = Op::apply(acc[u], Map::apply(InTraits<In>::template one<Acc>(v[u])));
+        }
+        Acc v = block_reduce<Op, BLOCK>(fold_all<Acc, Op, UNROLL>(acc));
+        if (a.split == 1) {
+            if (threadIdx.x == 0)
+                finish_store<Op>(a.fin, o, v);
+        } else if (a.arrive_slot < 0) {         // a second launch folds the chunks
+            if (threadIdx.x == 0)
+                ws[int64_t(sp) * a.n_out + o] = v;
+        } else {                                // the last chunk to arrive finishes
+            __shared__ int last;
+            if (threadIdx.x == 0) {
+                store_partial(ws + int64_t(sp) * a.n_out + o, v);
+                last = arrive_last(a.arrive_slot, o, (uint32_t)a.split);
+            }
+            __syncthreads();
+            // in split order, as the second launch folds them
+            if (last && threadIdx.x == 0)
+                finish_store<Op>(a.fin, o, fold_partials<Acc, Op>(ws, o, a.split, a.n_out));
+        }
+        __syncthreads();                        // LDS of block_reduce and `last` are reused
     }
 }
 
@@ -709,7 +761,9 @@ int run_typed(const Launch &L)
         split = L.dims.split;
         break;
     case K_GENERIC:
-        launch_first(&k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock>, grid, block, st, L, L.dims);
+        launch_first(&k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock, tune::kGenericUnroll>, grid, block, st,
+                     L, L.dims);
+        split = L.dims.split;
         break;
     default:
         return ST_INVALID;

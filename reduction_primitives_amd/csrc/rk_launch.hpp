@@ -48,11 +48,18 @@ struct DimsArgs {
     void *ws;             // split * n_out accumulators when split > 1
     int64_t n_out;
     int64_t m;            // elements per output
-    int64_t s_red;        // reduced stride (tile kernels)
+    int64_t s_red;        // tile kernels: stride of the row dim (one of the reduced dims)
+    int64_t row_len;      // tile kernels: extent of the row dim
+    int seg_nd;           // tile kernels: the other reduced dims; each index of them is a segment
+    int64_t seg_ext[3];
+    int64_t seg_str[3];
+    int64_t segs;         // segments (1 when the row dim is the only reduced dim)
+    int64_t segs_per_split;   // splits_per_seg == 1: whole segments per split unit
+    int64_t splits_per_seg;   // > 1: split units per segment, rows_per_split rows each
     int64_t run_len;      // contiguous outputs per run (tile kernels)
     int64_t tiles_per_run;
     int64_t tiles;
-    int64_t rows_per_split;
+    int64_t rows_per_split;   // row and generic kernels: reduced elements per split unit
     int split;
     int outer_nd;         // kept dims after the first (tile kernels): run offsets
     int64_t outer_ext[3];

@@ -173,7 +173,9 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
             d.kernel = K_GENERIC;           // nothing to reduce: f applied per element
         } else if (d.red.nd == 1 && d.red.str[0] == 1) {
             d.kernel = K_ROW;
-        } else if (d.red.nd == 1 && d.kept.str[0] == 1) {
+        } else if (d.kept.str[0] == 1) {
+            // contiguous runs of outputs over any reduced dims (PR #176's
+            // selector; several reduced dims become segments of rows)
             d.kernel = select_strided_kernel(d.kept.ext[0], n_out, m, isz, num_cus);
         } else {
             d.kernel = K_GENERIC;
@@ -216,7 +218,23 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
     case K_THREAD: case K_TILED: case K_COLUMNS: {
         d.run_len = d.kept.ext[0];
         d.runs = n_out / d.run_len;
-        d.s_red = d.red.str[0];
+        // rows run along the reduced dim of largest extent; the others
+        // index segments of such rows
+        int r = 0;
+        for (int i = 1; i < d.red.nd; ++i)
+            if (d.red.ext[i] > d.red.ext[r])
+                r = i;
+        d.s_red = d.red.str[r];
+        d.row_len = d.red.ext[r];
+        d.seg = Layout();
+        for (int i = 0; i < d.red.nd; ++i) {
+            if (i == r)
+                continue;
+            d.seg.ext[d.seg.nd] = d.red.ext[i];
+            d.seg.str[d.seg.nd] = d.red.str[i];
+            ++d.seg.nd;
+        }
+        d.segs = m / d.row_len;
         d.outer = Layout();
         for (int i = 1; i < d.kept.nd; ++i) {
             d.outer.ext[d.outer.nd] = d.kept.ext[i];
@@ -228,6 +246,8 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         bool vec_ok = (addr % 16) == 0 && d.run_len % v == 0 && (d.s_red * isz) % 16 == 0;
         for (int i = 0; i < d.outer.nd; ++i)
             vec_ok = vec_ok && (d.outer.str[i] * isz) % 16 == 0;
+        for (int i = 0; i < d.seg.nd; ++i)
+            vec_ok = vec_ok && (d.seg.str[i] * isz) % 16 == 0;
         d.vec = vec_ok ? v : 1;
         if (d.kernel == K_THREAD) {
             d.block = tune::kThreadBlock;
@@ -250,15 +270,28 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.tile_outputs = d.lanes * d.vec;
         d.tiles_per_run = ceil_div(d.run_len, d.tile_outputs);
         d.tiles = d.runs * d.tiles_per_run;
+        // split units: whole segments each, or pieces of rows_per_split
+        // rows of one segment
         d.split = 1;
+        d.rows_per_split = d.row_len;
+        d.segs_per_split = d.segs;
+        d.splits_per_seg = 1;
         if (d.kernel == K_COLUMNS) {
             const int64_t target = int64_t(num_cus) * tune::kColumnsBlocksPerCu;
             int64_t s = std::max<int64_t>(1, ceil_div(target, d.tiles));
             s = std::min<int64_t>(s, std::max<int64_t>(1, m / tune::kColumnsMinRows));
-            d.rows_per_split = ceil_div(m, s);
-            d.split = int(ceil_div(m, d.rows_per_split));
-        } else {
-            d.rows_per_split = m;
+            if (s <= d.segs) {
+                d.segs_per_split = ceil_div(d.segs, s);
+                d.split = int(ceil_div(d.segs, d.segs_per_split));
+            } else {
+                int64_t per = std::min<int64_t>(ceil_div(s, d.segs),
+                                                std::max<int64_t>(1, d.row_len / tune::kColumnsMinRows));
+                d.rows_per_split = ceil_div(d.row_len, per);
+                per = ceil_div(d.row_len, d.rows_per_split);
+                d.segs_per_split = 1;
+                d.splits_per_seg = per;
+                d.split = int(d.segs * per);
+            }
         }
         d.grid = d.tiles * d.split;
         d.launches = d.split > 1 ? 2 : 1;
@@ -286,11 +319,20 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         break;
     }
     case K_GENERIC: {
+        // units of (output, chunk of reduced elements): split an output over
+        // several blocks when the outputs alone would not fill the GPU
         d.vec = 1;
         d.block = tune::kDimsBlock;
-        d.grid = std::min<int64_t>(n_out, int64_t(num_cus) * tune::kGenericBlocksPerCu);
-        d.launches = 1;
-        d.ws_bytes = 0;
+        const int64_t target = int64_t(num_cus) * tune::kGenericBlocksPerCu;
+        int64_t s = 1;
+        if (n_out < target && m > 0)
+            s = std::min<int64_t>(ceil_div(target, n_out), std::max<int64_t>(1, m / tune::kGenericMinChunk));
+        d.rows_per_split = m > 0 ? ceil_div(m, s) : 0;
+        d.split = m > 0 ? int(ceil_div(m, d.rows_per_split)) : 1;
+        d.grid = std::min<int64_t>(n_out * d.split, target);
+        d.launches = d.split > 1 ? 2 : 1;
+        d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
+        d.fused_ok = d.split > 1 && n_out <= kArriveCapacity;      // one counter per output
         break;
     }
     default:

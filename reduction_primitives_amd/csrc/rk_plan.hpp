@@ -66,7 +66,9 @@ constexpr int kColumnsBlocksPerCu = 1;    // columns split target: CUs * this bl
 constexpr int64_t kColumnsMinRows = 128;  // rows per split chunk, at least
 constexpr int kRowWavesPerCu = 16;        // row kernel split target
 constexpr int64_t kRowMinChunk = 2048;    // elements per row chunk, at least
-constexpr int kGenericBlocksPerCu = 8;
+constexpr int kGenericBlocksPerCu = 8;   // generic kernel: grid cap, and split target
+constexpr int kGenericUnroll = 8;        // generic kernel: element loads in flight per thread
+constexpr int64_t kGenericMinChunk = 4096;   // generic kernel: reduced elements per split unit, at least
 constexpr int kDefaultCus = 256;          // MI355X
 }  // namespace tune
 
@@ -104,7 +106,12 @@ struct DimsPlan {
     // dims (`outer`) place the runs.
     int64_t run_len = 0;
     int64_t runs = 0;
-    int64_t s_red = 0;      // stride of the single reduced dim
+    int64_t s_red = 0;      // stride of the row dim: the reduced dim of largest extent
+    int64_t row_len = 0;    // its extent
+    Layout seg;             // the other reduced dims; one segment per index
+    int64_t segs = 1;
+    int64_t segs_per_split = 1;   // see DimsArgs
+    int64_t splits_per_seg = 1;
     Layout outer;
     int vec = 1;            // elements per load
     int lanes = 1;          // lanes across one row of a tile

@@ -139,3 +139,36 @@ def vector_pair(n: int) -> list:
     j = 0 if n <= 10**6 else 2
     return [Array("f32_n01_a", normal(n, 6000 + j), (n,), f"N(0,1) seed {6000 + j}"),
             Array("f32_n01_b", normal(n, 6001 + j), (n,), f"N(0,1) seed {6001 + j}")]
+
+
+@dataclass
+class View:
+    """A flat buffer read through an arbitrary column-major view."""
+    name: str
+    data: torch.Tensor
+    shape: tuple
+    view_strides: tuple
+    dims: tuple
+    recipe: str
+
+
+def general_layouts() -> list:
+    """Reductions over several reduced dims that do not merge into one, each
+    67,108,864 float32 U[-1,1) elements (268 MB, the size of the 8192x8192
+    rows).  PR #176's opening paragraphs speed up two common layouts of
+    strided reductions; other layouts keep the one-thread or one-block per
+    output kernels.  These are three of the others: per-channel statistics of a
+    (3136, 256, 84) array over dims 1 and 3 (a contiguous reduced dim plus a
+    strided one), a permuted (8192, 1024, 8) view over dims 2 and 3, and a
+    4-d (1024, 2048, 8, 4) array over dims 2 and 4."""
+    out = []
+    shape = (3136, 256, 84)
+    out.append(View("3136x256x84 f32 dims=(1,3)", uniform(math.prod(shape), -1.0, 1.0, 7000),
+                    shape, cm_strides(shape), (1, 3), "U[-1,1) seed 7000"))
+    shape = (8192, 1024, 8)           # storage (8192, 8, 1024), dims 2 and 3 swapped
+    out.append(View("8192x1024x8 f32 permuted dims=(2,3)", uniform(math.prod(shape), -1.0, 1.0, 7001),
+                    shape, (1, 8192 * 8, 8192), (2, 3), "U[-1,1) seed 7001"))
+    shape = (1024, 2048, 8, 4)
+    out.append(View("1024x2048x8x4 f32 dims=(2,4)", uniform(math.prod(shape), -1.0, 1.0, 7002),
+                    shape, cm_strides(shape), (2, 4), "U[-1,1) seed 7002"))
+    return out

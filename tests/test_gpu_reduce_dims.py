@@ -146,7 +146,7 @@ SELECTOR_CASES = [
     ((3000, 777), 1, torch.float32, "row", "contiguous reduced dim"),
     ((100003, 7), 1, torch.float32, "row", "few long rows (split row)"),
     ((5, 6, 7), (1, 3), torch.float32, "generic", "two non-adjacent reduced dims"),
-    ((33, 5, 9, 4), (2, 4), torch.float32, "generic", "4-d, two reduced dims"),
+    ((33, 5, 9, 4), (2, 4), torch.float32, "thread", "4-d, two short reduced dims"),
     ((1000, 1), (1, 2), torch.float32, "all", "single output, contiguous"),
 ]
 
@@ -214,6 +214,77 @@ def test_non_contiguous_views():
     assert p["launches"] in (1, 2)
     # broadcast (stride 0) dims
     dims_and_check(x, (64, 10), (1, 0), 2)
+
+
+# --------------------------------------------------------- general layouts
+# Several reduced dims that do not merge, 4-d arrays, outputs that are not
+# contiguous in the input.  Contiguous runs of outputs take the tile kernels
+# with the extra reduced dims as segments of rows; everything else takes the
+# generic kernel, split over blocks when there are few outputs.
+
+GENERAL_CASES = [
+    # (storage numel, shape, strides, dims, expected kernel, why)
+    (128 * 100 * 2 * 64, (128, 100, 2, 64), CM((128, 100, 2, 64)), (2, 4), "columns",
+     "4-d, dims 2 and 4: whole segments per split"),
+    (128 * 3 * 3000, (128, 3000, 3), (1, 384, 128), (2, 3), "columns",
+     "permuted view, dims 2 and 3: splits inside segments"),
+    (3072 * 8 * 20, (3072, 20, 8), (1, 3072 * 8, 3072), (2, 3), "tiled",
+     "permuted view, more outputs than elements"),
+    (64 * 500 * 16 * 6, (64, 500, 16, 6), CM((64, 500, 16, 6)), (2, 4), "columns",
+     "middle-dim runs with a second reduced dim"),
+    (64 * 50 * 16 * 6, (64, 50, 16, 6), CM((64, 50, 16, 6)), (2, 4), "tiled",
+     "middle-dim runs, more outputs than elements"),
+    (33 * 5 * 9 * 4, (33, 5, 9, 4), CM((33, 5, 9, 4)), (2, 4), "thread", "short reductions"),
+    (31000, (130, 7, 11, 3), (1, 130 * 11 * 3, 131, 130 * 11), (2, 3, 4), "columns",
+     "three reduced dims, strides not 16-byte multiples"),
+    (5 * 6 * 7, (5, 6, 7), CM((5, 6, 7)), (1, 3), "generic", "non-adjacent dims, kept dim strided"),
+    (49 * 64 * 256, (49, 64, 256), CM((49, 64, 256)), (1, 3), "generic",
+     "per-channel statistics of 7x7 maps"),
+    (3136 * 16 * 24, (3136, 16, 24), CM((3136, 16, 24)), (1, 3), "generic",
+     "per-channel statistics of 56x56 maps, split outputs"),
+    (2 * 300 * 40, (300, 40), (2, 600), 1, "generic", "strided gather along the reduced dim"),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_CASES, ids=lambda c: c[5].replace(" ", "_"))
+def test_general_layouts(case):
+    numel, shape, strides, dims, kern, _ = case
+    x = W.normal(numel, 9600 + numel % 97)
+    dims_and_check(x, shape, strides, dims, expect_kernel=kern, init=0.5)
+    dims_and_check(x, shape, strides, dims, op="max", expect_kernel=kern)
+    xb = W.normal(numel, 9700 + numel % 89, torch.bfloat16)
+    dims_and_check(xb, shape, strides, dims, out_dtype=torch.float32, map_="square")
+    xi = W.randint(numel, -10**6, 10**6, 9800 + numel % 83)
+    dims_and_check(xi, shape, strides, dims, acc=torch.int64, out_dtype=torch.int64, mode="fold")
+    dims_and_check(xi, shape, strides, dims, op="min", acc=torch.int32, out_dtype=torch.int32)
+
+
+@pytest.mark.parametrize("case", [c for c in GENERAL_CASES if c[4] in ("columns", "generic")],
+                         ids=lambda c: c[5].replace(" ", "_"))
+def test_general_layouts_both_finishes(case):
+    """Split general layouts: the one-launch and the two-launch finish agree
+    bit for bit (same partials, same fold order)."""
+    rk = _rk()
+    numel, shape, strides, dims, kern, _ = case
+    x = W.normal(numel, 9900 + numel % 79).to(DEV)
+    res = {}
+    for on in (1, 0):
+        prev = rk.rk_debug_set_fused_finish(on)
+        try:
+            res[on] = raw_np(rk.reduce_dims(x, shape, strides, dims, init=0.25))
+            torch.cuda.synchronize()
+        finally:
+            rk.rk_debug_set_fused_finish(prev)
+    assert np.array_equal(res[0], res[1])
+
+
+def test_general_layout_plans():
+    rk = _rk()
+    p = rk.plan_dims(torch.float32, (128, 3000, 3), (1, 384, 128), (2, 3))
+    assert p["kernel_name"] == "columns" and p["split"] > 3
+    p = rk.plan_dims(torch.float32, (3136, 16, 24), CM((3136, 16, 24)), (1, 3))
+    assert p["kernel_name"] == "generic" and p["split"] > 1
+    assert p["workspace_bytes"] >= p["split"] * 16 * 4
 
 
 def test_dims_all_masked_equals_whole_array():

@@ -134,6 +134,29 @@ def test_selector_rules():
     assert plan(torch.float32, (row_f32, 100), 2)["tile_outputs"] == t["kThreadBlock"] * 4
 
 
+def test_general_layouts_route():
+    """Reduced dims that do not merge: contiguous runs of outputs take the
+    tile kernels (the other reduced dims index segments of rows); anything
+    else the generic kernel, split over blocks when outputs are few."""
+    import torch
+    f32 = torch.float32
+    p = plan(f32, (128, 3000, 3), (2, 3), strides=(1, 384, 128))
+    assert p["kernel_name"] == "columns" and p["split"] == 69 and p["vec"] == 4
+    p = plan(f32, (128, 100, 2, 64), (2, 4))
+    assert p["kernel_name"] == "columns" and p["split"] == 32
+    p = plan(f32, (3072, 20, 8), (2, 3), strides=(1, 3072 * 8, 3072))
+    assert p["kernel_name"] == "tiled" and p["split"] == 1
+    p = plan(f32, (130, 7, 11, 3), (2, 3, 4), strides=(1, 4290, 131, 1430))
+    assert p["kernel_name"] == "columns" and p["vec"] == 1      # 131 * 4 bytes: no 16-byte rows
+    p = plan(f32, (49, 64, 256), (1, 3))
+    assert p["kernel_name"] == "generic" and p["split"] == 3 and p["launches"] == 1
+    p = plan(f32, (3136, 16, 24), (1, 3))
+    assert p["kernel_name"] == "generic" and p["split"] == 18 and p["grid"] == 16 * 18
+    assert p["workspace_bytes"] == 1280                              # 18 * 16 * 4 rounded to 256
+    p = plan(f32, (5000, 3000), (1,), strides=(3, 15000))            # no stride-1 dim
+    assert p["kernel_name"] == "generic" and p["split"] == 1
+
+
 def test_normalisation_drops_unit_dims_and_merges():
     import torch
     # (768, 1024, 8) reduced over dims 1 and 2 merges into one contiguous run per batch
