@@ -594,42 +594,75 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
 // Generic kernel: any layout.  A unit is (output, chunk of its reduced
 // elements); blocks take units grid-stride.  The block's threads share the
 // chunk, element j at layout offset walked from j - BLOCK without a
-// division, UNROLL loads in flight per thread.  A split output is finished
-// by the last of its chunks to arrive, or by a second launch.
-template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
+// division, UNROLL loads in flight per thread.  VECTOR: the innermost
+// reduced dim is contiguous and every reduced row starts 16-byte aligned, so
+// the units are 16-byte vectors (the planner scales the reduced layout and
+// the chunk to vectors).  A split output is finished by the last of its
+// chunks to arrive, or by a second launch.
+template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL, bool VECTOR>
 __global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
 {
     using S = typename InTraits<In>::S;
+    constexpr int V = VECTOR ? InTraits<In>::vec : 1;
     const S *x = static_cast<const S *>(a.x);
     Acc *ws = static_cast<Acc *>(a.ws);
     const int64_t units = a.n_out * a.split;
+    const int64_t len = a.m / V;               // reduced length in load units
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t o = unit / a.split;
         const int sp = (int)(unit - o * a.split);
         const int64_t j0 = int64_t(sp) * a.rows_per_split;
-        const int64_t j1 = j0 + a.rows_per_split < a.m ? j0 + a.rows_per_split : a.m;
+        const int64_t j1 = j0 + a.rows_per_split < len ? j0 + a.rows_per_split : len;
         const S *xo = x + layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o);
-        Acc acc[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            acc[u] = Op::template identity<Acc>();
+        Acc acc0[V], acc1[V];
+        set_identity<Acc, Op>(acc0);
+        set_identity<Acc, Op>(acc1);
         Walk w;
         w.init(a.red_nd, a.red_ext, a.red_str, j0 + threadIdx.x, BLOCK);
         for (int64_t j = j0 + threadIdx.x; j < j1; j += int64_t(BLOCK) * UNROLL) {
-            S v[UNROLL];
+            if constexpr (VECTOR) {
+                u32x4 v[UNROLL];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                if (j + int64_t(u) * BLOCK < j1)
-                    v[u] = load1(xo + w.off);
-                w.advance(a.red_nd, a.red_ext);
+                for (int u = 0; u < UNROLL; ++u) {
+                    if (j + int64_t(u) * BLOCK < j1)
+                        v[u] = load16(reinterpret_cast<const u32x4 *>(xo + w.off));
+                    w.advance(a.red_nd, a.red_ext);
+                }
+                issue_barrier();
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    if (j + int64_t(u) * BLOCK < j1) {
+                        if (u & 1)
+                            fold_vec<In, Acc, Op, Map, V>(acc1, v[u]);
+                        else
+                            fold_vec<In, Acc, Op, Map, V>(acc0, v[u]);
+                    }
+                }
+            } else {
+                S v[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    if (j + int64_t(u) * BLOCK < j1)
+                        v[u] = load1(xo + w.off);
+                    w.advance(a.red_nd, a.red_ext);
+                }
+                issue_barrier();
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    if (j + int64_t(u) * BLOCK < j1) {
+                        const Acc e = Map::apply(InTraits<In>::template one<Acc>(v[u]));
+                        if (u & 1)
+                            acc1[0] = Op::apply(acc1[0], e);
+                        else
+                            acc0[0] = Op::apply(acc0[0], e);
+                    }
+                }
             }
-            issue_barrier();
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                if (j + int64_t(u) * BLOCK < j1)
-                    acc[u] = Op::apply(acc[u], Map::apply(InTraits<In>::template one<Acc>(v[u])));
         }
-        Acc v = block_reduce<Op, BLOCK>(fold_all<Acc, Op, UNROLL>(acc));
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            acc0[i] = Op::apply(acc0[i], acc1[i]);
+        Acc v = block_reduce<Op, BLOCK>(fold_all<Acc, Op, V>(acc0));
         if (a.split == 1) {
             if (threadIdx.x == 0)
                 finish_store<Op>(a.fin, o, v);
@@ -761,8 +794,15 @@ int run_typed(const Launch &L)
         split = L.dims.split;
         break;
     case K_GENERIC:
-        launch_first(&k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock, tune::kGenericUnroll>, grid, block, st,
-                     L, L.dims);
+        if (L.vec > 1) {
+            if (L.vec != InTraits<In>::vec)
+                return ST_INVALID;
+            launch_first(&k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock, tune::kGenericUnroll, true>, grid,
+                         block, st, L, L.dims);
+        } else {
+            launch_first(&k_dims_generic<In, Acc, Op, Map, tune::kDimsBlock, tune::kGenericUnroll, false>, grid,
+                         block, st, L, L.dims);
+        }
         split = L.dims.split;
         break;
     default:

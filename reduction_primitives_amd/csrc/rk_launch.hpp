@@ -59,7 +59,7 @@ struct DimsArgs {
     int64_t run_len;      // contiguous outputs per run (tile kernels)
     int64_t tiles_per_run;
     int64_t tiles;
-    int64_t rows_per_split;   // row and generic kernels: reduced elements per split unit
+    int64_t rows_per_split;   // row kernel: reduced elements per split unit; generic: load units
     int split;
     int outer_nd;         // kept dims after the first (tile kernels): run offsets
     int64_t outer_ext[3];

@@ -321,14 +321,32 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
     case K_GENERIC: {
         // units of (output, chunk of reduced elements): split an output over
         // several blocks when the outputs alone would not fill the GPU
+        // 16-byte loads when the innermost reduced dim is contiguous and
+        // every reduced row and every output's base stay 16-byte aligned:
+        // the kernel then walks the reduced layout in vectors
         d.vec = 1;
+        {
+            const int v = 16 / isz;
+            bool vec_ok = m > 0 && d.red.nd >= 1 && d.red.str[0] == 1 && d.red.ext[0] % v == 0 && addr % 16 == 0;
+            for (int i = 1; i < d.red.nd; ++i)
+                vec_ok = vec_ok && (d.red.str[i] * isz) % 16 == 0;
+            for (int i = 0; i < d.kept.nd; ++i)
+                vec_ok = vec_ok && (d.kept.str[i] * isz) % 16 == 0;
+            if (vec_ok) {
+                d.vec = v;
+                d.red.ext[0] /= v;
+                d.red.str[0] = v;
+            }
+        }
+        const int64_t units = m / d.vec;            // reduced length in load units
         d.block = tune::kDimsBlock;
         const int64_t target = int64_t(num_cus) * tune::kGenericBlocksPerCu;
         int64_t s = 1;
         if (n_out < target && m > 0)
-            s = std::min<int64_t>(ceil_div(target, n_out), std::max<int64_t>(1, m / tune::kGenericMinChunk));
-        d.rows_per_split = m > 0 ? ceil_div(m, s) : 0;
-        d.split = m > 0 ? int(ceil_div(m, d.rows_per_split)) : 1;
+            s = std::min<int64_t>(ceil_div(target, n_out),
+                                  std::max<int64_t>(1, units * d.vec / tune::kGenericMinChunk));
+        d.rows_per_split = m > 0 ? ceil_div(units, s) : 0;
+        d.split = m > 0 ? int(ceil_div(units, d.rows_per_split)) : 1;
         d.grid = std::min<int64_t>(n_out * d.split, target);
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;

@@ -278,6 +278,18 @@ def test_general_layouts_both_finishes(case):
     assert np.array_equal(res[0], res[1])
 
 
+@pytest.mark.parametrize("offset", [1, 3, 4])
+def test_general_layout_offsets(offset):
+    """The generic kernel takes 16-byte loads only when every reduced row
+    starts 16-byte aligned; an offset view falls back to element loads."""
+    shape = (1000, 8, 12)
+    x = W.normal(math.prod(shape) + offset, 9950 + offset)
+    plan = dims_and_check(x, shape, CM(shape), (1, 3), offset=offset, expect_kernel="generic")
+    assert plan["vec"] == (4 if offset % 4 == 0 else 1)
+    xb = W.normal(math.prod(shape) + offset, 9960 + offset, torch.bfloat16)
+    dims_and_check(xb, shape, CM(shape), (1, 3), offset=offset, out_dtype=torch.float32)
+
+
 def test_general_layout_plans():
     rk = _rk()
     p = rk.plan_dims(torch.float32, (128, 3000, 3), (1, 384, 128), (2, 3))

@@ -150,8 +150,12 @@ def test_general_layouts_route():
     assert p["kernel_name"] == "columns" and p["vec"] == 1      # 131 * 4 bytes: no 16-byte rows
     p = plan(f32, (49, 64, 256), (1, 3))
     assert p["kernel_name"] == "generic" and p["split"] == 3 and p["launches"] == 1
+    assert p["vec"] == 1                                             # 49-element rows
     p = plan(f32, (3136, 16, 24), (1, 3))
     assert p["kernel_name"] == "generic" and p["split"] == 18 and p["grid"] == 16 * 18
+    assert p["vec"] == 4                                             # 16-byte loads along rows
+    assert plan(f32, (3136, 16, 24), (1, 3), ptr=4)["vec"] == 1
+    assert plan(torch.bfloat16, (3136, 16, 24), (1, 3))["vec"] == 8
     assert p["workspace_bytes"] == 1280                              # 18 * 16 * 4 rounded to 256
     p = plan(f32, (5000, 3000), (1,), strides=(3, 15000))            # no stride-1 dim
     assert p["kernel_name"] == "generic" and p["split"] == 1
