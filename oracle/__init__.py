@@ -80,8 +80,13 @@ def _load():
     lib.rko_cast_int.argtypes = [i32, vp, i64, vp]
     lib.rko_widen_fp.argtypes = [i32, vp, i64, vp]
     lib.rko_widen_int.argtypes = [i32, vp, i64, vp]
+    lib.rko_scan_fp.argtypes = [i32, i32, vp, i64, dbl, i32, vp]
+    lib.rko_scan_int.argtypes = [i32, i32, i32, vp, i64, i64, i32, vp]
+    lib.rko_scan_dims_fp.argtypes = [i32, i32, vp, i32, vp, vp, i32, dbl, i32, vp]
+    lib.rko_scan_dims_int.argtypes = [i32, i32, i32, vp, i32, vp, vp, i32, i64, i32, vp]
     for name in ("rko_all_fp", "rko_all_int", "rko_all2_fp", "rko_all2_int", "rko_dims_fp", "rko_dims_int",
-                 "rko_cast_fp", "rko_cast_int", "rko_widen_fp", "rko_widen_int"):
+                 "rko_cast_fp", "rko_cast_int", "rko_widen_fp", "rko_widen_int", "rko_scan_fp",
+                 "rko_scan_int", "rko_scan_dims_fp", "rko_scan_dims_int"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -276,3 +281,48 @@ def expected_dims(op, map_, in_dtype, acc_dtype, out_dtype, storage, shape, stri
     s = start_value(op, acc_dtype, out_dtype, mode, init, prev)
     r = reduce_dims(op, map_, in_dtype, acc_dtype, storage, shape, strides, mask, s)
     return r, cast(out_dtype, r)
+
+
+def scan(op: int, in_dtype: int, acc_dtype: int, x: np.ndarray, start, inclusive: bool) -> np.ndarray:
+    """Prefix fold of a contiguous 1-d array: one wide value per element
+    (float64 or int64 wrapped to the accumulator width)."""
+    lib = _load()
+    x = np.ascontiguousarray(_raw(x, in_dtype)).reshape(-1)
+    if is_fp(in_dtype):
+        out = np.zeros(x.size, np.float64)
+        rc = lib.rko_scan_fp(op, in_dtype, _ptr(x), x.size, float(start), int(bool(inclusive)), _ptr(out))
+    else:
+        out = np.zeros(x.size, np.int64)
+        rc = lib.rko_scan_int(op, in_dtype, acc_dtype, _ptr(x), x.size, wrap_int(int(start), I64),
+                              int(bool(inclusive)), _ptr(out))
+    if rc:
+        raise ValueError("oracle rejected arguments")
+    return out
+
+
+def scan_dims(op: int, in_dtype: int, acc_dtype: int, storage: np.ndarray, shape, strides, dim: int,
+              start, inclusive: bool) -> np.ndarray:
+    """Prefix fold along `dim` (0-based) of a strided column-major view of
+    `storage`; returns the wide results for the view's shape, flat in
+    column-major order."""
+    lib = _load()
+    storage = np.ascontiguousarray(_raw(storage, in_dtype)).reshape(-1)
+    shape_a = np.asarray(shape, np.int64)
+    strides_a = np.asarray(strides, np.int64)
+    total = int(np.prod(shape_a))
+    if total > 0:
+        last = int(sum((s - 1) * st for s, st in zip(shape_a, strides_a)))
+        if last >= storage.size:
+            raise ValueError("view reaches past the end of storage")
+    if is_fp(in_dtype):
+        out = np.zeros(total, np.float64)
+        rc = lib.rko_scan_dims_fp(op, in_dtype, _ptr(storage), shape_a.size, _ptr(shape_a), _ptr(strides_a),
+                                  int(dim), float(start), int(bool(inclusive)), _ptr(out))
+    else:
+        out = np.zeros(total, np.int64)
+        rc = lib.rko_scan_dims_int(op, in_dtype, acc_dtype, _ptr(storage), shape_a.size, _ptr(shape_a),
+                                   _ptr(strides_a), int(dim), wrap_int(int(start), I64),
+                                   int(bool(inclusive)), _ptr(out))
+    if rc:
+        raise ValueError("oracle rejected arguments")
+    return out

@@ -18,6 +18,9 @@
  *   - PR #139, "What changes" and the test list under "Compatibility": the
  *     source may be a lazy broadcast, here of two arrays, f(a_i, b_i), folded
  *     the same way (rko_all2_*).
+ *   - PR #202 (tile scans), opening paragraph: accumulate!, the same fold
+ *     with every prefix stored, over a whole array or along one dim
+ *     (rko_scan_*).
  * The GPU path reaches the same exact value by re-associating the fold; the
  * pages state that only rounding may differ when the reduction tree changes
  * (PR #139, "Compatibility").  So this file is the definition written out:
@@ -348,6 +351,161 @@ int rko_dims_int(int op, int map, int in_dtype, int acc_dtype, const void *x,
     }
     for (int64_t o = 0; o < n_out; ++o)
         result[o] = wrap_to(acc_dtype, result[o]);
+    return 0;
+}
+
+/* ------------------------------------------------------------------- scans */
+
+/*
+ * Prefix folds (scans): AcceleratedKernels.jl PR #202 (tile scans), opening
+ * paragraph -- accumulate! over a whole array, and along one dim.  Output k
+ * of a line is s (+) x_0 (+) ... (+) x_k when inclusive, and
+ * s (+) x_0 (+) ... (+) x_(k-1) when exclusive (so the first output is s).
+ * The running value is a double (floating inputs) or an int64 wrapped to the
+ * accumulator width after every step (integers), updated left to right.
+ */
+int rko_scan_fp(int op, int in_dtype, const void *x, int64_t n, double start, int inclusive,
+                double *out)
+{
+    if (!is_fp_dtype(in_dtype) || n < 0 || (n > 0 && (!x || !out)))
+        return -1;
+    double run = start;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = load_fp(in_dtype, x, i);
+        if (inclusive) {
+            run = op_fp(op, run, v);
+            out[i] = run;
+        } else {
+            out[i] = run;
+            run = op_fp(op, run, v);
+        }
+    }
+    return 0;
+}
+
+int rko_scan_int(int op, int in_dtype, int acc_dtype, const void *x, int64_t n, int64_t start,
+                 int inclusive, int64_t *out)
+{
+    if (!is_int_dtype(in_dtype) || !is_int_dtype(acc_dtype) || n < 0 || (n > 0 && (!x || !out)))
+        return -1;
+    int64_t run = wrap_to(acc_dtype, start);
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t v = wrap_to(acc_dtype, load_int(in_dtype, x, i));
+        if (inclusive) {
+            run = wrap_to(acc_dtype, op_int(op, run, v));
+            out[i] = run;
+        } else {
+            out[i] = run;
+            run = wrap_to(acc_dtype, op_int(op, run, v));
+        }
+    }
+    return 0;
+}
+
+/*
+ * Scan along dim `dim` (0-based) of a strided column-major view: every line
+ * (all indices fixed but the one along `dim`) is scanned on its own, from
+ * `start`.  The output has the view's shape, stored contiguously in
+ * column-major order.  The input is walked once in column-major order, which
+ * visits each line's elements in increasing order along `dim`.
+ */
+static int scan_dims_setup(int ndim, const int64_t *shape, const int64_t *strides, int dim,
+                           int64_t *line_stride, int64_t *n_lines, int64_t *total)
+{
+    if (ndim < 1 || ndim > 8 || !shape || !strides || dim < 0 || dim >= ndim)
+        return -1;
+    int64_t nl = 1, tot = 1;
+    for (int d = 0; d < ndim; ++d) {
+        if (shape[d] < 0 || strides[d] < 0)
+            return -1;
+        tot *= shape[d];
+        if (d == dim) {
+            line_stride[d] = 0;
+        } else {
+            line_stride[d] = nl;
+            nl *= shape[d];
+        }
+    }
+    *n_lines = nl;
+    *total = tot;
+    return 0;
+}
+
+int rko_scan_dims_fp(int op, int in_dtype, const void *x, int ndim, const int64_t *shape,
+                     const int64_t *strides, int dim, double start, int inclusive, double *out)
+{
+    int64_t lstr[8], n_lines, total;
+    if (!is_fp_dtype(in_dtype) || scan_dims_setup(ndim, shape, strides, dim, lstr, &n_lines, &total))
+        return -1;
+    if (total == 0)
+        return 0;
+    double *run = malloc(sizeof(double) * (size_t)n_lines);
+    if (!run)
+        return -1;
+    for (int64_t l = 0; l < n_lines; ++l)
+        run[l] = start;
+    int64_t idx[8] = {0};
+    for (int64_t t = 0; t < total; ++t) {       /* t is also the output's column-major index */
+        int64_t off = 0, l = 0;
+        for (int d = 0; d < ndim; ++d) {
+            off += idx[d] * strides[d];
+            l += idx[d] * lstr[d];
+        }
+        const double v = load_fp(in_dtype, x, off);
+        if (inclusive) {
+            run[l] = op_fp(op, run[l], v);
+            out[t] = run[l];
+        } else {
+            out[t] = run[l];
+            run[l] = op_fp(op, run[l], v);
+        }
+        for (int d = 0; d < ndim; ++d) {
+            if (++idx[d] < shape[d])
+                break;
+            idx[d] = 0;
+        }
+    }
+    free(run);
+    return 0;
+}
+
+int rko_scan_dims_int(int op, int in_dtype, int acc_dtype, const void *x, int ndim,
+                      const int64_t *shape, const int64_t *strides, int dim, int64_t start,
+                      int inclusive, int64_t *out)
+{
+    int64_t lstr[8], n_lines, total;
+    if (!is_int_dtype(in_dtype) || !is_int_dtype(acc_dtype) ||
+        scan_dims_setup(ndim, shape, strides, dim, lstr, &n_lines, &total))
+        return -1;
+    if (total == 0)
+        return 0;
+    int64_t *run = malloc(sizeof(int64_t) * (size_t)n_lines);
+    if (!run)
+        return -1;
+    for (int64_t l = 0; l < n_lines; ++l)
+        run[l] = wrap_to(acc_dtype, start);
+    int64_t idx[8] = {0};
+    for (int64_t t = 0; t < total; ++t) {
+        int64_t off = 0, l = 0;
+        for (int d = 0; d < ndim; ++d) {
+            off += idx[d] * strides[d];
+            l += idx[d] * lstr[d];
+        }
+        const int64_t v = wrap_to(acc_dtype, load_int(in_dtype, x, off));
+        if (inclusive) {
+            run[l] = wrap_to(acc_dtype, op_int(op, run[l], v));
+            out[t] = run[l];
+        } else {
+            out[t] = run[l];
+            run[l] = wrap_to(acc_dtype, op_int(op, run[l], v));
+        }
+        for (int d = 0; d < ndim; ++d) {
+            if (++idx[d] < shape[d])
+                break;
+            idx[d] = 0;
+        }
+    }
+    free(run);
     return 0;
 }
 

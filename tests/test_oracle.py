@@ -488,3 +488,98 @@ def test_two_input_maps_wrap_in_int32():
     b = np.array([-1], np.int32)
     assert o.reduce_all2(o.SUM, o.ABSDIFF, o.I32, o.I32, a, b, 0) == -2**31   # 2^31 wraps
     assert o.reduce_all2(o.SUM, o.ABSDIFF, o.I32, o.I64, a, b, 0) == 2**31
+
+
+# ------------------------------------------------------------------- scans
+
+def test_scan_closed_forms():
+    o = _o()
+    n = 5000
+    x = np.arange(1, n + 1, dtype=np.int32)
+    k = np.arange(1, n + 1, dtype=np.int64)
+    assert np.array_equal(o.scan(o.SUM, o.I32, o.I64, x, 0, True), k * (k + 1) // 2)
+    assert np.array_equal(o.scan(o.SUM, o.I32, o.I64, x, 7, False), 7 + (k - 1) * k // 2)
+    xf = x.astype(np.float32)                 # every prefix is an exact double
+    assert np.array_equal(o.scan(o.SUM, o.F32, o.F32, xf, 0.5, True), 0.5 + (k * (k + 1) // 2))
+    assert o.scan(o.SUM, o.F32, o.F32, xf[:0], 1.0, True).size == 0
+    # max/min of a permutation: the running max/min
+    p = _rng(50).permutation(n).astype(np.int32)
+    assert np.array_equal(o.scan(o.MAX, o.I32, o.I32, p, o.identity(o.MAX, o.I32), True),
+                          np.maximum.accumulate(p.astype(np.int64)))
+    assert np.array_equal(o.scan(o.MIN, o.I32, o.I32, p, o.identity(o.MIN, o.I32), True),
+                          np.minimum.accumulate(p.astype(np.int64)))
+    ex = o.scan(o.MAX, o.I32, o.I32, p, -1, False)
+    assert ex[0] == -1 and np.array_equal(ex[1:], np.maximum.accumulate(p.astype(np.int64))[:-1])
+
+
+def test_scan_matches_numpy_integer_cumsum():
+    o = _o()
+    x = _rng(51).integers(-2**31, 2**31, 100_001).astype(np.int32)
+    c = np.cumsum(x.astype(np.int64))
+    assert np.array_equal(o.scan(o.SUM, o.I32, o.I64, x, 0, True), c)
+    wrapped = ((c + 2**31) % 2**32) - 2**31
+    assert np.array_equal(o.scan(o.SUM, o.I32, o.I32, x, 0, True), wrapped)
+    y = _rng(52).integers(-2**62, 2**62, 1000).astype(np.int64)
+    c = np.cumsum(y.astype(object))
+    got = o.scan(o.SUM, o.I64, o.I64, y, 0, True)
+    assert all(int(g) == ((int(v) + 2**63) % 2**64) - 2**63 for g, v in zip(got, c))
+
+
+def test_scan_prefixes_equal_whole_array_folds():
+    """Every output of the scan is the whole-array fold of its prefix, with
+    the same start, bit for bit (both are the same left-to-right fold)."""
+    o = _o()
+    rng = _rng(53)
+    for dt in (o.F32, o.BF16, o.F16, o.F64):
+        v = rng.standard_normal(300).astype(np.float32)
+        x = {o.F32: v, o.F64: v.astype(np.float64), o.F16: v.astype(np.float16).view(np.uint16),
+             o.BF16: (v.view(np.uint32) >> 16).astype(np.uint16)}[dt]
+        for op in (o.SUM, o.MAX, o.MIN):
+            s = 0.25 if op == o.SUM else o.identity(op, o.F32)
+            inc = o.scan(op, dt, o.F32, x, s, True)
+            exc = o.scan(op, dt, o.F32, x, s, False)
+            for i in (0, 1, 2, 57, 299):
+                assert inc[i] == o.reduce_all(op, o.IDENTITY, dt, o.F32, x[:i + 1], s)
+                assert exc[i] == o.reduce_all(op, o.IDENTITY, dt, o.F32, x[:i], s)
+
+
+def test_scan_fp_exact_rational_small():
+    o = _o()
+    x = _rng(54).uniform(-1, 1, 400).astype(np.float32)
+    r = o.scan(o.SUM, o.F32, o.F32, x, 0.0, True)
+    exact = Fraction(0)
+    for i, v in enumerate(x):
+        exact += Fraction(float(v))
+        S = float(np.abs(x[:i + 1].astype(np.float64)).sum())
+        assert abs(Fraction(r[i]) - exact) <= Fraction((i + 1) * U53 * S)
+
+
+def test_scan_dims_equals_line_scans():
+    """Along each dim of a strided 3-d view, every line of the output is the
+    1-d scan of that line of the input (lines extracted by numpy indexing)."""
+    o = _o()
+    shape = (5, 7, 3)
+    storage = _rng(55).integers(-50, 50, 400).astype(np.int32)
+    strides = (1, 6, 50)                      # a padded view: 6 > 5, 50 > 6 * 7
+    idx = np.zeros(shape, np.int64)
+    for i in range(shape[0]):
+        for j in range(shape[1]):
+            for k in range(shape[2]):
+                idx[i, j, k] = i * strides[0] + j * strides[1] + k * strides[2]
+    view = storage[idx]                       # view[i, j, k]
+    for dim in range(3):
+        for inclusive in (True, False):
+            got = o.scan_dims(o.SUM, o.I32, o.I64, storage, shape, strides, dim, 3, inclusive)
+            got = got.reshape(shape, order="F")
+            want = np.moveaxis(view, dim, -1).astype(np.int64)
+            c = np.cumsum(want, axis=-1) + 3
+            if not inclusive:
+                c = np.concatenate([np.full(c.shape[:-1] + (1,), 3), c[..., :-1]], axis=-1)
+            assert np.array_equal(np.moveaxis(got, dim, -1), c), (dim, inclusive)
+    # floating input along dim 1 agrees with the 1-d oracle line by line
+    xf = _rng(56).standard_normal(400).astype(np.float32)
+    got = o.scan_dims(o.MAX, o.F32, o.F32, xf, shape, strides, 1, -math.inf, True).reshape(shape, order="F")
+    for i in range(shape[0]):
+        for k in range(shape[2]):
+            line = xf[[i * strides[0] + j * strides[1] + k * strides[2] for j in range(shape[1])]]
+            assert np.array_equal(got[i, :, k], o.scan(o.MAX, o.F32, o.F32, line, -math.inf, True))

@@ -45,6 +45,15 @@ MUTANTS = [
     ("map2_absdiff_no_abs", "case M2_ABSDIFF: return fabs(a - b);", "case M2_ABSDIFF: return a - b;"),
     ("map2_int_mul", "case M2_MUL: r = ua * ub; break;", "case M2_MUL: r = ua * ua; break;"),
     ("all2_second_operand", "load_fp(in_dtype, b, i)));", "load_fp(in_dtype, a, i)));"),
+    ("scan_inclusive_stores_before", "run = op_fp(op, run, v);\n            out[i] = run;",
+     "out[i] = run;\n            run = op_fp(op, run, v);"),
+    ("scan_int_start_dropped", "int64_t run = wrap_to(acc_dtype, start);", "int64_t run = 0;"),
+    ("scan_int_no_wrap", "run = wrap_to(acc_dtype, op_int(op, run, v));\n            out[i] = run;",
+     "run = op_int(op, run, v);\n            out[i] = run;"),
+    ("scan_dims_wrong_dim", "if (d == dim) {\n            line_stride[d] = 0;",
+     "if (d + 1 == dim) {\n            line_stride[d] = 0;"),
+    ("scan_dims_int_exclusive_swapped", "out[t] = run[l];\n            run[l] = wrap_to(acc_dtype, op_int(op, run[l], v));",
+     "run[l] = wrap_to(acc_dtype, op_int(op, run[l], v));\n            out[t] = run[l];"),
 ]
 
 
