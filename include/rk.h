@@ -177,6 +177,57 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
                    uint32_t reduce_mask, const void *init, int mode, void *out,
                    void *workspace, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Scans (prefix folds).  PR #202 (tile scans), opening paragraph:
+ * accumulate! over a whole array or along one dim.  Every line -- the
+ * elements whose indices differ only along the scan dim -- is scanned on its
+ * own: with x_0, x_1, ... its elements in order and s = *init (the op's
+ * identity when init is NULL), output k of the line is
+ *   inclusive = 1:  s (+) x_0 (+) ... (+) x_k
+ *   inclusive = 0:  s (+) x_0 (+) ... (+) x_(k-1)   (output 0 is s)
+ * with elements widened to the accumulator type, running values kept in it,
+ * and each output converted once to out_dtype (nearest even / wrap).  The
+ * association order is the library's own, so floating-point outputs may
+ * differ from a sequential loop by rounding.  The dtype table, ops and
+ * identities are those of the reductions; there is no map.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Bytes of device workspace rk_scan_dims (or rk_scan: ndim = 1, strides[0] =
+ * 1, dim = 0) needs for this layout on the current device: the tile state of
+ * a look-back scan (a counter, one flag and two accumulators per tile),
+ * rounded up to 256 bytes; 0 when the layout takes a kernel without tiles.
+ * Contents need not be initialised; the call clears what it uses.  Returns 0
+ * for invalid arguments as well.
+ */
+size_t rk_scan_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64_t *shape,
+                              const int64_t *strides, int dim);
+
+/*
+ * Scan along dim `dim` (0-based: Julia's dims=k is dim = k-1) of a strided
+ * column-major view with 1 <= ndim <= 4 dims.  `ptr` is the device address
+ * of element (0,...,0), aligned to its element size; `out` is a device
+ * pointer to prod(shape) out-typed elements, the view's shape stored
+ * contiguously in column-major order.  `out` may be `ptr` itself when the
+ * view is contiguous and the two dtypes have the same size (an in-place
+ * scan); any other overlap is rejected.  init: host pointer to one
+ * accumulator-typed value, or NULL.  inclusive: 1 or 0.  workspace: device
+ * pointer to >= rk_scan_workspace_size bytes, aligned to 8 (NULL allowed
+ * when that size is 0); a workspace must not be shared by calls that may run
+ * at the same time.  stream: hipStream_t or NULL; asynchronous.  A line
+ * contiguous along the scan dim and at least one tile long is scanned in one
+ * pass with decoupled look-back between tiles, after a small launch that
+ * clears the tile state.  Returns an rk_status.
+ */
+int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,
+                 const int64_t *shape, const int64_t *strides, int dim, const void *init,
+                 int inclusive, void *out, void *workspace, void *stream);
+
+/* Scan of n contiguous elements: rk_scan_dims with ndim = 1, shape = {n},
+ * strides = {1}, dim = 0. */
+int rk_scan(int op, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int64_t n,
+            const void *init, int inclusive, void *out, void *workspace, void *stream);
+
 /* Static, human-readable name of an rk_status value. */
 const char *rk_status_string(int status);
 
@@ -198,7 +249,10 @@ typedef enum {
     RK_KERNEL_COLUMNS = 5,      /* 2-d block over a wide tile of outputs, split along the reduced dim */
     RK_KERNEL_ROW = 6,          /* one wave per output over a contiguous reduced dim */
     RK_KERNEL_GENERIC = 7,      /* one block per output, any layout */
-    RK_KERNEL_ALL2 = 8          /* whole-array passes over a two-input source (rk_reduce_all2) */
+    RK_KERNEL_ALL2 = 8,         /* whole-array passes over a two-input source (rk_reduce_all2) */
+    RK_KERNEL_SCAN_TILE = 9,    /* scan: tiles of contiguous lines, decoupled look-back (+ a clearing launch) */
+    RK_KERNEL_SCAN_ROWWAVE = 10,/* scan: one wave per contiguous line shorter than a tile */
+    RK_KERNEL_SCAN_LINES = 11   /* scan: one thread per line along a strided scan dim */
 } rk_kernel;
 
 typedef struct {
@@ -224,6 +278,12 @@ int rk_plan_all2(int in_dtype, int acc_dtype, const void *a, const void *b, int6
                  rk_plan_info *info);
 int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const int64_t *shape,
                  const int64_t *strides, uint32_t reduce_mask, int num_cus,
+                 rk_plan_info *info);
+/* Plan of rk_scan_dims: kernel is one of the RK_KERNEL_SCAN_* values (NONE
+ * for an empty view), split is the tiles per line, tile_outputs the elements
+ * per tile, n_out the number of outputs and reduce_len the line length. */
+int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, const void *out, int ndim,
+                 const int64_t *shape, const int64_t *strides, int dim, int num_cus,
                  rk_plan_info *info);
 
 /* Whether a split reduction may finish in the last block to arrive (one

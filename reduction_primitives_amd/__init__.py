@@ -16,11 +16,13 @@ from ._native import (  # noqa: F401
     EXPORTS, KERNEL_NAMES, LIB_PATH, RK_BF16, RK_ERR_HIP, RK_ERR_INVALID_ARGUMENT,
     RK_ERR_UNSUPPORTED, RK_F16, RK_F32, RK_F64, RK_I32, RK_I64, RK_KERNEL_ALL,
     RK_KERNEL_ALL2, RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE,
-    RK_KERNEL_ROW, RK_KERNEL_THREAD, RK_KERNEL_TILED, RK_MAP2_ABSDIFF, RK_MAP2_MUL, RK_MAP2_SQDIFF,
+    RK_KERNEL_ROW, RK_KERNEL_SCAN_LINES, RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_TILE, RK_KERNEL_THREAD,
+    RK_KERNEL_TILED, RK_MAP2_ABSDIFF, RK_MAP2_MUL, RK_MAP2_SQDIFF,
     RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
     RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,
     RkError, load, rk_debug_set_fused_finish, rk_debug_set_launch_events, rk_plan_all, rk_plan_all2, rk_plan_dims,
-    rk_plan_info, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_workspace_size, status_string)
+    rk_plan_info, rk_plan_scan, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_scan, rk_scan_dims,
+    rk_scan_workspace_size, rk_workspace_size, status_string)
 
 OPS = {"sum": RK_OP_SUM, "max": RK_OP_MAX, "min": RK_OP_MIN}
 MAPS = {"identity": RK_MAP_IDENTITY, "square": RK_MAP_SQUARE, "abs": RK_MAP_ABS}
@@ -206,6 +208,47 @@ def reduce_dims(x, shape, strides, dims, op="sum", map="identity", acc=None, out
                         init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
     _check(rc, "rk_reduce_dims")
     return out
+
+
+def scan(x, shape=None, strides=None, dim=1, op="sum", acc=None, out_dtype=None, init=None,
+         inclusive=True, out=None, workspace=None, stream=None, offset=0):
+    """Scan along `dim` (1-based, Julia style) of the column-major view
+    (shape, strides in elements) of device tensor x's storage, starting
+    `offset` elements into x; shape/strides default to x as a flat 1-d
+    array.  Returns `out`: the view's shape, flat, column-major.  `out` may
+    be x itself for an in-place scan of a contiguous view."""
+    torch = _torch()
+    in_code = dtype_code(x.dtype)
+    acc_code = default_acc(in_code) if acc is None else dtype_code(acc)
+    out_code = in_code if out_dtype is None else dtype_code(out_dtype)
+    if out_code in (RK_I32, RK_I64) and in_code in (RK_I32, RK_I64) and out_dtype is None:
+        out_code = acc_code
+    if shape is None:
+        shape, strides = (x.numel() - int(offset),), (1,)
+    d0 = int(dim) - 1
+    total = math.prod(int(s) for s in shape)
+    ptr = x.data_ptr() + int(offset) * x.element_size()
+    if workspace is None:
+        workspace = workspace_for(rk_scan_workspace_size(in_code, acc_code, len(shape), shape, strides, d0),
+                                  x.device)
+    if out is None:
+        out = torch.empty(max(total, 1), dtype=torch_dtype(out_code), device=x.device)
+    rc = rk_scan_dims(_code(OPS, op), in_code, acc_code, out_code, ptr, len(shape), shape, strides, d0,
+                      init_arg(acc_code, init), int(bool(inclusive)), out.data_ptr(), workspace.data_ptr(),
+                      _stream_handle(stream))
+    _check(rc, "rk_scan_dims")
+    return out
+
+
+def plan_scan(dtype, shape, strides, dim, acc=None, out_dtype=None, ptr=0, out=0, num_cus=0) -> dict:
+    """The plan rk_scan_dims would use, as a dict (no launch)."""
+    in_code = dtype_code(dtype)
+    acc_code = default_acc(in_code) if acc is None else dtype_code(acc)
+    out_code = acc_code if out_dtype is None else dtype_code(out_dtype)
+    info = rk_plan_scan(in_code, acc_code, out_code, ptr, out, len(shape), shape, strides, int(dim) - 1, num_cus)
+    d = {f: getattr(info, f) for f, _ in rk_plan_info._fields_}
+    d["kernel_name"] = KERNEL_NAMES[info.kernel]
+    return d
 
 
 def plan_dims(dtype, shape, strides, dims, acc=None, ptr=0, num_cus=0) -> dict:

@@ -20,14 +20,17 @@ RK_MAP2_MUL, RK_MAP2_SQDIFF, RK_MAP2_ABSDIFF = 0, 1, 2
 RK_F32, RK_BF16, RK_F16, RK_F64, RK_I32, RK_I64 = 0, 1, 2, 3, 4, 5
 RK_MODE_OVERWRITE, RK_MODE_FOLD, RK_MODE_HOST = 0, 1, 2
 (RK_KERNEL_NONE, RK_KERNEL_ALL, RK_KERNEL_ALL_STRIDED, RK_KERNEL_THREAD, RK_KERNEL_TILED,
- RK_KERNEL_COLUMNS, RK_KERNEL_ROW, RK_KERNEL_GENERIC, RK_KERNEL_ALL2) = range(9)
+ RK_KERNEL_COLUMNS, RK_KERNEL_ROW, RK_KERNEL_GENERIC, RK_KERNEL_ALL2, RK_KERNEL_SCAN_TILE,
+ RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_LINES) = range(12)
 KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 5: "columns",
-                6: "row", 7: "generic", 8: "all2"}
+                6: "row", 7: "generic", 8: "all2", 9: "scan_tile", 10: "scan_rowwave",
+                11: "scan_lines"}
 
 # every function include/rk.h declares
 EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_dims", "rk_status_string",
            "rk_plan_all", "rk_plan_all2", "rk_plan_dims", "rk_debug_set_fused_finish",
-           "rk_debug_set_launch_events")
+           "rk_debug_set_launch_events", "rk_scan_workspace_size", "rk_scan", "rk_scan_dims",
+           "rk_plan_scan")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -70,6 +73,14 @@ def load() -> ctypes.CDLL:
     lib.rk_reduce_all2.restype = i32
     lib.rk_reduce_dims.argtypes = [i32, i32, i32, i32, i32, vp, i32, p64, p64, u32, vp, i32, vp, vp, vp]
     lib.rk_reduce_dims.restype = i32
+    lib.rk_scan_workspace_size.argtypes = [i32, i32, i32, p64, p64, i32]
+    lib.rk_scan_workspace_size.restype = sz
+    lib.rk_scan.argtypes = [i32, i32, i32, i32, vp, i64, vp, i32, vp, vp, vp]
+    lib.rk_scan.restype = i32
+    lib.rk_scan_dims.argtypes = [i32, i32, i32, i32, vp, i32, p64, p64, i32, vp, i32, vp, vp, vp]
+    lib.rk_scan_dims.restype = i32
+    lib.rk_plan_scan.argtypes = [i32, i32, i32, vp, vp, i32, p64, p64, i32, i32, ctypes.POINTER(rk_plan_info)]
+    lib.rk_plan_scan.restype = i32
     lib.rk_status_string.argtypes = [i32]
     lib.rk_status_string.restype = ctypes.c_char_p
     lib.rk_plan_all.argtypes = [i32, i32, vp, i64, i32, ctypes.POINTER(rk_plan_info)]
@@ -142,6 +153,31 @@ def rk_plan_dims(in_dtype, acc_dtype, ptr, ndim, shape, strides, reduce_mask, nu
                              reduce_mask, num_cus, ctypes.byref(info))
     if rc:
         raise RkError(rc, "rk_plan_dims")
+    return info
+
+
+def rk_scan_workspace_size(in_dtype, acc_dtype, ndim, shape, strides, dim) -> int:
+    return int(load().rk_scan_workspace_size(in_dtype, acc_dtype, ndim, _i64_array(shape),
+                                             _i64_array(strides), dim))
+
+
+def rk_scan(op, in_dtype, acc_dtype, out_dtype, ptr, n, init, inclusive, out, workspace, stream) -> int:
+    return int(load().rk_scan(op, in_dtype, acc_dtype, out_dtype, ptr, n, init, inclusive, out, workspace,
+                              stream))
+
+
+def rk_scan_dims(op, in_dtype, acc_dtype, out_dtype, ptr, ndim, shape, strides, dim, init, inclusive, out,
+                 workspace, stream) -> int:
+    return int(load().rk_scan_dims(op, in_dtype, acc_dtype, out_dtype, ptr, ndim, _i64_array(shape),
+                                   _i64_array(strides), dim, init, inclusive, out, workspace, stream))
+
+
+def rk_plan_scan(in_dtype, acc_dtype, out_dtype, ptr, out, ndim, shape, strides, dim, num_cus=0) -> rk_plan_info:
+    info = rk_plan_info()
+    rc = load().rk_plan_scan(in_dtype, acc_dtype, out_dtype, ptr, out, ndim, _i64_array(shape),
+                             _i64_array(strides), dim, num_cus, ctypes.byref(info))
+    if rc:
+        raise RkError(rc, "rk_plan_scan")
     return info
 
 

@@ -230,6 +230,19 @@ void host_finish(int op, int acc, uint64_t init_bits, const void *partial, int h
     }
 }
 
+int dispatch_scan(int in_dtype, const ScanLaunch &L)
+{
+    switch (in_dtype) {
+    case F32: return launch_scan_in_f32(L);
+    case BF16: return launch_scan_in_bf16(L);
+    case F16: return launch_scan_in_f16(L);
+    case F64: return launch_scan_in_f64(L);
+    case I32: return launch_scan_in_i32(L);
+    case I64: return launch_scan_in_i64(L);
+    }
+    return RK_ERR_INVALID_ARGUMENT;
+}
+
 int dispatch(int in_dtype, const Launch &L)
 {
     switch (in_dtype) {
@@ -657,6 +670,131 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
     L.ev_begin = t_ev_begin;
     L.ev_end = t_ev_end;
     return dispatch(in_dtype, L);
+}
+
+size_t rk_scan_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64_t *shape, const int64_t *strides,
+                              int dim)
+{
+    ScanPlan d;
+    if (plan_scan(in_dtype, acc_dtype, acc_dtype, 0, 0, ndim, shape, strides, dim, device_cus(), &d) != ST_OK)
+        return 0;
+    return d.ws_bytes;
+}
+
+int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, const void *out, int ndim,
+                 const int64_t *shape, const int64_t *strides, int dim, int num_cus, rk_plan_info *info)
+{
+    if (!info)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (num_cus <= 0)
+        num_cus = device_cus();
+    ScanPlan d;
+    int rc = plan_scan(in_dtype, acc_dtype, out_dtype, reinterpret_cast<uintptr_t>(ptr),
+                       reinterpret_cast<uintptr_t>(out), ndim, shape, strides, dim, num_cus, &d);
+    if (rc)
+        return rc;
+    std::memset(info, 0, sizeof *info);
+    info->kernel = d.kernel == SK_TILE ? RK_KERNEL_SCAN_TILE
+                   : d.kernel == SK_ROWWAVE ? RK_KERNEL_SCAN_ROWWAVE
+                   : d.kernel == SK_LINES ? RK_KERNEL_SCAN_LINES : RK_KERNEL_NONE;
+    info->launches = d.kernel == SK_TILE ? 2 : d.kernel == SK_NONE ? 0 : 1;
+    info->grid = d.grid;
+    info->block = d.block;
+    info->split = int(d.tiles_per_line > 0 ? d.tiles_per_line : 1);
+    info->vec = d.vec;
+    info->tile_outputs = int(d.tile_elems);
+    info->n_out = d.lines * d.m;
+    info->reduce_len = d.m;
+    info->workspace_bytes = d.ws_bytes;
+    return RK_OK;
+}
+
+int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,
+                 const int64_t *shape, const int64_t *strides, int dim, const void *init, int inclusive, void *out,
+                 void *workspace, void *stream)
+{
+    int rc = check_types(op, 0, in_dtype, acc_dtype, out_dtype, RK_MODE_OVERWRITE);
+    if (rc)
+        return rc;
+    if (!shape || !strides || ndim < 1 || ndim > kMaxDims || dim < 0 || dim >= ndim || !out)
+        return RK_ERR_INVALID_ARGUMENT;
+    if (inclusive != 0 && inclusive != 1)
+        return RK_ERR_INVALID_ARGUMENT;
+    ScanPlan d;
+    rc = plan_scan(in_dtype, acc_dtype, out_dtype, reinterpret_cast<uintptr_t>(ptr), reinterpret_cast<uintptr_t>(out),
+                   ndim, shape, strides, dim, device_cus(), &d);
+    if (rc)
+        return rc;
+    const int64_t total = d.lines * d.m;
+    const size_t isz = dtype_size(in_dtype), osz = dtype_size(out_dtype);
+    if ((total > 0 && !ptr) || (ptr && !aligned(ptr, isz)) || !aligned(out, osz))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (d.ws_bytes > 0 && (!workspace || !aligned(workspace, 8)))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (total > 0) {
+        // the output may be the input itself (same layout and element size), but may not overlap it otherwise
+        int64_t last = 0, cm = 1;
+        bool same_layout = isz == osz;
+        for (int i = 0; i < ndim; ++i) {
+            last += (shape[i] - 1) * strides[i];
+            same_layout = same_layout && (shape[i] == 1 || strides[i] == cm);
+            cm *= shape[i];
+        }
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(ptr), a1 = a0 + size_t(last + 1) * isz;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(out), b1 = b0 + size_t(total) * osz;
+        const bool overlap = a0 < b1 && b0 < a1;
+        if (overlap && !(b0 == a0 && same_layout))
+            return RK_ERR_INVALID_ARGUMENT;
+    }
+    if (d.grid > std::numeric_limits<int32_t>::max())
+        return RK_ERR_UNSUPPORTED;
+    if (debug_enabled())
+        std::fprintf(stderr, "rk_scan_dims: kernel=%d lines=%lld m=%lld grid=%lld vec=%d tiles=%lld ws=%zu\n",
+                     d.kernel, (long long)d.lines, (long long)d.m, (long long)d.grid, d.vec, (long long)d.tiles,
+                     d.ws_bytes);
+    if (d.kernel == SK_NONE)
+        return RK_OK;
+    ScanLaunch L;
+    std::memset(&L, 0, sizeof L);
+    L.kernel = d.kernel;
+    L.acc = acc_dtype;
+    L.op = op;
+    L.vec = d.vec;
+    L.grid = d.grid;
+    L.block = d.block;
+    ScanArgs &a = L.args;
+    a.x = ptr;
+    a.out = out;
+    a.ws = workspace;
+    a.m = d.m;
+    a.lines = d.lines;
+    a.kept_nd = d.kept_in.nd;
+    for (int i = 0; i < d.kept_in.nd; ++i) {
+        a.kept_ext[i] = d.kept_in.ext[i];
+        a.kept_in[i] = d.kept_in.str[i];
+        a.kept_out[i] = d.kept_out[i];
+    }
+    a.s_in = d.s_in;
+    a.s_out = d.s_out;
+    a.tiles_per_line = d.tiles_per_line;
+    a.tiles = d.tiles;
+    a.inclusive = inclusive;
+    a.out_dtype = out_dtype;
+    a.init_bits = start_bits(op, acc_dtype, init);
+    L.stream = stream;
+    L.ev_begin = t_ev_begin;
+    L.ev_end = t_ev_end;
+    return dispatch_scan(in_dtype, L);
+}
+
+int rk_scan(int op, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int64_t n, const void *init,
+            int inclusive, void *out, void *workspace, void *stream)
+{
+    if (n < 0)
+        return RK_ERR_INVALID_ARGUMENT;
+    const int64_t shape[1] = {n}, strides[1] = {1};
+    return rk_scan_dims(op, in_dtype, acc_dtype, out_dtype, ptr, 1, shape, strides, 0, init, inclusive, out,
+                        workspace, stream);
 }
 
 }  // extern "C"

@@ -20,6 +20,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "rk_device.hpp"
 
 namespace rk {

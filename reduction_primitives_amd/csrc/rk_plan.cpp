@@ -360,4 +360,88 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
     return ST_OK;
 }
 
+// ------------------------------------------------------------------ scans
+
+int64_t scan_tile_elems(int in_dtype)
+{
+    const int isz = dtype_size(in_dtype);
+    if (isz == 0)
+        return 0;
+    return int64_t(tune::kScanBlock / 64) * tune::kScanUnroll * 64 * (16 / isz);
+}
+
+int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
+              const int64_t *shape, const int64_t *strides, int dim, int num_cus, ScanPlan *p)
+{
+    if (!p || !shape || !strides || ndim < 1 || ndim > kMaxDims || dim < 0 || dim >= ndim)
+        return ST_INVALID;
+    if (!dtype_known(in_dtype) || !dtype_known(acc_dtype) || !dtype_known(out_dtype))
+        return ST_INVALID;
+    if (num_cus <= 0)
+        num_cus = tune::kDefaultCus;
+    const int isz = dtype_size(in_dtype), osz = dtype_size(out_dtype);
+    ScanPlan d;
+    int64_t total = 1, ostr[kMaxDims];
+    for (int i = 0; i < ndim; ++i) {
+        if (shape[i] < 0 || strides[i] < 0)
+            return ST_INVALID;
+        ostr[i] = total;                        // the output is contiguous, column-major
+        total *= shape[i];
+    }
+    d.m = shape[dim];
+    d.s_in = strides[dim];
+    d.s_out = ostr[dim];
+    if (total == 0) {
+        *p = d;
+        return ST_OK;
+    }
+    d.lines = total / d.m;
+    // kept dims: drop extent 1, merge neighbours whose input and output strides both chain
+    Layout &k = d.kept_in;
+    for (int i = 0; i < ndim; ++i) {
+        if (i == dim || shape[i] == 1)
+            continue;
+        if (k.nd > 0) {
+            const int j = k.nd - 1;
+            if (strides[i] == k.str[j] * k.ext[j] && ostr[i] == d.kept_out[j] * k.ext[j]) {
+                k.ext[j] *= shape[i];
+                continue;
+            }
+        }
+        k.ext[k.nd] = shape[i];
+        k.str[k.nd] = strides[i];
+        d.kept_out[k.nd] = ostr[i];
+        ++k.nd;
+    }
+    const int v = 16 / isz;
+    if (d.s_in == 1 && d.s_out == 1 && d.m >= tune::kScanWaveMinLen) {
+        // lines contiguous along the scan dim in both input and output
+        const int ob = std::min(16, v * osz);   // bytes of one lane's outputs, up to 16
+        bool vec_ok = in_addr % 16 == 0 && d.m % v == 0 && out_addr % ob == 0;
+        for (int i = 0; i < k.nd; ++i)
+            vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0 && (d.kept_out[i] * osz) % ob == 0;
+        d.vec = vec_ok ? v : 1;
+        d.tile_elems = scan_tile_elems(in_dtype);
+        if (d.m >= d.tile_elems) {
+            d.kernel = SK_TILE;
+            d.tiles_per_line = ceil_div(d.m, d.tile_elems);
+            d.tiles = d.lines * d.tiles_per_line;
+            d.grid = d.tiles;
+            // header, flags (rounded to 8 bytes), aggregates, prefixes
+            d.ws_bytes = round_up_256(8 + size_t((d.tiles + 1) & ~int64_t(1)) * 4 + size_t(d.tiles) * 16);
+        } else {
+            d.kernel = SK_ROWWAVE;
+            d.grid = ceil_div(d.lines, tune::kScanBlock / 64);
+        }
+    } else {
+        d.kernel = SK_LINES;
+        d.vec = 1;
+        d.grid = std::min<int64_t>(ceil_div(d.lines, tune::kScanBlock),
+                                   int64_t(num_cus) * tune::kScanLinesBlocksPerCu);
+    }
+    d.block = tune::kScanBlock;
+    *p = d;
+    return ST_OK;
+}
+
 }  // namespace rk

@@ -1,0 +1,577 @@
+// rk_scan.hpp -- scans (prefix folds) on gfx950.
+//
+// AcceleratedKernels.jl PR #202 (tile scans), opening paragraph: accumulate!
+// over a whole array or along one dim; every output k of a line is the fold
+// of the line's elements 0..k (inclusive) or 0..k-1 (exclusive), started
+// from init.  The page's kernels give each thread a run of consecutive
+// elements in shared memory and pad the runs to an odd stride against bank
+// conflicts.  Here a scan keeps the data in registers instead: lane l of a
+// wave holds the l-th 16-byte vector of a 64-vector chunk (one fully
+// coalesced load), scans its own few elements, and a wave64 DPP scan of the
+// lane totals gives every lane its offset, so no element goes through LDS.
+//
+// Three kernels, chosen by plan_scan():
+//   k_scan_tile     lines contiguous along the scan dim and at least one
+//                   tile long (the whole array included): one pass, tiles in
+//                   the order of a counter, each tile's prefix from its
+//                   predecessors by decoupled look-back (Merrill and Garland,
+//                   "Single-pass Parallel Prefix Scan with Decoupled
+//                   Look-back", 2016);
+//   k_scan_rowwave  shorter contiguous lines: one wave per line;
+//   k_scan_lines    a strided scan dim: one thread per line, walking it.
+#pragma once
+
+#include "rk_kernels.hpp"
+
+namespace rk {
+
+// ------------------------------------------------------------ lane moves
+
+// DPP row shifts: lane i of a 16-lane row reads lane i - n of the same row;
+// lanes without a source take `fill`.
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_shift(T v, T fill)
+{
+    if constexpr (sizeof(T) == 4) {
+        return bitcast<T>((uint32_t)__builtin_amdgcn_update_dpp((int)bitcast<uint32_t>(fill), (int)bitcast<uint32_t>(v),
+                                                                CTRL, 0xf, 0xf, false));
+    } else {
+        const uint64_t u = bitcast<uint64_t>(v), f = bitcast<uint64_t>(fill);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)f, (int)(uint32_t)u, CTRL, 0xf,
+                                                                  0xf, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(f >> 32), (int)(uint32_t)(u >> 32),
+                                                                  CTRL, 0xf, 0xf, false);
+        return bitcast<T>(((uint64_t)hi << 32) | lo);
+    }
+}
+
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+
+// Inclusive scan over the 64 lanes of a wave: lane i gets v_0 (+) ... (+) v_i.
+// Steps of 1, 2, 4 and 8 lanes inside each 16-lane row (Hillis and Steele),
+// then every row adds the totals of the rows before it, read from lanes 15,
+// 31 and 47.  All 64 lanes must be active.
+template <class Op, class T>
+__device__ __forceinline__ T wave_scan_incl(T v)
+{
+    const T id = Op::template identity<T>();
+    v = Op::apply(dpp_shift<kDppRowShr1>(v, id), v);
+    v = Op::apply(dpp_shift<kDppRowShr2>(v, id), v);
+    v = Op::apply(dpp_shift<kDppRowShr4>(v, id), v);
+    v = Op::apply(dpp_shift<kDppRowShr8>(v, id), v);
+    const T r0 = read_lane(v, 15), r1 = read_lane(v, 31), r2 = read_lane(v, 47);
+    const int row = lane_id() >> 4;
+    T pre = r0;
+    pre = row >= 2 ? Op::apply(pre, r1) : pre;
+    pre = row >= 3 ? Op::apply(pre, r2) : pre;
+    return row >= 1 ? Op::apply(pre, v) : v;
+}
+
+// Value of the previous lane; lane 0 gets `fill`.  All 64 lanes active.
+template <class T>
+__device__ __forceinline__ T lane_prev(T v, T fill)
+{
+    const int src = lane_id() > 0 ? lane_id() - 1 : 0;
+    const T p = move_words(v, [src](uint32_t w) { return bpermute32(w, src); });
+    return lane_id() > 0 ? p : fill;
+}
+
+// ---------------------------------------------------------------- outputs
+
+// Storage type and conversion of an accumulator for each output dtype (the
+// same rounding as store_out: nearest even, through round-to-odd from f64).
+template <int OD> struct OutT;
+template <> struct OutT<F32> {
+    using S = float;
+    template <class A> __device__ static S conv(A v) { return (float)v; }
+};
+template <> struct OutT<F64> {
+    using S = double;
+    template <class A> __device__ static S conv(A v) { return (double)v; }
+};
+template <> struct OutT<BF16> {
+    using S = uint16_t;
+    template <class A> __device__ static S conv(A v)
+    {
+        if constexpr (std::is_same_v<A, double>)
+            return f32_to_bf16_rne(f64_to_f32_odd(v));
+        else
+            return f32_to_bf16_rne((float)v);
+    }
+};
+template <> struct OutT<F16> {
+    using S = uint16_t;
+    template <class A> __device__ static S conv(A v)
+    {
+        float f;
+        if constexpr (std::is_same_v<A, double>)
+            f = f64_to_f32_odd(v);
+        else
+            f = (float)v;
+        return bitcast<uint16_t>((_Float16)f);
+    }
+};
+template <> struct OutT<I32> {
+    using S = int32_t;
+    template <class A> __device__ static S conv(A v) { return (int32_t)(uint32_t)(uint64_t)v; }
+};
+template <> struct OutT<I64> {
+    using S = int64_t;
+    template <class A> __device__ static S conv(A v) { return (int64_t)v; }
+};
+
+// Store V consecutive outputs at element idx of `out`, converted to OD, in
+// the widest pieces their byte count allows (the caller guarantees that
+// alignment when V > 1).
+template <int OD, class Acc, int V>
+__device__ __forceinline__ void store_run_as(void *out, int64_t idx, const Acc (&v)[V])
+{
+    using S = typename OutT<OD>::S;
+    S t[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        t[i] = OutT<OD>::conv(v[i]);
+    char *p = reinterpret_cast<char *>(static_cast<S *>(out) + idx);
+    constexpr int NB = int(sizeof(t));
+    if constexpr (NB % 16 == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; b += 16) {
+            u32x4 w;
+            __builtin_memcpy(&w, reinterpret_cast<const char *>(t) + b, 16);
+            *reinterpret_cast<u32x4 *>(p + b) = w;
+        }
+    } else if constexpr (NB % 8 == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; b += 8) {
+            uint64_t w;
+            __builtin_memcpy(&w, reinterpret_cast<const char *>(t) + b, 8);
+            *reinterpret_cast<uint64_t *>(p + b) = w;
+        }
+    } else if constexpr (NB % 4 == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; b += 4) {
+            uint32_t w;
+            __builtin_memcpy(&w, reinterpret_cast<const char *>(t) + b, 4);
+            *reinterpret_cast<uint32_t *>(p + b) = w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            reinterpret_cast<S *>(p)[i] = t[i];
+    }
+}
+
+template <class Acc, int V>
+__device__ __forceinline__ void store_run(void *out, int64_t idx, int out_dtype, const Acc (&v)[V])
+{
+    if constexpr (std::is_floating_point_v<Acc>) {
+        switch (out_dtype) {
+        case F32: store_run_as<F32, Acc, V>(out, idx, v); break;
+        case F64: store_run_as<F64, Acc, V>(out, idx, v); break;
+        case BF16: store_run_as<BF16, Acc, V>(out, idx, v); break;
+        case F16: store_run_as<F16, Acc, V>(out, idx, v); break;
+        default: break;
+        }
+    } else {
+        switch (out_dtype) {
+        case I32: store_run_as<I32, Acc, V>(out, idx, v); break;
+        case I64: store_run_as<I64, Acc, V>(out, idx, v); break;
+        default: break;
+        }
+    }
+}
+
+// ------------------------------------------------------------ chunk scans
+
+// A chunk is 64 * V consecutive elements of a line: lane l holds elements
+// l*V .. l*V+V-1 (one 16-byte load when V > 1).  Elements past the line's
+// end hold the identity.
+template <class In, class Acc, class Op, bool VECTOR>
+struct Chunk {
+    using S = typename InTraits<In>::S;
+    static constexpr int V = VECTOR ? InTraits<In>::vec : 1;
+    using Raw = std::conditional_t<VECTOR, u32x4, S>;
+
+    __device__ static Raw load(const S *x, int64_t i, int64_t m)
+    {
+        Raw r{};
+        if (i < m) {
+            if constexpr (VECTOR)
+                r = load16(reinterpret_cast<const u32x4 *>(x + i));
+            else
+                r = load1(x + i);
+        }
+        return r;
+    }
+
+    __device__ static void decode(Raw r, bool valid, Acc (&e)[V])
+    {
+        if constexpr (VECTOR)
+            InTraits<In>::template decode<Acc>(r, e);
+        else
+            e[0] = InTraits<In>::template one<Acc>(r);
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            e[i] = valid ? e[i] : Op::template identity<Acc>();
+    }
+};
+
+// Scan of one chunk: the lane's exclusive offset inside the chunk and the
+// chunk's total (wave-uniform).
+template <class Acc, class Op, int V>
+__device__ __forceinline__ void chunk_scan(const Acc (&e)[V], Acc &lane_excl, Acc &total)
+{
+    Acc t = e[0];
+#pragma unroll
+    for (int i = 1; i < V; ++i)
+        t = Op::apply(t, e[i]);
+    const Acc incl = wave_scan_incl<Op>(t);
+    total = read_lane(incl, 63);
+    lane_excl = lane_prev(incl, Op::template identity<Acc>());
+}
+
+// Outputs of one chunk from `run` = everything before the lane's first element.
+template <class Acc, class Op, int V>
+__device__ __forceinline__ void chunk_outputs(const Acc (&e)[V], Acc run, bool inclusive, Acc (&o)[V])
+{
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        if (inclusive) {
+            run = Op::apply(run, e[i]);
+            o[i] = run;
+        } else {
+            o[i] = run;
+            run = Op::apply(run, e[i]);
+        }
+    }
+}
+
+// ------------------------------------------------------- tile look-back
+
+// Tile state in the workspace: an 8-byte header holding the tile counter and
+// a timeout word (nonzero if a look-back wait gave up; never in normal runs),
+// one 32-bit flag per tile (0 nothing yet, 1 aggregate, 2 inclusive prefix),
+// then one 8-byte slot per tile for the aggregate and one for the prefix.
+// A value is stored, its store waited for, and only then its flag, all at
+// device scope; a reader loads the flag first and the value after it.
+struct ScanState {
+    uint32_t *counter;
+    uint32_t *flags;
+    uint64_t *aggs;
+    uint64_t *pres;
+
+    __device__ ScanState(void *ws, int64_t tiles)
+    {
+        counter = static_cast<uint32_t *>(ws);
+        flags = counter + 2;
+        aggs = reinterpret_cast<uint64_t *>(flags + ((tiles + 1) & ~int64_t(1)));
+        pres = aggs + tiles;
+    }
+};
+
+constexpr uint32_t kFlagAggregate = 1;
+constexpr uint32_t kFlagPrefix = 2;
+
+template <class Acc>
+__device__ __forceinline__ void publish(const ScanState &st, int64_t g, Acc v, uint32_t flag)
+{
+    store_partial(reinterpret_cast<Acc *>((flag == kFlagPrefix ? st.pres : st.aggs) + g), v);
+    wait_stores();
+    __hip_atomic_store(st.flags + g, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix of tile t (global index g) of a line, run by one whole
+// wave: publish the tile's aggregate, then read the predecessors 64 at a time
+// (lane 0 the nearest) until one with its inclusive prefix.  Every tile with
+// a smaller counter value has already started, and it publishes its
+// aggregate without waiting on anything, so every wait here ends.  As a
+// safety net each wait is still bounded (tune::kScanSpinLimit sleeps): past
+// it the tile records the timeout in the workspace header and goes on, so
+// every wave exits.  Publishes the tile's own inclusive prefix before
+// returning.
+template <class Acc, class Op>
+__device__ Acc scan_lookback(const ScanState &st, int64_t g, int64_t t, Acc agg, Acc init)
+{
+    const int lane = lane_id();
+    if (t == 0) {
+        if (lane == 0)
+            publish(st, g, Op::apply(init, agg), kFlagPrefix);
+        return init;
+    }
+    if (lane == 0)
+        publish(st, g, agg, kFlagAggregate);
+    const int64_t g0 = g - t;                  // the line's first tile
+    Acc acc = Op::template identity<Acc>();    // fold of the tiles after the window
+    int64_t top = t - 1;
+    for (;;) {
+        const int64_t j = top - lane;
+        const bool valid = j >= 0;
+        uint32_t f;
+        uint64_t pm, zm;
+        for (int spin = 0;; ++spin) {
+            f = valid ? __hip_atomic_load(st.flags + g0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : kFlagPrefix;
+            pm = __ballot(f == kFlagPrefix);
+            zm = __ballot(f == 0);
+            // done when every lane before the first prefix has published
+            const uint64_t need = pm ? (pm & (0 - pm)) - 1 : ~uint64_t(0);
+            if ((zm & need) == 0)
+                break;
+            if (spin >= tune::kScanSpinLimit) {
+                if (lane == 0)
+                    __hip_atomic_store(st.counter + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const int first = pm ? __builtin_ctzll(pm) : 64;   // lane of the nearest prefix
+        Acc v = Op::template identity<Acc>();
+        if (lane < first)
+            v = load_partial(reinterpret_cast<const Acc *>(st.aggs + g0 + j));
+        else if (lane == first)
+            v = load_partial(reinterpret_cast<const Acc *>(st.pres + g0 + j));
+        acc = Op::apply(wave_reduce<Op>(v), acc);
+        if (pm)
+            break;
+        top -= 64;
+    }
+    if (lane == 0)
+        publish(st, g, Op::apply(acc, agg), kFlagPrefix);
+    return acc;
+}
+
+// ------------------------------------------------------------------ kernels
+
+// Zero the tile counter and flags before a tile scan (a fill kernel, not a
+// memset, so the call can be captured in a graph).
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_scan_clear(uint32_t *w, int64_t words)
+{
+    for (int64_t i = int64_t(blockIdx.x) * BLOCK + threadIdx.x; i < words; i += int64_t(gridDim.x) * BLOCK)
+        w[i] = 0;
+}
+
+// Tile kernel: a tile is NW waves x UC chunks of consecutive elements of one
+// line; tiles are numbered by a counter in the order blocks start.
+template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR>
+__global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
+{
+    using C = Chunk<In, Acc, Op, VECTOR>;
+    using S = typename C::S;
+    constexpr int V = C::V;
+    constexpr int UC = VECTOR ? U : U * InTraits<In>::vec;   // chunks per wave
+    constexpr int64_t CH = 64 * V;
+    constexpr int NW = BLOCK / 64;
+    constexpr int64_t T = int64_t(NW) * UC * CH;
+
+    __shared__ uint32_t s_id;
+    __shared__ Acc s_wave[NW];
+    __shared__ Acc s_excl;
+    const ScanState st(a.ws, a.tiles);
+    if (threadIdx.x == 0)
+        s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t g = s_id;
+    const int64_t line = g / a.tiles_per_line;
+    const int64_t t = g - line * a.tiles_per_line;
+    const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
+    const int64_t ob = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
+    const int w = (int)(threadIdx.x >> 6);
+    const int64_t first = t * T + int64_t(w) * UC * CH + int64_t(lane_id()) * V;
+
+    typename C::Raw raw[UC];
+#pragma unroll
+    for (int k = 0; k < UC; ++k)
+        raw[k] = C::load(x, first + k * CH, a.m);
+    issue_barrier();
+
+    Acc lane_excl[UC], total[UC];
+#pragma unroll
+    for (int k = 0; k < UC; ++k) {
+        Acc e[V];
+        C::decode(raw[k], first + k * CH < a.m, e);
+        chunk_scan<Acc, Op, V>(e, lane_excl[k], total[k]);
+    }
+    Acc wt = total[0];
+#pragma unroll
+    for (int k = 1; k < UC; ++k)
+        wt = Op::apply(wt, total[k]);
+    if (lane_id() == 0)
+        s_wave[w] = wt;
+    __syncthreads();
+    Acc agg = s_wave[0], wpre = Op::template identity<Acc>();
+#pragma unroll
+    for (int v = 1; v < NW; ++v) {
+        if (v == w)
+            wpre = agg;
+        agg = Op::apply(agg, s_wave[v]);
+    }
+    if (w == 0) {
+        const Acc excl = scan_lookback<Acc, Op>(st, g, t, agg, from_bits<Acc>(a.init_bits));
+        if (lane_id() == 0)
+            s_excl = excl;
+    }
+    __syncthreads();
+
+    Acc carry = Op::apply(s_excl, wpre);
+#pragma unroll
+    for (int k = 0; k < UC; ++k) {
+        const int64_t i = first + k * CH;
+        Acc e[V], o[V];
+        C::decode(raw[k], i < a.m, e);
+        chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl[k]), a.inclusive != 0, o);
+        if (i < a.m)
+            store_run<Acc, V>(a.out, ob + i, a.out_dtype, o);
+        carry = Op::apply(carry, total[k]);
+    }
+}
+
+// Row-wave kernel: one wave per line, UC chunks in flight, the carry passed
+// from chunk to chunk.
+template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR>
+__global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
+{
+    using C = Chunk<In, Acc, Op, VECTOR>;
+    using S = typename C::S;
+    constexpr int V = C::V;
+    constexpr int UC = VECTOR ? U : U * InTraits<In>::vec;
+    constexpr int64_t CH = 64 * V;
+    const int64_t line = int64_t(blockIdx.x) * (BLOCK / 64) + (threadIdx.x >> 6);
+    if (line >= a.lines)
+        return;                                // whole wave; no block barrier below
+    const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
+    const int64_t ob = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
+    Acc carry = from_bits<Acc>(a.init_bits);
+    for (int64_t c0 = int64_t(lane_id()) * V; c0 - int64_t(lane_id()) * V < a.m; c0 += UC * CH) {
+        typename C::Raw raw[UC];
+#pragma unroll
+        for (int k = 0; k < UC; ++k)
+            raw[k] = C::load(x, c0 + k * CH, a.m);
+        issue_barrier();
+#pragma unroll
+        for (int k = 0; k < UC; ++k) {
+            const int64_t i = c0 + k * CH;
+            Acc e[V], o[V], lane_excl, total;
+            C::decode(raw[k], i < a.m, e);
+            chunk_scan<Acc, Op, V>(e, lane_excl, total);
+            chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl), a.inclusive != 0, o);
+            if (i < a.m)
+                store_run<Acc, V>(a.out, ob + i, a.out_dtype, o);
+            carry = Op::apply(carry, total);
+        }
+    }
+}
+
+// Lines kernel: one thread per line walking the scan dim, UNROLL elements in
+// flight.  Consecutive threads take consecutive lines (the first kept dim).
+template <class In, class Acc, class Op, int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void k_scan_lines(ScanArgs a)
+{
+    using S = typename InTraits<In>::S;
+    for (int64_t line = int64_t(blockIdx.x) * BLOCK + threadIdx.x; line < a.lines;
+         line += int64_t(gridDim.x) * BLOCK) {
+        const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
+        const int64_t ob = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
+        Acc run = from_bits<Acc>(a.init_bits);
+        for (int64_t k0 = 0; k0 < a.m; k0 += UNROLL) {
+            S v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (k0 + u < a.m)
+                    v[u] = load1(x + (k0 + u) * a.s_in);
+            issue_barrier();
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (k0 + u < a.m) {
+                    const Acc e = InTraits<In>::template one<Acc>(v[u]);
+                    Acc o[1];
+                    if (a.inclusive) {
+                        run = Op::apply(run, e);
+                        o[0] = run;
+                    } else {
+                        o[0] = run;
+                        run = Op::apply(run, e);
+                    }
+                    store_run<Acc, 1>(a.out, ob + (k0 + u) * a.s_out, a.out_dtype, o);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <class In, class Acc, class Op>
+int run_scan_typed(const ScanLaunch &L)
+{
+    hipStream_t st = static_cast<hipStream_t>(L.stream);
+    const dim3 grid((unsigned)L.grid), block((unsigned)L.block);
+    constexpr int B = tune::kScanBlock;
+    constexpr int U = tune::kScanUnroll;
+    const bool vec = L.vec > 1;
+    if (vec && L.vec != InTraits<In>::vec)
+        return ST_INVALID;
+    if (L.block != B)
+        return ST_INVALID;
+    // a ScanLaunch carries no Launch; launch_first only reads the events
+    Launch ev;
+    ev.ev_begin = L.ev_begin;
+    ev.ev_end = L.ev_end;
+    switch (L.kernel) {
+    case SK_TILE: {
+        const int64_t words = 2 + ((L.args.tiles + 1) & ~int64_t(1));
+        const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
+        hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(L.args.ws), words);
+        if (vec)
+            launch_first(&k_scan_tile<In, Acc, Op, B, U, true>, grid, block, st, ev, L.args);
+        else
+            launch_first(&k_scan_tile<In, Acc, Op, B, U, false>, grid, block, st, ev, L.args);
+        break;
+    }
+    case SK_ROWWAVE:
+        if (vec)
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, true>, grid, block, st, ev, L.args);
+        else
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, false>, grid, block, st, ev, L.args);
+        break;
+    case SK_LINES:
+        launch_first(&k_scan_lines<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
+        break;
+    default:
+        return ST_INVALID;
+    }
+    return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
+}
+
+template <class In, class Acc>
+int run_scan_acc(const ScanLaunch &L)
+{
+    switch (L.op) {
+    case 0: return run_scan_typed<In, Acc, OpSum>(L);
+    case 1: return run_scan_typed<In, Acc, OpMax>(L);
+    case 2: return run_scan_typed<In, Acc, OpMin>(L);
+    }
+    return ST_INVALID;
+}
+
+template <class In>
+int run_scan_in(const ScanLaunch &L)
+{
+    if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
+        if (L.acc == F32) return run_scan_acc<In, float>(L);
+        if (L.acc == F64) return run_scan_acc<In, double>(L);
+    } else if constexpr (std::is_same_v<In, double>) {
+        if (L.acc == F64) return run_scan_acc<In, double>(L);
+    } else if constexpr (std::is_same_v<In, int32_t>) {
+        if (L.acc == I32) return run_scan_acc<In, int32_t>(L);
+        if (L.acc == I64) return run_scan_acc<In, int64_t>(L);
+    } else if constexpr (std::is_same_v<In, int64_t>) {
+        if (L.acc == I64) return run_scan_acc<In, int64_t>(L);
+    }
+    return ST_UNSUPPORTED;
+}
+
+}  // namespace rk

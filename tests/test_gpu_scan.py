@@ -1,0 +1,286 @@
+"""GPU parity of the scans (rk_scan, rk_scan_dims) against the CPU oracle.
+
+AcceleratedKernels.jl PR #202 (tile scans): accumulate! over a whole array
+and along dims, inclusive and exclusive, with init; its test list scans runs
+of each parity and partials of several sizes, whole and along dims.  Here:
+lengths around chunk and tile boundaries, aligned and offset views, every
+dtype/op combination with 4- and 8-byte partials, each scan kernel, strided
+and permuted views, in-place scans, and the 10^8-element and 8192x8192 sizes.
+
+Bar: integers, and max/min of any type, bit-exact.  A floating-point sum
+output k of a line comes out of a tree of rounded additions in the
+accumulator type; its depth is at most the number of tiles before it on the
+line plus 64 (look-back chain, then the tile's waves, chunks and lanes), so
+|gpu - R_k| <= (t_k + 64) * u * S_k with u = 2^-24 (f32) or 2^-53 (f64) and
+S_k = |s| + sum of |x_j| up to k; a bf16 / f16 output adds its own rounding
+(8e-3 / 1e-3 relative, as for the reductions).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from reduction_primitives_amd import workloads as W
+from tests.parity import code_of, raw_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+OPS = {"sum": O.SUM, "max": O.MAX, "min": O.MIN}
+
+
+def _rk():
+    import reduction_primitives_amd as rk
+    rk.load()
+    return rk
+
+
+def _abs_prefix(storage_cpu, shape, strides, dim, in_c, start, inclusive):
+    """S_k per output: |s| + sum of |x_j| over the prefix (float64, a scale)."""
+    raw = raw_np(storage_cpu)
+    w = np.abs(O.widen(in_c, raw))
+    idx = np.zeros(tuple(shape), np.int64)
+    for d, (e, st) in enumerate(zip(shape, strides)):
+        sh = [1] * len(shape)
+        sh[d] = e
+        idx = idx + (np.arange(e, dtype=np.int64) * st).reshape(sh)
+    v = np.moveaxis(w[idx], dim, -1)
+    c = np.cumsum(v, axis=-1)
+    if not inclusive:
+        c = np.concatenate([np.zeros(c.shape[:-1] + (1,)), c[..., :-1]], axis=-1)
+    return np.moveaxis(c, -1, dim).reshape(-1, order="F") + abs(float(start))
+
+
+def scan_and_check(storage_cpu, shape=None, strides=None, dim=1, op="sum", acc=None, out_dtype=None,
+                   init=None, inclusive=True, offset=0, expect_kernel=None, inplace=False, what=""):
+    rk = _rk()
+    in_c = code_of(storage_cpu.dtype)
+    acc_c = rk.default_acc(in_c) if acc is None else code_of(acc)
+    out_c = (acc_c if not O.is_fp(in_c) else in_c) if out_dtype is None else code_of(out_dtype)
+    if shape is None:
+        shape, strides = (storage_cpu.numel() - offset,), (1,)
+    total = math.prod(shape)
+    last = sum((e - 1) * s for e, s in zip(shape, strides))
+    assert total == 0 or offset + last < storage_cpu.numel(), "view out of bounds"
+    xd = storage_cpu.to(DEV)
+    plan = rk.plan_scan(in_c, shape, strides, dim, acc=acc_c, out_dtype=out_c,
+                        ptr=xd.data_ptr() + offset * xd.element_size())
+    if expect_kernel is not None:
+        assert plan["kernel_name"] == expect_kernel, plan
+    out = xd if inplace else None
+    res = rk.scan(xd, shape, strides, dim, op=op, acc=acc_c, out_dtype=out_c, init=init, inclusive=inclusive,
+                  out=out, offset=offset)
+    torch.cuda.synchronize()
+    g = raw_np(res)[:total]
+    op_c = OPS[op]
+    s = init if init is not None else O.identity(op_c, acc_c)
+    if not O.is_fp(acc_c):
+        s = O.wrap_int(int(s), acc_c)
+    R = O.scan_dims(op_c, in_c, acc_c, raw_np(storage_cpu)[offset:], shape, strides, dim - 1, s, inclusive)
+    what = what or f"{plan['kernel_name']} {op} incl={inclusive} {shape} dim={dim}"
+    if not O.is_fp(out_c):
+        want = O.cast(out_c, R)
+        bad = np.nonzero(g.astype(np.int64) != want.astype(np.int64))[0]
+        assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[0]}: gpu {g[bad[0]]} want {want[bad[0]]}"
+        return plan
+    gw = O.widen(out_c, g)
+    both_nan = np.isnan(gw) & np.isnan(R)
+    if op_c != O.SUM:
+        want = O.widen(out_c, O.cast(out_c, R))
+        bad = np.nonzero(~((gw == want) | both_nan))[0]
+        assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[0]}: gpu {gw[bad[0]]!r} want {want[bad[0]]!r}"
+        return plan
+    S = _abs_prefix(storage_cpu[offset:], shape, strides, dim - 1, in_c, s, inclusive)
+    m = shape[dim - 1]
+    k = np.moveaxis(np.broadcast_to(np.arange(m).reshape([-1 if d == dim - 1 else 1 for d in range(len(shape))]),
+                                    shape), dim - 1, dim - 1).reshape(-1, order="F")
+    tile = max(plan["tile_outputs"], 1)
+    u = 2.0**-24 if acc_c == O.F32 else 2.0**-53
+    tol = (k // tile + 64) * u * S
+    if out_c == O.BF16:
+        tol = tol + 8e-3 * np.abs(R)
+    elif out_c == O.F16:
+        tol = tol + 1e-3 * np.abs(R)
+    stored = O.widen(out_c, O.cast(out_c, R))
+    ok = (np.abs(gw - R) <= tol) | both_nan | (np.isinf(stored) & (gw == stored))
+    bad = np.nonzero(~ok)[0]
+    assert bad.size == 0, f"{what}: {bad.size} outputs out of tolerance, first at {bad[0]}: gpu {gw[bad[0]]!r} " \
+                          f"oracle {R[bad[0]]!r} tol {tol[bad[0]]:.3e}"
+    return plan
+
+
+TILE = 4 * 8 * 64 * 4           # f32 elements per scan tile
+
+
+# ------------------------------------------------------------ whole arrays
+
+@pytest.mark.parametrize("n", [0, 1, 3, 63, 64, 65, 255, 256, 257, 1000, 2047, 2048, 2049, TILE - 1, TILE,
+                               TILE + 1, 3 * TILE + 5, 10**6 + 3])
+def test_whole_array_lengths(n):
+    x = W.uniform(n, -1.0, 1.0, 11000 + n % 997)
+    for inclusive in (True, False):
+        scan_and_check(x, init=0.5, inclusive=inclusive)
+    xi = W.randint(n, -10**6, 10**6, 11100 + n % 991)
+    scan_and_check(xi, acc=torch.int64, out_dtype=torch.int64, inclusive=False, init=7)
+    scan_and_check(xi, op="max", acc=torch.int32, out_dtype=torch.int32)
+    xb = W.normal(n, 11200 + n % 983, torch.bfloat16)
+    scan_and_check(xb, out_dtype=torch.float32, op="min")
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_whole_array_offsets(offset):
+    """Views that start off a 16-byte boundary take element loads."""
+    rk = _rk()
+    n = 3 * TILE + 17
+    x = W.uniform(n + offset, -1.0, 1.0, 11300 + offset)
+    xd = x.to(DEV)
+    assert rk.plan_scan(torch.float32, (n,), (1,), 1, ptr=xd[offset:].data_ptr())["vec"] == 1
+    scan_and_check(x, offset=offset, init=-1.0)
+    scan_and_check(x, offset=offset, op="max", inclusive=False)
+    xh = W.normal(n + offset, 11400 + offset, torch.float16)
+    scan_and_check(xh, offset=offset, out_dtype=torch.float32)
+
+
+COMBOS = [  # (input, accumulator, output)
+    (torch.float32, torch.float32, torch.float32),
+    (torch.float32, torch.float64, torch.float64),
+    (torch.float32, torch.float32, torch.bfloat16),
+    (torch.bfloat16, torch.float32, torch.float32),
+    (torch.bfloat16, torch.float32, torch.bfloat16),
+    (torch.float16, torch.float32, torch.float16),
+    (torch.float64, torch.float64, torch.float64),
+    (torch.int32, torch.int32, torch.int32),
+    (torch.int32, torch.int64, torch.int64),
+    (torch.int64, torch.int64, torch.int64),
+]
+
+
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: "-".join(str(t).split(".")[1] for t in c))
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+def test_dtype_op_matrix(combo, op):
+    in_t, acc_t, out_t = combo
+    n = 100003
+    x = W.normal(n, 11500, in_t) if in_t.is_floating_point else W.randint(n, -2**31, 2**31 - 1, 11501, in_t)
+    for inclusive in (True, False):
+        scan_and_check(x, op=op, acc=acc_t, out_dtype=out_t, inclusive=inclusive,
+                       init=None if op != "sum" else 1)
+
+
+def test_whole_array_1e8():
+    """The 10^8-element float32 scan (the whole-array reduction's size) and
+    int32 -> int64, every output compared."""
+    xf, perm = W.whole_large(10**8)
+    scan_and_check(xf.data, expect_kernel="scan_tile")
+    scan_and_check(perm.data, acc=torch.int64, out_dtype=torch.int64, inclusive=False)
+
+
+# ---------------------------------------------------------------- exactness
+
+def test_exact_results():
+    rk = _rk()
+    n = 10**6
+    ones = torch.ones(n, device=DEV)
+    c = rk.scan(ones)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_np(c), np.arange(1, n + 1, dtype=np.float32))   # exact below 2^24
+    i = torch.arange(1, n + 1, dtype=torch.int32, device=DEV)
+    c = rk.scan(i, acc=torch.int64, out_dtype=torch.int64)
+    k = np.arange(1, n + 1, dtype=np.int64)
+    assert np.array_equal(raw_np(c), k * (k + 1) // 2)
+    p = W.randperm(n, 11600)
+    c = rk.scan(p.to(DEV), op="max", acc=torch.int32, out_dtype=torch.int32)
+    assert np.array_equal(raw_np(c), np.maximum.accumulate(p.numpy()))
+    e = rk.scan(i, acc=torch.int64, out_dtype=torch.int64, inclusive=False, init=5)
+    assert np.array_equal(raw_np(e), 5 + (k - 1) * k // 2)
+
+
+def test_in_place():
+    rk = _rk()
+    for n in (1000, 5 * TILE + 3):
+        x = W.small_ints(n, -8, 8, 11700 + n)
+        xd = x.to(DEV)
+        rk.scan(xd, out=xd)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw_np(xd), np.cumsum(x.numpy().astype(np.float64)).astype(np.float32))
+
+
+def test_look_back_never_times_out():
+    """The tile kernel's bounded waits never run out in these scans: the
+    timeout word of the workspace header stays zero."""
+    rk = _rk()
+    for n in (TILE + 1, 10**6, 3 * 10**7):
+        x = W.uniform(n, -1.0, 1.0, 11750 + n % 7).to(DEV)
+        ws = rk.workspace_for(rk.rk_scan_workspace_size(rk.RK_F32, rk.RK_F32, 1, [n], [1], 0), DEV)
+        for _ in range(3):
+            rk.scan(x, workspace=ws)
+            torch.cuda.synchronize()
+            header = ws[:8].cpu().numpy().view(np.uint32)
+            assert header[1] == 0
+            assert header[0] == -(-n // TILE)      # every tile took one counter value
+
+
+def test_integer_scans_are_deterministic():
+    rk = _rk()
+    x = W.randint(3 * 10**6, -10**6, 10**6, 11800).to(DEV)
+    outs = [raw_np(rk.scan(x, acc=torch.int64, out_dtype=torch.int64)) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# --------------------------------------------------------------------- dims
+
+DIMS_CASES = [
+    # (shape, strides or None, dim, expected kernel, why)
+    ((8192, 64), None, 1, "scan_tile", "one tile per contiguous line"),
+    ((3 * TILE + 100, 3), None, 1, "scan_tile", "several tiles per line, look-back per line"),
+    ((5000, 40), None, 1, "scan_rowwave", "contiguous lines shorter than a tile"),
+    ((300, 200), None, 2, "scan_lines", "strided scan dim"),
+    ((100, 300), None, 1, "scan_lines", "short contiguous lines"),
+    ((64, 100, 8), None, 2, "scan_lines", "middle dim of a 3-d array"),
+    ((64, 100, 8), None, 3, "scan_lines", "last dim of a 3-d array"),
+    ((700, 9, 3), None, 1, "scan_rowwave", "lines at the offsets of two kept dims"),
+    ((33, 5, 9, 4), None, 4, "scan_lines", "4-d"),
+    ((256, 300), (300, 1), 1, "scan_lines", "transposed view: input lines strided"),
+    ((256, 300), (300, 1), 2, "scan_lines", "transposed view: output lines strided"),
+]
+
+
+@pytest.mark.parametrize("case", DIMS_CASES, ids=lambda c: c[4].replace(" ", "_"))
+def test_scan_dims(case):
+    shape, strides, dim, kern, _ = case
+    strides = strides or W.cm_strides(shape)
+    n = math.prod(shape)
+    x = W.normal(n, 11900 + n % 97)
+    scan_and_check(x, shape, strides, dim, expect_kernel=kern, init=0.25)
+    scan_and_check(x, shape, strides, dim, op="max", inclusive=False)
+    xi = W.randint(n, -2**20, 2**20, 12000 + n % 89)
+    scan_and_check(xi, shape, strides, dim, acc=torch.int64, out_dtype=torch.int64, inclusive=False, init=-3)
+    xb = W.normal(n, 12100 + n % 83, torch.bfloat16)
+    scan_and_check(xb, shape, strides, dim, out_dtype=torch.bfloat16)
+
+
+def test_scan_dims_8192_square():
+    """8192x8192 float32 along dims=1 and dims=2 (the dims reductions' size)."""
+    mf, _ = W.matrix_8192()
+    st = W.cm_strides(mf.shape)
+    scan_and_check(mf.data, mf.shape, st, 1, expect_kernel="scan_tile")
+    scan_and_check(mf.data, mf.shape, st, 2, expect_kernel="scan_lines")
+
+
+def test_padded_view_with_offset():
+    x = W.normal(40 * 60 + 7, 12200)
+    scan_and_check(x, (30, 50), (1, 40), 1, offset=3, init=1.0)
+    scan_and_check(x, (30, 50), (1, 40), 2, offset=3, op="min")
+
+
+def test_empty_views():
+    rk = _rk()
+    x = W.normal(10, 12300).to(DEV)
+    guard = torch.full((4,), 3.0, device=DEV)
+    rk.scan(x, (0, 5), (1, 1), 2, out=guard)
+    rk.scan(x, (5, 0), (1, 5), 1, out=guard)
+    torch.cuda.synchronize()
+    assert np.all(raw_np(guard) == 3.0)

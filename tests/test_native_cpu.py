@@ -278,3 +278,49 @@ def test_launch_event_hook_pairs():
     rk = _rk()
     assert rk.rk_debug_set_launch_events(FAKE, None) == rk.RK_ERR_INVALID_ARGUMENT
     assert rk.rk_debug_set_launch_events(None, None) == rk.RK_OK
+
+
+# ------------------------------------------------------------------- scans
+
+def test_scan_plans():
+    import reduction_primitives_amd as rk
+    f32 = rk.RK_F32
+    tile = 4 * 8 * 64 * 4                       # waves * chunks * lanes * floats per 16 bytes
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.tile_outputs == tile and p.vec == 4
+    assert p.split == (10**8 + tile - 1) // tile and p.grid == p.split and p.launches == 2
+    tiles = p.split
+    assert p.workspace_bytes == -(-(8 + ((tiles + 1) // 2 * 2) * 4 + tiles * 16) // 256) * 256
+    assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 1, [10**6], [1], 0, 256).vec == 1     # unaligned input
+    assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 2, 1, [10**6], [1], 0, 256).vec == 1   # 2-byte aligned out
+    assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 8, 1, [10**6], [1], 0, 256).vec == 4
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [5000], [1], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.workspace_bytes == 0
+    # 8192 x 8192 along dims=1 (contiguous lines of 8192: one tile each) and dims=2 (strided)
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.n_out == 8192 * 8192
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 1, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_LINES and p.workspace_bytes == 0
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [100, 300], [1, 100], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_LINES                      # lines shorter than a wave's chunk
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 3, [0, 5, 5], [1, 1, 5], 1, 256)
+    assert p.kernel == rk.RK_KERNEL_NONE and p.launches == 0
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [3, 4], [1, 3], 2, 256)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(op=3), 1), (dict(in_dtype=9), 1), (dict(acc=4), 2), (dict(out=4), 2),
+    (dict(dim=1), 1), (dict(dim=-1), 1), (dict(ndim=0), 1), (dict(inclusive=2), 1),
+    (dict(ptr=None), 1), (dict(ptr=FAKE + 2), 1), (dict(out_ptr=None), 1), (dict(out_ptr=FAKE + 2), 1),
+    (dict(out_ptr=FAKE + 4), 1),                # overlaps the input without being it
+    (dict(ws=None), 1), (dict(ws=FAKE + 4), 1),
+])
+def test_scan_validation(args, code):
+    rk = _rk()
+    n = 10**6                                   # takes the tile kernel, so it needs a workspace
+    rc = rk.rk_scan_dims(args.get("op", 0), args.get("in_dtype", 0), args.get("acc", 0), args.get("out", 0),
+                         args.get("ptr", FAKE), args.get("ndim", 1), [n], [1], args.get("dim", 0), None,
+                         args.get("inclusive", 1), args.get("out_ptr", FAKE + 8 * n),
+                         args.get("ws", FAKE + 16 * n), None)
+    assert rc == code
