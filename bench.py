@@ -412,6 +412,34 @@ def configs_table(rk, torch, dev, reps):
             return False
         timed(name, fn, math.prod(shape) * xd.element_size(), plan["kernel_name"])
 
+    def scan(name, xd, shape, strides, d, **kw):
+        in_c = rk.dtype_code(xd.dtype)
+        acc_c = rk.dtype_code(kw["acc"]) if "acc" in kw else rk.default_acc(in_c)
+        out_t = kw.get("out_dtype", xd.dtype)
+        ws = rk.workspace_for(rk.rk_scan_workspace_size(in_c, acc_c, len(shape), shape, strides, d - 1), dev)
+        out = torch.empty(math.prod(shape), dtype=out_t, device=dev)
+        plan = rk.plan_scan(xd.dtype, shape, strides, d, acc=acc_c, out_dtype=out_t, ptr=xd.data_ptr(),
+                            out=out.data_ptr())
+
+        def fn():
+            rk.scan(xd, shape, strides, d, workspace=ws, out=out, **kw)
+            return False
+        nbytes = math.prod(shape) * (xd.element_size() + out.element_size())
+        timed(name, fn, nbytes, plan["kernel_name"])
+
+    xf, perm = W.whole_large(10**8)
+    xd, pd = xf.data.to(dev), perm.data.to(dev)
+    scan("1e+08 f32 cumsum (read + write)", xd, (10**8,), (1,), 1)
+    scan("1e+08 f32 running max, exclusive", xd, (10**8,), (1,), 1, op="max", inclusive=False)
+    scan("1e+08 i32 cumsum -> int64", pd, (10**8,), (1,), 1, acc=torch.int64, out_dtype=torch.int64)
+    del xd, pd
+    xf, _ = W.whole_large(10**6)
+    scan("1e+06 f32 cumsum", xf.data.to(dev), (10**6,), (1,), 1)
+    mf, _ = W.matrix_8192()
+    md = mf.data.to(dev)
+    scan("8192x8192 f32 cumsum dims=1", md, mf.shape, mf.strides, 1)
+    scan("8192x8192 f32 cumsum dims=2", md, mf.shape, mf.strides, 2)
+    del md
     for arr in W.general_layouts():
         xd = arr.data.to(dev)
         view(arr.name, xd, arr.shape, arr.view_strides, arr.dims)

@@ -252,7 +252,9 @@ typedef enum {
     RK_KERNEL_ALL2 = 8,         /* whole-array passes over a two-input source (rk_reduce_all2) */
     RK_KERNEL_SCAN_TILE = 9,    /* scan: tiles of contiguous lines, decoupled look-back (+ a clearing launch) */
     RK_KERNEL_SCAN_ROWWAVE = 10,/* scan: one wave per contiguous line shorter than a tile */
-    RK_KERNEL_SCAN_LINES = 11   /* scan: one thread per line along a strided scan dim */
+    RK_KERNEL_SCAN_LINES = 11,  /* scan: one thread per line along a strided scan dim */
+    RK_KERNEL_SCAN_COLUMNS = 12 /* scan: tiles of contiguous lines x scan positions, look-back along
+                                   a strided scan dim (+ a clearing launch) */
 } rk_kernel;
 
 typedef struct {
@@ -280,8 +282,9 @@ int rk_plan_dims(int in_dtype, int acc_dtype, const void *ptr, int ndim, const i
                  const int64_t *strides, uint32_t reduce_mask, int num_cus,
                  rk_plan_info *info);
 /* Plan of rk_scan_dims: kernel is one of the RK_KERNEL_SCAN_* values (NONE
- * for an empty view), split is the tiles per line, tile_outputs the elements
- * per tile, n_out the number of outputs and reduce_len the line length. */
+ * for an empty view), split is the tiles along each line, tile_outputs the
+ * elements per tile, n_out the number of outputs and reduce_len the line
+ * length. */
 int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, const void *out, int ndim,
                  const int64_t *shape, const int64_t *strides, int dim, int num_cus,
                  rk_plan_info *info);

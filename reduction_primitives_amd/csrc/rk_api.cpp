@@ -696,11 +696,12 @@ int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, co
     std::memset(info, 0, sizeof *info);
     info->kernel = d.kernel == SK_TILE ? RK_KERNEL_SCAN_TILE
                    : d.kernel == SK_ROWWAVE ? RK_KERNEL_SCAN_ROWWAVE
-                   : d.kernel == SK_LINES ? RK_KERNEL_SCAN_LINES : RK_KERNEL_NONE;
-    info->launches = d.kernel == SK_TILE ? 2 : d.kernel == SK_NONE ? 0 : 1;
+                   : d.kernel == SK_LINES ? RK_KERNEL_SCAN_LINES
+                   : d.kernel == SK_COLUMNS ? RK_KERNEL_SCAN_COLUMNS : RK_KERNEL_NONE;
+    info->launches = (d.kernel == SK_TILE || d.kernel == SK_COLUMNS) ? 2 : d.kernel == SK_NONE ? 0 : 1;
     info->grid = d.grid;
     info->block = d.block;
-    info->split = int(d.tiles_per_line > 0 ? d.tiles_per_line : 1);
+    info->split = int(d.kernel == SK_COLUMNS ? d.chunks : d.tiles_per_line > 0 ? d.tiles_per_line : 1);
     info->vec = d.vec;
     info->tile_outputs = int(d.tile_elems);
     info->n_out = d.lines * d.m;
@@ -778,6 +779,8 @@ int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void 
     a.s_out = d.s_out;
     a.tiles_per_line = d.tiles_per_line;
     a.tiles = d.tiles;
+    a.col_tiles_per_run = d.col_tiles_per_run;
+    a.col_tiles = d.col_tiles;
     a.inclusive = inclusive;
     a.out_dtype = out_dtype;
     a.init_bits = start_bits(op, acc_dtype, init);

@@ -104,7 +104,9 @@ struct ScanArgs {
     int64_t kept_out[4];
     int64_t s_in, s_out;  // scan-dim strides in elements
     int64_t tiles_per_line;   // tile kernel
-    int64_t tiles;
+    int64_t tiles;            // tile and columns kernels
+    int64_t col_tiles_per_run;    // columns kernel: tiles across one run of lines (kept dim 0)
+    int64_t col_tiles;            //   ... across all runs; tiles = col_tiles * chunks of the scan dim
     int inclusive;
     int out_dtype;
     uint64_t init_bits;   // starting value, accumulator bits

@@ -367,7 +367,7 @@ int64_t scan_tile_elems(int in_dtype)
     const int isz = dtype_size(in_dtype);
     if (isz == 0)
         return 0;
-    return int64_t(tune::kScanBlock / 64) * tune::kScanUnroll * 64 * (16 / isz);
+    return int64_t(tune::kScanTileBlock / 64) * tune::kScanUnroll * 64 * (16 / isz);
 }
 
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
@@ -422,8 +422,10 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0 && (d.kept_out[i] * osz) % ob == 0;
         d.vec = vec_ok ? v : 1;
         d.tile_elems = scan_tile_elems(in_dtype);
-        if (d.m >= d.tile_elems) {
+        const bool few_lines = d.lines < int64_t(num_cus) * tune::kScanTileFewLines;
+        if (d.m >= d.tile_elems || (few_lines && d.m >= tune::kScanTileMinLen)) {
             d.kernel = SK_TILE;
+            d.block = tune::kScanTileBlock;
             d.tiles_per_line = ceil_div(d.m, d.tile_elems);
             d.tiles = d.lines * d.tiles_per_line;
             d.grid = d.tiles;
@@ -431,15 +433,48 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             d.ws_bytes = round_up_256(8 + size_t((d.tiles + 1) & ~int64_t(1)) * 4 + size_t(d.tiles) * 16);
         } else {
             d.kernel = SK_ROWWAVE;
+            d.block = tune::kScanBlock;
             d.grid = ceil_div(d.lines, tune::kScanBlock / 64);
         }
+    } else if (k.nd >= 1 && k.str[0] == 1 && d.kept_out[0] == 1 && k.ext[0] >= tune::kScanColMinRun) {
+        // contiguous runs of lines, strided scan dim: tiles of W lines x R
+        // positions, look-back along the scan dim.  The workspace covers both
+        // tile geometries, so its size does not depend on alignment.
+        d.kernel = SK_COLUMNS;
+        d.block = tune::kScanBlock;
+        const int ob = std::min(16, v * osz);
+        bool vec_ok = in_addr % 16 == 0 && k.ext[0] % v == 0 && (d.s_in * isz) % 16 == 0 &&
+                      out_addr % ob == 0 && (d.s_out * osz) % ob == 0;
+        for (int i = 1; i < k.nd; ++i)
+            vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0 && (d.kept_out[i] * osz) % ob == 0;
+        const int64_t runs = d.lines / k.ext[0];
+        size_t ws = 0;
+        for (int pass = 0; pass < 2; ++pass) {
+            const bool vec = pass == 0;
+            const int64_t lanes = vec ? tune::kScanColLanes : tune::kScanColLanesScalar;
+            const int64_t w = lanes * (vec ? v : 1);
+            const int64_t r = (tune::kScanBlock / lanes) * tune::kScanColRows;
+            const int64_t ctpr = ceil_div(k.ext[0], w), ct = runs * ctpr, ch = ceil_div(d.m, r);
+            const int64_t tiles = ct * ch;
+            ws = std::max(ws, round_up_256(8 + size_t((tiles + 1) & ~int64_t(1)) * 4 + size_t(tiles * w) * 16));
+            if (vec == vec_ok) {
+                d.vec = vec ? v : 1;
+                d.col_tiles_per_run = ctpr;
+                d.col_tiles = ct;
+                d.chunks = ch;
+                d.tiles = tiles;
+                d.tile_elems = w * r;
+                d.grid = tiles;
+            }
+        }
+        d.ws_bytes = ws;
     } else {
         d.kernel = SK_LINES;
+        d.block = tune::kScanBlock;
         d.vec = 1;
         d.grid = std::min<int64_t>(ceil_div(d.lines, tune::kScanBlock),
                                    int64_t(num_cus) * tune::kScanLinesBlocksPerCu);
     }
-    d.block = tune::kScanBlock;
     *p = d;
     return ST_OK;
 }

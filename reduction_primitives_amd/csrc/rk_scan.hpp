@@ -18,7 +18,9 @@
 //                   "Single-pass Parallel Prefix Scan with Decoupled
 //                   Look-back", 2016);
 //   k_scan_rowwave  shorter contiguous lines: one wave per line;
-//   k_scan_lines    a strided scan dim: one thread per line, walking it.
+//   k_scan_columns  a strided scan dim over runs of contiguous lines: tiles of
+//                   lines x scan positions, look-back along the scan dim;
+//   k_scan_lines    any other layout: one thread per line, walking it.
 #pragma once
 
 #include "rk_kernels.hpp"
@@ -126,7 +128,7 @@ template <> struct OutT<I64> {
 // Store V consecutive outputs at element idx of `out`, converted to OD, in
 // the widest pieces their byte count allows (the caller guarantees that
 // alignment when V > 1).
-template <int OD, class Acc, int V>
+template <int OD, class Acc, int V, bool NTS = false>
 __device__ __forceinline__ void store_run_as(void *out, int64_t idx, const Acc (&v)[V])
 {
     using S = typename OutT<OD>::S;
@@ -141,7 +143,10 @@ __device__ __forceinline__ void store_run_as(void *out, int64_t idx, const Acc (
         for (int b = 0; b < NB; b += 16) {
             u32x4 w;
             __builtin_memcpy(&w, reinterpret_cast<const char *>(t) + b, 16);
-            *reinterpret_cast<u32x4 *>(p + b) = w;
+            if constexpr (NTS)
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p + b));
+            else
+                *reinterpret_cast<u32x4 *>(p + b) = w;
         }
     } else if constexpr (NB % 8 == 0) {
 #pragma unroll
@@ -164,21 +169,21 @@ __device__ __forceinline__ void store_run_as(void *out, int64_t idx, const Acc (
     }
 }
 
-template <class Acc, int V>
+template <class Acc, int V, bool NTS = false>
 __device__ __forceinline__ void store_run(void *out, int64_t idx, int out_dtype, const Acc (&v)[V])
 {
     if constexpr (std::is_floating_point_v<Acc>) {
         switch (out_dtype) {
-        case F32: store_run_as<F32, Acc, V>(out, idx, v); break;
-        case F64: store_run_as<F64, Acc, V>(out, idx, v); break;
-        case BF16: store_run_as<BF16, Acc, V>(out, idx, v); break;
-        case F16: store_run_as<F16, Acc, V>(out, idx, v); break;
+        case F32: store_run_as<F32, Acc, V, NTS>(out, idx, v); break;
+        case F64: store_run_as<F64, Acc, V, NTS>(out, idx, v); break;
+        case BF16: store_run_as<BF16, Acc, V, NTS>(out, idx, v); break;
+        case F16: store_run_as<F16, Acc, V, NTS>(out, idx, v); break;
         default: break;
         }
     } else {
         switch (out_dtype) {
-        case I32: store_run_as<I32, Acc, V>(out, idx, v); break;
-        case I64: store_run_as<I64, Acc, V>(out, idx, v); break;
+        case I32: store_run_as<I32, Acc, V, NTS>(out, idx, v); break;
+        case I64: store_run_as<I64, Acc, V, NTS>(out, idx, v); break;
         default: break;
         }
     }
@@ -263,12 +268,13 @@ struct ScanState {
     uint64_t *aggs;
     uint64_t *pres;
 
-    __device__ ScanState(void *ws, int64_t tiles)
+    // `width` values per tile (1, or a columns tile's lines)
+    __device__ ScanState(void *ws, int64_t tiles, int64_t width = 1)
     {
         counter = static_cast<uint32_t *>(ws);
         flags = counter + 2;
         aggs = reinterpret_cast<uint64_t *>(flags + ((tiles + 1) & ~int64_t(1)));
-        pres = aggs + tiles;
+        pres = aggs + tiles * width;
     }
 };
 
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_clear(uint32_t *w, int64_t words
 
 // Tile kernel: a tile is NW waves x UC chunks of consecutive elements of one
 // line; tiles are numbered by a counter in the order blocks start.
-template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR>
+template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR, bool NTS = false>
 __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
 {
     using C = Chunk<In, Acc, Op, VECTOR>;
@@ -424,14 +430,14 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
         C::decode(raw[k], i < a.m, e);
         chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl[k]), a.inclusive != 0, o);
         if (i < a.m)
-            store_run<Acc, V>(a.out, ob + i, a.out_dtype, o);
+            store_run<Acc, V, NTS>(a.out, ob + i, a.out_dtype, o);
         carry = Op::apply(carry, total[k]);
     }
 }
 
 // Row-wave kernel: one wave per line, UC chunks in flight, the carry passed
 // from chunk to chunk.
-template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR>
+template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR, bool NTS = true>
 __global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
 {
     using C = Chunk<In, Acc, Op, VECTOR>;
@@ -459,9 +465,195 @@ __global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
             chunk_scan<Acc, Op, V>(e, lane_excl, total);
             chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl), a.inclusive != 0, o);
             if (i < a.m)
-                store_run<Acc, V>(a.out, ob + i, a.out_dtype, o);
+                store_run<Acc, V, NTS>(a.out, ob + i, a.out_dtype, o);
             carry = Op::apply(carry, total);
         }
+    }
+}
+
+// Columns kernel: a strided scan dim over runs of contiguous lines (kept dim
+// 0).  A tile is W = CL * V consecutive lines of one run by R = RG * RPG
+// consecutive scan positions; row group rg of the block scans positions
+// rg*RPG .. rg*RPG+RPG-1 for its V lines with 16-byte loads (a wave reads
+// 64 / CL rows of W lines per instruction), the row groups' totals are
+// combined through LDS, and the tile's prefix along the scan dim comes from
+// the tiles before it by decoupled look-back (numbered chunk-major, so the
+// tiles a tile waits on started before it).  Row group 0 does the look-back,
+// each thread for its own lines, a window of K predecessors at a time.
+template <class In, class Acc, class Op, int BLOCK, int CL, int RPG, bool VECTOR>
+__global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
+{
+    using S = typename InTraits<In>::S;
+    constexpr int V = VECTOR ? InTraits<In>::vec : 1;
+    constexpr int W = CL * V;
+    constexpr int RG = BLOCK / CL;
+    constexpr int64_t R = int64_t(RG) * RPG;
+    constexpr int K = 8;
+    using Raw = std::conditional_t<VECTOR, u32x4, S>;
+    static_assert(BLOCK % CL == 0, "whole row groups");
+
+    __shared__ uint32_t s_id;
+    __shared__ Acc s_part[RG][W];
+    __shared__ Acc s_excl[W];
+    const ScanState st(a.ws, a.tiles, W);
+    if (threadIdx.x == 0)
+        s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t g = s_id;
+    const int64_t t = g / a.col_tiles;                 // chunk along the scan dim
+    const int64_t ct = g - t * a.col_tiles;            // tile across the lines
+    const int64_t run = ct / a.col_tiles_per_run;
+    const int64_t col0 = (ct - run * a.col_tiles_per_run) * W;
+    const int c = (int)(threadIdx.x % CL), rg = (int)(threadIdx.x / CL);
+    const int64_t run_len = a.kept_ext[0];
+    const int64_t col = col0 + int64_t(c) * V;
+    const bool active = col < run_len;                 // 16-byte loads: run_len % V == 0
+    const S *x = static_cast<const S *>(a.x) +
+                 layout_offset(a.kept_nd - 1, a.kept_ext + 1, a.kept_in + 1, run) + col;
+    const int64_t ob = layout_offset(a.kept_nd - 1, a.kept_ext + 1, a.kept_out + 1, run) + col;
+    const int64_t r0 = t * R + int64_t(rg) * RPG;
+
+    Raw raw[RPG];
+#pragma unroll
+    for (int q = 0; q < RPG; ++q) {
+        raw[q] = Raw{};
+        if (active && r0 + q < a.m) {
+            if constexpr (VECTOR)
+                raw[q] = load16(reinterpret_cast<const u32x4 *>(x + (r0 + q) * a.s_in));
+            else
+                raw[q] = load1(x + (r0 + q) * a.s_in);
+        }
+    }
+    issue_barrier();
+
+    // this thread's totals over its RPG positions, per line
+    Acc tot[V];
+    set_identity<Acc, Op>(tot);
+#pragma unroll
+    for (int q = 0; q < RPG; ++q) {
+        Acc e[V];
+        Chunk<In, Acc, Op, VECTOR>::decode(raw[q], active && r0 + q < a.m, e);
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            tot[i] = Op::apply(tot[i], e[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        s_part[rg][c * V + i] = tot[i];
+    __syncthreads();
+    // offset of this row group and the tile's aggregate, per line
+    Acc gpre[V], agg[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        gpre[i] = Op::template identity<Acc>();
+        agg[i] = Op::template identity<Acc>();
+        for (int k = 0; k < RG; ++k) {
+            if (k == rg)
+                gpre[i] = agg[i];
+            agg[i] = Op::apply(agg[i], s_part[k][c * V + i]);
+        }
+    }
+    const int64_t slot = g * W + int64_t(c) * V;       // this thread's values of tile g
+    if (t > 0) {
+        if (rg == 0 && active) {
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                store_partial(reinterpret_cast<Acc *>(st.aggs + slot + i), agg[i]);
+            wait_stores();
+        }
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(st.flags + g, kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (rg == 0) {
+        Acc acc[V];
+        const Acc init = from_bits<Acc>(a.init_bits);
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            acc[i] = t == 0 ? init : Op::template identity<Acc>();
+        if (t > 0 && active) {
+            int64_t top = t - 1;
+            for (;;) {
+                uint32_t f[K];
+#pragma unroll
+                for (int q = 0; q < K; ++q)
+                    f[q] = top - q >= 0 ? __hip_atomic_load(st.flags + (top - q) * a.col_tiles + ct, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : kFlagPrefix;
+                int first = K;
+                for (int spin = 0;; ++spin) {
+                    first = K;
+                    bool ready = true;
+#pragma unroll
+                    for (int q = K - 1; q >= 0; --q)
+                        if (f[q] == kFlagPrefix)
+                            first = q;
+#pragma unroll
+                    for (int q = 0; q < K; ++q)
+                        if (q < first && f[q] == 0)
+                            ready = false;
+                    if (ready)
+                        break;
+                    if (spin >= tune::kScanSpinLimit) {
+                        __hip_atomic_store(st.counter + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                    for (int q = 0; q < K; ++q)
+                        if (f[q] == 0 && top - q >= 0)
+                            f[q] = __hip_atomic_load(st.flags + (top - q) * a.col_tiles + ct, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int q = 0; q < K; ++q) {
+                    const int64_t j = top - q;
+                    if (q <= first && j >= 0) {
+                        const uint64_t *src = f[q] == kFlagPrefix ? st.pres : st.aggs;
+                        const int64_t js = (j * a.col_tiles + ct) * W + int64_t(c) * V;
+#pragma unroll
+                        for (int i = 0; i < V; ++i)
+                            acc[i] = Op::apply(load_partial(reinterpret_cast<const Acc *>(src + js + i)), acc[i]);
+                    }
+                }
+                if (first < K)
+                    break;
+                top -= K;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            s_excl[c * V + i] = acc[i];
+            if (active)
+                store_partial(reinterpret_cast<Acc *>(st.pres + slot + i), Op::apply(acc[i], agg[i]));
+        }
+        wait_stores();
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(st.flags + g, kFlagPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    Acc runv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        runv[i] = Op::apply(s_excl[c * V + i], gpre[i]);
+#pragma unroll
+    for (int q = 0; q < RPG; ++q) {
+        const int64_t r = r0 + q;
+        Acc e[V], o[V];
+        Chunk<In, Acc, Op, VECTOR>::decode(raw[q], active && r < a.m, e);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            if (a.inclusive) {
+                runv[i] = Op::apply(runv[i], e[i]);
+                o[i] = runv[i];
+            } else {
+                o[i] = runv[i];
+                runv[i] = Op::apply(runv[i], e[i]);
+            }
+        }
+        if (active && r < a.m)
+            store_run<Acc, V, true>(a.out, ob + r * a.s_out, a.out_dtype, o);
     }
 }
 
@@ -510,11 +702,12 @@ int run_scan_typed(const ScanLaunch &L)
     hipStream_t st = static_cast<hipStream_t>(L.stream);
     const dim3 grid((unsigned)L.grid), block((unsigned)L.block);
     constexpr int B = tune::kScanBlock;
+    constexpr int BT = tune::kScanTileBlock;
     constexpr int U = tune::kScanUnroll;
     const bool vec = L.vec > 1;
     if (vec && L.vec != InTraits<In>::vec)
         return ST_INVALID;
-    if (L.block != B)
+    if (L.block != (L.kernel == SK_TILE ? BT : B))
         return ST_INVALID;
     // a ScanLaunch carries no Launch; launch_first only reads the events
     Launch ev;
@@ -526,9 +719,9 @@ int run_scan_typed(const ScanLaunch &L)
         const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
         hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(L.args.ws), words);
         if (vec)
-            launch_first(&k_scan_tile<In, Acc, Op, B, U, true>, grid, block, st, ev, L.args);
+            launch_first(&k_scan_tile<In, Acc, Op, BT, U, true, true>, grid, block, st, ev, L.args);
         else
-            launch_first(&k_scan_tile<In, Acc, Op, B, U, false>, grid, block, st, ev, L.args);
+            launch_first(&k_scan_tile<In, Acc, Op, BT, U, false, true>, grid, block, st, ev, L.args);
         break;
     }
     case SK_ROWWAVE:
@@ -540,6 +733,18 @@ int run_scan_typed(const ScanLaunch &L)
     case SK_LINES:
         launch_first(&k_scan_lines<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
         break;
+    case SK_COLUMNS: {
+        const int64_t words = 2 + ((L.args.tiles + 1) & ~int64_t(1));
+        const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
+        hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(L.args.ws), words);
+        if (vec)
+            launch_first(&k_scan_columns<In, Acc, Op, B, tune::kScanColLanes, tune::kScanColRows, true>, grid,
+                         block, st, ev, L.args);
+        else
+            launch_first(&k_scan_columns<In, Acc, Op, B, tune::kScanColLanesScalar, tune::kScanColRows, false>, grid,
+                         block, st, ev, L.args);
+        break;
+    }
     default:
         return ST_INVALID;
     }

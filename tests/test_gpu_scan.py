@@ -111,7 +111,7 @@ def scan_and_check(storage_cpu, shape=None, strides=None, dim=1, op="sum", acc=N
     return plan
 
 
-TILE = 4 * 8 * 64 * 4           # f32 elements per scan tile
+TILE = 16 * 8 * 64 * 4          # f32 elements per scan tile: 16 waves x 8 chunks x 64 lanes x 4
 
 
 # ------------------------------------------------------------ whole arrays
@@ -234,15 +234,20 @@ def test_integer_scans_are_deterministic():
 
 DIMS_CASES = [
     # (shape, strides or None, dim, expected kernel, why)
-    ((8192, 64), None, 1, "scan_tile", "one tile per contiguous line"),
+    ((TILE, 64), None, 1, "scan_tile", "one tile per contiguous line"),
+    ((8192, 64), None, 1, "scan_tile", "few lines shorter than a tile"),
     ((3 * TILE + 100, 3), None, 1, "scan_tile", "several tiles per line, look-back per line"),
-    ((5000, 40), None, 1, "scan_rowwave", "contiguous lines shorter than a tile"),
-    ((300, 200), None, 2, "scan_lines", "strided scan dim"),
+    ((3000, 40), None, 1, "scan_rowwave", "contiguous lines shorter than a tile"),
+    ((300, 5000), None, 1, "scan_rowwave", "many short contiguous lines"),
+    ((300, 200), None, 2, "scan_columns", "strided scan dim"),
     ((100, 300), None, 1, "scan_lines", "short contiguous lines"),
-    ((64, 100, 8), None, 2, "scan_lines", "middle dim of a 3-d array"),
-    ((64, 100, 8), None, 3, "scan_lines", "last dim of a 3-d array"),
+    ((64, 100, 8), None, 2, "scan_columns", "middle dim of a 3-d array"),
+    ((64, 100, 8), None, 3, "scan_columns", "last dim of a 3-d array"),
+    ((10, 100, 8), None, 2, "scan_lines", "runs of lines too narrow for tiles"),
+    ((40, 3000, 5), None, 2, "scan_columns", "long strided scan: look-back across chunks"),
+    ((130, 2000), (1, 131), 2, "scan_columns", "padded rows: element loads"),
     ((700, 9, 3), None, 1, "scan_rowwave", "lines at the offsets of two kept dims"),
-    ((33, 5, 9, 4), None, 4, "scan_lines", "4-d"),
+    ((33, 5, 9, 4), None, 4, "scan_columns", "4-d"),
     ((256, 300), (300, 1), 1, "scan_lines", "transposed view: input lines strided"),
     ((256, 300), (300, 1), 2, "scan_lines", "transposed view: output lines strided"),
 ]
@@ -252,7 +257,7 @@ DIMS_CASES = [
 def test_scan_dims(case):
     shape, strides, dim, kern, _ = case
     strides = strides or W.cm_strides(shape)
-    n = math.prod(shape)
+    n = max(math.prod(shape), sum((e - 1) * st for e, st in zip(shape, strides)) + 1)
     x = W.normal(n, 11900 + n % 97)
     scan_and_check(x, shape, strides, dim, expect_kernel=kern, init=0.25)
     scan_and_check(x, shape, strides, dim, op="max", inclusive=False)
@@ -266,8 +271,8 @@ def test_scan_dims_8192_square():
     """8192x8192 float32 along dims=1 and dims=2 (the dims reductions' size)."""
     mf, _ = W.matrix_8192()
     st = W.cm_strides(mf.shape)
-    scan_and_check(mf.data, mf.shape, st, 1, expect_kernel="scan_tile")
-    scan_and_check(mf.data, mf.shape, st, 2, expect_kernel="scan_lines")
+    scan_and_check(mf.data, mf.shape, st, 1, expect_kernel="scan_rowwave")
+    scan_and_check(mf.data, mf.shape, st, 2, expect_kernel="scan_columns")
 
 
 def test_padded_view_with_offset():

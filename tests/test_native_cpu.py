@@ -285,7 +285,7 @@ def test_launch_event_hook_pairs():
 def test_scan_plans():
     import reduction_primitives_amd as rk
     f32 = rk.RK_F32
-    tile = 4 * 8 * 64 * 4                       # waves * chunks * lanes * floats per 16 bytes
+    tile = 16 * 8 * 64 * 4                      # waves * chunks * lanes * floats per 16 bytes
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.tile_outputs == tile and p.vec == 4
     assert p.split == (10**8 + tile - 1) // tile and p.grid == p.split and p.launches == 2
@@ -294,13 +294,25 @@ def test_scan_plans():
     assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 1, [10**6], [1], 0, 256).vec == 1     # unaligned input
     assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 2, 1, [10**6], [1], 0, 256).vec == 1   # 2-byte aligned out
     assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 8, 1, [10**6], [1], 0, 256).vec == 4
-    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [5000], [1], 0, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.workspace_bytes == 0
-    # 8192 x 8192 along dims=1 (contiguous lines of 8192: one tile each) and dims=2 (strided)
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [4000], [1], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.workspace_bytes == 0 and p.block == 256
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [5000], [1], 0, 256)       # one short line: tiles
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 1024 and p.split == 1
+    # 8192 x 8192 along dims=1 (8192 contiguous lines: a wave each) and dims=2 (strided)
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 0, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.n_out == 8192 * 8192
+    assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.n_out == 8192 * 8192
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [tile, 8], [1, tile], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.grid == 8
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 1, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_LINES and p.workspace_bytes == 0
+    assert p.kernel == rk.RK_KERNEL_SCAN_COLUMNS and p.vec == 4 and p.launches == 2
+    assert p.tile_outputs == 128 * 128 and p.split == 64 and p.grid == 64 * 64
+    # the workspace covers both tile geometries: 16-byte loads (128 lines x 128
+    # positions) and element loads (64 lines x 64 positions)
+    scalar_tiles = 128 * 128
+    assert p.workspace_bytes == -(-(8 + scalar_tiles * 4 + scalar_tiles * 64 * 16) // 256) * 256
+    assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 2, [8192, 8192], [1, 8192], 1, 256).vec == 1
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10, 100], [1, 10], 1, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_LINES and p.workspace_bytes == 0        # runs of 10 lines
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [100, 300], [1, 100], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_LINES                      # lines shorter than a wave's chunk
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 3, [0, 5, 5], [1, 1, 5], 1, 256)
