@@ -40,15 +40,19 @@ HIP_HOST_UNITS = ["rk_api.cpp"]           # host code that calls the HIP runtime
 PURE_UNITS = ["rk_plan.cpp"]              # plain C++
 
 
+# The files the reduction kernels of kern_f32.hip are compiled from (the
+# scan translation units and the host code are not among them).
+REDUCTION_KERNEL_SOURCES = ["kern_f32.hip", "rk_kernels.hpp", "rk_device.hpp", "rk_launch.hpp", "rk_plan.hpp"]
+
+
 def kernel_source_digest() -> str:
-    """SHA-256 over the kernel sources and headers (identifies the kernels a
-    stored counter profile was taken on)."""
+    """SHA-256 over the sources and compile flags of the float32 reduction
+    kernels (identifies the kernels a stored counter profile was taken on)."""
     import hashlib
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    h = hashlib.sha256(" ".join(HIP_FLAGS[:-2]).encode())
+    for name in REDUCTION_KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
