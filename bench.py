@@ -291,14 +291,18 @@ def per_call_table(calls, torch, reps, dev):
                 # drains the stream itself and is timed by the wall clock
                 if not host:
                     torch.cuda._sleep(200_000)
+                if host:
+                    # the call returns once its value is on the host: time the call alone
+                    t0 = time.perf_counter()
+                    c()
+                    ts.append((time.perf_counter() - t0) * 1e6)
+                    continue
                 b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                t0 = time.perf_counter()
                 b.record()
                 c()
                 e.record()
                 e.synchronize()
-                wall = time.perf_counter() - t0
-                ts.append(wall * 1e6 if host else b.elapsed_time(e) * 1e3)
+                ts.append(b.elapsed_time(e) * 1e3)
             rows[mode] = dict(us_min=round(min(ts), 2), us_median=round(statistics.median(ts), 2),
                               GBps=round(c.bytes_alg / (min(ts) * 1e-6) / 1e9, 1))
         table[c.name] = rows
@@ -325,15 +329,19 @@ def configs_table(rk, torch, dev, reps):
                 if mode == "cold":
                     flush.sum()
                 torch.cuda.synchronize()
-                if not is_host:
-                    torch.cuda._sleep(1_000_000)
+                if is_host:
+                    # the call returns once its value is on the host: time the call alone
+                    t0 = time.perf_counter()
+                    fn()
+                    ts.append((time.perf_counter() - t0) * 1e6)
+                    continue
+                torch.cuda._sleep(1_000_000)
                 b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                t0 = time.perf_counter()
                 b.record()
-                host = fn()
+                fn()
                 e.record()
                 e.synchronize()
-                ts.append((time.perf_counter() - t0) * 1e6 if host else b.elapsed_time(e) * 1e3)
+                ts.append(b.elapsed_time(e) * 1e3)
             res[mode] = dict(us_min=round(min(ts), 2), us_median=round(statistics.median(ts), 2),
                              GBps=round(nbytes / (min(ts) * 1e-6) / 1e9, 1))
         rows.append(dict(call=name, kernel=kernel, bytes=nbytes, **res))

@@ -38,14 +38,19 @@ def _torch():
     return torch
 
 
+_DTYPE_CODES = None
+
+
 def dtype_code(dt) -> int:
     """rk dtype code of a torch dtype (or pass an int code through)."""
+    global _DTYPE_CODES
     if isinstance(dt, int):
         return dt
-    torch = _torch()
-    table = {torch.float32: RK_F32, torch.bfloat16: RK_BF16, torch.float16: RK_F16,
-             torch.float64: RK_F64, torch.int32: RK_I32, torch.int64: RK_I64}
-    return table[dt]
+    if _DTYPE_CODES is None:
+        torch = _torch()
+        _DTYPE_CODES = {torch.float32: RK_F32, torch.bfloat16: RK_BF16, torch.float16: RK_F16,
+                        torch.float64: RK_F64, torch.int32: RK_I32, torch.int64: RK_I64}
+    return _DTYPE_CODES[dt]
 
 
 def torch_dtype(code: int):
@@ -86,10 +91,15 @@ def decode_host_out(buf, out_code: int):
     return v
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device_index=None):
+    """hipStream_t of `stream`, or of the current stream of the device (read
+    without building a Stream object: host-mode calls are latency-bound)."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if device_index is None:
+        device_index = torch.cuda.current_device()
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(device_index))
 
 
 def workspace_for(nbytes: int, device):
@@ -119,7 +129,7 @@ def reduce_all(x, op="sum", map="identity", acc=None, out_dtype=None, init=None,
     n = x.numel()
     if workspace is None:
         workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), x.device)
-    st = _stream_handle(stream)
+    st = _stream_handle(stream, x.get_device())
     if mode_c == RK_MODE_HOST:
         buf = _CTYPE[out_code]()
         rc = rk_reduce_all(op_c, map_c, in_code, acc_code, out_code, x.data_ptr(), n,
@@ -154,7 +164,7 @@ def reduce_all2(a, b, map2="mul", op="sum", acc=None, out_dtype=None, init=None,
     n = a.numel()
     if workspace is None:
         workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), a.device)
-    st = _stream_handle(stream)
+    st = _stream_handle(stream, a.get_device())
     if mode_c == RK_MODE_HOST:
         buf = _CTYPE[out_code]()
         rc = rk_reduce_all2(op_c, map_c, in_code, acc_code, out_code, a.data_ptr(), b.data_ptr(), n,
@@ -194,7 +204,7 @@ def reduce_dims(x, shape, strides, dims, op="sum", map="identity", acc=None, out
     if workspace is None:
         workspace = workspace_for(rk_workspace_size(in_code, acc_code, ndim, shape, strides, mask),
                                   x.device)
-    st = _stream_handle(stream)
+    st = _stream_handle(stream, x.get_device())
     if mode_c == RK_MODE_HOST:
         buf = _CTYPE[out_code]()
         rc = rk_reduce_dims(op_c, map_c, in_code, acc_code, out_code, ptr, ndim, shape, strides,
@@ -235,7 +245,7 @@ def scan(x, shape=None, strides=None, dim=1, op="sum", acc=None, out_dtype=None,
         out = torch.empty(max(total, 1), dtype=torch_dtype(out_code), device=x.device)
     rc = rk_scan_dims(_code(OPS, op), in_code, acc_code, out_code, ptr, len(shape), shape, strides, d0,
                       init_arg(acc_code, init), int(bool(inclusive)), out.data_ptr(), workspace.data_ptr(),
-                      _stream_handle(stream))
+                      _stream_handle(stream, x.get_device()))
     _check(rc, "rk_scan_dims")
     return out
 

@@ -288,10 +288,12 @@ void *pinned_result()
 // Wait for the bare partial, then finish it on the host.  With the pinned
 // buffer the kernel stores the result and then this call's sequence number;
 // spinning on that number returns as soon as the result has landed, without
-// the wake-up latency of a blocking stream wait.  The spin checks the stream
-// for errors and gives way to a blocking wait after kSpinMicros.  Without the
-// buffer the partial is copied back from ws[grid].
+// the wake-up latency of a blocking stream wait.  Every kQueryMicros the spin
+// asks the stream for errors (a query takes microseconds, so it is kept out of
+// the path that sees the result), and after kSpinMicros it gives way to a
+// blocking wait.  Without the buffer the partial is copied back from ws[grid].
 constexpr int64_t kSpinMicros = 200;
+constexpr int64_t kQueryMicros = 20;
 
 int finish_on_host(int op, int acc, uint64_t init_bits, const Finish &fin, const void *ws, int grid, void *out,
                    int out_dtype, hipStream_t st)
@@ -302,18 +304,24 @@ int finish_on_host(int op, int acc, uint64_t init_bits, const Finish &fin, const
         const volatile uint32_t *seq = reinterpret_cast<const volatile uint32_t *>(
             static_cast<const char *>(fin.out) + 8);
         const auto t0 = std::chrono::steady_clock::now();
+        auto next_query = t0 + std::chrono::microseconds(kQueryMicros);
         bool arrived = false;
-        for (uint32_t i = 1; !arrived; ++i) {
+        for (uint32_t i = 1;; ++i) {
             if (*seq == fin.host_seq) {
                 arrived = true;
                 break;
             }
-            if ((i & 255) == 0) {
-                const hipError_t q = hipStreamQuery(st);
-                if (q != hipSuccess && q != hipErrorNotReady)
-                    return RK_ERR_HIP;
-                if (q == hipSuccess || std::chrono::steady_clock::now() - t0 >
-                                           std::chrono::microseconds(kSpinMicros))
+            if ((i & 63) == 0) {
+                const auto now = std::chrono::steady_clock::now();
+                if (now >= next_query) {
+                    const hipError_t q = hipStreamQuery(st);
+                    if (q != hipSuccess && q != hipErrorNotReady)
+                        return RK_ERR_HIP;
+                    if (q == hipSuccess)
+                        break;                     // drained: the result is checked below
+                    next_query = now + std::chrono::microseconds(kQueryMicros);
+                }
+                if (now - t0 > std::chrono::microseconds(kSpinMicros))
                     break;
             }
         }

@@ -138,12 +138,17 @@ __device__ __forceinline__ void store_run_as(void *out, int64_t idx, const Acc (
         t[i] = OutT<OD>::conv(v[i]);
     char *p = reinterpret_cast<char *>(static_cast<S *>(out) + idx);
     constexpr int NB = int(sizeof(t));
+    // Non-temporal only when one store covers the lane's whole run: a wave's
+    // store is then one contiguous piece.  Runs of 32 bytes and more take
+    // several stores at a lane stride, each leaving holes in the lines that the
+    // next one fills; streaming those past the cache measured 10-15% slower.
+    constexpr bool NT = NTS && NB <= 16;
     if constexpr (NB % 16 == 0) {
 #pragma unroll
         for (int b = 0; b < NB; b += 16) {
             u32x4 w;
             __builtin_memcpy(&w, reinterpret_cast<const char *>(t) + b, 16);
-            if constexpr (NTS)
+            if constexpr (NT)
                 __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p + b));
             else
                 *reinterpret_cast<u32x4 *>(p + b) = w;
