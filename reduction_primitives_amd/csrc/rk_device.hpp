@@ -205,7 +205,10 @@ struct OpSum {
     }
 };
 
-// max/min propagate NaN: the result is NaN when either operand is.
+// max/min propagate NaN: the result is NaN when either operand is.  For
+// floats this is IEEE 754-2019 maximum/minimum, which gfx950 executes as one
+// instruction (v_maximum3_f32 / v_minimum3_f32); ties of -0 and +0 may take
+// either sign.
 struct OpMax {
     template <class T> __device__ __forceinline__ static T identity()
     {
@@ -219,7 +222,7 @@ struct OpMax {
         if constexpr (std::is_integral_v<T>)
             return a > b ? a : b;
         else
-            return (a != a || b != b) ? a + b : (a > b ? a : b);
+            return __builtin_elementwise_maximum(a, b);
     }
 };
 
@@ -236,7 +239,7 @@ struct OpMin {
         if constexpr (std::is_integral_v<T>)
             return a < b ? a : b;
         else
-            return (a != a || b != b) ? a + b : (a < b ? a : b);
+            return __builtin_elementwise_minimum(a, b);
     }
 };
 
