@@ -110,7 +110,12 @@ struct ScanArgs {
     int inclusive;
     int out_dtype;
     uint64_t init_bits;   // starting value, accumulator bits
+    int slot;             // >= 0: tile counter and flags in the library's slot (reset by the last
+                          // block); < 0: in the workspace, cleared by a fill launch first
 };
+
+// Tiles whose flags fit one library slot of a look-back scan.
+constexpr int kScanFlagCapacity = 8192;
 
 struct ScanLaunch {
     int kernel;           // rk::ScanKernel

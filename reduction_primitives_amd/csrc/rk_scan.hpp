@@ -261,27 +261,80 @@ __device__ __forceinline__ void chunk_outputs(const Acc (&e)[V], Acc run, bool i
 
 // ------------------------------------------------------- tile look-back
 
-// Tile state in the workspace: an 8-byte header holding the tile counter and
-// a timeout word (nonzero if a look-back wait gave up; never in normal runs),
-// one 32-bit flag per tile (0 nothing yet, 1 aggregate, 2 inclusive prefix),
-// then one 8-byte slot per tile for the aggregate and one for the prefix.
-// A value is stored, its store waited for, and only then its flag, all at
-// device scope; a reader loads the flag first and the value after it.
+// Tile state.  The workspace holds an 8-byte header (tile counter, timeout
+// word: nonzero if a look-back wait gave up, never in normal runs), one
+// 32-bit flag per tile (0 nothing yet, 1 aggregate, 2 inclusive prefix), then
+// one 8-byte slot per tile for the aggregate and one for the prefix (`width`
+// of each per tile for the columns kernel).  A value is stored, its store
+// waited for, and only then its flag, all at device scope; a reader loads the
+// flag first and the value after it.
+//
+// With a library slot (ScanArgs::slot >= 0) the counter, timeout word and
+// flags live in g_scan_state instead, which starts zeroed and which the last
+// block of every scan puts back to zero (scan_release), so no launch has to
+// clear them; the workspace header then receives the call's tile count and
+// timeout word.  Calls on one stream share its slot in order; calls that may
+// overlap have different slots.
+constexpr int kScanSlotWords = 4 + kScanFlagCapacity;
+static __device__ uint32_t g_scan_state[kArriveSlots * kScanSlotWords];
+
 struct ScanState {
     uint32_t *counter;
+    uint32_t *timeout;
+    uint32_t *done;       // slot state only: blocks finished, wraps to zero
     uint32_t *flags;
     uint64_t *aggs;
     uint64_t *pres;
 
-    // `width` values per tile (1, or a columns tile's lines)
-    __device__ ScanState(void *ws, int64_t tiles, int64_t width = 1)
+    __device__ ScanState(void *ws, int64_t tiles, int slot, int64_t width = 1)
     {
-        counter = static_cast<uint32_t *>(ws);
-        flags = counter + 2;
-        aggs = reinterpret_cast<uint64_t *>(flags + ((tiles + 1) & ~int64_t(1)));
+        uint32_t *w = static_cast<uint32_t *>(ws);
+        uint32_t *wflags = w + 2;
+        aggs = reinterpret_cast<uint64_t *>(wflags + ((tiles + 1) & ~int64_t(1)));
         pres = aggs + tiles * width;
+        if (slot >= 0) {
+            counter = g_scan_state + int64_t(slot) * kScanSlotWords;
+            done = counter + 1;
+            timeout = counter + 2;
+            flags = counter + 4;
+        } else {
+            counter = w;
+            timeout = w + 1;
+            done = nullptr;
+            flags = wflags;
+        }
     }
 };
+
+// End of a block of a slot-state scan: count the block done; the last one
+// (every look-back has ended by then) zeroes the flags, the counter and the
+// timeout word for the next call, after copying the tile count and the
+// timeout word into the workspace header.  Called by every thread.
+template <int BLOCK>
+__device__ __forceinline__ void scan_release(const ScanState &st, void *ws, int64_t tiles)
+{
+    if (!st.done)
+        return;
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        wait_stores();
+        const uint32_t prev = __builtin_amdgcn_atomic_inc32(st.done, (uint32_t)(tiles - 1), __ATOMIC_RELAXED, "agent");
+        s_last = prev == (uint32_t)(tiles - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    for (int64_t i = threadIdx.x; i < tiles; i += BLOCK)
+        st.flags[i] = 0;
+    if (threadIdx.x == 0) {
+        uint32_t *hdr = static_cast<uint32_t *>(ws);
+        hdr[0] = __hip_atomic_load(st.counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hdr[1] = __hip_atomic_load(st.timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(st.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(st.timeout, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 constexpr uint32_t kFlagAggregate = 1;
 constexpr uint32_t kFlagPrefix = 2;
@@ -333,7 +386,7 @@ __device__ Acc scan_lookback(const ScanState &st, int64_t g, int64_t t, Acc agg,
                 break;
             if (spin >= tune::kScanSpinLimit) {
                 if (lane == 0)
-                    __hip_atomic_store(st.counter + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(st.timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -381,11 +434,16 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
     __shared__ uint32_t s_id;
     __shared__ Acc s_wave[NW];
     __shared__ Acc s_excl;
-    const ScanState st(a.ws, a.tiles);
+    const ScanState st(a.ws, a.tiles, a.slot);
     if (threadIdx.x == 0)
         s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int64_t g = s_id;
+    if (g >= a.tiles) {                        // never: the counter starts at zero every call
+        if (threadIdx.x == 0)
+            __hip_atomic_store(st.timeout, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const int64_t line = g / a.tiles_per_line;
     const int64_t t = g - line * a.tiles_per_line;
     const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
@@ -438,6 +496,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
             store_run<Acc, V, NTS>(a.out, ob + i, a.out_dtype, o);
         carry = Op::apply(carry, total[k]);
     }
+    scan_release<BLOCK>(st, a.ws, a.tiles);
 }
 
 // Row-wave kernel: one wave per line, UC chunks in flight, the carry passed
@@ -500,11 +559,16 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     __shared__ uint32_t s_id;
     __shared__ Acc s_part[RG][W];
     __shared__ Acc s_excl[W];
-    const ScanState st(a.ws, a.tiles, W);
+    const ScanState st(a.ws, a.tiles, a.slot, W);
     if (threadIdx.x == 0)
         s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int64_t g = s_id;
+    if (g >= a.tiles) {                        // never: the counter starts at zero every call
+        if (threadIdx.x == 0)
+            __hip_atomic_store(st.timeout, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const int64_t t = g / a.col_tiles;                 // chunk along the scan dim
     const int64_t ct = g - t * a.col_tiles;            // tile across the lines
     const int64_t run = ct / a.col_tiles_per_run;
@@ -600,7 +664,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
                     if (ready)
                         break;
                     if (spin >= tune::kScanSpinLimit) {
-                        __hip_atomic_store(st.counter + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(st.timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
                     __builtin_amdgcn_s_sleep(1);
@@ -660,6 +724,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
         if (active && r < a.m)
             store_run<Acc, V, true>(a.out, ob + r * a.s_out, a.out_dtype, o);
     }
+    scan_release<BLOCK>(st, a.ws, a.tiles);
 }
 
 // Lines kernel: one thread per line walking the scan dim, UNROLL elements in
@@ -701,6 +766,14 @@ __global__ __launch_bounds__(BLOCK) void k_scan_lines(ScanArgs a)
 
 // ---------------------------------------------------------------- launchers
 
+// Zero the workspace's tile counter, timeout word and flags (workspace state).
+inline void clear_state(const ScanArgs &a, hipStream_t st)
+{
+    const int64_t words = 2 + ((a.tiles + 1) & ~int64_t(1));
+    const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(a.ws), words);
+}
+
 template <class In, class Acc, class Op>
 int run_scan_typed(const ScanLaunch &L)
 {
@@ -720,9 +793,8 @@ int run_scan_typed(const ScanLaunch &L)
     ev.ev_end = L.ev_end;
     switch (L.kernel) {
     case SK_TILE: {
-        const int64_t words = 2 + ((L.args.tiles + 1) & ~int64_t(1));
-        const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
-        hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(L.args.ws), words);
+        if (L.args.slot < 0)
+            clear_state(L.args, st);
         if (vec)
             launch_first(&k_scan_tile<In, Acc, Op, BT, U, true, true>, grid, block, st, ev, L.args);
         else
@@ -739,9 +811,8 @@ int run_scan_typed(const ScanLaunch &L)
         launch_first(&k_scan_lines<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
         break;
     case SK_COLUMNS: {
-        const int64_t words = 2 + ((L.args.tiles + 1) & ~int64_t(1));
-        const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
-        hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(L.args.ws), words);
+        if (L.args.slot < 0)
+            clear_state(L.args, st);
         if (vec)
             launch_first(&k_scan_columns<In, Acc, Op, B, tune::kScanColLanes, tune::kScanColRows, true>, grid,
                          block, st, ev, L.args);

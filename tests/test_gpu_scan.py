@@ -289,3 +289,67 @@ def test_empty_views():
     rk.scan(x, (5, 0), (1, 5), 1, out=guard)
     torch.cuda.synchronize()
     assert np.all(raw_np(guard) == 3.0)
+
+
+# ------------------------------------------------------ look-back tile state
+
+def _fused(rk, on):
+    class _F:
+        def __enter__(self):
+            self.prev = rk.rk_debug_set_fused_finish(on)
+
+        def __exit__(self, *exc):
+            rk.rk_debug_set_fused_finish(self.prev)
+    return _F()
+
+
+@pytest.mark.parametrize("on", [1, 0], ids=["library_slot", "workspace_and_clear_launch"])
+def test_tile_state_paths(on):
+    """The look-back state lives in the library's stream slot (reset by each
+    call's last block) or in the workspace (cleared by a launch first); both
+    give exact integer scans, call after call with changing tile counts on
+    one stream, and leave the tile count and a zero timeout word in the
+    workspace header."""
+    rk = _rk()
+    cases = [((3 * TILE + 5,), (1,), 1), ((10**6 + 3,), (1,), 1), ((TILE,), (1,), 1),
+             ((300, 2000), (1, 300), 2), ((10**8,), (1,), 1), ((5000, 2), (1, 5000), 1)]
+    with _fused(rk, on):
+        for rep in range(2):
+            for shape, strides, dim in cases:
+                n = math.prod(shape)
+                x = W.randint(n, -1000, 1000, 12400 + n % 101 + rep)
+                xd = x.to(DEV)
+                plan = rk.plan_scan(torch.int32, shape, strides, dim, acc=torch.int64)
+                assert plan["launches"] == (1 if on else 2), plan
+                nb = rk.rk_scan_workspace_size(rk.RK_I32, rk.RK_I64, len(shape), shape, strides, dim - 1)
+                ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=DEV)   # garbage on entry
+                out = rk.scan(xd, shape, strides, dim, acc=torch.int64, out_dtype=torch.int64, workspace=ws)
+                torch.cuda.synchronize()
+                hdr = ws[:8].cpu().numpy().view(np.uint32)
+                tiles = plan["split"] * (plan["grid"] // plan["split"])
+                assert hdr[0] == plan["grid"] == tiles and hdr[1] == 0, (shape, hdr)
+                R = O.scan_dims(O.SUM, O.I32, O.I64, raw_np(x), shape, strides, dim - 1, 0, True)
+                assert np.array_equal(raw_np(out)[:n], R), (shape, dim, on, rep)
+
+
+def test_tile_state_on_many_streams():
+    """Look-back scans queued on 40 streams at once (more streams than
+    library slots: the rest take workspace state), each with its own
+    workspace: every result exact."""
+    rk = _rk()
+    n = 3 * TILE + 77
+    xs = [W.randint(n, -1000, 1000, 12500 + i) for i in range(8)]
+    xds = [x.to(DEV) for x in xs]
+    nb = rk.rk_scan_workspace_size(rk.RK_I32, rk.RK_I64, 1, [n], [1], 0)
+    wss = [torch.empty(nb, dtype=torch.uint8, device=DEV) for _ in range(40)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(40)]
+    outs = []
+    for i, s in enumerate(streams):
+        with torch.cuda.stream(s):
+            outs.append(rk.scan(xds[i % 8], acc=torch.int64, out_dtype=torch.int64, workspace=wss[i], init=i))
+    for s in streams:
+        s.synchronize()
+    for i, o in enumerate(outs):
+        R = O.scan(O.SUM, O.I32, O.I64, raw_np(xs[i % 8]), i, True)
+        assert np.array_equal(raw_np(o), R), i

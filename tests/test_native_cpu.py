@@ -288,7 +288,15 @@ def test_scan_plans():
     tile = 16 * 8 * 64 * 4                      # waves * chunks * lanes * floats per 16 bytes
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.tile_outputs == tile and p.vec == 4
-    assert p.split == (10**8 + tile - 1) // tile and p.grid == p.split and p.launches == 2
+    assert p.split == (10**8 + tile - 1) // tile and p.grid == p.split
+    assert p.launches == 1                      # tile state in a library slot: no clearing launch
+    prev = rk.rk_debug_set_fused_finish(0)
+    try:
+        assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256).launches == 2
+    finally:
+        rk.rk_debug_set_fused_finish(prev)
+    big = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [8193 * tile], [1], 0, 256)
+    assert big.split == 8193 and big.launches == 2      # more tiles than a slot holds
     tiles = p.split
     assert p.workspace_bytes == -(-(8 + ((tiles + 1) // 2 * 2) * 4 + tiles * 16) // 256) * 256
     assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 1, [10**6], [1], 0, 256).vec == 1     # unaligned input
@@ -304,7 +312,7 @@ def test_scan_plans():
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [tile, 8], [1, tile], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.grid == 8
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 1, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_COLUMNS and p.vec == 4 and p.launches == 2
+    assert p.kernel == rk.RK_KERNEL_SCAN_COLUMNS and p.vec == 4 and p.launches == 1
     assert p.tile_outputs == 128 * 128 and p.split == 64 and p.grid == 64 * 64
     # the workspace covers both tile geometries: 16-byte loads (128 lines x 128
     # positions) and element loads (64 lines x 64 positions)
