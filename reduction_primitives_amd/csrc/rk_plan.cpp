@@ -362,12 +362,12 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
 
 // ------------------------------------------------------------------ scans
 
-int64_t scan_tile_elems(int in_dtype)
+int64_t scan_tile_elems(int in_dtype, int block)
 {
     const int isz = dtype_size(in_dtype);
     if (isz == 0)
         return 0;
-    return int64_t(tune::kScanTileBlock / 64) * tune::kScanUnroll * 64 * (16 / isz);
+    return int64_t(block / 64) * tune::kScanUnroll * 64 * (16 / isz);
 }
 
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
@@ -421,11 +421,16 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         for (int i = 0; i < k.nd; ++i)
             vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0 && (d.kept_out[i] * osz) % ob == 0;
         d.vec = vec_ok ? v : 1;
-        d.tile_elems = scan_tile_elems(in_dtype);
+        d.tile_elems = scan_tile_elems(in_dtype, tune::kScanTileBlock);
         const bool few_lines = d.lines < int64_t(num_cus) * tune::kScanTileFewLines;
         if (d.m >= d.tile_elems || (few_lines && d.m >= tune::kScanTileMinLen)) {
             d.kernel = SK_TILE;
             d.block = tune::kScanTileBlock;
+            // fewer large tiles than CUs: a quarter of the size keeps more CUs busy
+            if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus) {
+                d.block = tune::kScanBlock;
+                d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock);
+            }
             d.tiles_per_line = ceil_div(d.m, d.tile_elems);
             d.tiles = d.lines * d.tiles_per_line;
             d.grid = d.tiles;

@@ -75,7 +75,8 @@ constexpr int64_t kGenericMinChunk = 4096;   // generic kernel: reduced elements
 // scans
 constexpr int kScanBlock = 256;           // threads per block of the row-wave and lines kernels
 constexpr int kScanTileBlock = 1024;      // tile kernel: 16 waves share a tile (fewer, larger tiles
-                                          // amortise the look-back; 1e8 f32: 177 us vs 236 us at 256)
+                                          // amortise the look-back; 1e8 f32: 177 us vs 236 us at 256);
+                                          // kScanBlock-thread tiles when the large ones number < CUs
 constexpr int kScanUnroll = 8;            // 16-byte chunks in flight per lane (tile and row-wave kernels)
 constexpr int kScanLinesUnroll = 8;       // elements in flight per thread (lines kernel)
 constexpr int kScanLinesBlocksPerCu = 8;  // lines kernel grid cap
@@ -171,8 +172,8 @@ struct ScanPlan {
     size_t ws_bytes = 0;
 };
 
-// Elements of one scan tile for an input dtype.
-int64_t scan_tile_elems(int in_dtype);
+// Elements of one scan tile for an input dtype and tile-kernel block size.
+int64_t scan_tile_elems(int in_dtype, int block);
 
 // Scan plan: `dim` is 0-based; addresses only matter through alignment.
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,

@@ -785,7 +785,7 @@ int run_scan_typed(const ScanLaunch &L)
     const bool vec = L.vec > 1;
     if (vec && L.vec != InTraits<In>::vec)
         return ST_INVALID;
-    if (L.block != (L.kernel == SK_TILE ? BT : B))
+    if (L.block != B && !(L.kernel == SK_TILE && L.block == BT))
         return ST_INVALID;
     // a ScanLaunch carries no Launch; launch_first only reads the events
     Launch ev;
@@ -795,10 +795,17 @@ int run_scan_typed(const ScanLaunch &L)
     case SK_TILE: {
         if (L.args.slot < 0)
             clear_state(L.args, st);
-        if (vec)
-            launch_first(&k_scan_tile<In, Acc, Op, BT, U, true, true>, grid, block, st, ev, L.args);
-        else
-            launch_first(&k_scan_tile<In, Acc, Op, BT, U, false, true>, grid, block, st, ev, L.args);
+        if (L.block == BT) {
+            if (vec)
+                launch_first(&k_scan_tile<In, Acc, Op, BT, U, true, true>, grid, block, st, ev, L.args);
+            else
+                launch_first(&k_scan_tile<In, Acc, Op, BT, U, false, true>, grid, block, st, ev, L.args);
+        } else {
+            if (vec)
+                launch_first(&k_scan_tile<In, Acc, Op, B, U, true, true>, grid, block, st, ev, L.args);
+            else
+                launch_first(&k_scan_tile<In, Acc, Op, B, U, false, true>, grid, block, st, ev, L.args);
+        }
         break;
     }
     case SK_ROWWAVE:

@@ -213,12 +213,13 @@ def test_look_back_never_times_out():
     for n in (TILE + 1, 10**6, 3 * 10**7):
         x = W.uniform(n, -1.0, 1.0, 11750 + n % 7).to(DEV)
         ws = rk.workspace_for(rk.rk_scan_workspace_size(rk.RK_F32, rk.RK_F32, 1, [n], [1], 0), DEV)
+        tiles = rk.plan_scan(torch.float32, (n,), (1,), 1)["grid"]
         for _ in range(3):
             rk.scan(x, workspace=ws)
             torch.cuda.synchronize()
             header = ws[:8].cpu().numpy().view(np.uint32)
             assert header[1] == 0
-            assert header[0] == -(-n // TILE)      # every tile took one counter value
+            assert header[0] == tiles               # every tile took one counter value
 
 
 def test_integer_scans_are_deterministic():

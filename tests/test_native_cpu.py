@@ -305,12 +305,18 @@ def test_scan_plans():
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [4000], [1], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.workspace_bytes == 0 and p.block == 256
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [5000], [1], 0, 256)       # one short line: tiles
-    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 1024 and p.split == 1
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 256 and p.split == 1
+    # fewer large tiles than CUs: quarter-size tiles of 256-thread blocks
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**6], [1], 0, 256)
+    assert p.block == 256 and p.tile_outputs == tile // 4 and p.split == -(-10**6 // (tile // 4))
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256).block == 1024
     # 8192 x 8192 along dims=1 (8192 contiguous lines: a wave each) and dims=2 (strided)
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.n_out == 8192 * 8192
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [tile, 8], [1, tile], 0, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.grid == 8
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 4 and p.grid == 32
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [tile, 300], [1, tile], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.grid == 300 and p.block == 1024
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_COLUMNS and p.vec == 4 and p.launches == 1
     assert p.tile_outputs == 128 * 128 and p.split == 64 and p.grid == 64 * 64
