@@ -21,6 +21,7 @@
 
 #include "rk_launch.hpp"
 #include "rk_plan.hpp"
+#include "rk_scan_plan.hpp"
 
 namespace {
 

@@ -88,54 +88,6 @@ struct Launch {
     void *ev_end;
 };
 
-// Scans (prefix folds) along one dim: every line -- all indices fixed but
-// the scan dim's -- is scanned on its own.  Line l starts at input element
-// layout_offset(kept_in, l) and output element layout_offset(kept_out, l);
-// element k of a line is s_in * k / s_out * k further on.
-struct ScanArgs {
-    const void *x;
-    void *out;
-    void *ws;             // tile kernel: [counter | flags[tiles] | aggregates[tiles] | prefixes[tiles]]
-    int64_t m;            // elements per line
-    int64_t lines;
-    int kept_nd;
-    int64_t kept_ext[4];
-    int64_t kept_in[4];
-    int64_t kept_out[4];
-    int64_t s_in, s_out;  // scan-dim strides in elements
-    int64_t tiles_per_line;   // tile kernel
-    int64_t tiles;            // tile and columns kernels
-    int64_t col_tiles_per_run;    // columns kernel: tiles across one run of lines (kept dim 0)
-    int64_t col_tiles;            //   ... across all runs; tiles = col_tiles * chunks of the scan dim
-    int inclusive;
-    int out_dtype;
-    uint64_t init_bits;   // starting value, accumulator bits
-    int slot;             // >= 0: tile counter and flags in the library's slot (reset by the last
-                          // block); < 0: in the workspace, cleared by a fill launch first
-};
-
-// Tiles whose flags fit one library slot of a look-back scan.
-constexpr int kScanFlagCapacity = 8192;
-
-struct ScanLaunch {
-    int kernel;           // rk::ScanKernel
-    int acc, op;
-    int vec;              // elements per load (1: element loads)
-    int64_t grid;
-    int block;
-    ScanArgs args;
-    void *stream;
-    void *ev_begin;       // optional hipEvent_t pair around the scan kernel
-    void *ev_end;
-};
-
-int launch_scan_in_f32(const ScanLaunch &L);
-int launch_scan_in_bf16(const ScanLaunch &L);
-int launch_scan_in_f16(const ScanLaunch &L);
-int launch_scan_in_f64(const ScanLaunch &L);
-int launch_scan_in_i32(const ScanLaunch &L);
-int launch_scan_in_i64(const ScanLaunch &L);
-
 int launch_in_f32(const Launch &L);
 int launch_in_bf16(const Launch &L);
 int launch_in_f16(const Launch &L);

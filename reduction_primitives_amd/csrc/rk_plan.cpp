@@ -1,5 +1,6 @@
 // rk_plan.cpp -- host-side planning (no HIP; unit-tested on the CPU).
 #include "rk_plan.hpp"
+#include "rk_scan_plan.hpp"
 
 #include <algorithm>
 

@@ -22,9 +22,6 @@ enum Kernel {
     K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7, K_ALL2 = 8
 };
 
-// Scan kernels (rk_scan.hpp).
-enum ScanKernel { SK_NONE = 0, SK_TILE = 1, SK_ROWWAVE = 2, SK_LINES = 3, SK_COLUMNS = 4 };
-
 int dtype_size(int d);            // bytes per element, 0 for an unknown code
 bool dtype_is_fp(int d);
 bool dtype_known(int d);
@@ -72,24 +69,6 @@ constexpr int64_t kRowMinChunk = 2048;    // elements per row chunk, at least
 constexpr int kGenericBlocksPerCu = 8;   // generic kernel: grid cap, and split target
 constexpr int kGenericUnroll = 8;        // generic kernel: element loads in flight per thread
 constexpr int64_t kGenericMinChunk = 4096;   // generic kernel: reduced elements per split unit, at least
-// scans
-constexpr int kScanBlock = 256;           // threads per block of the row-wave and lines kernels
-constexpr int kScanTileBlock = 1024;      // tile kernel: 16 waves share a tile (fewer, larger tiles
-                                          // amortise the look-back; 1e8 f32: 177 us vs 236 us at 256);
-                                          // kScanBlock-thread tiles when the large ones number < CUs
-constexpr int kScanUnroll = 8;            // 16-byte chunks in flight per lane (tile and row-wave kernels)
-constexpr int kScanLinesUnroll = 8;       // elements in flight per thread (lines kernel)
-constexpr int kScanLinesBlocksPerCu = 8;  // lines kernel grid cap
-constexpr int64_t kScanWaveMinLen = 256;  // contiguous lines at least this long take a wave (or tiles)
-constexpr int64_t kScanTileFewLines = 4;  // fewer lines than CUs * this, each >= kScanTileMinLen: tiles
-constexpr int64_t kScanTileMinLen = 4096;
-constexpr int kScanSpinLimit = 1 << 24;   // look-back: sleeps per wait before giving up (about a second)
-// columns scan (strided scan dim, contiguous lines): a tile is W lines x R
-// scan positions; W = lanes * elements per 16-byte load
-constexpr int kScanColLanes = 32;         // lanes across a tile row with 16-byte loads (512-byte rows)
-constexpr int kScanColLanesScalar = 64;   //   ... with element loads
-constexpr int kScanColRows = 16;          // consecutive scan positions per thread
-constexpr int64_t kScanColMinRun = 16;    // runs of lines narrower than this take the lines kernel
 constexpr int kDefaultCus = 256;          // MI355X
 }  // namespace tune
 
@@ -148,36 +127,6 @@ struct DimsPlan {
     // arrival counters fit one slot (see rk_launch.hpp)
     bool fused_ok = false;
 };
-
-// Scan along one dim.  Lines are the indices of the other dims (extent-1
-// dims dropped, neighbours merged when both their input and output strides
-// chain), numbered column-major; the output is the view's shape stored
-// contiguously in column-major order.
-struct ScanPlan {
-    int kernel = SK_NONE;
-    int64_t m = 0;          // elements per line
-    int64_t lines = 0;
-    Layout kept_in;         // line -> input offset
-    int64_t kept_out[kMaxDims] = {0, 0, 0, 0};   // line -> output offset (extents of kept_in)
-    int64_t s_in = 0, s_out = 0;
-    int vec = 1;
-    int64_t tile_elems = 0; // elements per tile (tile and columns kernels)
-    int64_t tiles_per_line = 0;
-    int64_t tiles = 0;
-    int64_t col_tiles_per_run = 0;   // columns kernel
-    int64_t col_tiles = 0;
-    int64_t chunks = 0;
-    int64_t grid = 0;
-    int block = tune::kScanBlock;
-    size_t ws_bytes = 0;
-};
-
-// Elements of one scan tile for an input dtype and tile-kernel block size.
-int64_t scan_tile_elems(int in_dtype, int block);
-
-// Scan plan: `dim` is 0-based; addresses only matter through alignment.
-int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
-              const int64_t *shape, const int64_t *strides, int dim, int num_cus, ScanPlan *p);
 
 // Status codes as in the public header.
 enum { ST_OK = 0, ST_INVALID = 1, ST_UNSUPPORTED = 2, ST_HIP = 3 };

@@ -24,6 +24,7 @@
 #pragma once
 
 #include "rk_kernels.hpp"
+#include "rk_scan_plan.hpp"
 
 namespace rk {
 

@@ -1,0 +1,118 @@
+// rk_scan_plan.hpp -- host-side planning of scans and what the C ABI hands
+// to the scan translation units (plain structs, no HIP types).
+//
+// Scans along one dim (AcceleratedKernels.jl PR #202, opening paragraph):
+// every line -- all indices fixed but the scan dim's -- is scanned on its own.
+// Kept apart from the reductions' plan and launch headers so that the two
+// families change independently.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "rk_plan.hpp"
+
+namespace rk {
+
+// Scan kernels (rk_scan.hpp).
+enum ScanKernel { SK_NONE = 0, SK_TILE = 1, SK_ROWWAVE = 2, SK_LINES = 3, SK_COLUMNS = 4 };
+
+namespace tune {
+constexpr int kScanBlock = 256;           // threads per block of the row-wave and lines kernels
+constexpr int kScanTileBlock = 1024;      // tile kernel: 16 waves share a tile (fewer, larger tiles
+                                          // amortise the look-back; 1e8 f32: 177 us vs 236 us at 256);
+                                          // kScanBlock-thread tiles when the large ones number < CUs
+constexpr int kScanUnroll = 8;            // 16-byte chunks in flight per lane (tile and row-wave kernels)
+constexpr int kScanLinesUnroll = 8;       // elements in flight per thread (lines kernel)
+constexpr int kScanLinesBlocksPerCu = 8;  // lines kernel grid cap
+constexpr int64_t kScanWaveMinLen = 256;  // contiguous lines at least this long take a wave (or tiles)
+constexpr int64_t kScanTileFewLines = 4;  // fewer lines than CUs * this, each >= kScanTileMinLen: tiles
+constexpr int64_t kScanTileMinLen = 4096;
+constexpr int kScanSpinLimit = 1 << 24;   // look-back: sleeps per wait before giving up (about a second)
+// columns scan (strided scan dim, contiguous lines): a tile is W lines x R
+// scan positions; W = lanes * elements per 16-byte load
+constexpr int kScanColLanes = 32;         // lanes across a tile row with 16-byte loads (512-byte rows)
+constexpr int kScanColLanesScalar = 64;   //   ... with element loads
+constexpr int kScanColRows = 16;          // consecutive scan positions per thread
+constexpr int64_t kScanColMinRun = 16;    // runs of lines narrower than this take the lines kernel
+}  // namespace tune
+
+// Scans (prefix folds) along one dim: every line -- all indices fixed but
+// the scan dim's -- is scanned on its own.  Line l starts at input element
+// layout_offset(kept_in, l) and output element layout_offset(kept_out, l);
+// element k of a line is s_in * k / s_out * k further on.
+struct ScanArgs {
+    const void *x;
+    void *out;
+    void *ws;             // tile kernel: [counter | flags[tiles] | aggregates[tiles] | prefixes[tiles]]
+    int64_t m;            // elements per line
+    int64_t lines;
+    int kept_nd;
+    int64_t kept_ext[4];
+    int64_t kept_in[4];
+    int64_t kept_out[4];
+    int64_t s_in, s_out;  // scan-dim strides in elements
+    int64_t tiles_per_line;   // tile kernel
+    int64_t tiles;            // tile and columns kernels
+    int64_t col_tiles_per_run;    // columns kernel: tiles across one run of lines (kept dim 0)
+    int64_t col_tiles;            //   ... across all runs; tiles = col_tiles * chunks of the scan dim
+    int inclusive;
+    int out_dtype;
+    uint64_t init_bits;   // starting value, accumulator bits
+    int slot;             // >= 0: tile counter and flags in the library's slot (reset by the last
+                          // block); < 0: in the workspace, cleared by a fill launch first
+};
+
+// Tiles whose flags fit one library slot of a look-back scan.
+constexpr int kScanFlagCapacity = 8192;
+
+struct ScanLaunch {
+    int kernel;           // rk::ScanKernel
+    int acc, op;
+    int vec;              // elements per load (1: element loads)
+    int64_t grid;
+    int block;
+    ScanArgs args;
+    void *stream;
+    void *ev_begin;       // optional hipEvent_t pair around the scan kernel
+    void *ev_end;
+};
+
+int launch_scan_in_f32(const ScanLaunch &L);
+int launch_scan_in_bf16(const ScanLaunch &L);
+int launch_scan_in_f16(const ScanLaunch &L);
+int launch_scan_in_f64(const ScanLaunch &L);
+int launch_scan_in_i32(const ScanLaunch &L);
+int launch_scan_in_i64(const ScanLaunch &L);
+
+// Scan along one dim.  Lines are the indices of the other dims (extent-1
+// dims dropped, neighbours merged when both their input and output strides
+// chain), numbered column-major; the output is the view's shape stored
+// contiguously in column-major order.
+struct ScanPlan {
+    int kernel = SK_NONE;
+    int64_t m = 0;          // elements per line
+    int64_t lines = 0;
+    Layout kept_in;         // line -> input offset
+    int64_t kept_out[kMaxDims] = {0, 0, 0, 0};   // line -> output offset (extents of kept_in)
+    int64_t s_in = 0, s_out = 0;
+    int vec = 1;
+    int64_t tile_elems = 0; // elements per tile (tile and columns kernels)
+    int64_t tiles_per_line = 0;
+    int64_t tiles = 0;
+    int64_t col_tiles_per_run = 0;   // columns kernel
+    int64_t col_tiles = 0;
+    int64_t chunks = 0;
+    int64_t grid = 0;
+    int block = tune::kScanBlock;
+    size_t ws_bytes = 0;
+};
+
+// Elements of one scan tile for an input dtype and tile-kernel block size.
+int64_t scan_tile_elems(int in_dtype, int block);
+
+// Scan plan: `dim` is 0-based; addresses only matter through alignment.
+int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
+              const int64_t *shape, const int64_t *strides, int dim, int num_cus, ScanPlan *p);
+
+}  // namespace rk
