@@ -447,7 +447,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         // positions, look-back along the scan dim.  The workspace covers both
         // tile geometries, so its size does not depend on alignment.
         d.kernel = SK_COLUMNS;
-        d.block = tune::kScanBlock;
+        d.block = tune::kScanColBlock;
         const int ob = std::min(16, v * osz);
         bool vec_ok = in_addr % 16 == 0 && k.ext[0] % v == 0 && (d.s_in * isz) % 16 == 0 &&
                       out_addr % ob == 0 && (d.s_out * osz) % ob == 0;
@@ -459,7 +459,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             const bool vec = pass == 0;
             const int64_t lanes = vec ? tune::kScanColLanes : tune::kScanColLanesScalar;
             const int64_t w = lanes * (vec ? v : 1);
-            const int64_t r = (tune::kScanBlock / lanes) * tune::kScanColRows;
+            const int64_t r = (tune::kScanColBlock / lanes) * tune::kScanColRows;
             const int64_t ctpr = ceil_div(k.ext[0], w), ct = runs * ctpr, ch = ceil_div(d.m, r);
             const int64_t tiles = ct * ch;
             ws = std::max(ws, round_up_256(8 + size_t((tiles + 1) & ~int64_t(1)) * 4 + size_t(tiles * w) * 16));

@@ -786,7 +786,8 @@ int run_scan_typed(const ScanLaunch &L)
     const bool vec = L.vec > 1;
     if (vec && L.vec != InTraits<In>::vec)
         return ST_INVALID;
-    if (L.block != B && !(L.kernel == SK_TILE && L.block == BT))
+    constexpr int BC = tune::kScanColBlock;
+    if (L.kernel == SK_COLUMNS ? L.block != BC : (L.block != B && !(L.kernel == SK_TILE && L.block == BT)))
         return ST_INVALID;
     // a ScanLaunch carries no Launch; launch_first only reads the events
     Launch ev;
@@ -822,11 +823,11 @@ int run_scan_typed(const ScanLaunch &L)
         if (L.args.slot < 0)
             clear_state(L.args, st);
         if (vec)
-            launch_first(&k_scan_columns<In, Acc, Op, B, tune::kScanColLanes, tune::kScanColRows, true>, grid,
+            launch_first(&k_scan_columns<In, Acc, Op, BC, tune::kScanColLanes, tune::kScanColRows, true>, grid,
                          block, st, ev, L.args);
         else
-            launch_first(&k_scan_columns<In, Acc, Op, B, tune::kScanColLanesScalar, tune::kScanColRows, false>, grid,
-                         block, st, ev, L.args);
+            launch_first(&k_scan_columns<In, Acc, Op, BC, tune::kScanColLanesScalar, tune::kScanColRows, false>,
+                         grid, block, st, ev, L.args);
         break;
     }
     default:

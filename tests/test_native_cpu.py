@@ -319,10 +319,10 @@ def test_scan_plans():
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.grid == 300 and p.block == 1024
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_COLUMNS and p.vec == 4 and p.launches == 1
-    assert p.tile_outputs == 128 * 128 and p.split == 64 and p.grid == 64 * 64
-    # the workspace covers both tile geometries: 16-byte loads (128 lines x 128
-    # positions) and element loads (64 lines x 64 positions)
-    scalar_tiles = 128 * 128
+    assert p.tile_outputs == 128 * 256 and p.split == 32 and p.grid == 64 * 32 and p.block == 512
+    # the workspace covers both tile geometries: 16-byte loads (128 lines x 256
+    # positions) and element loads (64 lines x 128 positions)
+    scalar_tiles = 128 * 64
     assert p.workspace_bytes == -(-(8 + scalar_tiles * 4 + scalar_tiles * 64 * 16) // 256) * 256
     assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 2, [8192, 8192], [1, 8192], 1, 256).vec == 1
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10, 100], [1, 10], 1, 256)
