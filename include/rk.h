@@ -14,6 +14,9 @@
  *     thread per output, a tiled 2-d block and a split columns kernel, and
  *     the columns kernel also takes runs of contiguous outputs such as the
  *     middle dim of a 3-d array (section "This PR").
+ *   - a two-input source f(a_i, b_i) on the whole-array passes
+ *     (rk_reduce_all2), and scans, the prefix folds of PR #202 (rk_scan,
+ *     rk_scan_dims).
  *
  * Conventions shared by every entry point
  * ---------------------------------------

@@ -45,14 +45,29 @@ PURE_UNITS = ["rk_plan.cpp"]              # plain C++
 REDUCTION_KERNEL_SOURCES = ["kern_f32.hip", "rk_kernels.hpp", "rk_device.hpp", "rk_launch.hpp", "rk_plan.hpp"]
 
 
-def kernel_source_digest() -> str:
-    """SHA-256 over the sources and compile flags of the float32 reduction
-    kernels (identifies the kernels a stored counter profile was taken on)."""
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed (the
+    kernel sources hold no string literals with comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_digest(sources=None) -> str:
+    """SHA-256 over the code (comments and layout ignored) and compile flags
+    of the float32 reduction kernels: identifies the kernels a stored counter
+    profile was taken on.  `sources` maps file names to text (default: the
+    files in csrc)."""
     import hashlib
     h = hashlib.sha256(" ".join(HIP_FLAGS[:-2]).encode())
     for name in REDUCTION_KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        if sources is None:
+            with open(os.path.join(CSRC, name)) as f:
+                text = f.read()
+        else:
+            text = sources[name]
+        h.update(name.encode() + b"\0" + _code_only(text).encode())
     return h.hexdigest()
 
 

@@ -2,17 +2,19 @@
 //
 // Whole array (AcceleratedKernels.jl PR #139, "What changes"): a first pass
 // of at most a grid cap of blocks, each striding over tiles of the input with
-// several 16-byte loads in flight per thread, then a one-block second pass;
+// several 16-byte loads in flight per thread; the last block to arrive folds
+// the partials (a one-block second pass when no arrival counters are free);
 // an input that fits one block finishes in the first pass.  A fused
 // two-input source f(x_i, y_i) takes the same passes with two loads per step.
 //
 // Strided dims (PR #176, "This PR"): one tile kernel serves the selector's
 // three shapes -- one thread per output (a tile one row tall), the narrow
 // tiled block (one pass) and the wide columns block (split along the reduced
-// dim, finished by the last block to arrive or a second pass) -- over runs of contiguous
-// outputs placed by the other kept dims (the middle dim of 3-d arrays).  A
-// contiguous reduced dim takes the row kernel (one wave per output); any
-// other layout the generic kernel (one block per output).
+// dim, finished by the last block to arrive or a second pass) -- over runs of
+// contiguous outputs placed by the other kept dims (the middle dim of 3-d
+// arrays); further reduced dims index segments of rows.  A contiguous reduced
+// dim takes the row kernel (one wave per output); any other layout the
+// generic kernel (blocks over (output, chunk) units).
 //
 // Every last pass stores through finish_store().  No kernel reads workspace
 // it did not write in the same call, so a workspace is reusable as is.
