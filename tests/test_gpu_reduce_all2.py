@@ -247,3 +247,16 @@ def test_invalid_arguments_are_rejected():
     assert call(acc=rk.RK_I32) == rk.RK_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert float(out.item()) == 100.0
+
+
+def test_beyond_2_31_elements():
+    """Two inputs of more than 2^31 elements (2 x 8.6 GB of int32 ones):
+    64-bit indexing on both load paths; the totals are closed forms."""
+    rk = _rk()
+    n = 2**31 + 5
+    ones = torch.ones(n + 1, dtype=torch.int32, device=DEV)
+    assert int(rk.reduce_all2(ones[:n], ones[1:], "mul", acc=torch.int64, out_dtype=torch.int64).item()) == n
+    twos = torch.full((n,), 2, dtype=torch.int32, device=DEV)
+    assert int(rk.reduce_all2(ones[:n], twos, "absdiff", acc=torch.int64, out_dtype=torch.int64).item()) == n
+    del ones, twos
+    torch.cuda.empty_cache()

@@ -354,3 +354,26 @@ def test_tile_state_on_many_streams():
     for i, o in enumerate(outs):
         R = O.scan(O.SUM, O.I32, O.I64, raw_np(xs[i % 8]), i, True)
         assert np.array_equal(raw_np(o), R), i
+
+
+def test_beyond_2_31_elements():
+    """A scan of more than 2^31 int32 ones into int64 (8.6 GB in, 17 GB out):
+    more tiles than a library slot holds, so the workspace state and its
+    clearing launch; output k is k + 1 (sampled), and along dims=2 of a
+    (2^16, 32769) view the last line's outputs sit past 2^31 elements."""
+    rk = _rk()
+    n = 2**31 + 3000
+    ones = torch.ones(n, dtype=torch.int32, device=DEV)
+    plan = rk.plan_scan(torch.int32, (n,), (1,), 1, acc=torch.int64)
+    assert plan["kernel_name"] == "scan_tile" and plan["launches"] == 2
+    out = rk.scan(ones, acc=torch.int64, out_dtype=torch.int64)
+    idx = torch.tensor([0, 1, 12345, 2**31 - 1, 2**31, n - 2, n - 1], device=DEV)
+    assert out[idx].cpu().tolist() == [int(i) + 1 for i in idx.cpu().tolist()]
+    del out
+    L, k = 1 << 16, n // (1 << 16)
+    cols = rk.scan(ones, (L, k), (1, L), 2, acc=torch.int64, out_dtype=torch.int64)
+    assert rk.plan_scan(torch.int32, (L, k), (1, L), 2, acc=torch.int64)["kernel_name"] == "scan_columns"
+    last = cols[(k - 1) * L:k * L]
+    assert bool((last == k).all().item()) and int(cols[L - 1].item()) == 1
+    del ones, cols
+    torch.cuda.empty_cache()
