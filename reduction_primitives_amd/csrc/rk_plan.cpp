@@ -415,20 +415,28 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         ++k.nd;
     }
     const int v = 16 / isz;
+    const int asz = dtype_size(acc_dtype);
     if (d.s_in == 1 && d.s_out == 1 && d.m >= tune::kScanWaveMinLen) {
-        // lines contiguous along the scan dim in both input and output
-        const int ob = std::min(16, v * osz);   // bytes of one lane's outputs, up to 16
-        bool vec_ok = in_addr % 16 == 0 && d.m % v == 0 && out_addr % ob == 0;
+        // lines contiguous along the scan dim in both input and output.  A
+        // lane loads vl elements: the input's 16 bytes, or, when the outputs
+        // are as wide as the accumulator and wider than the inputs, as many as
+        // make 16 bytes of output, so each store stays one contiguous piece.
+        const int vl = (osz > isz && osz == asz) ? 16 / osz : v;
+        const int lb = vl * isz;                // bytes of one lane's load
+        const int ob = std::min(16, vl * osz);  // bytes of one lane's outputs, up to 16
+        bool vec_ok = in_addr % lb == 0 && d.m % vl == 0 && out_addr % ob == 0;
         for (int i = 0; i < k.nd; ++i)
-            vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0 && (d.kept_out[i] * osz) % ob == 0;
-        d.vec = vec_ok ? v : 1;
+            vec_ok = vec_ok && (k.str[i] * isz) % lb == 0 && (d.kept_out[i] * osz) % ob == 0;
+        d.vec = vec_ok ? vl : 1;
         d.tile_elems = scan_tile_elems(in_dtype, tune::kScanTileBlock);
         const bool few_lines = d.lines < int64_t(num_cus) * tune::kScanTileFewLines;
         if (d.m >= d.tile_elems || (few_lines && d.m >= tune::kScanTileMinLen)) {
             d.kernel = SK_TILE;
             d.block = tune::kScanTileBlock;
-            // fewer large tiles than CUs: a quarter of the size keeps more CUs busy
-            if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus) {
+            // fewer large tiles than CUs: a quarter of the size keeps more CUs
+            // busy; element loads take the small tiles too (the large ones
+            // would need more than the 128 registers a 1024-thread block allows)
+            if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus || d.vec == 1) {
                 d.block = tune::kScanBlock;
                 d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock);
             }

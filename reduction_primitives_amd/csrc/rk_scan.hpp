@@ -197,33 +197,52 @@ __device__ __forceinline__ void store_run(void *out, int64_t idx, int out_dtype,
 
 // ------------------------------------------------------------ chunk scans
 
-// A chunk is 64 * V consecutive elements of a line: lane l holds elements
-// l*V .. l*V+V-1 (one 16-byte load when V > 1).  Elements past the line's
-// end hold the identity.
-template <class In, class Acc, class Op, bool VECTOR>
+// A chunk is 64 * VL consecutive elements of a line: lane l holds elements
+// l*VL .. l*VL+VL-1, loaded at once (16 bytes when VL is the input's 16-byte
+// vector; 8 or 4 bytes when the outputs are wider than the inputs, so that a
+// lane's outputs still make one 16-byte store).  Elements past the line's end
+// hold the identity.
+template <class In, int VL, int BYTES = VL * int(sizeof(typename InTraits<In>::S))>
+struct ChunkRaw {
+    using type = std::conditional_t<
+        VL == 1, typename InTraits<In>::S,
+        std::conditional_t<BYTES == 16, u32x4, std::conditional_t<BYTES == 8, uint64_t, uint32_t>>>;
+};
+
+template <class In, class Acc, class Op, int VL>
 struct Chunk {
     using S = typename InTraits<In>::S;
-    static constexpr int V = VECTOR ? InTraits<In>::vec : 1;
-    using Raw = std::conditional_t<VECTOR, u32x4, S>;
+    static constexpr int V = VL;
+    using Raw = typename ChunkRaw<In, VL>::type;
+    static_assert(VL == 1 || sizeof(Raw) == VL * sizeof(S), "a lane's elements are one load");
 
     __device__ static Raw load(const S *x, int64_t i, int64_t m)
     {
         Raw r{};
         if (i < m) {
-            if constexpr (VECTOR)
+            if constexpr (VL == 1)
+                r = load1(x + i);
+            else if constexpr (sizeof(Raw) == 16)
                 r = load16(reinterpret_cast<const u32x4 *>(x + i));
             else
-                r = load1(x + i);
+                r = load1(reinterpret_cast<const Raw *>(x + i));
         }
         return r;
     }
 
     __device__ static void decode(Raw r, bool valid, Acc (&e)[V])
     {
-        if constexpr (VECTOR)
-            InTraits<In>::template decode<Acc>(r, e);
-        else
+        if constexpr (VL == 1) {
             e[0] = InTraits<In>::template one<Acc>(r);
+        } else if constexpr (VL == InTraits<In>::vec) {
+            InTraits<In>::template decode<Acc>(r, e);
+        } else {
+            S t[VL];
+            __builtin_memcpy(t, &r, sizeof r);
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                e[i] = InTraits<In>::template one<Acc>(t[i]);
+        }
 #pragma unroll
         for (int i = 0; i < V; ++i)
             e[i] = valid ? e[i] : Op::template identity<Acc>();
@@ -421,13 +440,13 @@ __global__ __launch_bounds__(BLOCK) void k_scan_clear(uint32_t *w, int64_t words
 
 // Tile kernel: a tile is NW waves x UC chunks of consecutive elements of one
 // line; tiles are numbered by a counter in the order blocks start.
-template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR, bool NTS = false>
+template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = false>
 __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
 {
-    using C = Chunk<In, Acc, Op, VECTOR>;
+    using C = Chunk<In, Acc, Op, VL>;
     using S = typename C::S;
     constexpr int V = C::V;
-    constexpr int UC = VECTOR ? U : U * InTraits<In>::vec;   // chunks per wave
+    constexpr int UC = U * (InTraits<In>::vec / VL);         // chunks per wave: a tile is the same size for any VL
     constexpr int64_t CH = 64 * V;
     constexpr int NW = BLOCK / 64;
     constexpr int64_t T = int64_t(NW) * UC * CH;
@@ -458,17 +477,18 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
         raw[k] = C::load(x, first + k * CH, a.m);
     issue_barrier();
 
-    Acc lane_excl[UC], total[UC];
+    // the wave's total first (the look-back needs only the tile's); the
+    // chunks are scanned after it, so no per-chunk state is held across it
+    Acc lt = Op::template identity<Acc>();
 #pragma unroll
     for (int k = 0; k < UC; ++k) {
         Acc e[V];
         C::decode(raw[k], first + k * CH < a.m, e);
-        chunk_scan<Acc, Op, V>(e, lane_excl[k], total[k]);
-    }
-    Acc wt = total[0];
 #pragma unroll
-    for (int k = 1; k < UC; ++k)
-        wt = Op::apply(wt, total[k]);
+        for (int i = 0; i < V; ++i)
+            lt = Op::apply(lt, e[i]);
+    }
+    const Acc wt = wave_reduce<Op>(lt);
     if (lane_id() == 0)
         s_wave[w] = wt;
     __syncthreads();
@@ -486,29 +506,35 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
     }
     __syncthreads();
 
+    // decode the raw loads again below rather than keeping the first decode
+    // alive across the look-back (wider accumulators would double the registers)
+#pragma unroll
+    for (int k = 0; k < UC; ++k)
+        asm volatile("" : "+v"(raw[k]));
     Acc carry = Op::apply(s_excl, wpre);
 #pragma unroll
     for (int k = 0; k < UC; ++k) {
         const int64_t i = first + k * CH;
-        Acc e[V], o[V];
+        Acc e[V], o[V], lane_excl, total;
         C::decode(raw[k], i < a.m, e);
-        chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl[k]), a.inclusive != 0, o);
+        chunk_scan<Acc, Op, V>(e, lane_excl, total);
+        chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl), a.inclusive != 0, o);
         if (i < a.m)
             store_run<Acc, V, NTS>(a.out, ob + i, a.out_dtype, o);
-        carry = Op::apply(carry, total[k]);
+        carry = Op::apply(carry, total);
     }
     scan_release<BLOCK>(st, a.ws, a.tiles);
 }
 
 // Row-wave kernel: one wave per line, UC chunks in flight, the carry passed
 // from chunk to chunk.
-template <class In, class Acc, class Op, int BLOCK, int U, bool VECTOR, bool NTS = true>
+template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = true>
 __global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
 {
-    using C = Chunk<In, Acc, Op, VECTOR>;
+    using C = Chunk<In, Acc, Op, VL>;
     using S = typename C::S;
     constexpr int V = C::V;
-    constexpr int UC = VECTOR ? U : U * InTraits<In>::vec;
+    constexpr int UC = U * (InTraits<In>::vec / VL);
     constexpr int64_t CH = 64 * V;
     const int64_t line = int64_t(blockIdx.x) * (BLOCK / 64) + (threadIdx.x >> 6);
     if (line >= a.lines)
@@ -602,7 +628,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
 #pragma unroll
     for (int q = 0; q < RPG; ++q) {
         Acc e[V];
-        Chunk<In, Acc, Op, VECTOR>::decode(raw[q], active && r0 + q < a.m, e);
+        Chunk<In, Acc, Op, V>::decode(raw[q], active && r0 + q < a.m, e);
 #pragma unroll
         for (int i = 0; i < V; ++i)
             tot[i] = Op::apply(tot[i], e[i]);
@@ -703,6 +729,11 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     if (threadIdx.x == 0)
         __hip_atomic_store(st.flags + g, kFlagPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+    // decode the raw loads again below rather than keeping the first decode
+    // alive across the look-back (wider accumulators would double the registers)
+#pragma unroll
+    for (int q = 0; q < RPG; ++q)
+        asm volatile("" : "+v"(raw[q]));
     Acc runv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
@@ -711,7 +742,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     for (int q = 0; q < RPG; ++q) {
         const int64_t r = r0 + q;
         Acc e[V], o[V];
-        Chunk<In, Acc, Op, VECTOR>::decode(raw[q], active && r < a.m, e);
+        Chunk<In, Acc, Op, V>::decode(raw[q], active && r < a.m, e);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             if (a.inclusive) {
@@ -783,9 +814,6 @@ int run_scan_typed(const ScanLaunch &L)
     constexpr int B = tune::kScanBlock;
     constexpr int BT = tune::kScanTileBlock;
     constexpr int U = tune::kScanUnroll;
-    const bool vec = L.vec > 1;
-    if (vec && L.vec != InTraits<In>::vec)
-        return ST_INVALID;
     constexpr int BC = tune::kScanColBlock;
     if (L.kernel == SK_COLUMNS ? L.block != BC : (L.block != B && !(L.kernel == SK_TILE && L.block == BT)))
         return ST_INVALID;
@@ -793,36 +821,47 @@ int run_scan_typed(const ScanLaunch &L)
     Launch ev;
     ev.ev_begin = L.ev_begin;
     ev.ev_end = L.ev_end;
+    // elements per lane of the tile and row-wave kernels: the input's 16-byte
+    // vector, the accumulator's (outputs wider than inputs), or one
+    constexpr int VV = InTraits<In>::vec;
+    constexpr int VW = int(16 / sizeof(Acc)) < VV ? int(16 / sizeof(Acc)) : VV;
+    const int vl = L.vec;
+    if (vl != 1 && vl != VV && vl != VW)
+        return ST_INVALID;
     switch (L.kernel) {
     case SK_TILE: {
         if (L.args.slot < 0)
             clear_state(L.args, st);
+#define RK_SCAN_TILE(BK, VLN) launch_first(&k_scan_tile<In, Acc, Op, BK, U, VLN, true>, grid, block, st, ev, L.args)
         if (L.block == BT) {
-            if (vec)
-                launch_first(&k_scan_tile<In, Acc, Op, BT, U, true, true>, grid, block, st, ev, L.args);
-            else
-                launch_first(&k_scan_tile<In, Acc, Op, BT, U, false, true>, grid, block, st, ev, L.args);
+            if (vl == VV) RK_SCAN_TILE(BT, VV);
+            else if (vl == VW) RK_SCAN_TILE(BT, VW);
+            else return ST_INVALID;             // element loads take the small tiles
         } else {
-            if (vec)
-                launch_first(&k_scan_tile<In, Acc, Op, B, U, true, true>, grid, block, st, ev, L.args);
-            else
-                launch_first(&k_scan_tile<In, Acc, Op, B, U, false, true>, grid, block, st, ev, L.args);
+            if (vl == VV) RK_SCAN_TILE(B, VV);
+            else if (vl == VW) RK_SCAN_TILE(B, VW);
+            else RK_SCAN_TILE(B, 1);
         }
+#undef RK_SCAN_TILE
         break;
     }
     case SK_ROWWAVE:
-        if (vec)
-            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, true>, grid, block, st, ev, L.args);
+        if (vl == VV)
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, VV>, grid, block, st, ev, L.args);
+        else if (vl == VW)
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, VW>, grid, block, st, ev, L.args);
         else
-            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, false>, grid, block, st, ev, L.args);
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, 1>, grid, block, st, ev, L.args);
         break;
     case SK_LINES:
         launch_first(&k_scan_lines<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
         break;
     case SK_COLUMNS: {
+        if (vl != 1 && vl != VV)
+            return ST_INVALID;
         if (L.args.slot < 0)
             clear_state(L.args, st);
-        if (vec)
+        if (vl == VV)
             launch_first(&k_scan_columns<In, Acc, Op, BC, tune::kScanColLanes, tune::kScanColRows, true>, grid,
                          block, st, ev, L.args);
         else

@@ -299,7 +299,17 @@ def test_scan_plans():
     assert big.split == 8193 and big.launches == 2      # more tiles than a slot holds
     tiles = p.split
     assert p.workspace_bytes == -(-(8 + ((tiles + 1) // 2 * 2) * 4 + tiles * 16) // 256) * 256
-    assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 1, [10**6], [1], 0, 256).vec == 1     # unaligned input
+    p = rk.rk_plan_scan(f32, f32, f32, 4, 0, 1, [10**8], [1], 0, 256)                # unaligned input
+    assert p.vec == 1 and p.block == 256
+    # outputs wider than the inputs: lanes take as many elements as make 16 bytes of output
+    i32, i64, f64, bf16 = rk.RK_I32, rk.RK_I64, rk.RK_F64, rk.RK_BF16
+    assert rk.rk_plan_scan(i32, i64, i64, 0, 0, 1, [10**6], [1], 0, 256).vec == 2
+    assert rk.rk_plan_scan(i32, i64, i64, 8, 0, 1, [10**6], [1], 0, 256).vec == 2      # 8-byte loads
+    assert rk.rk_plan_scan(i32, i64, i64, 4, 0, 1, [10**6], [1], 0, 256).vec == 1
+    assert rk.rk_plan_scan(i32, i64, i32, 0, 0, 1, [10**6], [1], 0, 256).vec == 4      # narrow output
+    assert rk.rk_plan_scan(f32, f64, f64, 0, 0, 1, [10**6], [1], 0, 256).vec == 2
+    assert rk.rk_plan_scan(bf16, f32, f32, 0, 0, 1, [10**6], [1], 0, 256).vec == 4
+    assert rk.rk_plan_scan(bf16, f32, bf16, 0, 0, 1, [10**6], [1], 0, 256).vec == 8
     assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 2, 1, [10**6], [1], 0, 256).vec == 1   # 2-byte aligned out
     assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 8, 1, [10**6], [1], 0, 256).vec == 4
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [4000], [1], 0, 256)
