@@ -70,6 +70,12 @@
  * counters return to zero by themselves.  Calls from several host threads are
  * safe; two calls that share a workspace must be ordered by the caller.
  *
+ * Graph capture: OVERWRITE and FOLD calls enqueue kernels only (no memset,
+ * no copy, no allocation), so they may be captured into a HIP graph and the
+ * graph replayed.  Captured kernels keep the slot of the stream they were
+ * captured on: replays of one graph must not overlap each other or calls on
+ * that capture stream.  HOST mode waits on the stream and cannot be captured.
+ *
  * Errors: every argument is validated before any launch; a rejected call
  * returns a non-zero rk_status and writes nothing.  A HIP launch failure is
  * reported as RK_ERR_HIP.  The library prints nothing unless the environment
