@@ -6,7 +6,7 @@ One step runs every call of the hot path once over resident synthetic input:
   whole array, 10^8 elements (AcceleratedKernels.jl PR #139, "Numbers"):
     max and min of a permutation of 0..10^8-1 (int32), then float32 U[0,1)
     sums: into a device scalar with init = 1.5 (overwrite), folded into that
-    scalar, and to a host value (two launches + copy + host finish)
+    scalar, and to a host value (finished on the host, which waits for it)
   8192x8192 column-major (PR #176, "Timings", last row):
     float32 sum over dims=2, sum over dims=1, max over dims=2, sum of
     squares of the whole array; int32 sum over dims=1 into int64
@@ -15,8 +15,10 @@ Each call reads its own copy of the input, so no call finds its data in the
 
 Printed: one JSON line with the aggregate algorithmic bandwidth (bytes the
 method must move / time), the roofline of the dominant kernel (the float32
-sum first pass, timed per launch with HIP events on its stream), and the CPU
-oracle timed on the host over the same step as a baseline.
+sum first pass, timed per launch with HIP events on its stream) with the
+read ceiling beside it (a read-only kernel over the same inputs, timed the
+same way), and the CPU oracle timed on the host over the same step as a
+baseline.
 """
 from __future__ import annotations
 
@@ -437,6 +439,18 @@ def configs_table(rk, torch, dev, reps):
 
     xf, perm = W.whole_large(10**8)
     xd, pd = xf.data.to(dev), perm.data.to(dev)
+    # one GPU's shard of the 1e8 sum split over eight GPUs (50 MB: fits the
+    # Infinity Cache, so the cold figure is the one that counts)
+    shard = xd[: 10**8 // 8]
+    whole("1.25e7 f32 sum (1e8 over 8 GPUs, one shard)", shard, init=1.5)
+    # reference, not a library call: torch's plain copy moves a scan's bytes
+    dst = torch.empty_like(xd)
+
+    def copy_fn():
+        dst.copy_(xd)
+        return False
+    timed("1e+08 f32 copy (torch, read + write reference)", copy_fn, 8 * 10**8, "torch")
+    del dst
     scan("1e+08 f32 cumsum (read + write)", xd, (10**8,), (1,), 1)
     scan("1e+08 f32 running max, exclusive", xd, (10**8,), (1,), 1, op="max", inclusive=False)
     scan("1e+08 i32 cumsum -> int64", pd, (10**8,), (1,), 1, acc=torch.int64, out_dtype=torch.int64)
@@ -461,6 +475,38 @@ def configs_table(rk, torch, dev, reps):
     dims("8192x8192 i32 sum dims=1 -> int64", mi, mid, 1, acc=torch.int64, out_dtype=torch.int64)
     del flush
     return rows
+
+
+def read_ceiling(rk, torch, bufs, launches=30):
+    """The device's streaming-read ceiling: the library's read-only kernel
+    (16-byte non-temporal loads, one integer operation per word, no stores)
+    over the same 400 MB inputs as the dominant kernel, at a few grid sizes,
+    each launch timed by events around it as the dominant kernel's are.
+    Consecutive launches read different buffers, so none finds the previous
+    one's lines in the Infinity Cache.  Returns the best grid's figures."""
+    sink = torch.zeros(1, dtype=torch.int32, device=bufs[0].device)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    best = None
+    for grid in (512, 1024, 2048, 4096):
+        for i in range(3):
+            rk.rk_debug_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, sink.data_ptr(), st)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(launches)]
+        torch.cuda.synchronize()
+        for i, (b, e) in enumerate(ev):
+            b.record()
+            rk.rk_debug_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, sink.data_ptr(), st)
+            e.record()
+        torch.cuda.synchronize()
+        us = [b.elapsed_time(e) * 1e3 for b, e in ev]
+        row = dict(grid=grid, avg_launch_us=round(statistics.mean(us), 2), min_us=round(min(us), 2))
+        row["GBps"] = round(nbytes / (row["avg_launch_us"] * 1e-6) / 1e9, 1)
+        log(f"  read ceiling, grid {grid:5d}: {row['avg_launch_us']:.2f} us avg, {row['min_us']:.2f} us min,"
+            f" {row['GBps']:.1f} GB/s")
+        if best is None or row["avg_launch_us"] < best["avg_launch_us"]:
+            best = row
+    return best
 
 
 def main():
@@ -530,6 +576,11 @@ def main():
     log(f"step: {ms_per_step:.3f} ms, {value:.1f} GB/s aggregate ({value / PEAK_GBPS:.1%} of peak)")
     log(f"dominant kernel {DOMINANT}: {avg_launch_s * 1e6:.1f} us per launch, {achieved:.1f} GB/s")
 
+    ceiling = read_ceiling(rk, torch, keep[0] + keep[1])
+    mem = rk.rk_debug_device_info()
+    log(f"read ceiling: {ceiling['GBps']:.1f} GB/s (grid {ceiling['grid']}); dominant kernel at "
+        f"{achieved / ceiling['GBps']:.1%} of it")
+
     host_value = outs["host"].value
     snap = {k: (v.detach().cpu().clone() if hasattr(v, "detach") else v) for k, v in outs.items()}
     per_call = per_call_table(calls, torch, args.per_call_reps, dev) if args.per_call_reps > 0 else None
@@ -566,6 +617,8 @@ def main():
             "kernels_8192": kernels,
             "device": props.name,
             "cus": props.multi_processor_count,
+            "memory": dict(clock_khz=mem["mem_clock_khz"], bus_bits=mem["mem_bus_bits"],
+                           clock_x_bus_GBps=round(mem["mem_clock_khz"] * 1e3 * mem["mem_bus_bits"] / 8 / 1e9, 1)),
         },
         "roofline": {
             "bound": "hbm",
@@ -578,6 +631,9 @@ def main():
             "algorithmic_bytes_per_launch": N_WHOLE * 4,
             "avg_launch_us": round(avg_launch_s * 1e6, 2),
             "launches_timed": len(launch_ms),
+            "read_ceiling_GBps": ceiling["GBps"],
+            "read_ceiling_grid": ceiling["grid"],
+            "frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4),
         },
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

@@ -316,6 +316,20 @@ int rk_debug_set_fused_finish(int enable);
  * NULLs to stop.  Returns an rk_status. */
 int rk_debug_set_launch_events(void *begin, void *end);
 
+/* Benchmark hook: the device's read-bandwidth ceiling.  Enqueues on `stream`
+ * one kernel that loads each of the nbytes / 16 vectors at `ptr` once
+ * (16-byte non-temporal loads, `grid` blocks of 256 threads, 0 = 2048) and
+ * does one integer operation per word; it computes nothing a caller can use.
+ * `ptr`: device memory, 16-byte aligned; nbytes: a multiple of 16.  `sink`:
+ * one 4-byte device word that the kernel may overwrite with an unspecified
+ * value.  Asynchronous.  Returns an rk_status. */
+int rk_debug_stream_read(const void *ptr, int64_t nbytes, int grid, void *sink, void *stream);
+
+/* The current device's compute units, memory clock (kHz) and memory bus
+ * width (bits), as the HIP runtime reports them.  Returns an rk_status
+ * (RK_ERR_HIP without a usable device). */
+int rk_debug_device_info(int64_t *num_cus, int64_t *mem_clock_khz, int64_t *mem_bus_bits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 
 EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_dims", "rk_status_string",
            "rk_plan_all", "rk_plan_all2", "rk_plan_dims", "rk_debug_set_fused_finish",
            "rk_debug_set_launch_events", "rk_scan_workspace_size", "rk_scan", "rk_scan_dims",
-           "rk_plan_scan")
+           "rk_plan_scan", "rk_debug_stream_read", "rk_debug_device_info")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -93,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.rk_debug_set_fused_finish.restype = i32
     lib.rk_debug_set_launch_events.argtypes = [vp, vp]
     lib.rk_debug_set_launch_events.restype = i32
+    lib.rk_debug_stream_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.rk_debug_stream_read.restype = i32
+    lib.rk_debug_device_info.argtypes = [p64, p64, p64]
+    lib.rk_debug_device_info.restype = i32
     _lib = lib
     return lib
 
@@ -187,3 +191,19 @@ def rk_debug_set_fused_finish(enable: int) -> int:
 
 def rk_debug_set_launch_events(begin, end) -> int:
     return int(load().rk_debug_set_launch_events(begin, end))
+
+
+def rk_debug_stream_read(ptr, nbytes, grid, sink, stream) -> None:
+    rc = load().rk_debug_stream_read(ptr, nbytes, grid, sink, stream)
+    if rc:
+        raise RkError(rc, "rk_debug_stream_read")
+
+
+def rk_debug_device_info() -> dict:
+    """The current device's compute units, memory clock (kHz) and memory bus
+    width (bits)."""
+    vals = [ctypes.c_int64() for _ in range(3)]
+    rc = load().rk_debug_device_info(*(ctypes.byref(v) for v in vals))
+    if rc:
+        raise RkError(rc, "rk_debug_device_info")
+    return dict(num_cus=vals[0].value, mem_clock_khz=vals[1].value, mem_bus_bits=vals[2].value)

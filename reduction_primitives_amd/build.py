@@ -35,7 +35,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I" + INCLUDE, 
 KERNEL_UNITS = ["kern_f32.hip", "kern_bf16.hip", "kern_f16.hip", "kern_f64.hip",
                 "kern_i32.hip", "kern_i64.hip",
                 "scan_f32.hip", "scan_bf16.hip", "scan_f16.hip", "scan_f64.hip",
-                "scan_i32.hip", "scan_i64.hip"]
+                "scan_i32.hip", "scan_i64.hip", "diag.hip"]
 HIP_HOST_UNITS = ["rk_api.cpp"]           # host code that calls the HIP runtime
 PURE_UNITS = ["rk_plan.cpp"]              # plain C++
 

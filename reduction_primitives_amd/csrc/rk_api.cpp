@@ -23,6 +23,10 @@
 #include "rk_plan.hpp"
 #include "rk_scan_plan.hpp"
 
+namespace rk {
+int launch_stream_read(const void *x, int64_t nvec, int grid, void *sink, hipStream_t st);  // diag.hip
+}
+
 namespace {
 
 using namespace rk;
@@ -391,7 +395,7 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     }
     L.all.ws = ws;
     L.all.grid = a.grid;
-    L.all.arrive_slot = a.grid > 1 ? arrive_slot(st) : -1;
+    L.all.arrive_slot = a.grid > 1 && arrive_counters(a.grid) <= kArriveCapacity ? arrive_slot(st) : -1;
     L.all.fin = make_finish(op, acc, out_dtype, mode, init, out);
     L.stream = st;
     L.ev_begin = t_ev_begin;
@@ -433,6 +437,34 @@ int rk_debug_set_launch_events(void *begin, void *end)
     return RK_OK;
 }
 
+int rk_debug_stream_read(const void *ptr, int64_t nbytes, int grid, void *sink, void *stream)
+{
+    if (nbytes < 0 || nbytes % 16 != 0 || grid < 0 || grid > (1 << 20))
+        return RK_ERR_INVALID_ARGUMENT;
+    if (nbytes == 0)
+        return RK_OK;
+    if (!ptr || !sink || reinterpret_cast<uintptr_t>(ptr) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return RK_ERR_INVALID_ARGUMENT;
+    return launch_stream_read(ptr, nbytes / 16, grid > 0 ? grid : 2048, sink, static_cast<hipStream_t>(stream))
+               ? RK_ERR_HIP : RK_OK;
+}
+
+int rk_debug_device_info(int64_t *num_cus, int64_t *mem_clock_khz, int64_t *mem_bus_bits)
+{
+    if (!num_cus || !mem_clock_khz || !mem_bus_bits)
+        return RK_ERR_INVALID_ARGUMENT;
+    int dev = 0, cus = 0, clk = 0, bus = 0;
+    if (hipGetDevice(&dev) != hipSuccess
+        || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess
+        || hipDeviceGetAttribute(&clk, hipDeviceAttributeMemoryClockRate, dev) != hipSuccess
+        || hipDeviceGetAttribute(&bus, hipDeviceAttributeMemoryBusWidth, dev) != hipSuccess)
+        return RK_ERR_HIP;
+    *num_cus = cus;
+    *mem_clock_khz = clk;
+    *mem_bus_bits = bus;
+    return RK_OK;
+}
+
 int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num_cus, rk_plan_info *info)
 {
     if (!info || !dtype_known(in_dtype) || !dtype_known(acc_dtype) || n < 0)
@@ -445,7 +477,7 @@ int rk_plan_all(int in_dtype, int acc_dtype, const void *ptr, int64_t n, int num
         return rc;
     std::memset(info, 0, sizeof *info);
     info->kernel = RK_KERNEL_ALL;
-    info->launches = (a.grid > 1 && g_fused_finish.load()) ? 1 : a.launches;
+    info->launches = (a.grid > 1 && arrive_counters(a.grid) <= kArriveCapacity && g_fused_finish.load()) ? 1 : a.launches;
     info->grid = a.grid;
     info->block = a.block;
     info->split = 1;
@@ -471,7 +503,7 @@ int rk_plan_all2(int in_dtype, int acc_dtype, const void *a, const void *b, int6
         return rc;
     std::memset(info, 0, sizeof *info);
     info->kernel = RK_KERNEL_ALL2;
-    info->launches = (p.grid > 1 && g_fused_finish.load()) ? 1 : p.launches;
+    info->launches = (p.grid > 1 && arrive_counters(p.grid) <= kArriveCapacity && g_fused_finish.load()) ? 1 : p.launches;
     info->grid = p.grid;
     info->block = p.block;
     info->split = 1;

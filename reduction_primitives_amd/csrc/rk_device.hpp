@@ -520,7 +520,11 @@ __device__ __forceinline__ void finish_store(const Finish &f, int64_t o, Acc v)
 // atomicInc's wrap-around (n - 1 -> 0) leaves each one at zero again after
 // its n arrivals, so nothing has to be cleared between calls.  Each stream
 // gets its own slot of counters, so calls that may overlap never share one.
-static __device__ uint32_t g_arrive[kArriveSlots * kArriveCapacity];
+// Counter c of a slot sits in line c % kArriveLines, word c / kArriveLines,
+// so consecutive counters never share a 128-byte line.
+static __device__ __attribute__((aligned(128))) uint32_t g_arrive[kArriveSlots * kArriveCapacity];
+constexpr int kArriveLineWords = 32;
+constexpr int kArriveLines = kArriveCapacity / kArriveLineWords;
 
 // Partials cross XCDs, each with a private L2.  They are written with
 // device-scope atomic stores, which write through to the device's point of
@@ -561,15 +565,34 @@ __device__ __forceinline__ void issue_barrier() { __builtin_amdgcn_sched_barrier
 // (s_waitcnt with every counter at zero).
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Count one arrival on counter idx of a slot; true for the n-th (last) one.
-// Every thread that stored a partial must have called wait_stores() and met
-// the caller at a barrier first.
-__device__ __forceinline__ bool arrive_last(int slot, int64_t idx, uint32_t n)
+// One arrival on counter c of a slot; true for the n-th (last) one.
+__device__ __forceinline__ bool count_arrival(int slot, int64_t c, uint32_t n)
+{
+    uint32_t *p = &g_arrive[int64_t(slot) * kArriveCapacity + (c % kArriveLines) * kArriveLineWords
+                            + c / kArriveLines];
+    return __builtin_amdgcn_atomic_inc32(p, n - 1, __ATOMIC_RELAXED, "agent") == n - 1;
+}
+
+// Count the arrival of `member` (0 <= member < n) of output idx's n
+// contributors; true for the last of all n.  Up to kArriveGroup arrivals go
+// to the output's one counter; more are counted per group first, and only
+// the last of each group counts on the top counter.  Every thread that
+// stored a partial must have called wait_stores() and met the caller at a
+// barrier first.  A group's last arrival has seen every arrival of its
+// group, each made after that member's stores completed, so the top
+// counter's last arrival follows every member's stores.
+__device__ __forceinline__ bool arrive_last(int slot, int64_t idx, uint32_t member, uint32_t n)
 {
     wait_stores();
-    const uint32_t prev = __builtin_amdgcn_atomic_inc32(&g_arrive[int64_t(slot) * kArriveCapacity + idx], n - 1,
-                                                        __ATOMIC_RELAXED, "agent");
-    return prev == n - 1;
+    const int64_t top = idx * arrive_counters(n);
+    if (n <= uint32_t(kArriveGroup))
+        return count_arrival(slot, top, n);
+    const uint32_t g = member / kArriveGroup;
+    const uint32_t in_group = n - g * kArriveGroup < uint32_t(kArriveGroup) ? n - g * kArriveGroup
+                                                                            : uint32_t(kArriveGroup);
+    if (!count_arrival(slot, top + 1 + g, in_group))
+        return false;
+    return count_arrival(slot, top, (n + kArriveGroup - 1) / kArriveGroup);
 }
 
 // ------------------------------------------------------------------ misc

@@ -124,7 +124,7 @@ __device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v)
     __shared__ int last;
     if (threadIdx.x == 0) {
         store_partial(ws + blockIdx.x, v);
-        last = arrive_last(a.arrive_slot, 0, (uint32_t)a.grid);
+        last = arrive_last(a.arrive_slot, 0, blockIdx.x, (uint32_t)a.grid);
     }
     __syncthreads();
     if (!last)
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
         __shared__ int last;
         __syncthreads();
         if (threadIdx.x == 0)
-            last = arrive_last(a.arrive_slot, tile, (uint32_t)a.split);
+            last = arrive_last(a.arrive_slot, tile, (uint32_t)sp, (uint32_t)a.split);
         __syncthreads();
         if (!last)
             return;
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
     int last = 0;
     if (lane == 0) {
         store_partial(ws + int64_t(sp) * a.n_out + o, v);
-        last = arrive_last(a.arrive_slot, o, (uint32_t)a.split);
+        last = arrive_last(a.arrive_slot, o, (uint32_t)sp, (uint32_t)a.split);
     }
     last = __builtin_amdgcn_readfirstlane(last);
     if (!last)
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
             __shared__ int last;
             if (threadIdx.x == 0) {
                 store_partial(ws + int64_t(sp) * a.n_out + o, v);
-                last = arrive_last(a.arrive_slot, o, (uint32_t)a.split);
+                last = arrive_last(a.arrive_slot, o, (uint32_t)sp, (uint32_t)a.split);
             }
             __syncthreads();
             // in split order, as the second launch folds them

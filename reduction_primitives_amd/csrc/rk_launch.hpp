@@ -18,6 +18,19 @@ enum FinishMode { FIN_OVERWRITE = 0, FIN_FOLD = 1, FIN_HOST = 2, FIN_PARTIAL = 3
 // counters would not fit takes the two-launch path.
 constexpr int kArriveSlots = 32;
 constexpr int kArriveCapacity = 4096;
+// Atomics on one 128-byte line are serialised where device-scope atomics are
+// performed, about 10 ns each on MI355X: 1024 blocks counting themselves on
+// one counter queue for ~10 us when they end together.  So n > kArriveGroup
+// arrivals are counted in groups of kArriveGroup consecutive members, each
+// group on a counter of its own, and the last of each group counts the
+// group on the output's top counter.
+constexpr int kArriveGroup = 32;
+
+// Counters one output takes for n arrivals: the top one, plus one per group.
+constexpr int64_t arrive_counters(int64_t n)
+{
+    return n > kArriveGroup ? 1 + (n + kArriveGroup - 1) / kArriveGroup : 1;
+}
 
 struct Finish {
     void *out;            // device output (OVERWRITE / FOLD); HOST: pinned host result buffer or NULL

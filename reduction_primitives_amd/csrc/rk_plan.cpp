@@ -297,7 +297,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.grid = d.tiles * d.split;
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
-        d.fused_ok = d.split > 1 && d.tiles <= kArriveCapacity;   // one counter per tile
+        d.fused_ok = d.split > 1 && d.tiles * arrive_counters(d.split) <= kArriveCapacity;   // per tile
         break;
     }
     case K_ROW: {
@@ -316,7 +316,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.grid = ceil_div(n_out * d.split, waves_per_block);
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
-        d.fused_ok = d.split > 1 && n_out <= kArriveCapacity;      // one counter per output
+        d.fused_ok = d.split > 1 && n_out * arrive_counters(d.split) <= kArriveCapacity;   // per output
         break;
     }
     case K_GENERIC: {
@@ -351,7 +351,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.grid = std::min<int64_t>(n_out * d.split, target);
         d.launches = d.split > 1 ? 2 : 1;
         d.ws_bytes = d.split > 1 ? round_up_256(size_t(d.split) * n_out * asz) : 0;
-        d.fused_ok = d.split > 1 && n_out <= kArriveCapacity;      // one counter per output
+        d.fused_ok = d.split > 1 && n_out * arrive_counters(d.split) <= kArriveCapacity;   // per output
         break;
     }
     default:

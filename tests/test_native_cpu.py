@@ -280,6 +280,20 @@ def test_launch_event_hook_pairs():
     assert rk.rk_debug_set_launch_events(None, None) == rk.RK_OK
 
 
+def test_stream_read_validation():
+    rk = _rk()
+    lib = rk.load()
+    ok, bad = rk.RK_OK, rk.RK_ERR_INVALID_ARGUMENT
+    assert lib.rk_debug_stream_read(FAKE, 0, 0, FAKE, None) == ok          # nothing to read: no launch
+    assert lib.rk_debug_stream_read(FAKE, 8, 0, FAKE, None) == bad         # not whole vectors
+    assert lib.rk_debug_stream_read(FAKE, -16, 0, FAKE, None) == bad
+    assert lib.rk_debug_stream_read(FAKE, 16, -1, FAKE, None) == bad
+    assert lib.rk_debug_stream_read(FAKE + 4, 16, 0, FAKE, None) == bad    # unaligned
+    assert lib.rk_debug_stream_read(None, 16, 0, FAKE, None) == bad
+    assert lib.rk_debug_stream_read(FAKE, 16, 0, None, None) == bad
+    assert lib.rk_debug_device_info(None, None, None) == bad
+
+
 # ------------------------------------------------------------------- scans
 
 def test_scan_plans():
