@@ -742,8 +742,9 @@ int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, co
     const bool lookback = d.kernel == SK_TILE || d.kernel == SK_COLUMNS;
     // a look-back scan clears its state with a launch of its own unless the
     // state fits a library slot
+    const int64_t cap = d.kernel == SK_TILE ? kScanRecCapacity : kScanFlagCapacity;
     info->launches = d.kernel == SK_NONE ? 0
-                     : lookback && !(d.tiles <= kScanFlagCapacity && g_fused_finish.load()) ? 2 : 1;
+                     : lookback && !(d.tiles <= cap && g_fused_finish.load()) ? 2 : 1;
     info->grid = d.grid;
     info->block = d.block;
     info->split = int(d.kernel == SK_COLUMNS ? d.chunks : d.tiles_per_line > 0 ? d.tiles_per_line : 1);
@@ -829,8 +830,9 @@ int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void 
     a.inclusive = inclusive;
     a.out_dtype = out_dtype;
     a.init_bits = start_bits(op, acc_dtype, init);
-    // look-back state in a library slot when the tiles' flags fit one (no clearing launch)
-    a.slot = (d.kernel == SK_TILE || d.kernel == SK_COLUMNS) && d.tiles <= kScanFlagCapacity
+    // look-back state in a library slot when the tiles' state fits one (no clearing launch)
+    a.slot = (d.kernel == SK_TILE && d.tiles <= kScanRecCapacity) ||
+                     (d.kernel == SK_COLUMNS && d.tiles <= kScanFlagCapacity)
                  ? arrive_slot(static_cast<hipStream_t>(stream))
                  : -1;
     L.stream = stream;

@@ -442,9 +442,11 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             }
             d.tiles_per_line = ceil_div(d.m, d.tile_elems);
             d.tiles = d.lines * d.tiles_per_line;
+            if (d.tiles > INT32_MAX)            // tiles are numbered by a 32-bit counter
+                return ST_INVALID;
             d.grid = d.tiles;
-            // header, flags (rounded to 8 bytes), aggregates, prefixes
-            d.ws_bytes = round_up_256(8 + size_t((d.tiles + 1) & ~int64_t(1)) * 4 + size_t(d.tiles) * 16);
+            // header and one record per tile (the state when no library slot takes it)
+            d.ws_bytes = round_up_256(size_t(scan_tile_state_bytes(d.tiles)));
         } else {
             d.kernel = SK_ROWWAVE;
             d.block = tune::kScanBlock;
@@ -470,7 +472,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             const int64_t r = (tune::kScanColBlock / lanes) * tune::kScanColRows;
             const int64_t ctpr = ceil_div(k.ext[0], w), ct = runs * ctpr, ch = ceil_div(d.m, r);
             const int64_t tiles = ct * ch;
-            ws = std::max(ws, round_up_256(8 + size_t((tiles + 1) & ~int64_t(1)) * 4 + size_t(tiles * w) * 16));
+            ws = std::max(ws, round_up_256(size_t(scan_columns_state_bytes(tiles, w))));
             if (vec == vec_ok) {
                 d.vec = vec ? v : 1;
                 d.col_tiles_per_run = ctpr;
@@ -482,6 +484,8 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             }
         }
         d.ws_bytes = ws;
+        if (d.tiles > INT32_MAX)                // tiles are numbered by a 32-bit counter
+            return ST_INVALID;
     } else {
         d.kernel = SK_LINES;
         d.block = tune::kScanBlock;

@@ -279,92 +279,141 @@ __device__ __forceinline__ void chunk_outputs(const Acc (&e)[V], Acc run, bool i
     }
 }
 
-// ------------------------------------------------------- tile look-back
+// ------------------------------------------------------- look-back state
 
-// Tile state.  The workspace holds an 8-byte header (tile counter, timeout
-// word: nonzero if a look-back wait gave up, never in normal runs), one
-// 32-bit flag per tile (0 nothing yet, 1 aggregate, 2 inclusive prefix), then
-// one 8-byte slot per tile for the aggregate and one for the prefix (`width`
-// of each per tile for the columns kernel).  A value is stored, its store
-// waited for, and only then its flag, all at device scope; a reader loads the
-// flag first and the value after it.
+// Flags: 0 nothing yet, 1 aggregate, 2 inclusive prefix.  A value is stored,
+// its store waited for, and only then its flag, all at device scope; a
+// reader loads the flag first and the value after it.  The timeout word is
+// nonzero if a look-back wait gave up (never in normal runs).
 //
 // With a library slot (ScanArgs::slot >= 0) the counter, timeout word and
-// flags live in g_scan_state instead, which starts zeroed and which the last
-// block of every scan puts back to zero (scan_release), so no launch has to
-// clear them; the workspace header then receives the call's tile count and
+// flags live in library memory instead of the workspace.  It starts zeroed
+// and the last block of every scan puts it back to zero, so no launch has to
+// clear it; the workspace header then receives the call's tile count and
 // timeout word.  Calls on one stream share its slot in order; calls that may
 // overlap have different slots.
-constexpr int kScanSlotWords = 4 + kScanFlagCapacity;
-static __device__ uint32_t g_scan_state[kArriveSlots * kScanSlotWords];
+constexpr uint32_t kFlagAggregate = 1;
+constexpr uint32_t kFlagPrefix = 2;
+
+// Columns-scan state: the header, flags and values laid out as the plan
+// describes them (scan_columns_state_bytes); the flags of neighbouring tiles
+// sit in different 128-byte lines, for the reason given for the tile scan's
+// records below.
+constexpr int kScanSlotWords = 64 + kScanFlagCapacity;
+static __device__ __attribute__((aligned(128))) uint32_t g_scan_state[kArriveSlots * kScanSlotWords];
 
 struct ScanState {
     uint32_t *counter;
     uint32_t *timeout;
     uint32_t *done;       // slot state only: blocks finished, wraps to zero
-    uint32_t *flags;
+    uint32_t *flagw;      // flag words
+    uint32_t lines;       // flag lines
     uint64_t *aggs;
     uint64_t *pres;
 
     __device__ ScanState(void *ws, int64_t tiles, int slot, int64_t width = 1)
     {
         uint32_t *w = static_cast<uint32_t *>(ws);
-        uint32_t *wflags = w + 2;
-        aggs = reinterpret_cast<uint64_t *>(wflags + ((tiles + 1) & ~int64_t(1)));
+        lines = (uint32_t)scan_flag_lines(tiles);
+        aggs = reinterpret_cast<uint64_t *>(w + 64 + int64_t(lines) * 32);
         pres = aggs + tiles * width;
-        if (slot >= 0) {
-            counter = g_scan_state + int64_t(slot) * kScanSlotWords;
-            done = counter + 1;
-            timeout = counter + 2;
-            flags = counter + 4;
-        } else {
-            counter = w;
-            timeout = w + 1;
-            done = nullptr;
-            flags = wflags;
-        }
+        uint32_t *h = slot >= 0 ? g_scan_state + int64_t(slot) * kScanSlotWords : w;
+        counter = h;
+        timeout = h + 1;
+        done = slot >= 0 ? h + 32 : nullptr;   // a line of its own
+        flagw = h + 64;
+    }
+    __device__ uint32_t *flag(int64_t g) const
+    {
+        const uint32_t u = (uint32_t)g;
+        return flagw + (u % lines) * 32 + u / lines;
     }
 };
 
-// End of a block of a slot-state scan: count the block done; the last one
-// (every look-back has ended by then) zeroes the flags, the counter and the
-// timeout word for the next call, after copying the tile count and the
-// timeout word into the workspace header.  Called by every thread.
-template <int BLOCK>
-__device__ __forceinline__ void scan_release(const ScanState &st, void *ws, int64_t tiles)
+// Tile-scan state: the header and per-tile records laid out as the plan
+// describes them (kScanHeaderBytes, kScanRecBytes).  Device-scope accesses to
+// one 128-byte line are serialised where they are performed, so the tiles
+// that publish and poll at the same time -- neighbours -- are kept in
+// different lines, and a reader finds a tile's flag and values in one line.
+constexpr int kScanTileSlotWords = (kScanHeaderBytes + kScanRecCapacity * kScanRecBytes) / 4;
+static __device__ __attribute__((aligned(128))) uint32_t g_scan_tile_state[kArriveSlots * kScanTileSlotWords];
+
+struct TileState {
+    uint32_t *counter;
+    uint32_t *timeout;
+    uint32_t *done;       // slot state only: blocks finished, wraps to zero
+    char *recs;
+    uint32_t lines;       // tile counts fit 32 bits (the counter is a 32-bit word)
+
+    __device__ TileState(void *ws, int64_t tiles, int slot)
+    {
+        uint32_t *h = slot >= 0 ? g_scan_tile_state + int64_t(slot) * kScanTileSlotWords : static_cast<uint32_t *>(ws);
+        counter = h;
+        timeout = h + 1;
+        done = slot >= 0 ? h + 32 : nullptr;  // a line of its own
+        recs = reinterpret_cast<char *>(h) + kScanHeaderBytes;
+        lines = (uint32_t)scan_rec_lines(tiles);
+    }
+    __device__ char *rec(int64_t g) const
+    {
+        const uint32_t u = (uint32_t)g;
+        return recs + int64_t((u % lines) * 4 + u / lines) * kScanRecBytes;
+    }
+    __device__ uint32_t *flag(int64_t g) const { return reinterpret_cast<uint32_t *>(rec(g)); }
+    template <class Acc>
+    __device__ Acc *value(int64_t g, uint32_t flag) const
+    {
+        return reinterpret_cast<Acc *>(rec(g) + (flag == kFlagPrefix ? 16 : 8));
+    }
+};
+
+// End of a block of a slot-state scan, run by wave 0 alone once the block's
+// outputs are issued (the other waves end without waiting): lane 0 waits for
+// its flag and output stores, then counts the block done; the last block of
+// the call (every look-back has ended by then) copies the tile count and the
+// timeout word into the workspace header and zeroes the counter, the timeout
+// word and `nflags` flags (stride `fstride` words) for the next call.
+__device__ __forceinline__ void release_slot(uint32_t *done, int64_t tiles, uint32_t *counter, uint32_t *timeout,
+                                             uint32_t *flags, int64_t nflags, int64_t fstride, void *ws)
 {
-    if (!st.done)
+    if (!done || threadIdx.x >= 64)
         return;
-    __shared__ int s_last;
-    __syncthreads();
+    uint32_t prev = 0;
     if (threadIdx.x == 0) {
         wait_stores();
-        const uint32_t prev = __builtin_amdgcn_atomic_inc32(st.done, (uint32_t)(tiles - 1), __ATOMIC_RELAXED, "agent");
-        s_last = prev == (uint32_t)(tiles - 1);
+        prev = __builtin_amdgcn_atomic_inc32(done, (uint32_t)(tiles - 1), __ATOMIC_RELAXED, "agent");
     }
-    __syncthreads();
-    if (!s_last)
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != (uint32_t)(tiles - 1))
         return;
-    for (int64_t i = threadIdx.x; i < tiles; i += BLOCK)
-        st.flags[i] = 0;
+    for (int64_t i = threadIdx.x; i < nflags; i += 64)
+        flags[i * fstride] = 0;
     if (threadIdx.x == 0) {
         uint32_t *hdr = static_cast<uint32_t *>(ws);
-        hdr[0] = __hip_atomic_load(st.counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hdr[1] = __hip_atomic_load(st.timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(st.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(st.timeout, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hdr[0] = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hdr[1] = __hip_atomic_load(timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(timeout, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-constexpr uint32_t kFlagAggregate = 1;
-constexpr uint32_t kFlagPrefix = 2;
+__device__ __forceinline__ void scan_release(const ScanState &st, void *ws, int64_t tiles)
+{
+    release_slot(st.done, tiles, st.counter, st.timeout, st.flagw, int64_t(st.lines) * 32, 1, ws);
+}
+
+__device__ __forceinline__ void tile_release(const TileState &st, void *ws, int64_t tiles)
+{
+    release_slot(st.done, tiles, st.counter, st.timeout, reinterpret_cast<uint32_t *>(st.recs),
+                 int64_t(st.lines) * 4, kScanRecBytes / 4, ws);
+}
 
 template <class Acc>
-__device__ __forceinline__ void publish(const ScanState &st, int64_t g, Acc v, uint32_t flag)
+__device__ __forceinline__ void publish(const TileState &st, int64_t g, Acc v, uint32_t flag)
 {
-    store_partial(reinterpret_cast<Acc *>((flag == kFlagPrefix ? st.pres : st.aggs) + g), v);
+    store_partial(st.value<Acc>(g, flag), v);
     wait_stores();
-    __hip_atomic_store(st.flags + g, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(st.flag(g), flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Exclusive prefix of tile t (global index g) of a line, run by one whole
@@ -373,11 +422,10 @@ __device__ __forceinline__ void publish(const ScanState &st, int64_t g, Acc v, u
 // a smaller counter value has already started, and it publishes its
 // aggregate without waiting on anything, so every wait here ends.  As a
 // safety net each wait is still bounded (tune::kScanSpinLimit sleeps): past
-// it the tile records the timeout in the workspace header and goes on, so
-// every wave exits.  Publishes the tile's own inclusive prefix before
-// returning.
+// it the tile records the timeout in the header and goes on, so every wave
+// exits.  Publishes the tile's own inclusive prefix before returning.
 template <class Acc, class Op>
-__device__ Acc scan_lookback(const ScanState &st, int64_t g, int64_t t, Acc agg, Acc init)
+__device__ Acc scan_lookback(const TileState &st, int64_t g, int64_t t, Acc agg, Acc init)
 {
     const int lane = lane_id();
     if (t == 0) {
@@ -396,8 +444,7 @@ __device__ Acc scan_lookback(const ScanState &st, int64_t g, int64_t t, Acc agg,
         uint32_t f;
         uint64_t pm, zm;
         for (int spin = 0;; ++spin) {
-            f = valid ? __hip_atomic_load(st.flags + g0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : kFlagPrefix;
+            f = valid ? __hip_atomic_load(st.flag(g0 + j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kFlagPrefix;
             pm = __ballot(f == kFlagPrefix);
             zm = __ballot(f == 0);
             // done when every lane before the first prefix has published
@@ -413,10 +460,8 @@ __device__ Acc scan_lookback(const ScanState &st, int64_t g, int64_t t, Acc agg,
         }
         const int first = pm ? __builtin_ctzll(pm) : 64;   // lane of the nearest prefix
         Acc v = Op::template identity<Acc>();
-        if (lane < first)
-            v = load_partial(reinterpret_cast<const Acc *>(st.aggs + g0 + j));
-        else if (lane == first)
-            v = load_partial(reinterpret_cast<const Acc *>(st.pres + g0 + j));
+        if (valid && lane <= first)
+            v = load_partial(st.value<Acc>(g0 + j, lane == first ? kFlagPrefix : kFlagAggregate));
         acc = Op::apply(wave_reduce<Op>(v), acc);
         if (pm)
             break;
@@ -454,7 +499,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
     __shared__ uint32_t s_id;
     __shared__ Acc s_wave[NW];
     __shared__ Acc s_excl;
-    const ScanState st(a.ws, a.tiles, a.slot);
+    const TileState st(a.ws, a.tiles, a.slot);
     if (threadIdx.x == 0)
         s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -523,7 +568,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
             store_run<Acc, V, NTS>(a.out, ob + i, a.out_dtype, o);
         carry = Op::apply(carry, total);
     }
-    scan_release<BLOCK>(st, a.ws, a.tiles);
+    tile_release(st, a.ws, a.tiles);
 }
 
 // Row-wave kernel: one wave per line, UC chunks in flight, the carry passed
@@ -659,7 +704,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
         }
         __syncthreads();
         if (threadIdx.x == 0)
-            __hip_atomic_store(st.flags + g, kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(st.flag(g), kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (rg == 0) {
         Acc acc[V];
@@ -673,7 +718,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
                 uint32_t f[K];
 #pragma unroll
                 for (int q = 0; q < K; ++q)
-                    f[q] = top - q >= 0 ? __hip_atomic_load(st.flags + (top - q) * a.col_tiles + ct, __ATOMIC_RELAXED,
+                    f[q] = top - q >= 0 ? __hip_atomic_load(st.flag((top - q) * a.col_tiles + ct), __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT)
                                         : kFlagPrefix;
                 int first = K;
@@ -698,7 +743,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
 #pragma unroll
                     for (int q = 0; q < K; ++q)
                         if (f[q] == 0 && top - q >= 0)
-                            f[q] = __hip_atomic_load(st.flags + (top - q) * a.col_tiles + ct, __ATOMIC_RELAXED,
+                            f[q] = __hip_atomic_load(st.flag((top - q) * a.col_tiles + ct), __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
                 }
 #pragma unroll
@@ -727,7 +772,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     }
     __syncthreads();
     if (threadIdx.x == 0)
-        __hip_atomic_store(st.flags + g, kFlagPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(st.flag(g), kFlagPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // decode the raw loads again below rather than keeping the first decode
     // alive across the look-back (wider accumulators would double the registers)
@@ -756,7 +801,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
         if (active && r < a.m)
             store_run<Acc, V, true>(a.out, ob + r * a.s_out, a.out_dtype, o);
     }
-    scan_release<BLOCK>(st, a.ws, a.tiles);
+    scan_release(st, a.ws, a.tiles);
 }
 
 // Lines kernel: one thread per line walking the scan dim, UNROLL elements in
@@ -798,10 +843,10 @@ __global__ __launch_bounds__(BLOCK) void k_scan_lines(ScanArgs a)
 
 // ---------------------------------------------------------------- launchers
 
-// Zero the workspace's tile counter, timeout word and flags (workspace state).
-inline void clear_state(const ScanArgs &a, hipStream_t st)
+// Zero the first `words` 32-bit words of the workspace: the look-back
+// state's counter, timeout word and flags (workspace state).
+inline void clear_state(const ScanArgs &a, int64_t words, hipStream_t st)
 {
-    const int64_t words = 2 + ((a.tiles + 1) & ~int64_t(1));
     const unsigned cg = (unsigned)std::min<int64_t>((words + 255) / 256, 1024);
     hipLaunchKernelGGL(k_scan_clear<256>, dim3(cg), dim3(256), 0, st, static_cast<uint32_t *>(a.ws), words);
 }
@@ -831,7 +876,7 @@ int run_scan_typed(const ScanLaunch &L)
     switch (L.kernel) {
     case SK_TILE: {
         if (L.args.slot < 0)
-            clear_state(L.args, st);
+            clear_state(L.args, scan_tile_state_bytes(L.args.tiles) / 4, st);
 #define RK_SCAN_TILE(BK, VLN) launch_first(&k_scan_tile<In, Acc, Op, BK, U, VLN, true>, grid, block, st, ev, L.args)
         if (L.block == BT) {
             if (vl == VV) RK_SCAN_TILE(BT, VV);
@@ -860,7 +905,7 @@ int run_scan_typed(const ScanLaunch &L)
         if (vl != 1 && vl != VV)
             return ST_INVALID;
         if (L.args.slot < 0)
-            clear_state(L.args, st);
+            clear_state(L.args, 64 + scan_flag_lines(L.args.tiles) * 32, st);
         if (vl == VV)
             launch_first(&k_scan_columns<In, Acc, Op, BC, tune::kScanColLanes, tune::kScanColRows, true>, grid,
                          block, st, ev, L.args);

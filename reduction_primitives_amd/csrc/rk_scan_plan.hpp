@@ -61,12 +61,34 @@ struct ScanArgs {
     int inclusive;
     int out_dtype;
     uint64_t init_bits;   // starting value, accumulator bits
-    int slot;             // >= 0: tile counter and flags in the library's slot (reset by the last
+    int slot;             // >= 0: look-back state in the library's slot (reset by the last
                           // block); < 0: in the workspace, cleared by a fill launch first
 };
 
-// Tiles whose flags fit one library slot of a look-back scan.
-constexpr int kScanFlagCapacity = 8192;
+// Columns-scan state: a 256-byte header (as the tile scan's), the flags --
+// 32-bit words, the flag of tile g at word (g % lines) * 32 + g / lines,
+// lines = ceil(tiles / 32), so consecutive tiles sit in different 128-byte
+// lines -- then `width` 8-byte aggregates per tile and as many prefixes.
+constexpr int kScanFlagCapacity = 8192;  // tiles whose flags fit one library slot
+constexpr int64_t scan_flag_lines(int64_t tiles) { return (tiles + 31) / 32; }
+constexpr int64_t scan_columns_state_bytes(int64_t tiles, int64_t width)
+{
+    return 256 + scan_flag_lines(tiles) * 128 + tiles * width * 16;
+}
+
+// Tile-scan state: a 256-byte header (line 0: tile counter, timeout word;
+// line 1: blocks done) and one 32-byte record per tile {flag, -, aggregate,
+// inclusive prefix, -}, four records to a 128-byte line.  Record of tile g:
+// number (g % lines) * 4 + g / lines, lines = ceil(tiles / 4), so
+// consecutive tiles sit in different lines.
+constexpr int kScanHeaderBytes = 256;
+constexpr int kScanRecBytes = 32;
+constexpr int kScanRecCapacity = 4096;   // tiles whose records fit one library slot
+constexpr int64_t scan_rec_lines(int64_t tiles) { return (tiles + 3) / 4; }
+constexpr int64_t scan_tile_state_bytes(int64_t tiles)
+{
+    return kScanHeaderBytes + scan_rec_lines(tiles) * 4 * kScanRecBytes;
+}
 
 struct ScanLaunch {
     int kernel;           // rk::ScanKernel

@@ -278,6 +278,46 @@ def test_general_layouts_both_finishes(case):
     assert np.array_equal(res[0], res[1])
 
 
+# More than 32 blocks (or waves) per output: the one-launch finish counts
+# their arrivals in groups of 32, the last group possibly partial, then the
+# groups on the output's top counter.
+MANY_SPLIT_CASES = [
+    ((3, 1_000_000), 2, "columns"),          # 256 splits: 8 full groups
+    ((1_000_003, 3), 1, "row"),              # 488 splits: the last group holds 8
+    ((2, 50_000, 3), 2, "columns"),          # 86 splits: 32, 32, 22
+    ((999, 3, 1001), (1, 3), "generic"),     # 244 splits, element loads
+]
+
+
+@pytest.mark.parametrize("case", MANY_SPLIT_CASES, ids=lambda c: f"{c[2]}_{'x'.join(map(str, c[0]))}")
+def test_many_splits_grouped_arrivals(case):
+    rk = _rk()
+    shape, dims, kern = case
+    numel = math.prod(shape)
+    plan = rk.plan_dims(torch.float32, shape, CM(shape), dims)
+    assert plan["kernel_name"] == kern and plan["split"] > 32 and plan["launches"] == 1, plan
+    xi = W.randint(numel, -1000, 1000, 9970 + numel % 71)
+    dims_and_check(xi, shape, CM(shape), dims, acc=torch.int64, out_dtype=torch.int64, expect_kernel=kern)
+    xf = W.normal(numel, 9980 + numel % 73)
+    xd = xf.to(DEV)
+    res = {}
+    for on in (1, 0):
+        prev = rk.rk_debug_set_fused_finish(on)
+        try:
+            dims_and_check(xf, shape, CM(shape), dims, init=0.5, expect_kernel=kern, storage_dev=xd)
+            dims_and_check(xf, shape, CM(shape), dims, op="max", expect_kernel=kern, storage_dev=xd)
+            res[on] = raw_np(rk.reduce_dims(xd, shape, CM(shape), dims, init=0.5))
+            torch.cuda.synchronize()
+        finally:
+            rk.rk_debug_set_fused_finish(prev)
+    # the tile and generic kernels' last block folds the partials in split
+    # order, as the second launch does: the same bits.  The row kernel's last
+    # wave folds them across its lanes (one memory round trip for hundreds of
+    # partials), so only the oracle checks above bind it.
+    if kern != "row":
+        assert np.array_equal(res[0], res[1])
+
+
 @pytest.mark.parametrize("offset", [1, 3, 4])
 def test_general_layout_offsets(offset):
     """The generic kernel takes 16-byte loads only when every reduced row

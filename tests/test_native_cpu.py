@@ -309,10 +309,12 @@ def test_scan_plans():
         assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256).launches == 2
     finally:
         rk.rk_debug_set_fused_finish(prev)
-    big = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [8193 * tile], [1], 0, 256)
-    assert big.split == 8193 and big.launches == 2      # more tiles than a slot holds
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [4096 * tile], [1], 0, 256).launches == 1
+    big = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [4097 * tile], [1], 0, 256)
+    assert big.split == 4097 and big.launches == 2      # more tiles than a slot holds
+    # workspace: 256-byte header, then 32-byte records, four to a line
     tiles = p.split
-    assert p.workspace_bytes == -(-(8 + ((tiles + 1) // 2 * 2) * 4 + tiles * 16) // 256) * 256
+    assert p.workspace_bytes == -(-(256 + -(-tiles // 4) * 128) // 256) * 256
     p = rk.rk_plan_scan(f32, f32, f32, 4, 0, 1, [10**8], [1], 0, 256)                # unaligned input
     assert p.vec == 1 and p.block == 256
     # outputs wider than the inputs: lanes take as many elements as make 16 bytes of output
@@ -346,8 +348,9 @@ def test_scan_plans():
     assert p.tile_outputs == 128 * 256 and p.split == 32 and p.grid == 64 * 32 and p.block == 512
     # the workspace covers both tile geometries: 16-byte loads (128 lines x 256
     # positions) and element loads (64 lines x 128 positions)
+    # (256-byte header, flags 32 to a line, then 16 bytes per line of a tile)
     scalar_tiles = 128 * 64
-    assert p.workspace_bytes == -(-(8 + scalar_tiles * 4 + scalar_tiles * 64 * 16) // 256) * 256
+    assert p.workspace_bytes == -(-(256 + -(-scalar_tiles // 32) * 128 + scalar_tiles * 64 * 16) // 256) * 256
     assert rk.rk_plan_scan(f32, f32, f32, 4, 0, 2, [8192, 8192], [1, 8192], 1, 256).vec == 1
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10, 100], [1, 10], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_LINES and p.workspace_bytes == 0        # runs of 10 lines
