@@ -241,17 +241,55 @@ __device__ __forceinline__ Acc map2_one(typename InTraits<In>::S a, typename InT
     return Map2::apply(InTraits<In>::template one<Acc>(a), InTraits<In>::template one<Acc>(b));
 }
 
+// The 16 bytes that start K * 4 + r bytes into the 32 bytes c0:c1: whole
+// dwords picked at compile time, then (2-byte elements only: r = 2) a byte
+// funnel shift per dword.
+template <int K, bool HALF>
+__device__ __forceinline__ u32x4 join_shifted(u32x4 c0, u32x4 c1, uint32_t r)
+{
+    const uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = HALF ? __builtin_amdgcn_alignbyte(w[j + K + 1], w[j + K], r) : w[j + K];
+    return o;
+}
+
+// Lane l's value from lane (l + 1) mod 64: a DPP wavefront rotate.
+__device__ __forceinline__ u32x4 from_next_lane(u32x4 v)
+{
+    constexpr int kWaveRol1 = 0x134;
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[j], kWaveRol1, 0xf, 0xf, false);
+    return o;
+}
+
+// Two-input load modes: every element on its own; both inputs in 16-byte
+// vectors (same offset from a 16-byte boundary); x in vectors and y in
+// aligned 16-byte chunks shifted into place (different offsets).
+enum All2Mode { ALL2_ELEMENTS = 0, ALL2_VECTORS = 1, ALL2_SHIFTED = 2 };
+
 // First pass over a fused two-input source f(x_i, y_i) (PR #139: the source
-// may be a lazy broadcast).  VECTOR: x and y share their offset from a
-// 16-byte boundary, so both bodies take the one-input kernel's tiles with
-// UNROLL 16-byte loads of each input in flight.  Otherwise every element is
+// may be a lazy broadcast).  ALL2_VECTORS: both bodies take the one-input
+// kernel's tiles with UNROLL 16-byte loads of each input in flight.
+// ALL2_SHIFTED: the body starts where x is 16-byte aligned and y is not;
+// a wave covers UNROLL * 64 consecutive vectors (load u of lane l: vector
+// 64 u + l of the wave's span), every lane loads x's vector and the aligned
+// 16-byte chunk of y holding the start of its y elements, takes the
+// following chunk from the next lane by a wavefront rotate (lane 63: lane
+// 0's chunk of the next load, or, after the last, one more chunk it loads),
+// and shifts the pair into place -- every byte of both inputs is loaded
+// once, in 16-byte loads.  ALL2_ELEMENTS: every element is
 // loaded on its own, 2 * UNROLL per input in flight, each wave instruction
 // still reading consecutive elements.  Same grid, epilogue and workspace as
 // the one-input pass.
-template <class In, class Acc, class Op, class Map2, int BLOCK, int UNROLL, bool VECTOR>
+template <class In, class Acc, class Op, class Map2, int BLOCK, int UNROLL, int MODE, int K = 0>
 __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
 {
     using S = typename InTraits<In>::S;
+    constexpr bool VECTOR = MODE != ALL2_ELEMENTS;
     constexpr int V = VECTOR ? InTraits<In>::vec : 1;
     const S *x = static_cast<const S *>(a.x);
     const S *y = static_cast<const S *>(a.y);
@@ -263,7 +301,54 @@ __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
     const int64_t gtid = int64_t(blockIdx.x) * BLOCK + threadIdx.x;
     const int64_t gthreads = int64_t(gridDim.x) * BLOCK;
 
-    if constexpr (VECTOR) {
+    if constexpr (MODE == ALL2_SHIFTED) {
+        // y's elements of x's vector i: bytes sb + 16 i .. sb + 16 i + 15 of
+        // y's aligned chunk stream, i.e. the end of chunk i and the start of
+        // chunk i + 1.  The plan stops the body one chunk before y's last
+        // whole one, so chunk i + 1 always lies inside y.
+        const u32x4 *bx = reinterpret_cast<const u32x4 *>(x + a.head);
+        const uintptr_t yaddr = reinterpret_cast<uintptr_t>(y + a.head);
+        // sb = K * 4 + r bytes: K whole dwords (a template argument), r = 2
+        // only for 2-byte elements
+        const int sb = (int)(yaddr & 15);
+        const u32x4 *by = reinterpret_cast<const u32x4 *>(yaddr - uintptr_t(sb));
+        constexpr bool HALF = sizeof(S) == 2;
+        const uint32_t r = uint32_t(sb & 3);
+        const int lane = (int)(threadIdx.x & 63);
+        const bool last_lane = lane == 63;
+        constexpr int64_t kTile = int64_t(BLOCK) * UNROLL;
+        const int64_t full = a.nvec / kTile;
+        for (int64_t t = blockIdx.x; t < full; t += gridDim.x) {
+            const int64_t span = t * kTile + int64_t(threadIdx.x >> 6) * 64 * UNROLL;   // the wave's vectors
+            u32x4 wx[UNROLL], wy[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                wx[u] = load16(bx + span + u * 64 + lane);
+                wy[u] = load16(by + span + u * 64 + lane);
+            }
+            const u32x4 after = last_lane ? load16(by + span + UNROLL * 64) : u32x4{0u, 0u, 0u, 0u};
+            issue_barrier();
+            u32x4 rot = from_next_lane(wy[0]);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const u32x4 rot_next = u + 1 < UNROLL ? from_next_lane(wy[u + 1 < UNROLL ? u + 1 : u]) : after;
+                const u32x4 ys = join_shifted<K, HALF>(wy[u], last_lane ? rot_next : rot, r);
+                rot = rot_next;
+                if (u & 1)
+                    fold_vec2<In, Acc, Op, Map2, V>(acc1, wx[u], ys);
+                else
+                    fold_vec2<In, Acc, Op, Map2, V>(acc0, wx[u], ys);
+            }
+        }
+        for (int64_t i = full * kTile + gtid; i < a.nvec; i += gthreads)
+            fold_vec2<In, Acc, Op, Map2, V>(acc0, load16(bx + i),
+                                            join_shifted<K, HALF>(load16(by + i), load16(by + i + 1), r));
+        if (gtid < a.head)
+            s = Op::apply(s, map2_one<In, Acc, Map2>(load1(x + gtid), load1(y + gtid)));
+        const int64_t t0 = a.head + a.nvec * InTraits<In>::vec;
+        if (gtid < a.tail)
+            s = Op::apply(s, map2_one<In, Acc, Map2>(load1(x + t0 + gtid), load1(y + t0 + gtid)));
+    } else if constexpr (VECTOR) {
         const u32x4 *bx = reinterpret_cast<const u32x4 *>(x + a.head);
         const u32x4 *by = reinterpret_cast<const u32x4 *>(y + a.head);
         constexpr int64_t kTile = int64_t(BLOCK) * UNROLL;
@@ -836,12 +921,39 @@ int run_typed2(const Launch &L)
 {
     hipStream_t st = static_cast<hipStream_t>(L.stream);
     const dim3 grid((unsigned)L.grid), block(tune::kAllBlock);
-    if (L.vec > 1)
-        launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, true>, grid, block,
-                     st, L, L.all);
+    using S = typename InTraits<In>::S;
+    const bool same_phase = ((reinterpret_cast<uintptr_t>(static_cast<const S *>(L.all.x) + L.all.head) ^
+                              reinterpret_cast<uintptr_t>(static_cast<const S *>(L.all.y) + L.all.head)) & 15) == 0;
+    if (L.vec > 1 && same_phase)
+        launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, ALL2_VECTORS>, grid,
+                     block, st, L, L.all);
+    else if (L.vec > 1) {
+        // whole dwords of y's phase: 1..3 for 4-byte elements, 2 for 8-byte
+        // ones, 0..3 for 2-byte ones
+        const int k = int((reinterpret_cast<uintptr_t>(static_cast<const S *>(L.all.y) + L.all.head) & 15) >> 2);
+#define RK_ALL2_SHIFTED(KK) launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, \
+                                                       ALL2_SHIFTED, KK>, grid, block, st, L, L.all)
+        if constexpr (sizeof(S) == 8) {
+            RK_ALL2_SHIFTED(2);
+        } else {
+            if (k == 0) {
+                if constexpr (sizeof(S) == 2)
+                    RK_ALL2_SHIFTED(0);
+                else
+                    return ST_INVALID;          // 4-byte phases differ by whole dwords
+            } else if (k == 1) {
+                RK_ALL2_SHIFTED(1);
+            } else if (k == 2) {
+                RK_ALL2_SHIFTED(2);
+            } else {
+                RK_ALL2_SHIFTED(3);
+            }
+        }
+#undef RK_ALL2_SHIFTED
+    }
     else
-        launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, false>, grid, block,
-                     st, L, L.all);
+        launch_first(&k_all2_pass1<In, Acc, Op, Map2, tune::kAllBlock, tune::kAllUnroll, ALL2_ELEMENTS>, grid,
+                     block, st, L, L.all);
     if (hipGetLastError() != hipSuccess)
         return ST_HIP;
     if (L.all.grid > 1 && L.all.arrive_slot < 0) {

@@ -73,11 +73,27 @@ int plan_all2(int in_dtype, int acc_dtype, uintptr_t addr_a, uintptr_t addr_b, i
     const int rc = plan_all(in_dtype, acc_dtype, addr_a, n, num_cus, &a);
     if (rc)
         return rc;
-    if (((addr_a ^ addr_b) & 15) != 0) {
-        a.vec = 1;
-        a.head = 0;
-        a.nvec = n;
-        a.tail = 0;
+    if (a.vec > 1 && ((addr_a ^ addr_b) & 15) != 0) {
+        // different offsets from a 16-byte boundary: x in vectors from its
+        // head on; y read as aligned 16-byte chunks, vector i needing chunks
+        // i and i + 1, so the body ends one chunk before y's last whole one
+        const int64_t es = dtype_size(in_dtype);
+        const int64_t yphase = int64_t((addr_b + uintptr_t(a.head * es)) & 15);
+        // y's first chunk must not start before y: one more vector of head
+        // scalars when x's head is shorter than y's phase
+        if (a.head * es < yphase)
+            a.head = std::min<int64_t>(n, a.head + a.vec);
+        const int64_t rest = (n - a.head) * es;
+        const int64_t nv = std::min<int64_t>(rest / 16, (yphase + rest) / 16 - 1);
+        if (nv >= 1) {
+            a.nvec = nv;
+            a.tail = n - a.head - nv * a.vec;
+        } else {
+            a.vec = 1;
+            a.head = 0;
+            a.nvec = n;
+            a.tail = 0;
+        }
     }
     *p = a;
     return ST_OK;

@@ -126,7 +126,8 @@ def test_one_tile_one_pass_two_passes(n):
 @pytest.mark.parametrize("offs", [(0, 0), (1, 1), (3, 3), (0, 1), (1, 0), (2, 3), (3, 1), (5, 1)])
 def test_offsets(offs):
     """Equal offsets take 16-byte loads after a common head; unequal ones
-    element loads.  Checked against the plan and the oracle."""
+    16-byte loads of x and of y's aligned chunks, shifted into place (element
+    loads only when too short).  Checked against the plan and the oracle."""
     rk = _rk()
     oa, ob = offs
     for n in (5, 1000, 123457, 3 * 10**6 + 1):
@@ -134,11 +135,32 @@ def test_offsets(offs):
         b = W.uniform(n + 8, -1.0, 1.0, 7910 + ob)
         ad, bd = a.to(DEV), b.to(DEV)
         plan = rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, ad[oa:].data_ptr(), bd[ob:].data_ptr(), n)
-        assert (plan.vec == 4) == ((oa - ob) % 4 == 0)
+        assert plan.vec == (4 if (oa - ob) % 4 == 0 or n > 5 else 1)
         run2(a, b, "mul", init=0.5, off_a=oa, off_b=ob, n=n)
         run2(a, b, "absdiff", op="min", off_a=oa, off_b=ob, n=n)
         hb = W.normal(n + 8, 7920 + oa, torch.bfloat16)
         run2(hb, hb, "sqdiff", out_dtype=torch.float32, off_a=oa, off_b=ob, n=n)
+
+
+@pytest.mark.parametrize("dt", [torch.float64, torch.float16, torch.bfloat16, torch.int32, torch.int64],
+                         ids=lambda t: str(t).split(".")[1])
+@pytest.mark.parametrize("offs", [(0, 1), (1, 0), (1, 2), (0, 3), (3, 0), (2, 7)])
+def test_shifted_pairs_every_dtype(dt, offs):
+    """Inputs at different 16-byte phases for every input width: y's chunks
+    shifted by whole words (4- and 8-byte types) or by half words (2-byte
+    types); around tile boundaries and the grid's last tile."""
+    oa, ob = offs
+    tile = 256 * 8 * (16 // torch.empty(0, dtype=dt).element_size())
+    for n in (17, tile - 1, 3 * tile + 7, 123457):
+        if dt.is_floating_point:
+            a, b = W.normal(n + 8, 8100 + oa, dt), W.normal(n + 8, 8110 + ob, dt)
+            acc = torch.float64 if dt == torch.float64 else torch.float32
+            run2(a, b, "mul", acc=acc, out_dtype=acc, init=0.5, off_a=oa, off_b=ob, n=n)
+            run2(a, b, "absdiff", op="max", acc=acc, out_dtype=acc, off_a=oa, off_b=ob, n=n)
+        else:
+            a, b = W.randint(n + 8, -1000, 1000, 8120 + oa, dt), W.randint(n + 8, -1000, 1000, 8130 + ob, dt)
+            run2(a, b, "mul", acc=torch.int64, out_dtype=torch.int64, off_a=oa, off_b=ob, n=n)
+            run2(a, b, "sqdiff", op="min", acc=torch.int64, out_dtype=torch.int64, off_a=oa, off_b=ob, n=n)
 
 
 # ------------------------------------------------------------- dtype matrix

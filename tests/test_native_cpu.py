@@ -65,17 +65,21 @@ def test_whole_array_plan():
 
 
 def test_two_input_plan_matches_one_input_plan():
-    """Same grid and workspace as the one-input pass; 16-byte loads exactly
-    when the two inputs share their offset from a 16-byte boundary."""
+    """Same grid and workspace as the one-input pass; 16-byte loads of x
+    whenever there is a body of at least one vector beyond y's first chunk
+    (y in 16-byte loads too, shifted into place when the two inputs sit at
+    different offsets from a 16-byte boundary); element loads otherwise."""
     rk = _rk()
     for n in (0, 1, 10**4, 10**6 + 3, 10**8):
         one = rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, n, 256)
         two = rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 0, 0, n, 256)
         assert (two.grid, two.workspace_bytes, two.vec) == (one.grid, one.workspace_bytes, 4)
         assert two.kernel == rk.RK_KERNEL_ALL2
-        assert rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 16, 4, n, 256).vec == 1
+        shifted = n >= 16
+        assert rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 16, 4, n, 256).vec == (4 if shifted else 1)
         assert rk.rk_plan_all2(rk.RK_F32, rk.RK_F32, 20, 36, n, 256).vec == 4
-        assert rk.rk_plan_all2(rk.RK_BF16, rk.RK_F32, 2, 4, n, 256).vec == 1
+        assert rk.rk_plan_all2(rk.RK_BF16, rk.RK_F32, 2, 4, n, 256).vec == (8 if shifted else 1)
+        assert rk.rk_plan_all2(rk.RK_F64, rk.RK_F64, 8, 16, n, 256).vec == (2 if shifted else 1)
 
 
 def test_config_shapes_take_the_expected_kernels():
