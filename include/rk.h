@@ -204,9 +204,10 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
 /*
  * Bytes of device workspace rk_scan_dims (or rk_scan: ndim = 1, strides[0] =
  * 1, dim = 0) needs for this layout on the current device: the tile state of
- * a look-back scan (a counter, one flag and two accumulators per tile, and
- * per line of a tile for a strided scan dim), rounded up to 256 bytes; 0 when
- * the layout takes a kernel without tiles.  Contents need not be
+ * a look-back scan (a 256-byte header; per tile a flag and two accumulators,
+ * or two per line of a tile for a strided scan dim; neighbouring tiles'
+ * state in different 128-byte lines), rounded up to 256 bytes; 0 when the
+ * layout takes a kernel without tiles.  Contents need not be
  * initialised; the call clears what it uses.  After a look-back scan the
  * first two 32-bit words hold the number of tiles and a timeout word, which
  * is nonzero only if a bounded wait between tiles ever gave up (then the
@@ -229,10 +230,11 @@ size_t rk_scan_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64
  * at the same time.  stream: hipStream_t or NULL; asynchronous.  A line
  * contiguous along the scan dim and at least one tile long (or a strided scan
  * dim over runs of contiguous lines) is scanned in one pass with decoupled
- * look-back between tiles.  The tiles' counter and flags live in the
- * library's per-stream slot when they fit one (8192 tiles; the last block of
- * the call zeroes them again), otherwise in the workspace, cleared by a
- * small launch first.  Returns an rk_status.
+ * look-back between tiles.  The tiles' counter and flags (along contiguous
+ * lines: all of the per-tile state) live in the library's per-stream slot
+ * when they fit one (4096 tiles along contiguous lines, 8192 for a strided
+ * scan dim; the last block of the call zeroes them again), otherwise in the
+ * workspace, cleared by a small launch first.  Returns an rk_status.
  */
 int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,
                  const int64_t *shape, const int64_t *strides, int dim, const void *init,
