@@ -591,6 +591,10 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 }
 
 // Row kernel: one wave per (output, chunk) over a contiguous reduced dim.
+// With several reduced dims the others index segments of such rows; a chunk
+// is a run of whole segments or a piece of one segment's row.  Each row piece
+// takes a scalar head up to its first 16-byte boundary, 16-byte loads
+// (UNROLL in flight per lane) and a scalar tail.
 template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
 {
@@ -602,52 +606,64 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
         return;                                 // whole wave; no block barrier below
     const int64_t o = unit / a.split;
     const int sp = (int)(unit - o * a.split);
-    const int64_t j0 = int64_t(sp) * a.rows_per_split;
-    const int64_t len = a.m - j0 < a.rows_per_split ? a.m - j0 : a.rows_per_split;
-    const S *row = static_cast<const S *>(a.x) +
-                   layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o) + j0;
-
-    // scalar head up to the first 16-byte boundary, vector body, scalar tail
-    int64_t head = (int64_t)(((16u - ((uintptr_t)row & 15u)) & 15u) / sizeof(S));
-    head = head < len ? head : len;
-    const int64_t nv = (len - head) / V;
-    const int64_t tail = len - head - nv * V;
-    const u32x4 *body = reinterpret_cast<const u32x4 *>(row + head);
+    int64_t k0, k1, j0, j1;
+    if (a.splits_per_seg > 1) {
+        k0 = sp / a.splits_per_seg;
+        k1 = k0 + 1;
+        j0 = (sp - k0 * a.splits_per_seg) * a.rows_per_split;
+        j1 = j0 + a.rows_per_split < a.row_len ? j0 + a.rows_per_split : a.row_len;
+    } else {
+        k0 = int64_t(sp) * a.segs_per_split;
+        k1 = k0 + a.segs_per_split < a.segs ? k0 + a.segs_per_split : a.segs;
+        j0 = 0;
+        j1 = a.row_len;
+    }
+    const S *base = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_str, o) + j0;
+    const int64_t len = j1 - j0;
 
     Acc acc0[V], acc1[V];
     set_identity<Acc, Op>(acc0);
     set_identity<Acc, Op>(acc1);
-    int64_t i = lane;
-    for (; i + int64_t(UNROLL - 1) * 64 < nv; i += int64_t(UNROLL) * 64) {
-        u32x4 w[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            w[u] = load16(body + i + u * 64);
-        issue_barrier();
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            if (u & 1)
-                fold_vec<In, Acc, Op, Map, V>(acc1, w[u]);
-            else
-                fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
-        }
-    }
-    if (i < nv) {                               // last, partial group, loads together
-        u32x4 w[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            if (i + u * 64 < nv)
-                w[u] = load16(body + i + u * 64);
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            if (i + u * 64 < nv)
-                fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
-    }
     Acc s = Op::template identity<Acc>();
-    if (lane < head)
-        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(row + lane))));
-    if (lane < tail)
-        s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(row + head + nv * V + lane))));
+    for (int64_t k = k0; k < k1; ++k) {
+        const S *row = base + layout_offset(a.seg_nd, a.seg_ext, a.seg_str, k);
+        // scalar head up to the first 16-byte boundary, vector body, scalar tail
+        int64_t head = (int64_t)(((16u - ((uintptr_t)row & 15u)) & 15u) / sizeof(S));
+        head = head < len ? head : len;
+        const int64_t nv = (len - head) / V;
+        const int64_t tail = len - head - nv * V;
+        const u32x4 *body = reinterpret_cast<const u32x4 *>(row + head);
+        int64_t i = lane;
+        for (; i + int64_t(UNROLL - 1) * 64 < nv; i += int64_t(UNROLL) * 64) {
+            u32x4 w[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                w[u] = load16(body + i + u * 64);
+            issue_barrier();
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (u & 1)
+                    fold_vec<In, Acc, Op, Map, V>(acc1, w[u]);
+                else
+                    fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+            }
+        }
+        if (i < nv) {                           // last, partial group, loads together
+            u32x4 w[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (i + u * 64 < nv)
+                    w[u] = load16(body + i + u * 64);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (i + u * 64 < nv)
+                    fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
+        }
+        if (lane < head)
+            s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(row + lane))));
+        if (lane < tail)
+            s = Op::apply(s, Map::apply(InTraits<In>::template one<Acc>(load1(row + head + nv * V + lane))));
+    }
 #pragma unroll
     for (int k = 0; k < V; ++k)
         acc0[k] = Op::apply(acc0[k], acc1[k]);

@@ -188,7 +188,9 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
                 d.kernel = K_ALL_STRIDED;
         } else if (d.red.nd == 0) {
             d.kernel = K_GENERIC;           // nothing to reduce: f applied per element
-        } else if (d.red.nd == 1 && d.red.str[0] == 1) {
+        } else if (d.red.str[0] == 1 && (d.red.nd == 1 || d.red.ext[0] * isz >= tune::kRowSegMinBytes)) {
+            // a contiguous reduced dim: rows, and with several reduced dims
+            // the others index segments of such rows
             d.kernel = K_ROW;
         } else if (d.kept.str[0] == 1) {
             // contiguous runs of outputs over any reduced dims (PR #176's
@@ -318,15 +320,36 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
     }
     case K_ROW: {
         d.vec = 16 / isz;
+        d.row_len = d.red.ext[0];
+        d.seg = Layout();
+        for (int i = 1; i < d.red.nd; ++i) {
+            d.seg.ext[d.seg.nd] = d.red.ext[i];
+            d.seg.str[d.seg.nd] = d.red.str[i];
+            ++d.seg.nd;
+        }
+        d.segs = m / d.row_len;
         const int64_t waves_target = int64_t(num_cus) * tune::kRowWavesPerCu;
         int64_t s = 1;
         if (n_out < waves_target)
             s = std::min<int64_t>(ceil_div(waves_target, n_out),
                                   std::max<int64_t>(1, m / tune::kRowMinChunk));
-        int64_t rows = ceil_div(m, s);
-        rows = ceil_div(rows, d.vec) * d.vec;   // chunks keep the row's 16-byte phase
-        d.rows_per_split = rows;
-        d.split = int(ceil_div(m, rows));
+        // split units: whole segments each, or pieces of one segment's row
+        d.rows_per_split = d.row_len;
+        d.segs_per_split = d.segs;
+        d.splits_per_seg = 1;
+        if (s <= d.segs) {
+            d.segs_per_split = ceil_div(d.segs, s);
+            d.split = int(ceil_div(d.segs, d.segs_per_split));
+        } else {
+            int64_t per = std::min<int64_t>(ceil_div(s, d.segs), std::max<int64_t>(1, d.row_len / tune::kRowMinChunk));
+            int64_t rows = ceil_div(d.row_len, per);
+            rows = ceil_div(rows, d.vec) * d.vec;   // pieces keep the row's 16-byte phase
+            d.rows_per_split = rows;
+            per = ceil_div(d.row_len, rows);
+            d.segs_per_split = 1;
+            d.splits_per_seg = per;
+            d.split = int(d.segs * per);
+        }
         const int waves_per_block = tune::kDimsBlock / 64;
         d.block = tune::kDimsBlock;
         d.grid = ceil_div(n_out * d.split, waves_per_block);

@@ -66,6 +66,7 @@ constexpr int kColumnsBlocksPerCu = 1;    // columns split target: CUs * this bl
 constexpr int64_t kColumnsMinRows = 128;  // rows per split chunk, at least
 constexpr int kRowWavesPerCu = 16;        // row kernel split target
 constexpr int64_t kRowMinChunk = 2048;    // elements per row chunk, at least
+constexpr int64_t kRowSegMinBytes = 4096; // row kernel over several reduced dims: contiguous rows this long
 constexpr int kGenericBlocksPerCu = 8;   // generic kernel: grid cap, and split target
 constexpr int kGenericUnroll = 8;        // generic kernel: element loads in flight per thread
 constexpr int64_t kGenericMinChunk = 4096;   // generic kernel: reduced elements per split unit, at least

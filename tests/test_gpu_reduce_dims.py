@@ -240,8 +240,14 @@ GENERAL_CASES = [
     (5 * 6 * 7, (5, 6, 7), CM((5, 6, 7)), (1, 3), "generic", "non-adjacent dims, kept dim strided"),
     (49 * 64 * 256, (49, 64, 256), CM((49, 64, 256)), (1, 3), "generic",
      "per-channel statistics of 7x7 maps"),
-    (3136 * 16 * 24, (3136, 16, 24), CM((3136, 16, 24)), (1, 3), "generic",
-     "per-channel statistics of 56x56 maps, split outputs"),
+    (3136 * 16 * 24, (3136, 16, 24), CM((3136, 16, 24)), (1, 3), "row",
+     "per-channel statistics of 56x56 maps: rows of 12.5 KB as segments"),
+    (100000 * 3 * 2, (100000, 3, 2), CM((100000, 3, 2)), (1, 3), "row",
+     "few outputs: pieces of one segment's row"),
+    (2000 * 3 * 5 * 7, (2000, 3, 5, 7), CM((2000, 3, 5, 7)), (1, 3, 4), "row",
+     "three reduced dims, rows of 8 KB"),
+    (1025 * 9 * 5, (1025, 9, 5), CM((1025, 9, 5)), (1, 3), "row",
+     "rows of 4100 bytes: every row at its own 16-byte phase"),
     (2 * 300 * 40, (300, 40), (2, 600), 1, "generic", "strided gather along the reduced dim"),
 ]
 
@@ -330,13 +336,28 @@ def test_general_layout_offsets(offset):
     dims_and_check(xb, shape, CM(shape), (1, 3), offset=offset, out_dtype=torch.float32)
 
 
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_row_segments_offsets(offset):
+    """The row kernel over segments peels a scalar head and tail off every
+    row piece, so views at any element offset keep 16-byte loads."""
+    shape = (3136, 16, 24)
+    x = W.normal(math.prod(shape) + offset, 9990 + offset)
+    plan = dims_and_check(x, shape, CM(shape), (1, 3), offset=offset, expect_kernel="row")
+    assert plan["vec"] == 4
+    xi = W.randint(math.prod(shape) + offset, -10**6, 10**6, 9995 + offset)
+    dims_and_check(xi, shape, CM(shape), (1, 3), offset=offset, acc=torch.int64, out_dtype=torch.int64,
+                   expect_kernel="row")
+
+
 def test_general_layout_plans():
     rk = _rk()
     p = rk.plan_dims(torch.float32, (128, 3000, 3), (1, 384, 128), (2, 3))
     assert p["kernel_name"] == "columns" and p["split"] > 3
     p = rk.plan_dims(torch.float32, (3136, 16, 24), CM((3136, 16, 24)), (1, 3))
-    assert p["kernel_name"] == "generic" and p["split"] > 1
+    assert p["kernel_name"] == "row" and p["split"] > 1
     assert p["workspace_bytes"] >= p["split"] * 16 * 4
+    p = rk.plan_dims(torch.float32, (1000, 16, 24), CM((1000, 16, 24)), (1, 3))
+    assert p["kernel_name"] == "generic" and p["split"] > 1
 
 
 def test_dims_all_masked_equals_whole_array():

@@ -140,8 +140,10 @@ def test_selector_rules():
 
 def test_general_layouts_route():
     """Reduced dims that do not merge: contiguous runs of outputs take the
-    tile kernels (the other reduced dims index segments of rows); anything
-    else the generic kernel, split over blocks when outputs are few."""
+    tile kernels (the other reduced dims index segments of rows); a
+    contiguous reduced dim of at least 4 KB rows takes the row kernel (the
+    other reduced dims index segments of those rows); anything else the
+    generic kernel, split over blocks when outputs are few."""
     import torch
     f32 = torch.float32
     p = plan(f32, (128, 3000, 3), (2, 3), strides=(1, 384, 128))
@@ -155,12 +157,18 @@ def test_general_layouts_route():
     p = plan(f32, (49, 64, 256), (1, 3))
     assert p["kernel_name"] == "generic" and p["split"] == 3 and p["launches"] == 1
     assert p["vec"] == 1                                             # 49-element rows
-    p = plan(f32, (3136, 16, 24), (1, 3))
-    assert p["kernel_name"] == "generic" and p["split"] == 18 and p["grid"] == 16 * 18
-    assert p["vec"] == 4                                             # 16-byte loads along rows
-    assert plan(f32, (3136, 16, 24), (1, 3), ptr=4)["vec"] == 1
+    p = plan(f32, (3136, 16, 24), (1, 3))                           # 12.5 KB rows, 24 segments
+    assert p["kernel_name"] == "row" and p["split"] == 24 and p["grid"] == 16 * 24 // 4
+    assert p["vec"] == 4                                             # 16-byte loads after each row's head
+    assert plan(f32, (3136, 16, 24), (1, 3), ptr=4)["vec"] == 4
     assert plan(torch.bfloat16, (3136, 16, 24), (1, 3))["vec"] == 8
-    assert p["workspace_bytes"] == 1280                              # 18 * 16 * 4 rounded to 256
+    assert p["workspace_bytes"] == 1536                              # 24 * 16 * 4 rounded to 256
+    p = plan(f32, (3136, 256, 84), (1, 3))                          # per-channel statistics
+    assert p["kernel_name"] == "row" and p["split"] == 14 and p["launches"] == 1
+    p = plan(f32, (100_000, 3, 2), (1, 3))                          # pieces of one segment's row
+    assert p["kernel_name"] == "row" and p["split"] > 2 and p["split"] % 2 == 0
+    p = plan(f32, (1000, 8, 12), (1, 3))                            # 4000-byte rows: generic
+    assert p["kernel_name"] == "generic"
     p = plan(f32, (5000, 3000), (1,), strides=(3, 15000))            # no stride-1 dim
     assert p["kernel_name"] == "generic" and p["split"] == 1
 
