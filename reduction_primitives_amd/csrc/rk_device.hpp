@@ -595,6 +595,109 @@ __device__ __forceinline__ bool arrive_last(int slot, int64_t idx, uint32_t memb
     return count_arrival(slot, top, (n + kArriveGroup - 1) / kArriveGroup);
 }
 
+// --------------------------------------- whole-array finish by collection
+// A whole-array pass needs its blocks' partials in one place, and counting
+// arrivals puts a chain of dependent memory round trips behind the last
+// block (store and wait, group counter, top counter, loads).  Instead every
+// block stores its partial with the call's tag in the same 64-bit word (one
+// device-scope store, no wait; 8-byte partials take two words, a tagged
+// half each), and block 0, after its own tiles, polls the words until every
+// one carries the tag, folds them in block order -- the order of the second
+// launch -- and finishes.  No block waits on block 0, so the poll always
+// ends; a bounded spin is the safety net.
+//
+// Tags: each stream slot keeps the last call's tag E; a call's tag is E + 1,
+// read by every block when it starts, and block 0 stores it back into E when
+// it is done, so the next call on the stream (a graph replay included) gets
+// a fresh one.  E is kept in kFinalTagCopies copies, a 128-byte line each,
+// and block b reads copy b mod kFinalTagCopies: a thousand blocks reading one
+// line would queue where device-scope accesses are performed.  Tags run
+// 1 .. 2^32 - 1; the call that reaches 2^32 - 1 zeroes every word of the
+// slot and sets E to 0, so a word never carries a stale tag that equals the
+// current one.
+constexpr int kFinalTagCopies = 32;
+constexpr int kFinalHeaderWords = 16 * kFinalTagCopies;
+constexpr int kFinalSlotWords = kFinalHeaderWords + 2 * kFinalCapacity;
+static __device__ __attribute__((aligned(128))) uint64_t g_final[kArriveSlots * kFinalSlotWords];
+
+// The call's tag (read when a block starts; thread 0 only).
+__device__ __forceinline__ uint32_t final_tag(int slot)
+{
+    const int64_t copy = int64_t(blockIdx.x % kFinalTagCopies) * 16;
+    return uint32_t(__hip_atomic_load(&g_final[int64_t(slot) * kFinalSlotWords + copy], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+}
+
+template <class Acc>
+__device__ __forceinline__ void publish_tagged(int slot, int b, Acc v, uint32_t tag)
+{
+    uint64_t *w = &g_final[int64_t(slot) * kFinalSlotWords + kFinalHeaderWords];
+    const uint64_t t = uint64_t(tag) << 32;
+    if constexpr (sizeof(Acc) == 4) {
+        __hip_atomic_store(w + b, t | bitcast<uint32_t>(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        const uint64_t bits = bitcast<uint64_t>(v);
+        __hip_atomic_store(w + 2 * b, t | (bits & 0xffffffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(w + 2 * b + 1, t | (bits >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Block 0: wait until all `grid` partials carry `tag`, then fold thread t's
+// partials t, t + BLOCK, ... in that order (every thread's result, before
+// the block reduction).  Called by every thread of block 0.
+template <class Acc, class Op, int BLOCK>
+__device__ Acc collect_tagged(int slot, int grid, uint32_t tag)
+{
+    const uint64_t *w = &g_final[int64_t(slot) * kFinalSlotWords + kFinalHeaderWords];
+    __shared__ int s_ready;
+    Acc v = Op::template identity<Acc>();
+    for (int spin = 0;; ++spin) {
+        bool ok = true;
+        v = Op::template identity<Acc>();
+        for (int k = threadIdx.x; k < grid; k += BLOCK) {
+            if constexpr (sizeof(Acc) == 4) {
+                const uint64_t x = __hip_atomic_load(w + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && uint32_t(x >> 32) == tag;
+                v = Op::apply(v, bitcast<Acc>(uint32_t(x)));
+            } else {
+                const uint64_t lo = __hip_atomic_load(w + 2 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t hi = __hip_atomic_load(w + 2 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && uint32_t(lo >> 32) == tag && uint32_t(hi >> 32) == tag;
+                v = Op::apply(v, bitcast<Acc>((lo & 0xffffffffu) | (hi << 32)));
+            }
+        }
+        if (threadIdx.x == 0)
+            s_ready = 1;
+        __syncthreads();
+        if (!ok)
+            s_ready = 0;
+        __syncthreads();
+        const bool ready = s_ready != 0;
+        __syncthreads();
+        if (ready || spin >= kFinalSpinLimit)
+            break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return v;
+}
+
+// Block 0, once the result is stored: hand the next call its tag base.
+// Called by every thread of block 0.
+template <int BLOCK>
+__device__ __forceinline__ void advance_tag(int slot, uint32_t tag)
+{
+    static_assert(BLOCK >= kFinalTagCopies, "one thread per copy of the tag");
+    uint64_t *s = &g_final[int64_t(slot) * kFinalSlotWords];
+    uint64_t next = tag;
+    if (tag == 0xffffffffu) {                  // wrap: no word may keep an old tag
+        for (int i = threadIdx.x; i < 2 * kFinalCapacity; i += BLOCK)
+            __hip_atomic_store(s + kFinalHeaderWords + i, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        next = 0;
+    }
+    if (threadIdx.x < kFinalTagCopies)
+        __hip_atomic_store(s + threadIdx.x * 16, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ misc
 
 // Offset of linear index idx in a column-major layout of nd <= 4 dims.

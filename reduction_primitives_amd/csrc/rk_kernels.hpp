@@ -102,9 +102,19 @@ __device__ __forceinline__ void fold_partials_and_finish(Acc *ws, int grid, cons
     }
 }
 
-// End of a first-pass block holding its reduced value v (valid in thread 0).
+// Start of a first-pass block: the call's tag when it finishes by collection
+// (thread 0; read early, so the load is long done by the end).
+__device__ __forceinline__ uint32_t whole_prologue(const AllArgs &a)
+{
+    return threadIdx.x == 0 && a.grid > 1 && a.grid <= kFinalCapacity && a.arrive_slot >= 0
+               ? final_tag(a.arrive_slot)
+               : 0u;
+}
+
+// End of a first-pass block holding its reduced value v (valid in thread 0)
+// and the call's tag (thread 0).
 template <class Acc, class Op, int BLOCK>
-__device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v)
+__device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v, uint32_t tag)
 {
     Acc *ws = static_cast<Acc *>(a.ws);
     if (a.grid == 1) {                          // the whole input in one block
@@ -119,6 +129,26 @@ __device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v)
     if (a.arrive_slot < 0) {                    // a second launch folds the partials
         if (threadIdx.x == 0)
             ws[blockIdx.x] = v;
+        return;
+    }
+    if (a.grid <= kFinalCapacity) {             // tagged partials, collected by block 0
+        if (threadIdx.x == 0)
+            publish_tagged(a.arrive_slot, blockIdx.x, v, tag);
+        if (blockIdx.x != 0)
+            return;
+        __shared__ uint32_t s_tag;
+        if (threadIdx.x == 0)
+            s_tag = tag;
+        __syncthreads();
+        const uint32_t t = s_tag;
+        Acc r = block_reduce<Op, BLOCK>(collect_tagged<Acc, Op, BLOCK>(a.arrive_slot, a.grid, t));
+        if (threadIdx.x == 0) {
+            if (a.fin.mode == FIN_HOST)
+                store_host_result(a.fin, ws, a.grid, r);
+            else
+                finish_store<Op>(a.fin, 0, r);
+        }
+        advance_tag<BLOCK>(a.arrive_slot, t);
         return;
     }
     __shared__ int last;
@@ -137,6 +167,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
 {
     using S = typename InTraits<In>::S;
     constexpr int V = InTraits<In>::vec;
+    const uint32_t tag = whole_prologue(a);
     const S *x = static_cast<const S *>(a.x);
     const u32x4 *body = reinterpret_cast<const u32x4 *>(x + a.head);
 
@@ -180,7 +211,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
         acc0[i] = Op::apply(acc0[i], acc1[i]);
     Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
     v = block_reduce<Op, BLOCK>(v);
-    whole_epilogue<Acc, Op, BLOCK>(a, v);
+    whole_epilogue<Acc, Op, BLOCK>(a, v, tag);
 }
 
 // Single output over a non-contiguous view: element i lives at
@@ -189,6 +220,7 @@ template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
 {
     using S = typename InTraits<In>::S;
+    const uint32_t tag = whole_prologue(a);
     const S *x = static_cast<const S *>(a.x);
     Acc acc[UNROLL];
 #pragma unroll
@@ -213,7 +245,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
     }
     Acc v = fold_all<Acc, Op, UNROLL>(acc);
     v = block_reduce<Op, BLOCK>(v);
-    whole_epilogue<Acc, Op, BLOCK>(a, v);
+    whole_epilogue<Acc, Op, BLOCK>(a, v, tag);
 }
 
 template <class Acc, class Op, int BLOCK>
@@ -289,6 +321,7 @@ template <class In, class Acc, class Op, class Map2, int BLOCK, int UNROLL, int 
 __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
 {
     using S = typename InTraits<In>::S;
+    const uint32_t tag = whole_prologue(a);
     constexpr bool VECTOR = MODE != ALL2_ELEMENTS;
     constexpr int V = VECTOR ? InTraits<In>::vec : 1;
     const S *x = static_cast<const S *>(a.x);
@@ -410,7 +443,7 @@ __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
         acc0[i] = Op::apply(acc0[i], acc1[i]);
     Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
     v = block_reduce<Op, BLOCK>(v);
-    whole_epilogue<Acc, Op, BLOCK>(a, v);
+    whole_epilogue<Acc, Op, BLOCK>(a, v, tag);
 }
 
 // ======================================================================= dims

@@ -32,6 +32,12 @@ constexpr int64_t arrive_counters(int64_t n)
     return n > kArriveGroup ? 1 + (n + kArriveGroup - 1) / kArriveGroup : 1;
 }
 
+// A whole-array pass of up to kFinalCapacity blocks finishes without
+// counters: every block stores its partial tagged with the call's number,
+// and block 0 collects them (see rk_device.hpp).
+constexpr int kFinalCapacity = 2048;
+constexpr int kFinalSpinLimit = 1 << 24;   // block 0's polls (with a short sleep each): far beyond any run
+
 struct Finish {
     void *out;            // device output (OVERWRITE / FOLD); HOST: pinned host result buffer or NULL
     int out_dtype;
