@@ -249,8 +249,9 @@ int rk_scan(int op, int in_dtype, int acc_dtype, int out_dtype, const void *ptr,
 const char *rk_status_string(int status);
 
 /* ------------------------------------------------------------------------
- * Diagnostics.  They launch nothing; tests and benchmarks use them to see
- * which kernel a call takes and to time its first pass.
+ * Diagnostics and hooks for tests and benchmarks: which kernel a call takes
+ * and its plan (these launch nothing), timing of a call's first pass, the
+ * device's read ceiling, and the finishing tags of a stream's slot.
  * ---------------------------------------------------------------------- */
 
 /* Kernels a call can take.  The dims selector (PR #176, "This PR" item 1)
@@ -317,6 +318,13 @@ int rk_debug_set_fused_finish(int enable);
  * kernel launch and `end` immediately after it, on the call's stream.  Pass
  * NULLs to stop.  Returns an rk_status. */
 int rk_debug_set_launch_events(void *begin, void *end);
+
+/* Test hook: make the last whole-array finishing tag of `stream`'s slot `e`
+ * (every kernel translation unit), so a test can run calls across the wrap
+ * of the tags: e = 2^32 - 2 makes the next call the one that wraps.  Enqueued
+ * on `stream`.  Returns an rk_status: RK_ERR_INVALID_ARGUMENT for e above
+ * 2^32 - 2, RK_ERR_UNSUPPORTED when the stream gets no slot. */
+int rk_debug_set_finish_tag(void *stream, uint32_t e);
 
 /* Benchmark hook: the device's read-bandwidth ceiling.  Enqueues on `stream`
  * one kernel that loads each of the nbytes / 16 vectors at `ptr` once

@@ -20,7 +20,8 @@ from ._native import (  # noqa: F401
     RK_KERNEL_TILED, RK_MAP2_ABSDIFF, RK_MAP2_MUL, RK_MAP2_SQDIFF,
     RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
     RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,
-    RkError, load, rk_debug_device_info, rk_debug_set_fused_finish, rk_debug_set_launch_events,
+    RkError, load, rk_debug_device_info, rk_debug_set_finish_tag, rk_debug_set_fused_finish,
+    rk_debug_set_launch_events,
     rk_debug_stream_read, rk_plan_all, rk_plan_all2, rk_plan_dims,
     rk_plan_info, rk_plan_scan, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_scan, rk_scan_dims,
     rk_scan_workspace_size, rk_workspace_size, status_string)

@@ -30,7 +30,7 @@ KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 
 EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_dims", "rk_status_string",
            "rk_plan_all", "rk_plan_all2", "rk_plan_dims", "rk_debug_set_fused_finish",
            "rk_debug_set_launch_events", "rk_scan_workspace_size", "rk_scan", "rk_scan_dims",
-           "rk_plan_scan", "rk_debug_stream_read", "rk_debug_device_info")
+           "rk_plan_scan", "rk_debug_stream_read", "rk_debug_device_info", "rk_debug_set_finish_tag")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -97,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.rk_debug_stream_read.restype = i32
     lib.rk_debug_device_info.argtypes = [p64, p64, p64]
     lib.rk_debug_device_info.restype = i32
+    lib.rk_debug_set_finish_tag.argtypes = [vp, u32]
+    lib.rk_debug_set_finish_tag.restype = i32
     _lib = lib
     return lib
 
@@ -191,6 +193,10 @@ def rk_debug_set_fused_finish(enable: int) -> int:
 
 def rk_debug_set_launch_events(begin, end) -> int:
     return int(load().rk_debug_set_launch_events(begin, end))
+
+
+def rk_debug_set_finish_tag(stream, e: int) -> int:
+    return int(load().rk_debug_set_finish_tag(stream, int(e)))
 
 
 def rk_debug_stream_read(ptr, nbytes, grid, sink, stream) -> None:

@@ -428,6 +428,28 @@ int rk_debug_set_fused_finish(int enable)
     return g_fused_finish.exchange(enable != 0) ? 1 : 0;
 }
 
+int rk_debug_set_finish_tag(void *stream, uint32_t e)
+{
+    if (e > 0xfffffffeu)
+        return RK_ERR_INVALID_ARGUMENT;
+    const int slot = arrive_slot(static_cast<hipStream_t>(stream));
+    if (slot < 0)
+        return RK_ERR_UNSUPPORTED;
+    const int dtypes[] = {F32, BF16, F16, F64, I32, I64};
+    for (int d : dtypes) {
+        Launch L;
+        std::memset(&L, 0, sizeof L);
+        L.kernel = K_SET_TAG;
+        L.all.arrive_slot = slot;
+        L.all.n = e;
+        L.stream = stream;
+        const int rc = dispatch(d, L);
+        if (rc != RK_OK)
+            return rc;
+    }
+    return RK_OK;
+}
+
 int rk_debug_set_launch_events(void *begin, void *end)
 {
     if ((begin == nullptr) != (end == nullptr))

@@ -698,6 +698,18 @@ __device__ __forceinline__ void advance_tag(int slot, uint32_t tag)
         __hip_atomic_store(s + threadIdx.x * 16, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Test hook: make the slot's last tag `e` (every copy), so a test can run
+// calls across the wrap of the tags.  One block of kFinalTagCopies threads.
+// (A template, so that each translation unit keeps its own kernel, as it
+// keeps its own g_final.)
+template <int UNUSED = 0>
+__global__ void k_set_final_tag(int slot, uint32_t e)
+{
+    if (threadIdx.x < kFinalTagCopies)
+        __hip_atomic_store(&g_final[int64_t(slot) * kFinalSlotWords + threadIdx.x * 16], uint64_t(e), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ misc
 
 // Offset of linear index idx in a column-major layout of nd <= 4 dims.

@@ -1066,6 +1066,11 @@ int run_acc(const Launch &L)
 template <class In>
 int run_in(const Launch &L)
 {
+    if (L.kernel == K_SET_TAG) {                // this translation unit's copy of the slot
+        hipLaunchKernelGGL(k_set_final_tag<0>, dim3(1), dim3(kFinalTagCopies), 0, static_cast<hipStream_t>(L.stream),
+                           L.all.arrive_slot, uint32_t(L.all.n));
+        return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
+    }
     if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
         if (L.acc == F32) return run_acc<In, float>(L);
         if (L.acc == F64) return run_acc<In, double>(L);

@@ -19,7 +19,8 @@ enum Dtype { F32 = 0, BF16 = 1, F16 = 2, F64 = 3, I32 = 4, I64 = 5 };
 enum Mode { OVERWRITE = 0, FOLD = 1, HOST = 2 };
 enum Kernel {
     K_NONE = 0, K_ALL = 1, K_ALL_STRIDED = 2, K_THREAD = 3, K_TILED = 4,
-    K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7, K_ALL2 = 8
+    K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7, K_ALL2 = 8,
+    K_SET_TAG = 100               // test hook: set a slot's whole-array tag (no reduction)
 };
 
 int dtype_size(int d);            // bytes per element, 0 for an unknown code

@@ -8,6 +8,7 @@ must agree bit for bit.  Also covered: counters returning to zero across many
 calls, calls on several streams at once, and more streams than counter slots
 (the overflow takes the second-launch path).
 """
+import ctypes
 import math
 
 import numpy as np
@@ -182,3 +183,33 @@ def test_host_mode_copy_back_path():
     assert abs(float(res[True][0]) - R) <= 1e-5 * S
     xi = W.randint(1000, -50, 50, 9501)
     assert int(res[True][1]) == int(xi.long().sum())
+
+
+def test_collection_tags_across_the_wrap():
+    """Whole-array passes collect their blocks' partials by the call's tag;
+    the call that reaches the last tag (2^32 - 1) clears the slot's words
+    and the next starts again at 1.  Calls on one stream across that wrap,
+    with 4-byte (f32) and 8-byte (int32 -> int64) partials, give exact
+    results; so do calls after it."""
+    import reduction_primitives_amd as rk
+    rk.load()
+    s = torch.cuda.Stream()
+    st = ctypes.c_void_p(s.cuda_stream)
+    n = 3 * 10**6 + 11
+    assert rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, n, 256).grid > 1
+    xs = [W.small_ints(n, -8, 8, 15000 + i) for i in range(6)]          # exact in f32 in any order
+    xis = [W.randint(n, -10**6, 10**6, 15100 + i) for i in range(6)]
+    xds = [x.to("cuda") for x in xs]
+    xids = [x.to("cuda") for x in xis]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        assert rk.rk_debug_set_finish_tag(st, 0xFFFFFFFD) == rk.RK_OK    # next tags: ..FE, ..FF (wrap), 1, 2
+        outs = []
+        for i in range(6):
+            outs.append(rk.reduce_all(xds[i], init=0.0))
+            outs.append(rk.reduce_all(xids[i], acc=torch.int64, out_dtype=torch.int64))
+    s.synchronize()
+    for i in range(6):
+        assert float(outs[2 * i].item()) == float(xs[i].double().sum()), i
+        assert int(outs[2 * i + 1].item()) == int(xis[i].long().sum()), i
+    assert rk.rk_debug_set_finish_tag(st, 0xFFFFFFFF) == rk.RK_ERR_INVALID_ARGUMENT

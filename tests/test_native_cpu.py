@@ -304,6 +304,7 @@ def test_stream_read_validation():
     assert lib.rk_debug_stream_read(None, 16, 0, FAKE, None) == bad
     assert lib.rk_debug_stream_read(FAKE, 16, 0, None, None) == bad
     assert lib.rk_debug_device_info(None, None, None) == bad
+    assert lib.rk_debug_set_finish_tag(None, 0xFFFFFFFF) == bad            # above the last tag
 
 
 # ------------------------------------------------------------------- scans
