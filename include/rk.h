@@ -64,10 +64,11 @@
  * `stream` (a hipStream_t; NULL is the null stream) of the current device.
  * OVERWRITE and FOLD calls are asynchronous: buffers must stay alive until
  * the stream's work has completed.  Between calls the library keeps only
- * cached device properties and, per (device, stream), a slot of arrival
- * counters in its own device memory: a reduction split across blocks is
- * finished by the last block to arrive instead of a second launch, and its
- * counters return to zero by themselves.  Calls from several host threads are
+ * cached device properties and, per (device, stream), a slot of state in its
+ * own device memory, so a reduction split across blocks finishes inside its
+ * one launch: a whole-array pass's blocks store their partials tagged with
+ * the call's number and block 0 collects them; split dims reductions count
+ * arrivals on counters that return to zero by themselves.  Calls from several host threads are
  * safe; two calls that share a workspace must be ordered by the caller.
  *
  * Graph capture: OVERWRITE and FOLD calls enqueue kernels only (no memset,
@@ -278,7 +279,7 @@ typedef enum {
 typedef struct {
     int kernel;               /* rk_kernel */
     int launches;             /* kernel launches the call makes: 0, 1 or 2 (1 when a split
-                                 reduction finishes in its last block to arrive) */
+                                 reduction finishes inside its first launch) */
     int64_t grid;             /* blocks of the first launch */
     int block;                /* threads per block of the first launch */
     int split;                /* blocks sharing one output's reduction (1 = no second pass) */
@@ -307,8 +308,9 @@ int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, co
                  const int64_t *shape, const int64_t *strides, int dim, int num_cus,
                  rk_plan_info *info);
 
-/* Whether a split reduction may finish in the last block to arrive (one
- * launch; the default) instead of a second launch.  Both give the same
+/* Whether a split reduction may finish inside its first launch (block 0
+ * collecting tagged partials, or the last block to arrive; the default)
+ * instead of a second launch.  Both give the same
  * results; tests switch it off to cover the second-launch path.  Process-
  * wide.  Returns the previous setting (1 or 0). */
 int rk_debug_set_fused_finish(int enable);

@@ -2,9 +2,9 @@
 //
 // Whole array (AcceleratedKernels.jl PR #139, "What changes"): a first pass
 // of at most a grid cap of blocks, each striding over tiles of the input with
-// several 16-byte loads in flight per thread; the last block to arrive folds
-// the partials (a one-block second pass when no arrival counters are free);
-// an input that fits one block finishes in the first pass.  A fused
+// several 16-byte loads in flight per thread; block 0 collects the blocks'
+// tagged partials and finishes (a one-block second pass when the stream has
+// no slot); an input that fits one block finishes in the first pass.  A fused
 // two-input source f(x_i, y_i) takes the same passes with two loads per step.
 //
 // Strided dims (PR #176, "This PR"): one tile kernel serves the selector's
@@ -66,7 +66,8 @@ __device__ __forceinline__ Acc fold_all(const Acc (&a)[V])
 
 // Fold a whole-array call's `grid` block partials and finish: store into
 // the output, or leave the bare result in ws[grid] for the host.  Run by one
-// block (the second launch, or the last block to arrive).
+// block (the second launch, or the last block to arrive when a grid is too
+// large for collection).
 // Fold `count` partials p[first + k * stride], k < count, issuing up to 8
 // loads at a time: the partials come from memory, and one round trip per
 // partial would dominate the finishing step.
