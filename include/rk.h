@@ -60,7 +60,9 @@
  * width of that kind; it may be narrower than the accumulator.
  *
  * Ownership: the caller owns every buffer (`ptr`, `out`, `workspace`).  The
- * library allocates and frees no device memory.  Kernels are enqueued on
+ * library allocates and frees no device memory; its per-stream slots are
+ * static device memory of its code objects (about 42 MB per device, loaded
+ * with the library).  Kernels are enqueued on
  * `stream` (a hipStream_t; NULL is the null stream) of the current device.
  * OVERWRITE and FOLD calls are asynchronous: buffers must stay alive until
  * the stream's work has completed.  Between calls the library keeps only
