@@ -950,7 +950,7 @@ int run_typed(const Launch &L)
     if (hipGetLastError() != hipSuccess)
         return ST_HIP;
 
-    // second launches, unless the last block to arrive finished the call
+    // second launches, unless the call finished inside its first launch
     if ((L.kernel == K_ALL || L.kernel == K_ALL_STRIDED) && L.all.grid > 1 && L.all.arrive_slot < 0) {
         hipLaunchKernelGGL((k_all_pass2<Acc, Op, tune::kPass2Block>), dim3(1), dim3(tune::kPass2Block), 0,
                            st, static_cast<Acc *>(L.all.ws), L.all.grid, L.all.fin);
