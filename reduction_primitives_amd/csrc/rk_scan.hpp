@@ -635,34 +635,42 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     if (threadIdx.x == 0)
         s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int64_t g = s_id;
-    if (g >= a.tiles) {                        // never: the counter starts at zero every call
+    const uint32_t gu = s_id;
+    if (gu >= a.tiles) {                       // never: the counter starts at zero every call
         if (threadIdx.x == 0)
             __hip_atomic_store(st.timeout, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const int64_t t = g / a.col_tiles;                 // chunk along the scan dim
-    const int64_t ct = g - t * a.col_tiles;            // tile across the lines
-    const int64_t run = ct / a.col_tiles_per_run;
-    const int64_t col0 = (ct - run * a.col_tiles_per_run) * W;
+    // tile numbers fit 32 bits (the plan refuses more), so they split in 32-bit
+    // arithmetic: chunk t along the scan dim, tile ct across the lines
+    const uint32_t t32 = gu / (uint32_t)a.col_tiles;
+    const uint32_t ct32 = gu - t32 * (uint32_t)a.col_tiles;
+    const uint32_t run32 = ct32 / (uint32_t)a.col_tiles_per_run;
+    const int64_t g = gu, t = t32, ct = ct32;
+    const int64_t col0 = int64_t(ct32 - run32 * (uint32_t)a.col_tiles_per_run) * W;
     const int c = (int)(threadIdx.x % CL), rg = (int)(threadIdx.x / CL);
     const int64_t run_len = a.kept_ext[0];
     const int64_t col = col0 + int64_t(c) * V;
     const bool active = col < run_len;                 // 16-byte loads: run_len % V == 0
-    const S *x = static_cast<const S *>(a.x) +
-                 layout_offset(a.kept_nd - 1, a.kept_ext + 1, a.kept_in + 1, run) + col;
-    const int64_t ob = layout_offset(a.kept_nd - 1, a.kept_ext + 1, a.kept_out + 1, run) + col;
     const int64_t r0 = t * R + int64_t(rg) * RPG;
+    // this thread's positions r0 .. r0+nv-1 exist (none for lines past the run);
+    // one count instead of a 64-bit row index per position keeps registers free
+    const int nv = active ? (int)(a.m - r0 < RPG ? (a.m - r0 > 0 ? a.m - r0 : 0) : RPG) : 0;
+    const S *x = static_cast<const S *>(a.x) +
+                 layout_offset(a.kept_nd - 1, a.kept_ext + 1, a.kept_in + 1, int64_t(run32)) + col;
+    const int64_t xo = r0 * a.s_in;
+    const int64_t ob = layout_offset(a.kept_nd - 1, a.kept_ext + 1, a.kept_out + 1, int64_t(run32)) + col +
+                       r0 * a.s_out;
 
     Raw raw[RPG];
 #pragma unroll
     for (int q = 0; q < RPG; ++q) {
         raw[q] = Raw{};
-        if (active && r0 + q < a.m) {
+        if (q < nv) {
             if constexpr (VECTOR)
-                raw[q] = load16(reinterpret_cast<const u32x4 *>(x + (r0 + q) * a.s_in));
+                raw[q] = load16(reinterpret_cast<const u32x4 *>(x + (xo + q * a.s_in)));
             else
-                raw[q] = load1(x + (r0 + q) * a.s_in);
+                raw[q] = load1(x + (xo + q * a.s_in));
         }
     }
     issue_barrier();
@@ -673,7 +681,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
 #pragma unroll
     for (int q = 0; q < RPG; ++q) {
         Acc e[V];
-        Chunk<In, Acc, Op, V>::decode(raw[q], active && r0 + q < a.m, e);
+        Chunk<In, Acc, Op, V>::decode(raw[q], q < nv, e);
 #pragma unroll
         for (int i = 0; i < V; ++i)
             tot[i] = Op::apply(tot[i], e[i]);
@@ -682,24 +690,32 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     for (int i = 0; i < V; ++i)
         s_part[rg][c * V + i] = tot[i];
     __syncthreads();
-    // offset of this row group and the tile's aggregate, per line
+    // offset of this row group and the tile's aggregate, per line.  The loop
+    // over row groups stays rolled: unrolled, every running value would stay
+    // live until the pick by rg (RG * V registers on top of the raw loads).
     Acc gpre[V], agg[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         gpre[i] = Op::template identity<Acc>();
         agg[i] = Op::template identity<Acc>();
-        for (int k = 0; k < RG; ++k) {
+    }
+#pragma unroll 1
+    for (int k = 0; k < RG; ++k) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
             if (k == rg)
                 gpre[i] = agg[i];
             agg[i] = Op::apply(agg[i], s_part[k][c * V + i]);
         }
     }
-    const int64_t slot = g * W + int64_t(c) * V;       // this thread's values of tile g
+    // tile g's W partials, packed as Acc, element i of thread c at i * CL + c:
+    // the stores go through to memory, so one instruction must cover whole lines
+    const int64_t slot = g * W + c;
     if (t > 0) {
         if (rg == 0 && active) {
 #pragma unroll
             for (int i = 0; i < V; ++i)
-                store_partial(reinterpret_cast<Acc *>(st.aggs + slot + i), agg[i]);
+                store_partial(reinterpret_cast<Acc *>(st.aggs) + slot + i * CL, agg[i]);
             wait_stores();
         }
         __syncthreads();
@@ -750,11 +766,11 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
                 for (int q = 0; q < K; ++q) {
                     const int64_t j = top - q;
                     if (q <= first && j >= 0) {
-                        const uint64_t *src = f[q] == kFlagPrefix ? st.pres : st.aggs;
-                        const int64_t js = (j * a.col_tiles + ct) * W + int64_t(c) * V;
+                        const Acc *src = reinterpret_cast<const Acc *>(f[q] == kFlagPrefix ? st.pres : st.aggs);
+                        const int64_t js = (j * a.col_tiles + ct) * W + c;
 #pragma unroll
                         for (int i = 0; i < V; ++i)
-                            acc[i] = Op::apply(load_partial(reinterpret_cast<const Acc *>(src + js + i)), acc[i]);
+                            acc[i] = Op::apply(load_partial(src + js + i * CL), acc[i]);
                     }
                 }
                 if (first < K)
@@ -766,7 +782,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
         for (int i = 0; i < V; ++i) {
             s_excl[c * V + i] = acc[i];
             if (active)
-                store_partial(reinterpret_cast<Acc *>(st.pres + slot + i), Op::apply(acc[i], agg[i]));
+                store_partial(reinterpret_cast<Acc *>(st.pres) + slot + i * CL, Op::apply(acc[i], agg[i]));
         }
         wait_stores();
     }
@@ -785,9 +801,8 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
         runv[i] = Op::apply(s_excl[c * V + i], gpre[i]);
 #pragma unroll
     for (int q = 0; q < RPG; ++q) {
-        const int64_t r = r0 + q;
         Acc e[V], o[V];
-        Chunk<In, Acc, Op, V>::decode(raw[q], active && r < a.m, e);
+        Chunk<In, Acc, Op, V>::decode(raw[q], q < nv, e);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             if (a.inclusive) {
@@ -798,8 +813,8 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
                 runv[i] = Op::apply(runv[i], e[i]);
             }
         }
-        if (active && r < a.m)
-            store_run<Acc, V, true>(a.out, ob + r * a.s_out, a.out_dtype, o);
+        if (q < nv)
+            store_run<Acc, V, true>(a.out, ob + q * a.s_out, a.out_dtype, o);
     }
     scan_release(st, a.ws, a.tiles);
 }

@@ -31,11 +31,11 @@ constexpr int64_t kScanTileMinLen = 4096;
 constexpr int kScanSpinLimit = 1 << 24;   // look-back: sleeps per wait before giving up (about a second)
 // columns scan (strided scan dim, contiguous lines): a tile is W lines x R
 // scan positions; W = lanes * elements per 16-byte load
-constexpr int kScanColBlock = 512;        // threads per block (8192x8192 f32 dims=2: 119.7 us against
-                                          // 123.8 us at 256 threads, 252.9 us at 1024 with spills)
+constexpr int kScanColBlock = 512;        // threads per block (8192x8192 f32 dims=2: 105.4 us against
+                                          // 110.6 us at 256 threads and 110.7 us at 1024)
 constexpr int kScanColLanes = 32;         // lanes across a tile row with 16-byte loads (512-byte rows)
 constexpr int kScanColLanesScalar = 64;   //   ... with element loads
-constexpr int kScanColRows = 16;          // consecutive scan positions per thread
+constexpr int kScanColRows = 16;          // consecutive scan positions per thread (8: 125.7 us at 1024 threads)
 constexpr int64_t kScanColMinRun = 16;    // runs of lines narrower than this take the lines kernel
 }  // namespace tune
 
@@ -68,7 +68,9 @@ struct ScanArgs {
 // Columns-scan state: a 256-byte header (as the tile scan's), the flags --
 // 32-bit words, the flag of tile g at word (g % lines) * 32 + g / lines,
 // lines = ceil(tiles / 32), so consecutive tiles sit in different 128-byte
-// lines -- then `width` 8-byte aggregates per tile and as many prefixes.
+// lines -- then room for `width` 8-byte aggregates per tile and as many
+// prefixes.  The kernel packs them at its accumulator's width, a tile's
+// values in line order of the threads that store them.
 constexpr int kScanFlagCapacity = 8192;  // tiles whose flags fit one library slot
 constexpr int64_t scan_flag_lines(int64_t tiles) { return (tiles + 31) / 32; }
 constexpr int64_t scan_columns_state_bytes(int64_t tiles, int64_t width)
