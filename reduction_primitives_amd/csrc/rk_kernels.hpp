@@ -635,7 +635,10 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
     using S = typename InTraits<In>::S;
     constexpr int V = InTraits<In>::vec;
     const int lane = lane_id();
-    const int64_t unit = int64_t(blockIdx.x) * (BLOCK / 64) + (threadIdx.x >> 6);
+    // the wave's number, read as uniform so that the index arithmetic below
+    // runs on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t unit = int64_t(blockIdx.x) * (BLOCK / 64) + wave;
     if (unit >= a.n_out * a.split)
         return;                                 // whole wave; no block barrier below
     const int64_t o = unit / a.split;
@@ -683,14 +686,26 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
             }
         }
         if (i < nv) {                           // last, partial group, loads together
+            // this lane's loads in the group, one count rather than a 64-bit
+            // index per load; lane 0 needs the most, and no lane needs fewer
+            // than one less.  Loads up to lane 0's count are issued by the whole
+            // wave (a uniform branch), a lane's extra one at its first vector,
+            // and each lane folds its own.  Each vector holds zero where its load
+            // is skipped: left undefined there, every one kept registers of its
+            // own (170 VGPRs in all, against 94).
+            const int nu = (int)((nv - i + 63) / 64);
+            const int nw = __builtin_amdgcn_readfirstlane(nu);
             u32x4 w[UNROLL];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                if (i + u * 64 < nv)
-                    w[u] = load16(body + i + u * 64);
+            for (int u = 0; u < UNROLL; ++u) {
+                w[u] = u32x4{0u, 0u, 0u, 0u};
+                if (u < nw)
+                    w[u] = load16(body + i + (u < nu ? u * 64 : 0));
+            }
+            issue_barrier();
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u)
-                if (i + u * 64 < nv)
+                if (u < nu)
                     fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
         }
         if (lane < head)

@@ -581,7 +581,10 @@ __global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
     constexpr int V = C::V;
     constexpr int UC = U * (InTraits<In>::vec / VL);
     constexpr int64_t CH = 64 * V;
-    const int64_t line = int64_t(blockIdx.x) * (BLOCK / 64) + (threadIdx.x >> 6);
+    // the wave's number, read as uniform so that the index arithmetic runs on
+    // the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t line = int64_t(blockIdx.x) * (BLOCK / 64) + wave;
     if (line >= a.lines)
         return;                                // whole wave; no block barrier below
     const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
