@@ -486,7 +486,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_clear(uint32_t *w, int64_t words
 // Tile kernel: a tile is NW waves x UC chunks of consecutive elements of one
 // line; tiles are numbered by a counter in the order blocks start.
 template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = false>
-__global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_tile(ScanArgs a)
 {
     using C = Chunk<In, Acc, Op, VL>;
     using S = typename C::S;
@@ -513,13 +513,20 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
     const int64_t t = g - line * a.tiles_per_line;
     const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
     const int64_t ob = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
-    const int w = (int)(threadIdx.x >> 6);
+    // the wave's number, read as uniform so that its arithmetic is scalar
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t first = t * T + int64_t(w) * UC * CH + int64_t(lane_id()) * V;
+    // this lane's chunks inside the line, a count rather than a 64-bit index
+    // per chunk held from the loads to the stores
+    const int nk = first < a.m ? (int)((a.m - first + CH - 1) / CH < UC ? (a.m - first + CH - 1) / CH : UC) : 0;
 
     typename C::Raw raw[UC];
 #pragma unroll
-    for (int k = 0; k < UC; ++k)
-        raw[k] = C::load(x, first + k * CH, a.m);
+    for (int k = 0; k < UC; ++k) {
+        raw[k] = typename C::Raw{};
+        if (k < nk)
+            raw[k] = C::load(x, first + k * CH, a.m);
+    }
     issue_barrier();
 
     // the wave's total first (the look-back needs only the tile's); the
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
 #pragma unroll
     for (int k = 0; k < UC; ++k) {
         Acc e[V];
-        C::decode(raw[k], first + k * CH < a.m, e);
+        C::decode(raw[k], k < nk, e);
 #pragma unroll
         for (int i = 0; i < V; ++i)
             lt = Op::apply(lt, e[i]);
@@ -559,13 +566,12 @@ __global__ __launch_bounds__(BLOCK) void k_scan_tile(ScanArgs a)
     Acc carry = Op::apply(s_excl, wpre);
 #pragma unroll
     for (int k = 0; k < UC; ++k) {
-        const int64_t i = first + k * CH;
         Acc e[V], o[V], lane_excl, total;
-        C::decode(raw[k], i < a.m, e);
+        C::decode(raw[k], k < nk, e);
         chunk_scan<Acc, Op, V>(e, lane_excl, total);
         chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl), a.inclusive != 0, o);
-        if (i < a.m)
-            store_run<Acc, V, NTS>(a.out, ob + i, a.out_dtype, o);
+        if (k < nk)
+            store_run<Acc, V, NTS>(a.out, ob + first + k * CH, a.out_dtype, o);
         carry = Op::apply(carry, total);
     }
     tile_release(st, a.ws, a.tiles);
