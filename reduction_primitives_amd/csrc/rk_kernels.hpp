@@ -532,25 +532,39 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
         // the last, partial group (fewer than UNROLL rows left per thread),
         // still with all of its loads in flight together
         if (j < j1) {
+            // this thread's rows in the group, a count rather than a 64-bit
+            // index per load; registers zeroed where a load is skipped, so the
+            // group shares the registers of the full ones (f32: 56 VGPRs against
+            // 88).  Not with 64 bytes of accumulators per lane (2-byte inputs
+            // into 8-byte ones), where zeroing spilled instead.
+            const int nu = (int)((j1 - j + RG - 1) / RG);
             if constexpr (VECTOR) {
+                constexpr bool kZero = V * sizeof(Acc) <= 32;
                 u32x4 w[UNROLL];
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
-                    if (j + int64_t(u) * RG < j1)
+                for (int u = 0; u < UNROLL; ++u) {
+                    if constexpr (kZero)
+                        w[u] = u32x4{0u, 0u, 0u, 0u};
+                    if (u < nu)
                         w[u] = load16<NT>(reinterpret_cast<const u32x4 *>(x + (j + int64_t(u) * RG) * s));
+                }
+                issue_barrier();
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
-                    if (j + int64_t(u) * RG < j1)
+                    if (u < nu)
                         fold_vec<In, Acc, Op, Map, V>(acc0, w[u]);
             } else {
                 S w[UNROLL];
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
-                    if (j + int64_t(u) * RG < j1)
+                for (int u = 0; u < UNROLL; ++u) {
+                    w[u] = S{};
+                    if (u < nu)
                         w[u] = load1<NT>(x + (j + int64_t(u) * RG) * s);
+                }
+                issue_barrier();
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
-                    if (j + int64_t(u) * RG < j1)
+                    if (u < nu)
                         acc0[0] = Op::apply(acc0[0], Map::apply(InTraits<In>::template one<Acc>(w[u])));
             }
         }
@@ -687,20 +701,17 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
         }
         if (i < nv) {                           // last, partial group, loads together
             // this lane's loads in the group, one count rather than a 64-bit
-            // index per load; lane 0 needs the most, and no lane needs fewer
-            // than one less.  Loads up to lane 0's count are issued by the whole
-            // wave (a uniform branch), a lane's extra one at its first vector,
-            // and each lane folds its own.  Each vector holds zero where its load
-            // is skipped: left undefined there, every one kept registers of its
-            // own (170 VGPRs in all, against 94).
+            // index per load.  Each vector holds zero where its load is
+            // skipped: left undefined there, every one kept registers of its
+            // own (170 VGPRs in all, against 94).  No load is issued twice: the
+            // loads bypass the cache, so a repeat is fetched from memory again.
             const int nu = (int)((nv - i + 63) / 64);
-            const int nw = __builtin_amdgcn_readfirstlane(nu);
             u32x4 w[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 w[u] = u32x4{0u, 0u, 0u, 0u};
-                if (u < nw)
-                    w[u] = load16(body + i + (u < nu ? u * 64 : 0));
+                if (u < nu)
+                    w[u] = load16(body + i + u * 64);
             }
             issue_barrier();
 #pragma unroll
