@@ -407,7 +407,8 @@ int64_t scan_tile_elems(int in_dtype, int block)
     const int isz = dtype_size(in_dtype);
     if (isz == 0)
         return 0;
-    return int64_t(block / 64) * tune::kScanUnroll * 64 * (16 / isz);
+    const int unroll = block == tune::kScanTileBlock ? tune::kScanTileUnroll : tune::kScanUnroll;
+    return int64_t(block / 64) * unroll * 64 * (16 / isz);
 }
 
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,

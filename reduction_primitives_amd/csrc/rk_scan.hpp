@@ -883,6 +883,7 @@ int run_scan_typed(const ScanLaunch &L)
     constexpr int B = tune::kScanBlock;
     constexpr int BT = tune::kScanTileBlock;
     constexpr int U = tune::kScanUnroll;
+    constexpr int UT = tune::kScanTileUnroll;
     constexpr int BC = tune::kScanColBlock;
     if (L.kernel == SK_COLUMNS ? L.block != BC : (L.block != B && !(L.kernel == SK_TILE && L.block == BT)))
         return ST_INVALID;
@@ -901,15 +902,15 @@ int run_scan_typed(const ScanLaunch &L)
     case SK_TILE: {
         if (L.args.slot < 0)
             clear_state(L.args, scan_tile_state_bytes(L.args.tiles) / 4, st);
-#define RK_SCAN_TILE(BK, VLN) launch_first(&k_scan_tile<In, Acc, Op, BK, U, VLN, true>, grid, block, st, ev, L.args)
+#define RK_SCAN_TILE(BK, UK, VLN) launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true>, grid, block, st, ev, L.args)
         if (L.block == BT) {
-            if (vl == VV) RK_SCAN_TILE(BT, VV);
-            else if (vl == VW) RK_SCAN_TILE(BT, VW);
+            if (vl == VV) RK_SCAN_TILE(BT, UT, VV);
+            else if (vl == VW) RK_SCAN_TILE(BT, UT, VW);
             else return ST_INVALID;             // element loads take the small tiles
         } else {
-            if (vl == VV) RK_SCAN_TILE(B, VV);
-            else if (vl == VW) RK_SCAN_TILE(B, VW);
-            else RK_SCAN_TILE(B, 1);
+            if (vl == VV) RK_SCAN_TILE(B, U, VV);
+            else if (vl == VW) RK_SCAN_TILE(B, U, VW);
+            else RK_SCAN_TILE(B, U, 1);
         }
 #undef RK_SCAN_TILE
         break;

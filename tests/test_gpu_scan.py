@@ -9,11 +9,11 @@ and permuted views, in-place scans, and the 10^8-element and 8192x8192 sizes.
 
 Bar: integers, and max/min of any type, bit-exact.  A floating-point sum
 output k of a line comes out of a tree of rounded additions in the
-accumulator type; its depth is at most the number of tiles before it on the
-line plus 64 (look-back chain, then the tile's waves, chunks and lanes), so
-|gpu - R_k| <= (t_k + 64) * u * S_k with u = 2^-24 (f32) or 2^-53 (f64) and
-S_k = |s| + sum of |x_j| up to k; a bf16 / f16 output adds its own rounding
-(8e-3 / 1e-3 relative, as for the reductions).
+accumulator type, so |gpu - R_k| <= D_k * u * S_k with u = 2^-24 (f32) or
+2^-53 (f64), S_k = |s| + sum of |x_j| up to k, and D_k the number of
+additions any term passes through on its way to output k, which `_depth`
+bounds for each kernel from its association order; a bf16 / f16 output adds
+its own rounding (8e-3 / 1e-3 relative, as for the reductions).
 """
 import math
 
@@ -51,6 +51,36 @@ def _abs_prefix(storage_cpu, shape, strides, dim, in_c, start, inclusive):
     if not inclusive:
         c = np.concatenate([np.zeros(c.shape[:-1] + (1,)), c[..., :-1]], axis=-1)
     return np.moveaxis(c, -1, dim).reshape(-1, order="F") + abs(float(start))
+
+
+def _depth(plan, k):
+    """Upper bound on the rounded additions a term passes through on its way
+    to output k of a line (k counts from 0 along the scan dim), from each
+    kernel's association order."""
+    name, blk = plan["kernel_name"], plan["block"]
+    v, tile = max(plan["vec"], 1), max(plan["tile_outputs"], 1)
+    if name == "scan_tile":
+        e, nw = tile // blk, blk // 64          # elements per lane of a tile, waves
+        # a tile's aggregate: a lane folds its e elements, 6 levels across the
+        # wave, then the waves in order; the look-back adds one term per tile
+        # before it; inside the tile an output takes the waves before it, the
+        # prefix, the chunk totals before it (e / v), the lane offset (its
+        # lanes' v elements and 6 levels) and its lane's own elements
+        return k // tile + (e + 6 + nw) + (nw + 1 + e // v + (v + 6) + 1 + v)
+    if name == "scan_rowwave":
+        # one carry per chunk of 64 * v elements, then the lane offset and the
+        # lane's own elements
+        return k // (64 * v) + (v + 6) + 1 + v + 1
+    if name == "scan_columns":
+        lanes = 32 if v > 1 else 64
+        rows = tile // (lanes * v)              # scan positions per tile
+        rg = blk // lanes                       # row groups
+        rpg = rows // rg                        # positions per thread
+        # aggregate: a thread's positions, then the row groups in order; the
+        # look-back chain; in the tile the row groups before it, the prefix and
+        # the thread's positions up to k
+        return k // rows + (rpg + rg) + (rg + 1 + rpg) + 1
+    return k + 1                                # lines: one thread walks the line
 
 
 def scan_and_check(storage_cpu, shape=None, strides=None, dim=1, op="sum", acc=None, out_dtype=None,
@@ -96,9 +126,8 @@ def scan_and_check(storage_cpu, shape=None, strides=None, dim=1, op="sum", acc=N
     m = shape[dim - 1]
     k = np.moveaxis(np.broadcast_to(np.arange(m).reshape([-1 if d == dim - 1 else 1 for d in range(len(shape))]),
                                     shape), dim - 1, dim - 1).reshape(-1, order="F")
-    tile = max(plan["tile_outputs"], 1)
     u = 2.0**-24 if acc_c == O.F32 else 2.0**-53
-    tol = (k // tile + 64) * u * S
+    tol = _depth(plan, k) * u * S
     if out_c == O.BF16:
         tol = tol + 8e-3 * np.abs(R)
     elif out_c == O.F16:
@@ -111,7 +140,7 @@ def scan_and_check(storage_cpu, shape=None, strides=None, dim=1, op="sum", acc=N
     return plan
 
 
-TILE = 16 * 8 * 64 * 4          # f32 elements per scan tile: 16 waves x 8 chunks x 64 lanes x 4
+TILE = 16 * 16 * 64 * 4         # f32 elements per scan tile: 16 waves x 16 chunks x 64 lanes x 4
 
 
 # ------------------------------------------------------------ whole arrays
@@ -141,6 +170,29 @@ def test_whole_array_offsets(offset):
     scan_and_check(x, offset=offset, op="max", inclusive=False)
     xh = W.normal(n + offset, 11400 + offset, torch.float16)
     scan_and_check(xh, offset=offset, out_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("combo,n", [
+    ((torch.int32, torch.int64, torch.int64), 2 * 10**7 + 2),
+    ((torch.float32, torch.float64, torch.float64), 2 * 10**7 + 2),
+    ((torch.bfloat16, torch.float32, torch.float32), 4 * 10**7 + 4)], ids=["i32-i64", "f32-f64", "bf16-f32"])
+def test_large_tiles_wide_outputs(combo, n):
+    """Outputs wider than the inputs on the 1024-thread tiles: a lane loads as
+    many elements as make 16 bytes of output, over 300 tiles with a ragged
+    last one."""
+    rk = _rk()
+    tin, tacc, tout = combo
+    if tin == torch.int32:
+        x = W.randint(n, -10**6, 10**6, 11900)
+    elif tin == torch.bfloat16:
+        x = W.normal(n, 11901, torch.bfloat16)
+    else:
+        x = W.uniform(n, -1.0, 1.0, 11902)
+    plan = scan_and_check(x, acc=tacc, out_dtype=tout, expect_kernel="scan_tile")
+    assert plan["block"] == 1024 and plan["vec"] == 16 // tout.itemsize
+    assert plan["split"] > 300 and n % plan["tile_outputs"] != 0
+    if tin == torch.int32:
+        scan_and_check(x, op="max", acc=tacc, out_dtype=tout, inclusive=False)
 
 
 COMBOS = [  # (input, accumulator, output)

@@ -312,7 +312,8 @@ def test_stream_read_validation():
 def test_scan_plans():
     import reduction_primitives_amd as rk
     f32 = rk.RK_F32
-    tile = 16 * 8 * 64 * 4                      # waves * chunks * lanes * floats per 16 bytes
+    tile = 16 * 16 * 64 * 4                     # waves * chunks * lanes * floats per 16 bytes
+    small = 4 * 8 * 64 * 4                      # 256-thread tiles: 4 waves of 8 chunks
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.tile_outputs == tile and p.vec == 4
     assert p.split == (10**8 + tile - 1) // tile and p.grid == p.split
@@ -347,13 +348,13 @@ def test_scan_plans():
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 256 and p.split == 1
     # fewer large tiles than CUs: quarter-size tiles of 256-thread blocks
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**6], [1], 0, 256)
-    assert p.block == 256 and p.tile_outputs == tile // 4 and p.split == -(-10**6 // (tile // 4))
+    assert p.block == 256 and p.tile_outputs == small and p.split == -(-10**6 // small)
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [10**8], [1], 0, 256).block == 1024
     # 8192 x 8192 along dims=1 (8192 contiguous lines: a wave each) and dims=2 (strided)
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.n_out == 8192 * 8192
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [tile, 8], [1, tile], 0, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 4 and p.grid == 32
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == tile // small and p.grid == 8 * (tile // small)
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [tile, 300], [1, tile], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.split == 1 and p.grid == 300 and p.block == 1024
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8192, 8192], [1, 8192], 1, 256)
