@@ -23,7 +23,7 @@ constexpr int kScanTileBlock = 1024;      // tile kernel: 16 waves share a tile 
                                           // amortise the look-back; 1e8 f32: 177 us vs 236 us at 256);
                                           // kScanBlock-thread tiles when the large ones number < CUs
 constexpr int kScanTileUnroll = 16;       // 16-byte chunks per lane of a large tile (10^8 f32 cumsum: 151.7 us
-                                          // against 165.7 at 8; the look-back costs per tile)
+                                          // against 165.7 at 8 and 157.5 at 24; the look-back costs per tile)
 constexpr int kScanUnroll = 8;            // 16-byte chunks in flight per lane (quarter tiles, row-wave kernel)
 constexpr int kScanLinesUnroll = 8;       // elements in flight per thread (lines kernel)
 constexpr int kScanLinesBlocksPerCu = 8;  // lines kernel grid cap
