@@ -115,7 +115,7 @@ def test_two_input_workspace():
 
 
 @pytest.mark.parametrize("shape,strides,dim", [
-    ((10**8,), (1,), 1),                    # tile kernel, 3,052 tiles
+    ((10**8,), (1,), 1),                    # tile kernel, 1,526 tiles
     ((100003, 3), (1, 100003), 1),          # tile kernel, look-back per line
     ((8192, 8192), (1, 8192), 2),           # columns kernel, 16-byte loads
     ((130, 2000), (1, 131), 2),             # columns kernel, element loads
