@@ -884,6 +884,7 @@ int run_scan_typed(const ScanLaunch &L)
     constexpr int BT = tune::kScanTileBlock;
     constexpr int U = tune::kScanUnroll;
     constexpr int UT = tune::kScanTileUnroll;
+    constexpr int UW = tune::kScanWaveUnroll;
     constexpr int BC = tune::kScanColBlock;
     if (L.kernel == SK_COLUMNS ? L.block != BC : (L.block != B && !(L.kernel == SK_TILE && L.block == BT)))
         return ST_INVALID;
@@ -917,9 +918,9 @@ int run_scan_typed(const ScanLaunch &L)
     }
     case SK_ROWWAVE:
         if (vl == VV)
-            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, VV>, grid, block, st, ev, L.args);
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, UW, VV>, grid, block, st, ev, L.args);
         else if (vl == VW)
-            launch_first(&k_scan_rowwave<In, Acc, Op, B, U, VW>, grid, block, st, ev, L.args);
+            launch_first(&k_scan_rowwave<In, Acc, Op, B, UW, VW>, grid, block, st, ev, L.args);
         else
             launch_first(&k_scan_rowwave<In, Acc, Op, B, U, 1>, grid, block, st, ev, L.args);
         break;
