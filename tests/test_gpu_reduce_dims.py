@@ -187,6 +187,20 @@ def test_selector_kernels_max_fold_int(case):
     dims_and_check(xf, shape, CM(shape), dims, map_="square", init=2.0)
 
 
+@pytest.mark.parametrize("case", SELECTOR_CASES, ids=lambda c: c[4].replace(" ", "_"))
+def test_selector_kernels_wide_accumulators(case):
+    """Each kernel with float64 accumulators over bf16 and f32 inputs: a bf16
+    lane's 16-byte load widens into 8 doubles, the widest accumulator state a
+    kernel holds; ragged row groups take the last, partial group."""
+    shape, dims, _, _, _ = case
+    n = math.prod(shape)
+    for dt in (torch.bfloat16, torch.float32):
+        x = W.normal(n, 8500 + n % 79, dt)
+        dims_and_check(x, shape, CM(shape), dims, acc=torch.float64, out_dtype=torch.float64)
+    x = W.normal(n, 8600 + n % 73, torch.bfloat16)
+    dims_and_check(x, shape, CM(shape), dims, op="max", acc=torch.float64, out_dtype=torch.bfloat16)
+
+
 # ------------------------------------------------------------------ layouts
 
 @pytest.mark.parametrize("offset", [1, 2, 3, 5])
