@@ -703,7 +703,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
             // this lane's loads in the group, one count rather than a 64-bit
             // index per load.  Each vector holds zero where its load is
             // skipped: left undefined there, every one kept registers of its
-            // own (170 VGPRs in all, against 94).  No load is issued twice: the
+            // own (170 VGPRs in all, against 91).  No load is issued twice: the
             // loads bypass the cache, so a repeat is fetched from memory again.
             const int nu = (int)((nv - i + 63) / 64);
             u32x4 w[UNROLL];
