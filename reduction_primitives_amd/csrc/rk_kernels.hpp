@@ -341,11 +341,13 @@ __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
         // chunk i + 1.  The plan stops the body one chunk before y's last
         // whole one, so chunk i + 1 always lies inside y.
         const u32x4 *bx = reinterpret_cast<const u32x4 *>(x + a.head);
-        const uintptr_t yaddr = reinterpret_cast<uintptr_t>(y + a.head);
+        const S *yh = y + a.head;
         // sb = K * 4 + r bytes: K whole dwords (a template argument), r = 2
-        // only for 2-byte elements
-        const int sb = (int)(yaddr & 15);
-        const u32x4 *by = reinterpret_cast<const u32x4 *>(yaddr - uintptr_t(sb));
+        // only for 2-byte elements.  The aligned base comes from pointer
+        // arithmetic, not from an integer: a pointer rebuilt from an integer
+        // loses its global address space, and its loads compile to flat ones.
+        const int sb = (int)(reinterpret_cast<uintptr_t>(yh) & 15);
+        const u32x4 *by = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(yh) - sb);
         constexpr bool HALF = sizeof(S) == 2;
         const uint32_t r = uint32_t(sb & 3);
         const int lane = (int)(threadIdx.x & 63);
