@@ -402,13 +402,13 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
 
 // ------------------------------------------------------------------ scans
 
-int64_t scan_tile_elems(int in_dtype, int block)
+int64_t scan_tile_elems(int in_dtype, int block, int vl)
 {
     const int isz = dtype_size(in_dtype);
-    if (isz == 0)
+    if (isz == 0 || vl < 1)
         return 0;
     const int unroll = block == tune::kScanTileBlock ? tune::kScanTileUnroll : tune::kScanUnroll;
-    return int64_t(block / 64) * unroll * 64 * (16 / isz);
+    return int64_t(block / 64) * scan_lane_chunks(unroll, 16 / isz, vl) * 64 * vl;
 }
 
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
@@ -468,7 +468,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         for (int i = 0; i < k.nd; ++i)
             vec_ok = vec_ok && (k.str[i] * isz) % lb == 0 && (d.kept_out[i] * osz) % ob == 0;
         d.vec = vec_ok ? vl : 1;
-        d.tile_elems = scan_tile_elems(in_dtype, tune::kScanTileBlock);
+        d.tile_elems = scan_tile_elems(in_dtype, tune::kScanTileBlock, d.vec);
         const bool few_lines = d.lines < int64_t(num_cus) * tune::kScanTileFewLines;
         if (d.m >= d.tile_elems || (few_lines && d.m >= tune::kScanTileMinLen)) {
             d.kernel = SK_TILE;
@@ -478,7 +478,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             // would need more than the 128 registers a 1024-thread block allows)
             if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus || d.vec == 1) {
                 d.block = tune::kScanBlock;
-                d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock);
+                d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock, d.vec);
             }
             d.tiles_per_line = ceil_div(d.m, d.tile_elems);
             d.tiles = d.lines * d.tiles_per_line;

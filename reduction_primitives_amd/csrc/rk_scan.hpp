@@ -491,7 +491,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     using C = Chunk<In, Acc, Op, VL>;
     using S = typename C::S;
     constexpr int V = C::V;
-    constexpr int UC = U * (InTraits<In>::vec / VL);         // chunks per wave: a tile is the same size for any VL
+    constexpr int UC = scan_lane_chunks(U, InTraits<In>::vec, VL);   // chunks per lane (the plan's tile size)
     constexpr int64_t CH = 64 * V;
     constexpr int NW = BLOCK / 64;
     constexpr int64_t T = int64_t(NW) * UC * CH;
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
     using C = Chunk<In, Acc, Op, VL>;
     using S = typename C::S;
     constexpr int V = C::V;
-    constexpr int UC = U * (InTraits<In>::vec / VL);
+    constexpr int UC = scan_lane_chunks(U, InTraits<In>::vec, VL);
     constexpr int64_t CH = 64 * V;
     // the wave's number, read as uniform so that the index arithmetic runs on
     // the scalar unit

@@ -24,6 +24,8 @@ constexpr int kScanTileBlock = 1024;      // tile kernel: 16 waves share a tile 
                                           // kScanBlock-thread tiles when the large ones number < CUs
 constexpr int kScanTileUnroll = 16;       // 16-byte chunks per lane of a large tile (10^8 f32 cumsum: 151.7 us
                                           // against 165.7 at 8 and 157.5 at 24; the look-back costs per tile)
+constexpr int kScanMaxChunks = 32;        // chunks a lane holds with vector loads: 64 (bf16 -> f64 at
+                                          // 16 chunks) went to scratch memory
 constexpr int kScanWaveUnroll = 16;       // chunks in flight per lane, row-wave kernel with vector loads (16
                                           // bytes of input or of output; 8192x8192 f32 dims=1: 93.0 us
                                           // against 104.0 at 8)
@@ -140,8 +142,16 @@ struct ScanPlan {
     size_t ws_bytes = 0;
 };
 
-// Elements of one scan tile for an input dtype and tile-kernel block size.
-int64_t scan_tile_elems(int in_dtype, int block);
+// Elements of one scan tile for an input dtype, tile-kernel block size and
+// lane load width vl (elements).
+// Chunks per lane of the tile and row-wave kernels: U chunks of the input's
+// 16-byte vector, counted in loads of vl elements, at most kScanMaxChunks
+// with vector loads.  Shared by the kernels and the plan's tile size.
+constexpr int scan_lane_chunks(int unroll, int vec, int vl)
+{
+    return vl > 1 && unroll * (vec / vl) > tune::kScanMaxChunks ? tune::kScanMaxChunks : unroll * (vec / vl);
+}
+int64_t scan_tile_elems(int in_dtype, int block, int vl);
 
 // Scan plan: `dim` is 0-based; addresses only matter through alignment.
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,

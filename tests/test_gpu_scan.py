@@ -175,11 +175,12 @@ def test_whole_array_offsets(offset):
 @pytest.mark.parametrize("combo,n", [
     ((torch.int32, torch.int64, torch.int64), 2 * 10**7 + 2),
     ((torch.float32, torch.float64, torch.float64), 2 * 10**7 + 2),
-    ((torch.bfloat16, torch.float32, torch.float32), 4 * 10**7 + 4)], ids=["i32-i64", "f32-f64", "bf16-f32"])
+    ((torch.bfloat16, torch.float32, torch.float32), 4 * 10**7 + 4),
+    ((torch.bfloat16, torch.float64, torch.float64), 2 * 10**7 + 2)], ids=["i32-i64", "f32-f64", "bf16-f32", "bf16-f64"])
 def test_large_tiles_wide_outputs(combo, n):
     """Outputs wider than the inputs on the 1024-thread tiles: a lane loads as
     many elements as make 16 bytes of output, over 300 tiles with a ragged
-    last one."""
+    last one (bf16 -> f64 holds its 32-chunk cap: half-size tiles)."""
     rk = _rk()
     tin, tacc, tout = combo
     if tin == torch.int32:
