@@ -342,6 +342,12 @@ def test_scan_plans():
     assert rk.rk_plan_scan(bf16, f32, bf16, 0, 0, 1, [10**6], [1], 0, 256).vec == 8
     assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 2, 1, [10**6], [1], 0, 256).vec == 1   # 2-byte aligned out
     assert rk.rk_plan_scan(f32, f32, rk.RK_BF16, 0, 8, 1, [10**6], [1], 0, 256).vec == 4
+    # large tiles: 16 chunks of the input's 16-byte vector per lane, counted in
+    # loads of `vec` elements and at most 32 of them (64 had gone to scratch)
+    n = 4 * 10**7
+    for tin, tacc, vec, lane_elems in ((bf16, f32, 4, 128), (bf16, f64, 2, 64), (i32, i64, 2, 64), (f32, f32, 4, 64)):
+        p = rk.rk_plan_scan(tin, tacc, tacc, 0, 0, 1, [n], [1], 0, 256)
+        assert p.block == 1024 and p.vec == vec and p.tile_outputs == 1024 * lane_elems, (tin, tacc)
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [4000], [1], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE and p.workspace_bytes == 0 and p.block == 256
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 1, [5000], [1], 0, 256)       # one short line: tiles
