@@ -469,7 +469,11 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 
     const int c = (int)(threadIdx.x % CL);
     const int rg = (int)(threadIdx.x / CL);
-    const uint32_t b = xcd_block(blockIdx.x, gridDim.x);
+    // neighbouring tiles on one XCD share its L2 where a tile row is narrower
+    // than a line (the tiled shape); columns tiles read whole lines, and
+    // spread round-robin over the XCDs they measured 0.5-2% faster
+    constexpr bool kColumns = NT && CL < BLOCK;
+    const uint32_t b = kColumns ? blockIdx.x : xcd_block(blockIdx.x, gridDim.x);
     const int64_t tile = int64_t(b % (uint64_t)a.tiles);
     const int sp = (int)(b / (uint64_t)a.tiles);
     const int64_t run = tile / a.tiles_per_run;
