@@ -83,6 +83,14 @@
  * returns a non-zero rk_status and writes nothing.  A HIP launch failure is
  * reported as RK_ERR_HIP.  The library prints nothing unless the environment
  * variable RK_DEBUG is set.
+ *
+ * Waits inside a launch: block 0 of a whole-array pass waits for the other
+ * blocks' partials, and a scan tile waits for its predecessors' prefixes.  No
+ * block waits on the block that waits for it, so these waits end; as a
+ * safety net each is bounded (about a second).  A wait that gives up stores
+ * no result (out keeps its previous contents; a scan's outputs after that
+ * tile are wrong) and is counted: HOST mode then returns RK_ERR_HIP, and
+ * rk_stream_timeouts reports the count for OVERWRITE, FOLD and scan calls.
  */
 #ifndef RK_H
 #define RK_H
@@ -124,7 +132,8 @@ typedef enum { RK_MODE_OVERWRITE = 0, RK_MODE_FOLD = 1, RK_MODE_HOST = 2 } rk_mo
  * strides[0] = 1, shape[0] = n) or rk_reduce_dims needs for this layout on the
  * current device.  For a whole array this is one accumulator per first-pass
  * block plus one for the bare final partial (PR #139, "What changes": the
- * workspace holds target_blocks + 1 partial results), rounded up to 256
+ * workspace holds target_blocks + 1 partial results) and a 4-byte word for
+ * host mode's copied-back result, rounded up to 256
  * bytes; for a dims reduction split across blocks it is split * n_out
  * accumulators; otherwise 0.  The contents need not be initialised and the
  * same workspace may be reused by later calls of any shape and type.
@@ -343,6 +352,32 @@ int rk_debug_stream_read(const void *ptr, int64_t nbytes, int grid, void *sink, 
  * width (bits), as the HIP runtime reports them.  Returns an rk_status
  * (RK_ERR_HIP without a usable device). */
 int rk_debug_device_info(int64_t *num_cus, int64_t *mem_clock_khz, int64_t *mem_bus_bits);
+
+/* How many waits inside launches gave up (see "Waits inside a launch" above)
+ * in calls on `stream` since the last query, plus those of calls on streams
+ * that have no library slot; the counts are cleared.  It waits for `stream`
+ * to drain (hipStreamSynchronize), then reads the library's counts with
+ * synchronous copies, so it must not be called during graph capture.  After
+ * a whole-array wait gave up it also clears the stream's tagged partials,
+ * so a block of that call that had not even started when the wait gave up
+ * cannot be taken for one of a later call.  `*count` receives the number
+ * (0 in every normal run).  Returns an rk_status: RK_ERR_INVALID_ARGUMENT
+ * for a NULL count, RK_ERR_HIP when the stream or a copy fails. */
+int rk_stream_timeouts(void *stream, uint64_t *count);
+
+/* Test hook: with polls >= 0, every later whole-array collection (split
+ * whole-array calls that finish in one launch) and scan look-back waits for
+ * a tag or flag that never comes and gives up after `polls` polls, as a real
+ * wait would after its bound; polls < 0 restores normal waits.  Every kernel
+ * still ends; the calls store no result or wrong scan outputs, and count
+ * their waits for rk_stream_timeouts.  Process-wide.  Returns an rk_status. */
+int rk_debug_force_wait_timeout(int64_t polls);
+
+/* Test hook: the next `count` reduction or scan calls that pass validation
+ * return RK_ERR_HIP where they would launch their first kernel, and launch
+ * nothing (out and workspace untouched), as after a launch the runtime
+ * rejected.  Process-wide; 0 switches it off.  Returns an rk_status. */
+int rk_debug_fail_launches(int count);
 
 #ifdef __cplusplus
 }

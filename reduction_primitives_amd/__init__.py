@@ -9,6 +9,7 @@ in the library's kernels; there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 
@@ -20,8 +21,8 @@ from ._native import (  # noqa: F401
     RK_KERNEL_TILED, RK_MAP2_ABSDIFF, RK_MAP2_MUL, RK_MAP2_SQDIFF,
     RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
     RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,
-    RkError, load, rk_debug_device_info, rk_debug_set_finish_tag, rk_debug_set_fused_finish,
-    rk_debug_set_launch_events,
+    RkError, load, rk_debug_device_info, rk_debug_fail_launches, rk_debug_force_wait_timeout,
+    rk_debug_set_finish_tag, rk_debug_set_fused_finish, rk_debug_set_launch_events, rk_stream_timeouts,
     rk_debug_stream_read, rk_plan_all, rk_plan_all2, rk_plan_dims,
     rk_plan_info, rk_plan_scan, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_scan, rk_scan_dims,
     rk_scan_workspace_size, rk_workspace_size, status_string)
@@ -104,6 +105,17 @@ def _stream_handle(stream, device_index=None):
     return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(device_index))
 
 
+def _on(stream):
+    """Allocate on `stream` when one is given: a buffer the call allocates
+    (workspace, output) then belongs to the stream its kernels run on, so
+    the caching allocator hands its bytes to no other stream's work before
+    those kernels are done (it is freed, or returned, while they may still
+    run)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def workspace_for(nbytes: int, device):
     torch = _torch()
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -129,8 +141,11 @@ def reduce_all(x, op="sum", map="identity", acc=None, out_dtype=None, init=None,
         out_code = acc_code
     op_c, map_c, mode_c = _code(OPS, op), _code(MAPS, map), _code(MODES, mode)
     n = x.numel()
-    if workspace is None:
-        workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), x.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), x.device)
+        if out is None and mode_c != RK_MODE_HOST:
+            out = torch.empty(1, dtype=torch_dtype(out_code), device=x.device)
     st = _stream_handle(stream, x.get_device())
     if mode_c == RK_MODE_HOST:
         buf = _CTYPE[out_code]()
@@ -139,8 +154,6 @@ def reduce_all(x, op="sum", map="identity", acc=None, out_dtype=None, init=None,
                            workspace.data_ptr(), st)
         _check(rc, "rk_reduce_all")
         return decode_host_out(buf, out_code)
-    if out is None:
-        out = torch.empty(1, dtype=torch_dtype(out_code), device=x.device)
     rc = rk_reduce_all(op_c, map_c, in_code, acc_code, out_code, x.data_ptr(), n,
                        init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
     _check(rc, "rk_reduce_all")
@@ -164,8 +177,11 @@ def reduce_all2(a, b, map2="mul", op="sum", acc=None, out_dtype=None, init=None,
         out_code = acc_code
     op_c, map_c, mode_c = _code(OPS, op), _code(MAPS2, map2), _code(MODES, mode)
     n = a.numel()
-    if workspace is None:
-        workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), a.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = workspace_for(rk_workspace_size(in_code, acc_code, 1, [n], [1], 1), a.device)
+        if out is None and mode_c != RK_MODE_HOST:
+            out = torch.empty(1, dtype=torch_dtype(out_code), device=a.device)
     st = _stream_handle(stream, a.get_device())
     if mode_c == RK_MODE_HOST:
         buf = _CTYPE[out_code]()
@@ -174,8 +190,6 @@ def reduce_all2(a, b, map2="mul", op="sum", acc=None, out_dtype=None, init=None,
                             workspace.data_ptr(), st)
         _check(rc, "rk_reduce_all2")
         return decode_host_out(buf, out_code)
-    if out is None:
-        out = torch.empty(1, dtype=torch_dtype(out_code), device=a.device)
     rc = rk_reduce_all2(op_c, map_c, in_code, acc_code, out_code, a.data_ptr(), b.data_ptr(), n,
                         init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
     _check(rc, "rk_reduce_all2")
@@ -203,9 +217,12 @@ def reduce_dims(x, shape, strides, dims, op="sum", map="identity", acc=None, out
     ndim = len(shape)
     n_out = math.prod(int(s) for i, s in enumerate(shape) if not (mask >> i) & 1)
     ptr = x.data_ptr() + int(offset) * x.element_size()
-    if workspace is None:
-        workspace = workspace_for(rk_workspace_size(in_code, acc_code, ndim, shape, strides, mask),
-                                  x.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = workspace_for(rk_workspace_size(in_code, acc_code, ndim, shape, strides, mask),
+                                      x.device)
+        if out is None and mode_c != RK_MODE_HOST:
+            out = torch.empty(max(n_out, 1), dtype=torch_dtype(out_code), device=x.device)
     st = _stream_handle(stream, x.get_device())
     if mode_c == RK_MODE_HOST:
         buf = _CTYPE[out_code]()
@@ -214,8 +231,6 @@ def reduce_dims(x, shape, strides, dims, op="sum", map="identity", acc=None, out
                             workspace.data_ptr(), st)
         _check(rc, "rk_reduce_dims")
         return decode_host_out(buf, out_code)
-    if out is None:
-        out = torch.empty(max(n_out, 1), dtype=torch_dtype(out_code), device=x.device)
     rc = rk_reduce_dims(op_c, map_c, in_code, acc_code, out_code, ptr, ndim, shape, strides, mask,
                         init_arg(acc_code, init), mode_c, out.data_ptr(), workspace.data_ptr(), st)
     _check(rc, "rk_reduce_dims")
@@ -240,11 +255,12 @@ def scan(x, shape=None, strides=None, dim=1, op="sum", acc=None, out_dtype=None,
     d0 = int(dim) - 1
     total = math.prod(int(s) for s in shape)
     ptr = x.data_ptr() + int(offset) * x.element_size()
-    if workspace is None:
-        workspace = workspace_for(rk_scan_workspace_size(in_code, acc_code, len(shape), shape, strides, d0),
-                                  x.device)
-    if out is None:
-        out = torch.empty(max(total, 1), dtype=torch_dtype(out_code), device=x.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = workspace_for(rk_scan_workspace_size(in_code, acc_code, len(shape), shape, strides, d0),
+                                      x.device)
+        if out is None:
+            out = torch.empty(max(total, 1), dtype=torch_dtype(out_code), device=x.device)
     rc = rk_scan_dims(_code(OPS, op), in_code, acc_code, out_code, ptr, len(shape), shape, strides, d0,
                       init_arg(acc_code, init), int(bool(inclusive)), out.data_ptr(), workspace.data_ptr(),
                       _stream_handle(stream, x.get_device()))

@@ -30,7 +30,8 @@ KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 
 EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_dims", "rk_status_string",
            "rk_plan_all", "rk_plan_all2", "rk_plan_dims", "rk_debug_set_fused_finish",
            "rk_debug_set_launch_events", "rk_scan_workspace_size", "rk_scan", "rk_scan_dims",
-           "rk_plan_scan", "rk_debug_stream_read", "rk_debug_device_info", "rk_debug_set_finish_tag")
+           "rk_plan_scan", "rk_debug_stream_read", "rk_debug_device_info", "rk_debug_set_finish_tag",
+           "rk_stream_timeouts", "rk_debug_force_wait_timeout", "rk_debug_fail_launches")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -99,6 +100,12 @@ def load() -> ctypes.CDLL:
     lib.rk_debug_device_info.restype = i32
     lib.rk_debug_set_finish_tag.argtypes = [vp, u32]
     lib.rk_debug_set_finish_tag.restype = i32
+    lib.rk_stream_timeouts.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
+    lib.rk_stream_timeouts.restype = i32
+    lib.rk_debug_force_wait_timeout.argtypes = [i64]
+    lib.rk_debug_force_wait_timeout.restype = i32
+    lib.rk_debug_fail_launches.argtypes = [i32]
+    lib.rk_debug_fail_launches.restype = i32
     _lib = lib
     return lib
 
@@ -213,3 +220,21 @@ def rk_debug_device_info() -> dict:
     if rc:
         raise RkError(rc, "rk_debug_device_info")
     return dict(num_cus=vals[0].value, mem_clock_khz=vals[1].value, mem_bus_bits=vals[2].value)
+
+
+def rk_stream_timeouts(stream) -> int:
+    """Waits that gave up in calls on `stream` (a hipStream_t handle) since
+    the last query; waits for the stream and clears the count."""
+    n = ctypes.c_uint64()
+    rc = load().rk_stream_timeouts(stream, ctypes.byref(n))
+    if rc:
+        raise RkError(rc, "rk_stream_timeouts")
+    return int(n.value)
+
+
+def rk_debug_force_wait_timeout(polls: int) -> int:
+    return int(load().rk_debug_force_wait_timeout(int(polls)))
+
+
+def rk_debug_fail_launches(count: int) -> int:
+    return int(load().rk_debug_fail_launches(int(count)))

@@ -1,5 +1,6 @@
 // kern_i64.hip -- kernels instantiated for one input dtype (i64); each input
 // dtype has its own translation unit so the library builds in parallel.
+#define RK_UNIT unit_kern_i64
 #include "rk_kernels.hpp"
 
 namespace rk {

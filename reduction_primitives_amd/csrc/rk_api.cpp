@@ -10,6 +10,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <sys/syscall.h>
+#include <unistd.h>
+
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -83,6 +86,34 @@ int arrive_slot(hipStream_t st)
         }
     }
     return -1;                                  // all slots taken: two launches
+}
+
+// The slot a stream already has, or -1 (never takes a new one).
+int existing_slot(hipStream_t st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    std::lock_guard<std::mutex> lock(g_slot_mu);
+    for (int i = 0; i < kArriveSlots; ++i)
+        if (g_slots[i].used && g_slots[i].dev == dev && g_slots[i].stream == (void *)st)
+            return i;
+    return -1;
+}
+
+// Test hooks.  g_force_wait >= 0: every whole-array collection and scan
+// look-back waits for what never comes and gives up after that many polls.
+// g_fail_launches > 0: that many calls return RK_ERR_HIP where they would
+// launch their first kernel, launching nothing.
+std::atomic<int64_t> g_force_wait{-1};
+std::atomic<int> g_fail_launches{0};
+
+bool injected_launch_failure()
+{
+    int n = g_fail_launches.load(std::memory_order_relaxed);
+    while (n > 0 && !g_fail_launches.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) {
+    }
+    return n > 0;
 }
 
 bool debug_enabled()
@@ -270,24 +301,35 @@ const char *kernel_name(int k)
 
 // Host mode: a small pinned host buffer per host thread, which the last
 // pass writes the bare result into, so no copy has to be launched.  A
-// host-mode call returns only after its stream drained, so one buffer per
-// thread is never shared by two calls in flight.  Allocated once, kept for
-// the thread's lifetime; NULL (copy back from the workspace) if pinned
-// memory is unavailable.
+// host-mode call returns only after its result arrived, so one buffer per
+// thread is never shared by two calls in flight.  Allocated on the thread's
+// first host-mode call and freed when the thread ends (the main thread's at
+// the process's end, by the system: the HIP runtime may already be shutting
+// down when the main thread's thread-local objects go); NULL (copy back from
+// the workspace) if pinned memory is unavailable.
+struct PinnedResult {
+    void *buf = nullptr;
+    bool tried = false;
+    ~PinnedResult()
+    {
+        if (buf && long(syscall(SYS_gettid)) != long(getpid()))
+            (void)hipHostFree(buf);
+    }
+};
+
 void *pinned_result()
 {
-    thread_local void *buf = nullptr;
-    thread_local bool tried = false;
-    if (!tried) {
-        tried = true;
+    thread_local PinnedResult r;
+    if (!r.tried) {
+        r.tried = true;
         // RK_HOST_COPY set: always copy back from the workspace (tests use it)
         if (std::getenv("RK_HOST_COPY") != nullptr ||
-            hipHostMalloc(&buf, 64, hipHostMallocPortable) != hipSuccess)
-            buf = nullptr;
+            hipHostMalloc(&r.buf, 64, hipHostMallocPortable) != hipSuccess)
+            r.buf = nullptr;
         else
-            std::memset(buf, 0, 64);            // sequence numbers start at 1
+            std::memset(r.buf, 0, 64);          // sequence numbers start at 1
     }
-    return buf;
+    return r.buf;
 }
 
 // Wait for the bare partial, then finish it on the host.  With the pinned
@@ -296,7 +338,10 @@ void *pinned_result()
 // the wake-up latency of a blocking stream wait.  Every kQueryMicros the spin
 // asks the stream for errors (a query takes microseconds, so it is kept out of
 // the path that sees the result), and after kSpinMicros it gives way to a
-// blocking wait.  Without the buffer the partial is copied back from ws[grid].
+// blocking wait.  Without the buffer the partial is copied back from ws[grid]
+// with the sequence word after it.  A drained stream without this call's
+// sequence number means the kernel stored no result (its collection gave
+// up): RK_ERR_HIP, and *out is left as it was.
 constexpr int64_t kSpinMicros = 200;
 constexpr int64_t kQueryMicros = 20;
 
@@ -339,11 +384,20 @@ int finish_on_host(int op, int acc, uint64_t init_bits, const Finish &fin, const
         std::atomic_thread_fence(std::memory_order_acquire);
         std::memcpy(partial, fin.out, asz);
     } else {
-        const unsigned char *src = static_cast<const unsigned char *>(ws) + size_t(grid) * asz;
-        if (hipMemcpyAsync(partial, src, asz, hipMemcpyDeviceToHost, st) != hipSuccess)
+        // result and sequence word: bytes [grid * asz, host_seq_offset + 4)
+        const size_t first = size_t(grid) * asz;
+        const size_t bytes = size_t(host_seq_offset(grid, asz)) + 4 - first;
+        unsigned char back[16];
+        const unsigned char *src = static_cast<const unsigned char *>(ws) + first;
+        if (hipMemcpyAsync(back, src, bytes, hipMemcpyDeviceToHost, st) != hipSuccess)
             return RK_ERR_HIP;
         if (hipStreamSynchronize(st) != hipSuccess)
             return RK_ERR_HIP;
+        uint32_t seq = 0;
+        std::memcpy(&seq, back + bytes - 4, 4);
+        if (seq != fin.host_seq)
+            return RK_ERR_HIP;                     // the kernel finished without a result
+        std::memcpy(partial, back, asz);
     }
     host_finish(op, acc, init_bits, partial, 1, out, out_dtype);
     return RK_OK;
@@ -354,7 +408,7 @@ Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, v
     Finish f;
     f.out = mode == RK_MODE_HOST ? pinned_result() : out;
     f.host_seq = 0;
-    if (mode == RK_MODE_HOST && f.out) {
+    if (mode == RK_MODE_HOST) {
         // a fresh sequence number per host-mode call of this thread
         thread_local uint32_t seq = 0;
         seq = seq + 1 == 0 ? 1 : seq + 1;
@@ -396,10 +450,15 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     L.all.ws = ws;
     L.all.grid = a.grid;
     L.all.arrive_slot = a.grid > 1 && arrive_counters(a.grid) <= kArriveCapacity ? arrive_slot(st) : -1;
+    const int64_t force = g_force_wait.load(std::memory_order_relaxed);
+    L.all.spin_limit = force >= 0 ? uint32_t(force) : kFinalSpinLimit;
+    L.all.tag_xor = force >= 0 ? 0x80000000u : 0u;
     L.all.fin = make_finish(op, acc, out_dtype, mode, init, out);
     L.stream = st;
     L.ev_begin = t_ev_begin;
     L.ev_end = t_ev_end;
+    if (injected_launch_failure())
+        return RK_ERR_HIP;
     int rc = dispatch(in, L);
     if (rc != RK_OK)
         return rc;
@@ -447,6 +506,54 @@ int rk_debug_set_finish_tag(void *stream, uint32_t e)
         if (rc != RK_OK)
             return rc;
     }
+    return RK_OK;
+}
+
+int rk_stream_timeouts(void *stream, uint64_t *count)
+{
+    if (!count)
+        return RK_ERR_INVALID_ARGUMENT;
+    *count = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(st) != hipSuccess)
+        return RK_ERR_HIP;
+    const int slot = existing_slot(st);
+    const int dtypes[] = {F32, BF16, F16, F64, I32, I64};
+    for (int d : dtypes) {
+        Launch L;
+        std::memset(&L, 0, sizeof L);
+        L.kernel = K_TAKE_TIMEOUTS;
+        L.all.arrive_slot = slot;
+        L.all.ws = count;
+        L.all.n = 1;                            // repair the slot's tagged words after a give-up
+        int rc = dispatch(d, L);
+        if (rc != RK_OK)
+            return rc;
+        ScanLaunch S;
+        std::memset(&S, 0, sizeof S);
+        S.kernel = SK_TAKE_TIMEOUTS;
+        S.args.slot = slot;
+        S.args.ws = count;
+        rc = dispatch_scan(d, S);
+        if (rc != RK_OK)
+            return rc;
+    }
+    return RK_OK;
+}
+
+int rk_debug_force_wait_timeout(int64_t polls)
+{
+    if (polls > int64_t(0xffffffffu))
+        return RK_ERR_INVALID_ARGUMENT;
+    g_force_wait.store(polls < 0 ? -1 : polls, std::memory_order_relaxed);
+    return RK_OK;
+}
+
+int rk_debug_fail_launches(int count)
+{
+    if (count < 0)
+        return RK_ERR_INVALID_ARGUMENT;
+    g_fail_launches.store(count, std::memory_order_relaxed);
     return RK_OK;
 }
 
@@ -732,6 +839,8 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
     L.stream = st;
     L.ev_begin = t_ev_begin;
     L.ev_end = t_ev_end;
+    if (injected_launch_failure())
+        return RK_ERR_HIP;
     return dispatch(in_dtype, L);
 }
 
@@ -857,9 +966,14 @@ int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void 
                      (d.kernel == SK_COLUMNS && d.tiles <= kScanFlagCapacity)
                  ? arrive_slot(static_cast<hipStream_t>(stream))
                  : -1;
+    const int64_t force = g_force_wait.load(std::memory_order_relaxed);
+    a.spin_limit = force >= 0 ? uint32_t(force) : uint32_t(tune::kScanSpinLimit);
+    a.force_wait = force >= 0 ? 1u : 0u;
     L.stream = stream;
     L.ev_begin = t_ev_begin;
     L.ev_end = t_ev_end;
+    if (injected_launch_failure())
+        return RK_ERR_HIP;
     return dispatch_scan(in_dtype, L);
 }
 

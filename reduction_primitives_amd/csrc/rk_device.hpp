@@ -18,6 +18,15 @@
 #include "rk_launch.hpp"
 #include "rk_plan.hpp"
 
+// Every kernel translation unit defines RK_UNIT, a name of its own, before
+// including this header.  The library state each unit keeps in device memory
+// (the tables below) lives in a namespace of that name, so its device symbols
+// differ from unit to unit: the runtime finds a symbol the host names by
+// its device name, and equal names would all resolve to one unit's copy.
+#ifndef RK_UNIT
+#error "define RK_UNIT (a name unique to the translation unit) before including rk_device.hpp"
+#endif
+
 namespace rk {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -483,7 +492,8 @@ __device__ __forceinline__ Acc from_bits(uint64_t b)
 // Host mode: the bare result goes straight to the library's pinned host
 // buffer (f.out) with a system-scope store, followed -- once that store has
 // completed -- by the call's sequence number at byte 8, which the host waits
-// for.  Without such a buffer the result goes to ws[grid] for a copy back.
+// for.  Without such a buffer the result goes to ws[grid] and the sequence
+// number to host_seq_offset, both copied back once the stream has drained.
 template <class Acc>
 __device__ __forceinline__ void store_host_result(const Finish &f, Acc *ws, int grid, Acc v)
 {
@@ -499,6 +509,8 @@ __device__ __forceinline__ void store_host_result(const Finish &f, Acc *ws, int 
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     } else {
         ws[grid] = v;
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + host_seq_offset(grid, sizeof(Acc))) =
+            f.host_seq;
     }
 }
 
@@ -513,6 +525,23 @@ __device__ __forceinline__ void finish_store(const Finish &f, int64_t o, Acc v)
     store_out<Acc>(f.out, o, f.out_dtype, Op::apply(s, v));
 }
 
+// ------------------------------------------------- waits that give up
+// Every wait of one block on others is bounded.  One that gives up (never in
+// a normal run: no block waits on the block that waits) is counted here, per
+// stream slot, plus one entry shared by calls on streams without a slot; the
+// host reads and clears the counts (rk_stream_timeouts).  Each translation
+// unit has its own table, as it has its own slots.
+namespace RK_UNIT {
+static __device__ __attribute__((aligned(128))) uint32_t g_timeouts[kTimeoutEntries];
+}
+using RK_UNIT::g_timeouts;
+
+__device__ __forceinline__ void record_timeout(int slot)
+{
+    __hip_atomic_fetch_add(&g_timeouts[slot >= 0 && slot < kArriveSlots ? slot : kArriveSlots], 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------- finishing in one launch
 // The blocks that share an output store their partials, and the last one to
 // arrive folds them and finishes: one launch instead of a second pass.  The
@@ -522,7 +551,10 @@ __device__ __forceinline__ void finish_store(const Finish &f, int64_t o, Acc v)
 // gets its own slot of counters, so calls that may overlap never share one.
 // Counter c of a slot sits in line c % kArriveLines, word c / kArriveLines,
 // so consecutive counters never share a 128-byte line.
+namespace RK_UNIT {
 static __device__ __attribute__((aligned(128))) uint32_t g_arrive[kArriveSlots * kArriveCapacity];
+}
+using RK_UNIT::g_arrive;
 constexpr int kArriveLineWords = 32;
 constexpr int kArriveLines = kArriveCapacity / kArriveLineWords;
 
@@ -618,7 +650,10 @@ __device__ __forceinline__ bool arrive_last(int slot, int64_t idx, uint32_t memb
 constexpr int kFinalTagCopies = 32;
 constexpr int kFinalHeaderWords = 16 * kFinalTagCopies;
 constexpr int kFinalSlotWords = kFinalHeaderWords + 2 * kFinalCapacity;
+namespace RK_UNIT {
 static __device__ __attribute__((aligned(128))) uint64_t g_final[kArriveSlots * kFinalSlotWords];
+}
+using RK_UNIT::g_final;
 
 // The call's tag (read when a block starts; thread 0 only).
 __device__ __forceinline__ uint32_t final_tag(int slot)
@@ -644,14 +679,16 @@ __device__ __forceinline__ void publish_tagged(int slot, int b, Acc v, uint32_t 
 
 // Block 0: wait until all `grid` partials carry `tag`, then fold thread t's
 // partials t, t + BLOCK, ... in that order (every thread's result, before
-// the block reduction).  Called by every thread of block 0.
+// the block reduction).  Called by every thread of block 0.  After
+// `spin_limit` polls without every tag it gives up and returns false in
+// `*ok` (the same in every thread): the fold is then incomplete.
 template <class Acc, class Op, int BLOCK>
-__device__ Acc collect_tagged(int slot, int grid, uint32_t tag)
+__device__ Acc collect_tagged(int slot, int grid, uint32_t tag, uint32_t spin_limit, bool *ok_out)
 {
     const uint64_t *w = &g_final[int64_t(slot) * kFinalSlotWords + kFinalHeaderWords];
     __shared__ int s_ready;
     Acc v = Op::template identity<Acc>();
-    for (int spin = 0;; ++spin) {
+    for (uint32_t spin = 0;; ++spin) {
         bool ok = true;
         v = Op::template identity<Acc>();
         for (int k = threadIdx.x; k < grid; k += BLOCK) {
@@ -674,15 +711,19 @@ __device__ Acc collect_tagged(int slot, int grid, uint32_t tag)
         __syncthreads();
         const bool ready = s_ready != 0;
         __syncthreads();
-        if (ready || spin >= kFinalSpinLimit)
+        if (ready || spin >= spin_limit) {
+            *ok_out = ready;
             break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
     return v;
 }
 
-// Block 0, once the result is stored: hand the next call its tag base.
-// Called by every thread of block 0.
+// Block 0, once the result is stored (or its collection gave up): hand the
+// next call its tag base.  Called by every thread of block 0.  After a
+// collection that gave up, the tag still moves on: blocks that have started
+// carry the old tag, which no later call's collection takes for its own.
 template <int BLOCK>
 __device__ __forceinline__ void advance_tag(int slot, uint32_t tag)
 {
@@ -700,15 +741,17 @@ __device__ __forceinline__ void advance_tag(int slot, uint32_t tag)
 
 // Test hook: make the slot's last tag `e` (every copy), so a test can run
 // calls across the wrap of the tags.  One block of kFinalTagCopies threads.
-// (A template, so that each translation unit keeps its own kernel, as it
-// keeps its own g_final.)
-template <int UNUSED = 0>
+// In the unit's own namespace: it writes this unit's g_final, and a kernel of
+// one name in every unit would be launched through one host stub, the
+// linker's pick, and so always reach one unit's copy.
+namespace RK_UNIT {
 __global__ void k_set_final_tag(int slot, uint32_t e)
 {
     if (threadIdx.x < kFinalTagCopies)
         __hip_atomic_store(&g_final[int64_t(slot) * kFinalSlotWords + threadIdx.x * 16], uint64_t(e), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
+}  // namespace RK_UNIT
 
 // ------------------------------------------------------------------ misc
 

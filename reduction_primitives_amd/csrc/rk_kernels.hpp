@@ -142,9 +142,13 @@ __device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v, uint32_t
             s_tag = tag;
         __syncthreads();
         const uint32_t t = s_tag;
-        Acc r = block_reduce<Op, BLOCK>(collect_tagged<Acc, Op, BLOCK>(a.arrive_slot, a.grid, t));
+        bool ok = false;
+        Acc r = collect_tagged<Acc, Op, BLOCK>(a.arrive_slot, a.grid, t ^ a.tag_xor, a.spin_limit, &ok);
+        r = block_reduce<Op, BLOCK>(r);
         if (threadIdx.x == 0) {
-            if (a.fin.mode == FIN_HOST)
+            if (!ok)                            // an incomplete fold is no result: store nothing
+                record_timeout(a.arrive_slot);
+            else if (a.fin.mode == FIN_HOST)
                 store_host_result(a.fin, ws, a.grid, r);
             else
                 finish_store<Op>(a.fin, 0, r);
@@ -1095,15 +1099,49 @@ int run_acc(const Launch &L)
     return ST_INVALID;
 }
 
+// Add this unit's count of waits that gave up on `slot` (slot < 0: the
+// entry of calls without a slot) and on the shared entry to *count, and
+// clear both.  With `repair` and a count, also zero the slot's tagged words:
+// a block that had not even started when its collection gave up publishes
+// under the next call's tag, and the drained stream guarantees every such
+// block has ended.  Synchronous (hipMemcpy to and from the tables).  In the
+// unit's own namespace: an inline function of one name in every unit is
+// merged by the linker into one copy, which would only see that unit's tables.
+namespace RK_UNIT {
+inline int take_timeouts(int slot, uint64_t *count, bool repair)
+{
+    uint32_t t[kTimeoutEntries];
+    if (hipMemcpyFromSymbol(t, HIP_SYMBOL(g_timeouts), sizeof t, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return ST_HIP;
+    const int e = slot >= 0 && slot < kArriveSlots ? slot : kArriveSlots;
+    const uint64_t n = uint64_t(t[e]) + (e != kArriveSlots ? t[kArriveSlots] : 0u);
+    const uint32_t zero = 0;
+    if ((t[e] && hipMemcpyToSymbol(HIP_SYMBOL(g_timeouts), &zero, 4, size_t(e) * 4, hipMemcpyHostToDevice) != hipSuccess) ||
+        (t[kArriveSlots] && hipMemcpyToSymbol(HIP_SYMBOL(g_timeouts), &zero, 4, size_t(kArriveSlots) * 4,
+                                              hipMemcpyHostToDevice) != hipSuccess))
+        return ST_HIP;
+    if (repair && t[e] && e != kArriveSlots) {
+        static const uint64_t zeros[2 * kFinalCapacity] = {};
+        const size_t off = (size_t(e) * kFinalSlotWords + kFinalHeaderWords) * sizeof(uint64_t);
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_final), zeros, sizeof zeros, off, hipMemcpyHostToDevice) != hipSuccess)
+            return ST_HIP;
+    }
+    *count += n;
+    return ST_OK;
+}
+}  // namespace RK_UNIT
+
 // Accumulators a given input type may use (the public dtype table).
 template <class In>
 int run_in(const Launch &L)
 {
     if (L.kernel == K_SET_TAG) {                // this translation unit's copy of the slot
-        hipLaunchKernelGGL(k_set_final_tag<0>, dim3(1), dim3(kFinalTagCopies), 0, static_cast<hipStream_t>(L.stream),
-                           L.all.arrive_slot, uint32_t(L.all.n));
+        hipLaunchKernelGGL(RK_UNIT::k_set_final_tag, dim3(1), dim3(kFinalTagCopies), 0,
+                           static_cast<hipStream_t>(L.stream), L.all.arrive_slot, uint32_t(L.all.n));
         return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
     }
+    if (L.kernel == K_TAKE_TIMEOUTS)            // this translation unit's counts (the stream has drained)
+        return RK_UNIT::take_timeouts(L.all.arrive_slot, static_cast<uint64_t *>(L.all.ws), L.all.n != 0);
     if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
         if (L.acc == F32) return run_acc<In, float>(L);
         if (L.acc == F64) return run_acc<In, double>(L);

@@ -36,14 +36,27 @@ constexpr int64_t arrive_counters(int64_t n)
 // counters: every block stores its partial tagged with the call's number,
 // and block 0 collects them (see rk_device.hpp).
 constexpr int kFinalCapacity = 2048;
-constexpr int kFinalSpinLimit = 1 << 24;   // block 0's polls (with a short sleep each): far beyond any run
+constexpr uint32_t kFinalSpinLimit = 1u << 24;   // block 0's polls (with a short sleep each): far beyond any run
+
+// Waits that give up (block 0's collection, a scan's look-back) are counted
+// per stream slot, plus one shared entry for calls on streams without a
+// slot, in each translation unit's own table; the host reads and clears
+// them (rk_stream_timeouts).
+constexpr int kTimeoutEntries = kArriveSlots + 1;
+
+// Host mode without the pinned result buffer: the bare result goes to
+// ws[grid] and the call's sequence number to the 4 bytes at this byte offset
+// of the workspace, so the host can tell a result of this call from stale
+// bytes after copying both back.
+constexpr int64_t host_seq_offset(int64_t grid, int acc_size) { return ((grid + 1) * acc_size + 7) / 8 * 8; }
 
 struct Finish {
     void *out;            // device output (OVERWRITE / FOLD); HOST: pinned host result buffer or NULL
     int out_dtype;
     int mode;             // FinishMode
     uint64_t init_bits;   // starting value, accumulator bits (identity when no init)
-    uint32_t host_seq;    // HOST with a result buffer: stored after the result, at byte 8
+    uint32_t host_seq;    // HOST: stored after the result (result buffer: at byte 8;
+                          // workspace: at host_seq_offset)
 };
 
 struct AllArgs {
@@ -56,9 +69,11 @@ struct AllArgs {
     int nd;               // strided variant: element i sits at sum_d ((i / prod ext[<d]) % ext[d]) * str[d]
     int64_t ext[4];
     int64_t str[4];
-    void *ws;             // grid + 1 accumulators
+    void *ws;             // grid + 1 accumulators, then (host mode, copied back) the sequence word
     int grid;
     int arrive_slot;      // >= 0: the last block to arrive finishes (one launch)
+    uint32_t spin_limit;  // block 0's polls before its collection gives up
+    uint32_t tag_xor;     // 0; nonzero only to make block 0 wait for a tag no block carries (a test hook)
     Finish fin;
 };
 

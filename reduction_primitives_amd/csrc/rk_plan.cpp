@@ -60,8 +60,9 @@ int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus
         a.grid = int(std::min<int64_t>(a.tiles, int64_t(num_cus) * tune::kAllBlocksPerCu));
     }
     a.launches = a.grid == 1 ? 1 : 2;
-    // pass-1 partials plus one slot for the bare final partial
-    a.ws_bytes = round_up_256(size_t(a.grid + 1) * dtype_size(acc_dtype));
+    // pass-1 partials, one slot for the bare final partial, and the host-mode
+    // sequence word after it
+    a.ws_bytes = round_up_256(size_t(host_seq_offset(a.grid, dtype_size(acc_dtype))) + 4);
     *p = a;
     return ST_OK;
 }
@@ -225,7 +226,7 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
                      ? 1
                      : int(std::min<int64_t>(a.tiles, int64_t(num_cus) * tune::kAllBlocksPerCu));
         a.launches = a.grid == 1 ? 1 : 2;
-        a.ws_bytes = round_up_256(size_t(a.grid + 1) * asz);
+        a.ws_bytes = round_up_256(size_t(host_seq_offset(a.grid, asz)) + 4);
         d.all = a;
         d.launches = a.launches;
         d.grid = a.grid;

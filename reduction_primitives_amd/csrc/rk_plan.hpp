@@ -20,7 +20,8 @@ enum Mode { OVERWRITE = 0, FOLD = 1, HOST = 2 };
 enum Kernel {
     K_NONE = 0, K_ALL = 1, K_ALL_STRIDED = 2, K_THREAD = 3, K_TILED = 4,
     K_COLUMNS = 5, K_ROW = 6, K_GENERIC = 7, K_ALL2 = 8,
-    K_SET_TAG = 100               // test hook: set a slot's whole-array tag (no reduction)
+    K_SET_TAG = 100,              // test hook: set a slot's whole-array tag (no reduction)
+    K_TAKE_TIMEOUTS = 101         // read and clear a slot's count of waits that gave up (no reduction)
 };
 
 int dtype_size(int d);            // bytes per element, 0 for an unknown code

@@ -300,7 +300,10 @@ constexpr uint32_t kFlagPrefix = 2;
 // sit in different 128-byte lines, for the reason given for the tile scan's
 // records below.
 constexpr int kScanSlotWords = 64 + kScanFlagCapacity;
+namespace RK_UNIT {
 static __device__ __attribute__((aligned(128))) uint32_t g_scan_state[kArriveSlots * kScanSlotWords];
+}
+using RK_UNIT::g_scan_state;
 
 struct ScanState {
     uint32_t *counter;
@@ -336,7 +339,10 @@ struct ScanState {
 // that publish and poll at the same time -- neighbours -- are kept in
 // different lines, and a reader finds a tile's flag and values in one line.
 constexpr int kScanTileSlotWords = (kScanHeaderBytes + kScanRecCapacity * kScanRecBytes) / 4;
+namespace RK_UNIT {
 static __device__ __attribute__((aligned(128))) uint32_t g_scan_tile_state[kArriveSlots * kScanTileSlotWords];
+}
+using RK_UNIT::g_scan_tile_state;
 
 struct TileState {
     uint32_t *counter;
@@ -421,11 +427,12 @@ __device__ __forceinline__ void publish(const TileState &st, int64_t g, Acc v, u
 // (lane 0 the nearest) until one with its inclusive prefix.  Every tile with
 // a smaller counter value has already started, and it publishes its
 // aggregate without waiting on anything, so every wait here ends.  As a
-// safety net each wait is still bounded (tune::kScanSpinLimit sleeps): past
-// it the tile records the timeout in the header and goes on, so every wave
-// exits.  Publishes the tile's own inclusive prefix before returning.
+// safety net each wait is still bounded (a.spin_limit sleeps): past it the
+// tile records the timeout in the header and in the library's count of waits
+// that gave up, and goes on, so every wave exits.  Publishes the tile's own
+// inclusive prefix before returning.
 template <class Acc, class Op>
-__device__ Acc scan_lookback(const TileState &st, int64_t g, int64_t t, Acc agg, Acc init)
+__device__ Acc scan_lookback(const TileState &st, const ScanArgs &a, int64_t g, int64_t t, Acc agg, Acc init)
 {
     const int lane = lane_id();
     if (t == 0) {
@@ -443,17 +450,19 @@ __device__ Acc scan_lookback(const TileState &st, int64_t g, int64_t t, Acc agg,
         const bool valid = j >= 0;
         uint32_t f;
         uint64_t pm, zm;
-        for (int spin = 0;; ++spin) {
+        for (uint32_t spin = 0;; ++spin) {
             f = valid ? __hip_atomic_load(st.flag(g0 + j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kFlagPrefix;
             pm = __ballot(f == kFlagPrefix);
             zm = __ballot(f == 0);
             // done when every lane before the first prefix has published
             const uint64_t need = pm ? (pm & (0 - pm)) - 1 : ~uint64_t(0);
-            if ((zm & need) == 0)
+            if ((zm & need) == 0 && !a.force_wait)
                 break;
-            if (spin >= tune::kScanSpinLimit) {
-                if (lane == 0)
+            if (spin >= a.spin_limit) {
+                if (lane == 0) {
                     __hip_atomic_store(st.timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    record_timeout(a.slot);
+                }
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -505,8 +514,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     __syncthreads();
     const int64_t g = s_id;
     if (g >= a.tiles) {                        // never: the counter starts at zero every call
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             __hip_atomic_store(st.timeout, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            record_timeout(a.slot);
+        }
         return;
     }
     const int64_t line = g / a.tiles_per_line;
@@ -552,7 +563,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         agg = Op::apply(agg, s_wave[v]);
     }
     if (w == 0) {
-        const Acc excl = scan_lookback<Acc, Op>(st, g, t, agg, from_bits<Acc>(a.init_bits));
+        const Acc excl = scan_lookback<Acc, Op>(st, a, g, t, agg, from_bits<Acc>(a.init_bits));
         if (lane_id() == 0)
             s_excl = excl;
     }
@@ -646,8 +657,10 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
     __syncthreads();
     const uint32_t gu = s_id;
     if (gu >= a.tiles) {                       // never: the counter starts at zero every call
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             __hip_atomic_store(st.timeout, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            record_timeout(a.slot);
+        }
         return;
     }
     // tile numbers fit 32 bits (the plan refuses more), so they split in 32-bit
@@ -747,9 +760,9 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
                                                             __HIP_MEMORY_SCOPE_AGENT)
                                         : kFlagPrefix;
                 int first = K;
-                for (int spin = 0;; ++spin) {
+                for (uint32_t spin = 0;; ++spin) {
                     first = K;
-                    bool ready = true;
+                    bool ready = !a.force_wait;
 #pragma unroll
                     for (int q = K - 1; q >= 0; --q)
                         if (f[q] == kFlagPrefix)
@@ -760,8 +773,9 @@ __global__ __launch_bounds__(BLOCK) void k_scan_columns(ScanArgs a)
                             ready = false;
                     if (ready)
                         break;
-                    if (spin >= tune::kScanSpinLimit) {
+                    if (spin >= a.spin_limit) {
                         __hip_atomic_store(st.timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        record_timeout(a.slot);
                         break;
                     }
                     __builtin_amdgcn_s_sleep(1);
@@ -960,6 +974,8 @@ int run_scan_acc(const ScanLaunch &L)
 template <class In>
 int run_scan_in(const ScanLaunch &L)
 {
+    if (L.kernel == SK_TAKE_TIMEOUTS)           // this translation unit's counts (the stream has drained)
+        return RK_UNIT::take_timeouts(L.args.slot, static_cast<uint64_t *>(L.args.ws), false);
     if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
         if (L.acc == F32) return run_scan_acc<In, float>(L);
         if (L.acc == F64) return run_scan_acc<In, double>(L);

@@ -15,7 +15,8 @@
 namespace rk {
 
 // Scan kernels (rk_scan.hpp).
-enum ScanKernel { SK_NONE = 0, SK_TILE = 1, SK_ROWWAVE = 2, SK_LINES = 3, SK_COLUMNS = 4 };
+enum ScanKernel { SK_NONE = 0, SK_TILE = 1, SK_ROWWAVE = 2, SK_LINES = 3, SK_COLUMNS = 4,
+                  SK_TAKE_TIMEOUTS = 100 };   // read and clear the count of waits that gave up (no scan)
 
 namespace tune {
 constexpr int kScanBlock = 256;           // threads per block of the row-wave and lines kernels
@@ -71,6 +72,8 @@ struct ScanArgs {
     uint64_t init_bits;   // starting value, accumulator bits
     int slot;             // >= 0: look-back state in the library's slot (reset by the last
                           // block); < 0: in the workspace, cleared by a fill launch first
+    uint32_t spin_limit;  // look-back: polls of one window before the wait gives up
+    uint32_t force_wait;  // 0; nonzero only to make every look-back wait until it gives up (a test hook)
 };
 
 // Columns-scan state: a 256-byte header (as the tile scan's), the flags --

@@ -1,4 +1,5 @@
 // scan_bf16.hip -- scan kernels instantiated for one input dtype (bf16).
+#define RK_UNIT unit_scan_bf16
 #include "rk_scan.hpp"
 
 namespace rk {

@@ -1,4 +1,5 @@
 // scan_f16.hip -- scan kernels instantiated for one input dtype (f16).
+#define RK_UNIT unit_scan_f16
 #include "rk_scan.hpp"
 
 namespace rk {

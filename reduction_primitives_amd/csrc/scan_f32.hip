@@ -1,4 +1,5 @@
 // scan_f32.hip -- scan kernels instantiated for one input dtype (f32).
+#define RK_UNIT unit_scan_f32
 #include "rk_scan.hpp"
 
 namespace rk {

@@ -1,4 +1,5 @@
 // scan_f64.hip -- scan kernels instantiated for one input dtype (f64).
+#define RK_UNIT unit_scan_f64
 #include "rk_scan.hpp"
 
 namespace rk {

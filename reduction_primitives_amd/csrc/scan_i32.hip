@@ -1,4 +1,5 @@
 // scan_i32.hip -- scan kernels instantiated for one input dtype (i32).
+#define RK_UNIT unit_scan_i32
 #include "rk_scan.hpp"
 
 namespace rk {

@@ -1,4 +1,5 @@
 // scan_i64.hip -- scan kernels instantiated for one input dtype (i64).
+#define RK_UNIT unit_scan_i64
 #include "rk_scan.hpp"
 
 namespace rk {

@@ -30,7 +30,7 @@ def _rk():
 
 
 def run_and_check(x_cpu, op="sum", map_="identity", acc=None, out_dtype=None, mode="overwrite",
-                  init=None, offset=0, what=""):
+                  init=None, offset=0, what="", allow_inf=False):
     """Reduce x_cpu[offset:] on the GPU and compare with the oracle."""
     rk = _rk()
     op_c, map_c, mode_c = rk.OPS[op], rk.MAPS[map_], rk.MODES[mode]
@@ -62,7 +62,7 @@ def run_and_check(x_cpu, op="sum", map_="identity", acc=None, out_dtype=None, mo
     if mode == "fold":
         start = start[0]
     S = magnitude(map_c, in_c, acc_c, xr, start if op_c == O.SUM else 0.0)
-    check(op_c, out_c, gpu_raw, [R], S, what or f"{op}/{map_}/{mode} n={view.numel()}")
+    check(op_c, out_c, gpu_raw, [R], S, what or f"{op}/{map_}/{mode} n={view.numel()}", allow_inf=allow_inf)
     return res
 
 
@@ -152,9 +152,15 @@ COMBOS = [  # (input, accumulator, output)
 ]
 
 
-def _draw(dtype, n, seed):
+def _draw(dtype, n, seed, out_dtype=None):
     if dtype.is_floating_point:
-        return W.normal(n, seed, dtype) if dtype != torch.float64 else W.normal(n, seed).double()
+        x = W.normal(n, seed, dtype) if dtype != torch.float64 else W.normal(n, seed).double()
+        if out_dtype == torch.float16:
+            # N(0, 1/16): sum |x| ~ 2.0e4 and sum x^2 ~ 6.3e3 over 100,003
+            # values, twice that after a fold, all below float16's 65,504, so
+            # every mode compares finite values (scaling by 1/4 is exact)
+            x = x * 0.25
+        return x
     return W.randint(n, -2**20, 2**20, seed, dtype)
 
 
@@ -163,9 +169,26 @@ def _draw(dtype, n, seed):
 @pytest.mark.parametrize("map_", ["identity", "square", "abs"])
 def test_dtype_op_map_matrix(combo, op, map_):
     in_dt, acc_dt, out_dt = combo
-    x = _draw(in_dt, 100_003, 7500)
+    x = _draw(in_dt, 100_003, 7500, out_dt)
     run_and_check(x, op=op, map_=map_, acc=acc_dt, out_dtype=out_dt, init=None)
     run_and_check(x, op=op, map_=map_, acc=acc_dt, out_dtype=out_dt, mode="fold")
+
+
+def test_f16_output_overflows_to_inf():
+    """A float32 accumulator holds a sum that float16 cannot: the sum of
+    squares of 100,003 N(0,1) values (~1.0e5) stays finite in the
+    accumulator, and only the single final conversion to float16 gives +inf
+    (partials keep the accumulator's type: PR #139, "Compatibility").  The
+    same call into float32 is checked by value."""
+    x = W.normal(100_003, 7500, torch.float16)
+    for map_ in ("square", "abs"):
+        R = run_and_check(x, map_=map_, acc=torch.float32, out_dtype=torch.float32)
+        assert 6.6e4 < float(R.item()) < 1.2e5
+        res = run_and_check(x, map_=map_, acc=torch.float32, out_dtype=torch.float16, allow_inf=True)
+        assert float(res.float().item()) == float("inf")
+        res = run_and_check(x, map_=map_, acc=torch.float32, out_dtype=torch.float16, mode="host",
+                            allow_inf=True)
+        assert res == float("inf")
 
 
 # ---------------------------------------------------------- exactness pins
@@ -288,6 +311,64 @@ def test_runs_on_a_side_stream():
     s.synchronize()
     R = O.reduce_all(O.SUM, O.IDENTITY, O.F32, O.F32, raw_np(x), 2.0)
     assert abs(out.item() - R) <= 1e-5 * (2.0 + R)
+
+
+def test_stream_argument_allocates_on_that_stream(monkeypatch):
+    """stream= names a stream other than the current one: the workspace the
+    binding allocates belongs to that stream, so once the call returns (and
+    frees it) the current stream cannot be handed its bytes while the call's
+    kernels -- queued behind other work -- still write and read them.  Two
+    launches, so the partials really pass through the workspace."""
+    rk = _rk()
+    seen = []
+    real = rk.workspace_for
+
+    def spy(nbytes, device):
+        t = real(nbytes, device)
+        seen.append((t.data_ptr(), t.numel()))
+        return t
+    monkeypatch.setattr(rk, "workspace_for", spy)
+    x = W.uniform(10**6 + 3, 0.0, 1.0, 7965)
+    a, b = W.vector_pair(10**5 + 1)
+    m = W.uniform(512 * 8192, -1.0, 1.0, 7966)
+    xd, ad, bd, md = x.to(DEV), a.data.to(DEV), b.data.to(DEV), m.to(DEV)
+    assert rk.plan_dims(torch.float32, (512, 8192), (1, 512), 2)["workspace_bytes"] > 0
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    prev = rk.rk_debug_set_fused_finish(0)
+    try:
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(50_000_000)       # the calls below queue behind this
+        r_all = rk.reduce_all(xd, init=2.0, stream=side)
+        r_all2 = rk.reduce_all2(ad, bd, "mul", stream=side)
+        r_dims = rk.reduce_dims(md, (512, 8192), (1, 512), 2, stream=side)
+        r_scan = rk.scan(xd, stream=side)
+        assert len(seen) == 4
+        # the current stream allocates and scribbles while the side stream waits
+        junk = [torch.empty(nb, dtype=torch.uint8, device=DEV) for _, nb in seen]
+        for (p, nb), j in zip(seen, junk):
+            q = j.data_ptr()
+            assert q + j.numel() <= p or p + nb <= q, "a freed workspace went to the current stream"
+            j.fill_(0xFF)
+        side.synchronize()
+    finally:
+        rk.rk_debug_set_fused_finish(prev)
+    torch.cuda.synchronize()
+    xr = raw_np(x)
+    R = O.reduce_all(O.SUM, O.IDENTITY, O.F32, O.F32, xr, 2.0)
+    check(O.SUM, O.F32, raw_np(r_all), [R], 2.0 + float(np.abs(xr.astype(np.float64)).sum()), "all")
+    R2 = O.reduce_all2(O.SUM, O.MUL, O.F32, O.F32, raw_np(a.data), raw_np(b.data), 0.0)
+    S2 = float(np.abs(a.data.double() * b.data.double()).sum())
+    check(O.SUM, O.F32, raw_np(r_all2), [R2], S2, "all2")
+    mr = raw_np(m)
+    Rd = O.reduce_dims(O.SUM, O.IDENTITY, O.F32, O.F32, mr, (512, 8192), (1, 512), 0b10, 0.0)
+    Sd = O.reduce_dims(O.SUM, O.ABS, O.F32, O.F32, mr, (512, 8192), (1, 512), 0b10, 0.0)
+    check(O.SUM, O.F32, raw_np(r_dims), Rd, Sd, "dims")
+    # inclusive prefix sums of values in [0, 1): S_k = R_k, and the tile
+    # scan's longest rounding chain here is below 160 additions
+    Rs = O.scan_dims(O.SUM, O.F32, O.F32, xr, (xr.size,), (1,), 0, 0.0, True)
+    c = raw_np(r_scan).astype(np.float64)
+    assert np.all(np.abs(c - Rs) <= 1e-5 * Rs)
 
 
 def test_launch_event_hook_times_first_pass():

@@ -187,6 +187,11 @@ def test_dtype_op_map_matrix(combo, op):
     if in_t.is_floating_point:
         a = W.normal(n, 8000, in_t)
         b = W.normal(n, 8001, in_t)
+        if out_t == torch.float16:
+            # N(0, 1/16) inputs: sum (a-b)^2 ~ 1.5e4 and sum |a-b| ~ 3.5e4 over
+            # 123,457 pairs stay below float16's 65,504, so the sums compare
+            # finite values (scaling by 1/4 is exact)
+            a, b = a * 0.25, b * 0.25
     else:
         a = W.randint(n, -50000, 50000, 8002, in_t)     # products overflow int32
         b = W.randint(n, -50000, 50000, 8003, in_t)
