@@ -106,7 +106,8 @@ typedef enum {
     RK_OK = 0,
     RK_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size, shape, mask, mode or alignment */
     RK_ERR_UNSUPPORTED = 2,      /* dtype combination outside the table above */
-    RK_ERR_HIP = 3               /* the HIP runtime reported an error */
+    RK_ERR_HIP = 3,              /* the HIP runtime reported an error */
+    RK_ERR_TOO_LARGE = 4         /* rk_reduce_dims_no_workspace: the call needs more than the scratch */
 } rk_status;
 
 typedef enum { RK_OP_SUM = 0, RK_OP_MAX = 1, RK_OP_MIN = 2 } rk_op;
@@ -197,6 +198,28 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
                    const void *ptr, int ndim, const int64_t *shape, const int64_t *strides,
                    uint32_t reduce_mask, const void *init, int mode, void *out,
                    void *workspace, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * rk_reduce_dims without the workspace argument.  Same arguments, results
+ * and errors as rk_reduce_dims, and the same kernels, but the partials go to
+ * a scratch array of the library's own (static device memory of 2 MiB per
+ * GPU, held until the process ends) instead of a workspace; the call
+ * allocates nothing (HOST mode copies its result back from that scratch
+ * rather than using the pinned host buffer).  Every call on one GPU shares
+ * that GPU's scratch: calls on one stream are ordered and safe, but calls
+ * that may overlap on one GPU (different streams, or host threads without
+ * ordering) race on it and must be ordered by the caller.  The scratch keeps
+ * the last call's contents; no call reads what it did not write.  Returns
+ * RK_ERR_TOO_LARGE, before any launch, when the call's plan needs more
+ * workspace than the scratch holds (rk_workspace_size above 2 MiB; no plan
+ * on a 256-CU GPU does).
+ */
+int rk_reduce_dims_no_workspace(int op, int map, int in_dtype, int acc_dtype, int out_dtype,
+                                const void *ptr, int ndim, const int64_t *shape,
+                                const int64_t *strides, uint32_t reduce_mask, const void *init,
+                                int mode, void *out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Scans (prefix folds).  PR #202 (tile scans), opening paragraph:

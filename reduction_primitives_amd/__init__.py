@@ -14,7 +14,7 @@ import ctypes
 import math
 
 from ._native import (  # noqa: F401
-    EXPORTS, KERNEL_NAMES, LIB_PATH, RK_BF16, RK_ERR_HIP, RK_ERR_INVALID_ARGUMENT,
+    EXPORTS, KERNEL_NAMES, LIB_PATH, RK_BF16, RK_ERR_HIP, RK_ERR_INVALID_ARGUMENT, RK_ERR_TOO_LARGE,
     RK_ERR_UNSUPPORTED, RK_F16, RK_F32, RK_F64, RK_I32, RK_I64, RK_KERNEL_ALL,
     RK_KERNEL_ALL2, RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE,
     RK_KERNEL_ROW, RK_KERNEL_SCAN_COLUMNS, RK_KERNEL_SCAN_LINES, RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_TILE, RK_KERNEL_THREAD,
@@ -24,7 +24,8 @@ from ._native import (  # noqa: F401
     RkError, load, rk_debug_device_info, rk_debug_fail_launches, rk_debug_force_wait_timeout,
     rk_debug_set_finish_tag, rk_debug_set_fused_finish, rk_debug_set_launch_events, rk_stream_timeouts,
     rk_debug_stream_read, rk_plan_all, rk_plan_all2, rk_plan_dims,
-    rk_plan_info, rk_plan_scan, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_scan, rk_scan_dims,
+    rk_plan_info, rk_plan_scan, rk_reduce_all, rk_reduce_all2, rk_reduce_dims, rk_reduce_dims_no_workspace,
+    rk_scan, rk_scan_dims,
     rk_scan_workspace_size, rk_workspace_size, status_string)
 
 OPS = {"sum": RK_OP_SUM, "max": RK_OP_MAX, "min": RK_OP_MIN}

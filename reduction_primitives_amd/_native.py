@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librk.so")
 
 # enums of include/rk.h
-RK_OK, RK_ERR_INVALID_ARGUMENT, RK_ERR_UNSUPPORTED, RK_ERR_HIP = 0, 1, 2, 3
+RK_OK, RK_ERR_INVALID_ARGUMENT, RK_ERR_UNSUPPORTED, RK_ERR_HIP, RK_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 RK_OP_SUM, RK_OP_MAX, RK_OP_MIN = 0, 1, 2
 RK_MAP_IDENTITY, RK_MAP_SQUARE, RK_MAP_ABS = 0, 1, 2
 RK_MAP2_MUL, RK_MAP2_SQDIFF, RK_MAP2_ABSDIFF = 0, 1, 2
@@ -31,7 +31,8 @@ EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_di
            "rk_plan_all", "rk_plan_all2", "rk_plan_dims", "rk_debug_set_fused_finish",
            "rk_debug_set_launch_events", "rk_scan_workspace_size", "rk_scan", "rk_scan_dims",
            "rk_plan_scan", "rk_debug_stream_read", "rk_debug_device_info", "rk_debug_set_finish_tag",
-           "rk_stream_timeouts", "rk_debug_force_wait_timeout", "rk_debug_fail_launches")
+           "rk_stream_timeouts", "rk_debug_force_wait_timeout", "rk_debug_fail_launches",
+           "rk_reduce_dims_no_workspace")
 
 
 class rk_plan_info(ctypes.Structure):
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.rk_reduce_all2.restype = i32
     lib.rk_reduce_dims.argtypes = [i32, i32, i32, i32, i32, vp, i32, p64, p64, u32, vp, i32, vp, vp, vp]
     lib.rk_reduce_dims.restype = i32
+    lib.rk_reduce_dims_no_workspace.argtypes = [i32, i32, i32, i32, i32, vp, i32, p64, p64, u32, vp, i32, vp, vp]
+    lib.rk_reduce_dims_no_workspace.restype = i32
     lib.rk_scan_workspace_size.argtypes = [i32, i32, i32, p64, p64, i32]
     lib.rk_scan_workspace_size.restype = sz
     lib.rk_scan.argtypes = [i32, i32, i32, i32, vp, i64, vp, i32, vp, vp, vp]
@@ -142,6 +145,14 @@ def rk_reduce_dims(op, map_, in_dtype, acc_dtype, out_dtype, ptr, ndim, shape, s
     return int(load().rk_reduce_dims(op, map_, in_dtype, acc_dtype, out_dtype, ptr, ndim,
                                      _i64_array(shape), _i64_array(strides), reduce_mask, init,
                                      mode, out, workspace, stream))
+
+
+def rk_reduce_dims_no_workspace(op, map_, in_dtype, acc_dtype, out_dtype, ptr, ndim, shape, strides,
+                                reduce_mask, init, mode, out, stream) -> int:
+    """rk_reduce_dims with the library's scratch in place of a workspace."""
+    return int(load().rk_reduce_dims_no_workspace(op, map_, in_dtype, acc_dtype, out_dtype, ptr, ndim,
+                                                  _i64_array(shape), _i64_array(strides), reduce_mask, init,
+                                                  mode, out, stream))
 
 
 def rk_plan_all(in_dtype, acc_dtype, ptr, n, num_cus=0) -> rk_plan_info:

@@ -403,10 +403,10 @@ int finish_on_host(int op, int acc, uint64_t init_bits, const Finish &fin, const
     return RK_OK;
 }
 
-Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, void *out)
+Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, void *out, bool pinned_ok = true)
 {
     Finish f;
-    f.out = mode == RK_MODE_HOST ? pinned_result() : out;
+    f.out = mode == RK_MODE_HOST ? (pinned_ok ? pinned_result() : nullptr) : out;
     f.host_seq = 0;
     if (mode == RK_MODE_HOST) {
         // a fresh sequence number per host-mode call of this thread
@@ -422,7 +422,7 @@ Finish make_finish(int op, int acc, int out_dtype, int mode, const void *init, v
 
 int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, const AllPlan &a,
               int kernel, const Layout *red, const void *init, int mode, void *out, void *ws,
-              hipStream_t st, const void *ptr2 = nullptr)
+              hipStream_t st, const void *ptr2 = nullptr, bool pinned_ok = true)
 {
     Launch L;
     std::memset(&L, 0, sizeof L);
@@ -453,7 +453,7 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     const int64_t force = g_force_wait.load(std::memory_order_relaxed);
     L.all.spin_limit = force >= 0 ? uint32_t(force) : kFinalSpinLimit;
     L.all.tag_xor = force >= 0 ? 0x80000000u : 0u;
-    L.all.fin = make_finish(op, acc, out_dtype, mode, init, out);
+    L.all.fin = make_finish(op, acc, out_dtype, mode, init, out, pinned_ok);
     L.stream = st;
     L.ev_begin = t_ev_begin;
     L.ev_end = t_ev_end;
@@ -467,6 +467,46 @@ int run_whole(int op, int map, int in, int acc, int out_dtype, const void *ptr, 
     return RK_OK;
 }
 
+// ---- the library's scratch, for rk_reduce_dims_no_workspace: device memory
+// that stands in for the caller's workspace, for callers that cannot
+// allocate.  Every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  The array's name is a host-side stand-in
+// here, never a device address: host code only uses the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(2) << 20;
+namespace scratch_unit {
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+}
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch's device address on the current device (looked up on the
+// first call on each device).
+int scratch_address(void **p)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return RK_ERR_HIP;
+    if (dev >= kMaxDevices)
+        return RK_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch_unit::scratch)) != hipSuccess || !ptr)
+            return RK_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *p = g_scratch_ptr[dev];
+    return RK_OK;
+}
+
+// rk_reduce_dims with the workspace given (scratch: the library's own, of
+// kScratchBytes; host mode then copies its result back from it instead of
+// using the pinned buffer, whose first use allocates).
+int reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,
+                const int64_t *shape, const int64_t *strides, uint32_t reduce_mask, const void *init, int mode,
+                void *out, void *workspace, void *stream, bool scratch);
+
 }  // namespace
 
 extern "C" {
@@ -478,6 +518,7 @@ const char *rk_status_string(int status)
     case RK_ERR_INVALID_ARGUMENT: return "invalid argument";
     case RK_ERR_UNSUPPORTED: return "unsupported dtype combination";
     case RK_ERR_HIP: return "HIP runtime error";
+    case RK_ERR_TOO_LARGE: return "the call needs more workspace than the library's scratch holds (2 MiB)";
     }
     return "unknown status";
 }
@@ -744,6 +785,26 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
                    const int64_t *shape, const int64_t *strides, uint32_t reduce_mask, const void *init, int mode,
                    void *out, void *workspace, void *stream)
 {
+    return reduce_dims(op, map, in_dtype, acc_dtype, out_dtype, ptr, ndim, shape, strides, reduce_mask, init, mode,
+                       out, workspace, stream, false);
+}
+
+int rk_reduce_dims_no_workspace(int op, int map, int in_dtype, int acc_dtype, int out_dtype, const void *ptr,
+                                int ndim, const int64_t *shape, const int64_t *strides, uint32_t reduce_mask,
+                                const void *init, int mode, void *out, void *stream)
+{
+    return reduce_dims(op, map, in_dtype, acc_dtype, out_dtype, ptr, ndim, shape, strides, reduce_mask, init, mode,
+                       out, nullptr, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, const void *ptr, int ndim,
+                const int64_t *shape, const int64_t *strides, uint32_t reduce_mask, const void *init, int mode,
+                void *out, void *workspace, void *stream, bool scratch)
+{
     int rc = check_types(op, map, in_dtype, acc_dtype, out_dtype, mode);
     if (rc)
         return rc;
@@ -763,8 +824,12 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
         return RK_ERR_INVALID_ARGUMENT;
     if (mode != RK_MODE_HOST && out == ptr)
         return RK_ERR_INVALID_ARGUMENT;
-    if (d.ws_bytes > 0 && (!workspace || !aligned(workspace, 8)))
+    if (scratch) {
+        if (d.ws_bytes > kScratchBytes)
+            return RK_ERR_TOO_LARGE;
+    } else if (d.ws_bytes > 0 && (!workspace || !aligned(workspace, 8))) {
         return RK_ERR_INVALID_ARGUMENT;
+    }
     if (d.grid > std::numeric_limits<int32_t>::max())
         return RK_ERR_UNSUPPORTED;
     if (debug_enabled())
@@ -780,12 +845,17 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
         host_finish(op, acc_dtype, start_bits(op, acc_dtype, init), nullptr, 0, out, out_dtype);
         return RK_OK;
     }
+    if (scratch) {
+        rc = scratch_address(&workspace);
+        if (rc)
+            return rc;
+    }
     if (d.kernel == K_ALL)
         return run_whole(op, map, in_dtype, acc_dtype, out_dtype, ptr, d.all, K_ALL, nullptr, init, mode, out,
-                         workspace, st);
+                         workspace, st, nullptr, !scratch);
     if (d.kernel == K_ALL_STRIDED)
         return run_whole(op, map, in_dtype, acc_dtype, out_dtype, ptr, d.all, K_ALL_STRIDED, &d.red, init, mode,
-                         out, workspace, st);
+                         out, workspace, st, nullptr, !scratch);
     if (mode == RK_MODE_HOST)
         return RK_ERR_INVALID_ARGUMENT;   // single outputs always take a whole-array path above
 
@@ -843,6 +913,10 @@ int rk_reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, 
         return RK_ERR_HIP;
     return dispatch(in_dtype, L);
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t rk_scan_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64_t *shape, const int64_t *strides,
                               int dim)
