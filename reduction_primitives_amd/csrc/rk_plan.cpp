@@ -34,6 +34,34 @@ size_t round_up_256(size_t b) { return (b + 255) & ~size_t(255); }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool view_fits(int ndim, const int64_t *shape, const int64_t *strides, uint32_t mask, int isz)
+{
+    // Every element count, offset and byte count the planner and the kernels
+    // form from a view stays below 2^62: extents and strides are each below
+    // it, and so are the outputs (at 8 bytes each), the elements, and the
+    // bytes from the first element to the last, all computed with overflow
+    // checks (128-bit products).
+    constexpr __int128 kLimit = __int128(1) << 62;
+    __int128 n_out = 1, m = 1, span = 0;
+    for (int i = 0; i < ndim; ++i) {
+        if (shape[i] < 0 || strides[i] < 0 || shape[i] >= kLimit || strides[i] >= kLimit)
+            return false;
+        if ((mask >> i) & 1)
+            m *= shape[i];
+        else
+            n_out *= shape[i];
+        if (n_out >= kLimit / 8 || m >= kLimit)      // both stay below 2^62: their product fits 128 bits
+            return false;
+        if (shape[i] > 0)
+            span += __int128(shape[i] - 1) * strides[i];
+        if (span >= kLimit)
+            return false;
+    }
+    if (n_out * m == 0)
+        return true;                                 // nothing is read
+    return n_out * m * isz < kLimit && (span + 1) * isz < kLimit;
+}
+
 int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus, AllPlan *p)
 {
     if (!p || n < 0 || !dtype_known(in_dtype) || !dtype_known(acc_dtype))
@@ -41,6 +69,8 @@ int plan_all(int in_dtype, int acc_dtype, uintptr_t addr, int64_t n, int num_cus
     if (num_cus <= 0)
         num_cus = tune::kDefaultCus;
     const int isz = dtype_size(in_dtype);
+    if (n >= (int64_t(1) << 62) / isz)
+        return ST_INVALID;                  // bytes of the input beyond 2^62
     AllPlan a;
     a.n = n;
     a.vec = 16 / isz;
@@ -123,7 +153,7 @@ static void push_dim(Layout &l, int64_t e, int64_t s)
 {
     if (l.nd > 0) {
         const int i = l.nd - 1;
-        if (s == l.str[i] * l.ext[i]) {
+        if (__int128(s) == __int128(l.str[i]) * l.ext[i]) {   // exact, for any strides view_fits accepts
             l.ext[i] *= e;
             return;
         }
@@ -146,6 +176,8 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         num_cus = tune::kDefaultCus;
     const int isz = dtype_size(in_dtype);
     const int asz = dtype_size(acc_dtype);
+    if (!view_fits(ndim, shape, strides, mask, isz))
+        return ST_INVALID;
 
     DimsPlan d;
     int64_t n_out = 1, m = 1;
@@ -422,6 +454,8 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
     if (num_cus <= 0)
         num_cus = tune::kDefaultCus;
     const int isz = dtype_size(in_dtype), osz = dtype_size(out_dtype);
+    if (!view_fits(ndim, shape, strides, 0u, isz))
+        return ST_INVALID;
     ScanPlan d;
     int64_t total = 1, ostr[kMaxDims];
     for (int i = 0; i < ndim; ++i) {
@@ -445,7 +479,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             continue;
         if (k.nd > 0) {
             const int j = k.nd - 1;
-            if (strides[i] == k.str[j] * k.ext[j] && ostr[i] == d.kept_out[j] * k.ext[j]) {
+            if (__int128(strides[i]) == __int128(k.str[j]) * k.ext[j] && ostr[i] == d.kept_out[j] * k.ext[j]) {
                 k.ext[j] *= shape[i];
                 continue;
             }
@@ -513,6 +547,8 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             const int64_t r = (tune::kScanColBlock / lanes) * tune::kScanColRows;
             const int64_t ctpr = ceil_div(k.ext[0], w), ct = runs * ctpr, ch = ceil_div(d.m, r);
             const int64_t tiles = ct * ch;
+            if (tiles > INT32_MAX)              // tiles are numbered by a 32-bit counter (both
+                return ST_INVALID;              // geometries: the workspace covers either)
             ws = std::max(ws, round_up_256(size_t(scan_columns_state_bytes(tiles, w))));
             if (vec == vec_ok) {
                 d.vec = vec ? v : 1;
@@ -525,8 +561,6 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             }
         }
         d.ws_bytes = ws;
-        if (d.tiles > INT32_MAX)                // tiles are numbered by a 32-bit counter
-            return ST_INVALID;
     } else {
         d.kernel = SK_LINES;
         d.block = tune::kScanBlock;

@@ -156,4 +156,10 @@ int select_strided_kernel(int64_t run_len, int64_t n_out, int64_t m, int in_size
 
 size_t round_up_256(size_t b);
 
+// Whether a view's counts and offsets stay below 2^62: extents and strides,
+// outputs (the kept dims' product, at up to 8 bytes each), elements and
+// bytes (at isz bytes each) from the first element to the last.  Bit d of
+// mask marks dim d as reduced (0 for a scan: every element is an output).
+bool view_fits(int ndim, const int64_t *shape, const int64_t *strides, uint32_t mask, int isz);
+
 }  // namespace rk

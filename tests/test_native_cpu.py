@@ -220,6 +220,28 @@ def test_plan_rejects_bad_layouts():
         rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, 2, (3, 4), (1, 3), 0b100)
 
 
+def test_plan_rejects_views_beyond_62_bit_counts():
+    """Extents, strides, element counts and byte spans at or above 2^62 are
+    rejected before any product could overflow (the planner's 64-bit
+    arithmetic, exercised at random under the sanitizers in
+    tests/test_sanitizers.py); the largest views below the limit plan."""
+    rk = _rk()
+    big = 2**62
+    bad = [((big,), (1,), 1), ((2**31, 2**31), (1, 2**31), 1), ((4, 5), (1, big // 2), 1),
+           ((2**32, 2**30), (1, 2**32), 2), ((3, 4), (1, big), 1), ((2**60,), (1,), 1)]
+    for shape, strides, mask in bad:
+        with pytest.raises(rk.RkError):
+            rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, len(shape), shape, strides, mask, 256)
+        assert rk.rk_workspace_size(rk.RK_F32, rk.RK_F32, len(shape), shape, strides, mask) == 0
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 2**60, 256)
+    with pytest.raises(rk.RkError):
+        rk.rk_plan_scan(rk.RK_F32, rk.RK_F32, rk.RK_F32, 0, 0, 2, (2**31, 2**31), (1, 2**31), 0, 256)
+    # just below: 2^59 f32 elements (2^61 bytes) in one dim, and a broadcast dim
+    assert rk.rk_plan_all(rk.RK_F32, rk.RK_F32, 0, 2**59, 256).grid == 1024
+    assert rk.rk_plan_dims(rk.RK_F32, rk.RK_F32, 0, 2, (2**20, 2**30), (1, 0), 2, 256).n_out == 2**20
+
+
 # -------------------------------------------------------------- validation
 
 FAKE = 0x10000          # never dereferenced: every call below fails validation
