@@ -54,8 +54,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=30.0,
                     help="seconds of oracle work allowed for the CPU baseline")
-    ap.add_argument("--per-call-reps", type=int, default=5,
-                    help="reps of the per-call table (0 skips it)")
+    ap.add_argument("--per-call-reps", type=int, default=50,
+                    help="reps per round of the per-call table (0 skips it)")
+    ap.add_argument("--per-call-rounds", type=int, default=3,
+                    help="rounds of the per-call table (the round with the lowest median is reported)")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time every configuration's calls one by one (cold and warm)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -273,43 +275,50 @@ def traffic_from_profile():
         return None
 
 
-def per_call_table(calls, torch, reps, dev):
-    """Per call: warm (the same input again, back to back) and cold (the
-    Infinity Cache first filled with other, clean lines by reading a 1 GiB
-    buffer) times of the whole rk call, min and median."""
+def per_call_table(calls, torch, reps, rounds, dev):
+    """Per call, the whole rk call timed cold (the Infinity Cache first filled
+    with other, clean lines by reading a 1 GiB buffer) and warm (the same call
+    again right after, back to back): `reps` samples of each in each of
+    `rounds` rounds, the calls interleaved within a round.  Reported per call
+    and mode: the min and the median of the round with the lowest median."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    ts = {c.name: {m: [[] for _ in range(rounds)] for m in ("cold", "warm")} for c in calls}
+
+    def one(c):
+        # queue work ahead of a device-mode call, so its start event does not
+        # wait on the host's launch latency; a host-mode call drains the
+        # stream itself and is timed by the wall clock of the call
+        if c.name.endswith("_host"):
+            t0 = time.perf_counter()
+            c()
+            return (time.perf_counter() - t0) * 1e6
+        torch.cuda._sleep(200_000)
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        c()
+        e.record()
+        e.synchronize()
+        return b.elapsed_time(e) * 1e3
+
+    for r in range(rounds):
+        for _ in range(reps):
+            for c in calls:
+                flush.sum()
+                torch.cuda.synchronize()
+                ts[c.name]["cold"][r].append(one(c))
+                torch.cuda.synchronize()
+                ts[c.name]["warm"][r].append(one(c))
     table = {}
     for c in calls:
         rows = {}
         for mode in ("warm", "cold"):
-            ts = []
-            for _ in range(reps):
-                host = c.name.endswith("_host")
-                if mode == "cold":
-                    flush.sum()
-                torch.cuda.synchronize()
-                # queue work ahead of a device-mode call, so its start event
-                # does not wait on the host's launch latency; a host-mode call
-                # drains the stream itself and is timed by the wall clock
-                if not host:
-                    torch.cuda._sleep(200_000)
-                if host:
-                    # the call returns once its value is on the host: time the call alone
-                    t0 = time.perf_counter()
-                    c()
-                    ts.append((time.perf_counter() - t0) * 1e6)
-                    continue
-                b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                b.record()
-                c()
-                e.record()
-                e.synchronize()
-                ts.append(b.elapsed_time(e) * 1e3)
-            rows[mode] = dict(us_min=round(min(ts), 2), us_median=round(statistics.median(ts), 2),
-                              GBps=round(c.bytes_alg / (min(ts) * 1e-6) / 1e9, 1))
+            best = min(ts[c.name][mode], key=statistics.median)
+            rows[mode] = dict(us_min=round(min(best), 2), us_median=round(statistics.median(best), 2),
+                              GBps=round(c.bytes_alg / (min(best) * 1e-6) / 1e9, 1),
+                              GBps_median=round(c.bytes_alg / (statistics.median(best) * 1e-6) / 1e9, 1))
         table[c.name] = rows
-        log(f"  {c.name:28s} warm {rows['warm']['us_min']:8.1f} us ({rows['warm']['GBps']:7.1f} GB/s)"
-            f"  cold {rows['cold']['us_min']:8.1f} us ({rows['cold']['GBps']:7.1f} GB/s)")
+        log(f"  {c.name:28s} warm {rows['warm']['us_min']:8.1f} / {rows['warm']['us_median']:8.1f} us"
+            f"  cold {rows['cold']['us_min']:8.1f} / {rows['cold']['us_median']:8.1f} us (min / median)")
     del flush
     return table
 
@@ -480,8 +489,9 @@ def configs_table(rk, torch, dev, reps):
 def read_ceiling(rk, torch, bufs, launches=30):
     """The device's streaming-read ceiling: the library's read-only kernel
     (16-byte non-temporal loads, one integer operation per word, no stores)
-    over the same 400 MB inputs as the dominant kernel, at a few grid sizes,
-    each launch timed by events around it as the dominant kernel's are.
+    over buffers of the size a set of calls reads (the 400 MB whole-array
+    inputs, the 268 MB matrices), at a few grid sizes, each launch timed by
+    events around it as the calls' kernels are.
     Consecutive launches read different buffers, so none finds the previous
     one's lines in the Infinity Cache.  Returns the best grid's figures."""
     sink = torch.zeros(1, dtype=torch.int32, device=bufs[0].device)
@@ -493,11 +503,16 @@ def read_ceiling(rk, torch, bufs, launches=30):
             rk.rk_debug_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, sink.data_ptr(), st)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(launches)]
+        for b, e in ev:
+            b.record(); e.record()      # creates the HIP events
         torch.cuda.synchronize()
         for i, (b, e) in enumerate(ev):
-            b.record()
-            rk.rk_debug_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, sink.data_ptr(), st)
-            e.record()
+            # the events on the kernel's own dispatch packet, as the calls' are
+            rk.rk_debug_set_launch_events(ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(e.cuda_event))
+            try:
+                rk.rk_debug_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, grid, sink.data_ptr(), st)
+            finally:
+                rk.rk_debug_set_launch_events(None, None)
         torch.cuda.synchronize()
         us = [b.elapsed_time(e) * 1e3 for b, e in ev]
         row = dict(grid=grid, avg_launch_us=round(statistics.mean(us), 2), min_us=round(min(us), 2))
@@ -536,9 +551,9 @@ def main():
     kernels = plan_names(rk, torch)
     bytes_step = sum(c.bytes_alg for c in calls)
 
-    def step(events=None):
+    def step(events=None, every=False):
         for c in calls:
-            if events is not None and c.timed:
+            if events is not None and (c.timed or every):
                 b, e = events.pop()
                 rk.rk_debug_set_launch_events(ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(e.cuda_event))
                 try:
@@ -576,16 +591,45 @@ def main():
     log(f"step: {ms_per_step:.3f} ms, {value:.1f} GB/s aggregate ({value / PEAK_GBPS:.1%} of peak)")
     log(f"dominant kernel {DOMINANT}: {avg_launch_s * 1e6:.1f} us per launch, {achieved:.1f} GB/s")
 
+    # every call's first kernel on its own dispatch packet's events, over as
+    # many more steps (outside the timed region above)
+    ev_all = []
+    for _ in range(len(calls) * args.steps):
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record(); e.record()
+        ev_all.append((b, e))
+    torch.cuda.synchronize()
+    pending = list(reversed(ev_all))
+    for _ in range(args.steps):
+        step(pending, every=True)
+    torch.cuda.synchronize()
+    per_kernel_us = {c.name: [] for c in calls}
+    for i, (b, e) in enumerate(ev_all):
+        per_kernel_us[calls[i % len(calls)].name].append(b.elapsed_time(e) * 1e3)
+
     ceiling = read_ceiling(rk, torch, keep[0] + keep[1])
+    ceiling_268 = read_ceiling(rk, torch, keep[2])
     mem = rk.rk_debug_device_info()
     log(f"read ceiling: {ceiling['GBps']:.1f} GB/s (grid {ceiling['grid']}); dominant kernel at "
         f"{achieved / ceiling['GBps']:.1%} of it")
+    log(f"read ceiling over 268 MB: {ceiling_268['GBps']:.1f} GB/s (grid {ceiling_268['grid']})")
+    kernels_table = {}
+    for c in calls:
+        us = statistics.mean(per_kernel_us[c.name])
+        ceil = ceiling_268 if "8192" in c.name else ceiling
+        gbps = c.bytes_alg / (us * 1e-6) / 1e9
+        kernels_table[c.name] = dict(avg_us=round(us, 2), min_us=round(min(per_kernel_us[c.name]), 2),
+                                     GBps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_GBPS, 4),
+                                     frac_of_read_ceiling=round(us and ceil["avg_launch_us"] / us, 4))
+        log(f"  kernel of {c.name:28s} {us:7.2f} us avg  {gbps:7.1f} GB/s  {gbps / PEAK_GBPS:6.1%} of peak  "
+            f"{ceil['avg_launch_us'] / us:6.1%} of the read ceiling at its size")
 
     host_value = outs["host"].value
     snap = {k: (v.detach().cpu().clone() if hasattr(v, "detach") else v) for k, v in outs.items()}
-    per_call = per_call_table(calls, torch, args.per_call_reps, dev) if args.per_call_reps > 0 else None
+    per_call = (per_call_table(calls, torch, args.per_call_reps, args.per_call_rounds, dev)
+                if args.per_call_reps > 0 else None)
 
-    configs = configs_table(rk, torch, dev, max(3, args.per_call_reps)) if args.all_configs else None
+    configs = configs_table(rk, torch, dev, 5) if args.all_configs else None
 
     cpu, parity = None, None
     if not args.no_cpu:
@@ -634,10 +678,15 @@ def main():
             "read_ceiling_GBps": ceiling["GBps"],
             "read_ceiling_grid": ceiling["grid"],
             "frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4),
+            "read_ceiling_268MB_GBps": ceiling_268["GBps"],
+            "read_ceiling_268MB_us": ceiling_268["avg_launch_us"],
         },
+        "kernels": kernels_table,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "per_call": per_call,
+        "per_call_method": (f"{args.per_call_reps} reps x {args.per_call_rounds} rounds, calls interleaved; "
+                            "min and median of the round with the lowest median" if per_call else None),
         "configs": configs,
     }
     del keep

@@ -349,10 +349,11 @@ int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, co
  * wide.  Returns the previous setting (1 or 0). */
 int rk_debug_set_fused_finish(int enable);
 
-/* Benchmark hook: while both are non-NULL, every later rk_reduce_* call made
- * by this host thread records hipEvent_t `begin` immediately before its first
- * kernel launch and `end` immediately after it, on the call's stream.  Pass
- * NULLs to stop.  Returns an rk_status. */
+/* Benchmark hook: while both are non-NULL, every later rk_reduce_*, rk_scan*
+ * and rk_debug_stream_read call made by this host thread records hipEvent_t
+ * `begin` when its first kernel starts and `end` when it ends, on the call's
+ * stream (the events ride on that kernel's dispatch packet).  Pass NULLs to
+ * stop.  Returns an rk_status. */
 int rk_debug_set_launch_events(void *begin, void *end);
 
 /* Test hook: make the last whole-array finishing tag of `stream`'s slot `e`
@@ -368,7 +369,9 @@ int rk_debug_set_finish_tag(void *stream, uint32_t e);
  * does one integer operation per word; it computes nothing a caller can use.
  * `ptr`: device memory, 16-byte aligned; nbytes: a multiple of 16.  `sink`:
  * one 4-byte device word that the kernel may overwrite with an unspecified
- * value.  Asynchronous.  Returns an rk_status. */
+ * value.  Asynchronous.  Honours rk_debug_set_launch_events like the
+ * reductions, so both are timed on their own dispatch packets.  Returns an
+ * rk_status. */
 int rk_debug_stream_read(const void *ptr, int64_t nbytes, int grid, void *sink, void *stream);
 
 /* The current device's compute units, memory clock (kHz) and memory bus

@@ -6,6 +6,7 @@
 // combination equals a fixed magic word.  A whole-array reduction moves the
 // same bytes, so its time against this kernel's is the part of the
 // achievable read bandwidth it reaches.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -46,12 +47,20 @@ __global__ __launch_bounds__(kReadBlock) void k_stream_read(const u32x4_t *x, in
 }  // namespace
 
 // nvec 16-byte vectors at x (16-byte aligned); grid blocks of 256 threads.
-int launch_stream_read(const void *x, int64_t nvec, int grid, void *sink, hipStream_t st)
+// With an event pair the events ride on the kernel's own dispatch packet, as
+// the reductions' first launches do under the same timing hook.
+int launch_stream_read(const void *x, int64_t nvec, int grid, void *sink, hipStream_t st, void *ev_begin,
+                       void *ev_end)
 {
     if (nvec <= 0)
         return 0;
-    k_stream_read<<<grid, kReadBlock, 0, st>>>(static_cast<const u32x4_t *>(x), nvec,
-                                                static_cast<uint32_t *>(sink));
+    const u32x4_t *p = static_cast<const u32x4_t *>(x);
+    uint32_t *s = static_cast<uint32_t *>(sink);
+    if (ev_begin && ev_end)
+        hipExtLaunchKernelGGL(k_stream_read, dim3(grid), dim3(kReadBlock), 0, st, static_cast<hipEvent_t>(ev_begin),
+                              static_cast<hipEvent_t>(ev_end), 0, p, nvec, s);
+    else
+        k_stream_read<<<grid, kReadBlock, 0, st>>>(p, nvec, s);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -27,7 +27,8 @@
 #include "rk_scan_plan.hpp"
 
 namespace rk {
-int launch_stream_read(const void *x, int64_t nvec, int grid, void *sink, hipStream_t st);  // diag.hip
+int launch_stream_read(const void *x, int64_t nvec, int grid, void *sink, hipStream_t st, void *ev_begin,
+                       void *ev_end);  // diag.hip
 }
 
 namespace {
@@ -615,7 +616,8 @@ int rk_debug_stream_read(const void *ptr, int64_t nbytes, int grid, void *sink, 
         return RK_OK;
     if (!ptr || !sink || reinterpret_cast<uintptr_t>(ptr) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
         return RK_ERR_INVALID_ARGUMENT;
-    return launch_stream_read(ptr, nbytes / 16, grid > 0 ? grid : 2048, sink, static_cast<hipStream_t>(stream))
+    return launch_stream_read(ptr, nbytes / 16, grid > 0 ? grid : 2048, sink, static_cast<hipStream_t>(stream),
+                              t_ev_begin, t_ev_end)
                ? RK_ERR_HIP : RK_OK;
 }
 

@@ -588,6 +588,24 @@ __device__ __forceinline__ T load_partial(const T *p)
                                             __HIP_MEMORY_SCOPE_AGENT));
 }
 
+// Take wave-uniform values -- kernel arguments, addresses of library
+// memory -- into scalar registers here, all together.  Left to itself the
+// compiler loads a kernel's arguments in several dependent batches, each a
+// memory round trip, before a block issues its first data load.
+// (One asm statement for all of them: with several, the compiler may wait for
+// the first statement's loads before it issues the next statement's.)
+template <class T0, class T1, class T2, class T3, class T4, class T5, class T6, class T7, class T8, class T9,
+          class T10, class T11, class T12, class T13, class T14, class T15, class T16, class T17, class T18, class T19>
+__device__ __forceinline__ void sgpr_ready(const T0 &v0, const T1 &v1, const T2 &v2, const T3 &v3, const T4 &v4,
+                                           const T5 &v5, const T6 &v6, const T7 &v7, const T8 &v8, const T9 &v9,
+                                           const T10 &v10, const T11 &v11, const T12 &v12, const T13 &v13,
+                                           const T14 &v14, const T15 &v15, const T16 &v16, const T17 &v17,
+                                           const T18 &v18, const T19 &v19)
+{
+    asm volatile("" ::"s"(v0), "s"(v1), "s"(v2), "s"(v3), "s"(v4), "s"(v5), "s"(v6), "s"(v7), "s"(v8), "s"(v9),
+                 "s"(v10), "s"(v11), "s"(v12), "s"(v13), "s"(v14), "s"(v15), "s"(v16), "s"(v17), "s"(v18), "s"(v19));
+}
+
 // Keep every load of an unrolled group ahead of the arithmetic that consumes
 // it: without this the scheduler may interleave a wait (and cut the loads in
 // flight) to pair loads up for v_max3 and the like.
@@ -655,12 +673,17 @@ static __device__ __attribute__((aligned(128))) uint64_t g_final[kArriveSlots * 
 }
 using RK_UNIT::g_final;
 
-// The call's tag (read when a block starts; thread 0 only).
-__device__ __forceinline__ uint32_t final_tag(int slot)
+// The slot's last tag E (read when a block starts; thread 0 only): the
+// call's tag is E + 1.  Callers add the 1 only where they use the tag, at the
+// block's end, so nothing waits for this load before the block's first tiles
+// are loaded: it returns while they are in flight.
+__device__ __forceinline__ uint32_t last_tag(int slot)
 {
+    // the low 32 bits of the 64-bit word (tags fit 32 bits): a 64-bit load
+    // would leave a dead half whose register reuse waits for the load
     const int64_t copy = int64_t(blockIdx.x % kFinalTagCopies) * 16;
-    return uint32_t(__hip_atomic_load(&g_final[int64_t(slot) * kFinalSlotWords + copy], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT)) + 1u;
+    return __hip_atomic_load(reinterpret_cast<const uint32_t *>(&g_final[int64_t(slot) * kFinalSlotWords + copy]),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class Acc>
@@ -755,20 +778,52 @@ __global__ void k_set_final_tag(int slot, uint32_t e)
 
 // ------------------------------------------------------------------ misc
 
-// Offset of linear index idx in a column-major layout of nd <= 4 dims.
+// Offset of linear index idx (below the product of the extents) in a
+// column-major layout of nd <= 4 dims.  The last dim takes what is left of
+// idx without a division: a 64-bit division is a long VALU sequence, and the
+// kernels form these offsets before their first loads.
 __device__ __forceinline__ int64_t layout_offset(int nd, const int64_t *ext, const int64_t *str,
                                                  int64_t idx)
 {
     int64_t off = 0;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        if (d < nd) {
+        if (d + 1 < nd) {
             const int64_t q = idx / ext[d];
             off += (idx - q * ext[d]) * str[d];
             idx = q;
+        } else if (d + 1 == nd) {
+            off += idx * str[d];
         }
     }
     return off;
+}
+
+// The same for an index below 2^32 (so is every extent it divides by):
+// 32-bit divisions, a handful of instructions each.
+__device__ __forceinline__ int64_t layout_offset32(int nd, const int64_t *ext, const int64_t *str, uint32_t idx)
+{
+    int64_t off = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        if (d + 1 < nd) {
+            const uint32_t e = uint32_t(ext[d]);
+            const uint32_t q = idx / e;
+            off += int64_t(idx - q * e) * str[d];
+            idx = q;
+        } else if (d + 1 == nd) {
+            off += int64_t(idx) * str[d];
+        }
+    }
+    return off;
+}
+
+// a / b for 0 <= a and 0 < b, in 32-bit arithmetic when both fit.
+__device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b)
+{
+    if (uint64_t(a) <= 0xffffffffu && uint64_t(b) <= 0xffffffffu)
+        return uint32_t(a) / uint32_t(b);
+    return a / b;
 }
 
 // A position in a column-major layout of nd <= 4 dims that moves forward by

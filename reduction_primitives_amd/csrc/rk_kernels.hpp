@@ -103,20 +103,24 @@ __device__ __forceinline__ void fold_partials_and_finish(Acc *ws, int grid, cons
     }
 }
 
-// Start of a first-pass block: the call's tag when it finishes by collection
-// (thread 0; read early, so the load is long done by the end).
+// Start of a first-pass block: the slot's last tag E, used when the call
+// finishes by collection (read early, so the load is long done by the end;
+// the call's tag is E + 1, formed in the epilogue).  Every thread loads it,
+// unconditionally: a load made in a branch is waited for where the branch
+// ends, which would hold the block's first tile loads behind a device-scope
+// round trip.  (One load per wave; calls without a slot read slot 0's copy
+// and never use it.)
 __device__ __forceinline__ uint32_t whole_prologue(const AllArgs &a)
 {
-    return threadIdx.x == 0 && a.grid > 1 && a.grid <= kFinalCapacity && a.arrive_slot >= 0
-               ? final_tag(a.arrive_slot)
-               : 0u;
+    return last_tag(a.arrive_slot >= 0 ? a.arrive_slot : 0);
 }
 
 // End of a first-pass block holding its reduced value v (valid in thread 0)
-// and the call's tag (thread 0).
+// and the slot's last tag E from whole_prologue (thread 0).
 template <class Acc, class Op, int BLOCK>
-__device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v, uint32_t tag)
+__device__ __forceinline__ void whole_epilogue(const AllArgs &a, Acc v, uint32_t last_e)
 {
+    const uint32_t tag = last_e + 1u;
     Acc *ws = static_cast<Acc *>(a.ws);
     if (a.grid == 1) {                          // the whole input in one block
         if (threadIdx.x == 0) {
@@ -172,7 +176,10 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
 {
     using S = typename InTraits<In>::S;
     constexpr int V = InTraits<In>::vec;
-    const uint32_t tag = whole_prologue(a);
+    sgpr_ready(a.x, a.head, a.nvec, a.tail, a.arrive_slot, gridDim.x, static_cast<const void *>(g_final), a.grid,
+               a.ws, a.fin.out, a.fin.init_bits, a.fin.mode, a.fin.out_dtype, a.fin.host_seq, a.spin_limit, a.tag_xor,
+               a.n, a.y, blockIdx.x, a.nd);
+    const uint32_t last_e = whole_prologue(a);
     const S *x = static_cast<const S *>(a.x);
     const u32x4 *body = reinterpret_cast<const u32x4 *>(x + a.head);
 
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1(AllArgs a)
         acc0[i] = Op::apply(acc0[i], acc1[i]);
     Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
     v = block_reduce<Op, BLOCK>(v);
-    whole_epilogue<Acc, Op, BLOCK>(a, v, tag);
+    whole_epilogue<Acc, Op, BLOCK>(a, v, last_e);
 }
 
 // Single output over a non-contiguous view: element i lives at
@@ -225,7 +232,7 @@ template <class In, class Acc, class Op, class Map, int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
 {
     using S = typename InTraits<In>::S;
-    const uint32_t tag = whole_prologue(a);
+    const uint32_t last_e = whole_prologue(a);
     const S *x = static_cast<const S *>(a.x);
     Acc acc[UNROLL];
 #pragma unroll
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(BLOCK) void k_all_pass1_strided(AllArgs a)
     }
     Acc v = fold_all<Acc, Op, UNROLL>(acc);
     v = block_reduce<Op, BLOCK>(v);
-    whole_epilogue<Acc, Op, BLOCK>(a, v, tag);
+    whole_epilogue<Acc, Op, BLOCK>(a, v, last_e);
 }
 
 template <class Acc, class Op, int BLOCK>
@@ -326,7 +333,10 @@ template <class In, class Acc, class Op, class Map2, int BLOCK, int UNROLL, int 
 __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
 {
     using S = typename InTraits<In>::S;
-    const uint32_t tag = whole_prologue(a);
+    sgpr_ready(a.x, a.y, a.head, a.nvec, a.tail, a.arrive_slot, gridDim.x, static_cast<const void *>(g_final),
+               a.grid, a.ws, a.fin.out, a.fin.init_bits, a.fin.mode, a.fin.out_dtype, a.fin.host_seq, a.spin_limit,
+               a.tag_xor, a.n, blockIdx.x, a.nd);
+    const uint32_t last_e = whole_prologue(a);
     constexpr bool VECTOR = MODE != ALL2_ELEMENTS;
     constexpr int V = VECTOR ? InTraits<In>::vec : 1;
     const S *x = static_cast<const S *>(a.x);
@@ -450,7 +460,7 @@ __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
         acc0[i] = Op::apply(acc0[i], acc1[i]);
     Acc v = Op::apply(fold_all<Acc, Op, V>(acc0), s);
     v = block_reduce<Op, BLOCK>(v);
-    whole_epilogue<Acc, Op, BLOCK>(a, v, tag);
+    whole_epilogue<Acc, Op, BLOCK>(a, v, last_e);
 }
 
 // ======================================================================= dims
@@ -461,7 +471,13 @@ __global__ __launch_bounds__(BLOCK) void k_all2_pass1(AllArgs a)
 // W * sizeof(In) bytes per instruction.  Row groups stride over the reduced
 // dim with UNROLL loads in flight, then fold together (in-wave lane moves,
 // then LDS across waves).  CL == BLOCK is the thread-per-output shape.
-template <class In, class Acc, class Op, class Map, bool VECTOR, int CL, int BLOCK, int UNROLL, bool NT>
+// PLAIN: one reduced dim (no segments) and at most one kept dim after the
+// run's -- a 2-d array, or the middle dim of a 3-d one.  The block then finds
+// its place from a few arguments: the general form keeps the segment and
+// run layouts in scalar registers, whose loads the compiler spreads over
+// several dependent batches before the first data load.
+template <class In, class Acc, class Op, class Map, bool VECTOR, int CL, int BLOCK, int UNROLL, bool NT,
+          bool PLAIN = false>
 __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 {
     using S = typename InTraits<In>::S;
@@ -473,23 +489,39 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
 
     const int c = (int)(threadIdx.x % CL);
     const int rg = (int)(threadIdx.x / CL);
+    if constexpr (PLAIN)
+        sgpr_ready(a.x, a.tiles, a.tiles_per_run, a.run_len, a.s_red, a.row_len, a.rows_per_split, a.outer_str[0],
+                   a.split, a.ws, a.n_out, a.arrive_slot, a.segs, a.fin.out, a.fin.init_bits, a.fin.mode,
+                   a.fin.out_dtype, blockIdx.x, gridDim.x, a.splits_per_seg);
     // neighbouring tiles on one XCD share its L2 where a tile row is narrower
     // than a line (the tiled shape); columns tiles read whole lines, and
     // spread round-robin over the XCDs they measured 0.5-2% faster
     constexpr bool kColumns = NT && CL < BLOCK;
     const uint32_t b = kColumns ? blockIdx.x : xcd_block(blockIdx.x, gridDim.x);
-    const int64_t tile = int64_t(b % (uint64_t)a.tiles);
-    const int sp = (int)(b / (uint64_t)a.tiles);
-    const int64_t run = tile / a.tiles_per_run;
-    const int64_t col0 = (tile - run * a.tiles_per_run) * W;
+    // tiles, runs and splits number below 2^31 (the grid does): 32-bit
+    // arithmetic for the block's place, before its first loads
+    const uint32_t tiles32 = uint32_t(a.tiles), tpr32 = uint32_t(a.tiles_per_run);
+    const uint32_t tile32 = b % tiles32;
+    const int64_t tile = tile32;
+    const int sp = (int)(b / tiles32);
+    const uint32_t run32 = tile32 / tpr32;
+    const int64_t run = run32;
+    const int64_t col0 = int64_t(tile32 - run32 * tpr32) * W;
     const int64_t col = col0 + int64_t(c) * V;
     const bool active = col < a.run_len;       // vector loads: run_len % V == 0
-    const int64_t in_base = layout_offset(a.outer_nd, a.outer_ext, a.outer_str, run) + col;
+    const int64_t in_base =
+        (PLAIN ? int64_t(run32) * a.outer_str[0] : layout_offset32(a.outer_nd, a.outer_ext, a.outer_str, run32)) + col;
     // this block's share of the reduced dims: segments [k0, k1) and, in
     // each, rows [j0, j1) of the row dim
     int64_t k0, k1, j0, j1;
-    if (a.splits_per_seg > 1) {
-        k0 = sp / a.splits_per_seg;
+    if (PLAIN) {                                // one segment: split units are pieces of the rows
+        k0 = 0;
+        k1 = a.segs;                            // 1; left to the argument, the tail group below keeps
+                                                // the general form's registers (known to be 1 it took 236 VGPRs)
+        j0 = int64_t(sp) * a.rows_per_split;
+        j1 = j0 + a.rows_per_split < a.row_len ? j0 + a.rows_per_split : a.row_len;
+    } else if (a.splits_per_seg > 1) {
+        k0 = uint32_t(sp) / uint32_t(a.splits_per_seg);
         k1 = k0 + 1;
         j0 = (sp - k0 * a.splits_per_seg) * a.rows_per_split;
         j1 = j0 + a.rows_per_split < a.row_len ? j0 + a.rows_per_split : a.row_len;
@@ -506,7 +538,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
     set_identity<Acc, Op>(acc0);
     set_identity<Acc, Op>(acc1);
     for (int64_t k = k0; active && k < k1; ++k) {
-        const S *x = xt + layout_offset(a.seg_nd, a.seg_ext, a.seg_str, k);
+        const S *x = PLAIN ? xt : xt + layout_offset(a.seg_nd, a.seg_ext, a.seg_str, k);
         int64_t j = j0 + rg;
         // full groups of UNROLL rows per thread, every load issued first
         for (; j + int64_t(UNROLL - 1) * RG < j1; j += int64_t(UNROLL) * RG) {
@@ -662,14 +694,17 @@ __global__ __launch_bounds__(BLOCK) void k_dims_row(DimsArgs a)
     // the wave's number, read as uniform so that the index arithmetic below
     // runs on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    sgpr_ready(a.x, a.n_out, a.split, a.splits_per_seg, a.rows_per_split, a.row_len, a.segs_per_split, a.segs,
+               a.kept_nd, a.kept_ext[0], a.kept_str[0], a.seg_nd, a.arrive_slot, a.ws, a.fin.out, a.fin.mode,
+               a.fin.init_bits, a.fin.out_dtype, a.kept_ext[1], a.kept_str[1]);
     const int64_t unit = int64_t(blockIdx.x) * (BLOCK / 64) + wave;
     if (unit >= a.n_out * a.split)
         return;                                 // whole wave; no block barrier below
-    const int64_t o = unit / a.split;
+    const int64_t o = a.split == 1 ? unit : div_nonneg(unit, a.split);
     const int sp = (int)(unit - o * a.split);
     int64_t k0, k1, j0, j1;
     if (a.splits_per_seg > 1) {
-        k0 = sp / a.splits_per_seg;
+        k0 = uint32_t(sp) / uint32_t(a.splits_per_seg);
         k1 = k0 + 1;
         j0 = (sp - k0 * a.splits_per_seg) * a.rows_per_split;
         j1 = j0 + a.rows_per_split < a.row_len ? j0 + a.rows_per_split : a.row_len;
@@ -784,7 +819,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
     const int64_t units = a.n_out * a.split;
     const int64_t len = a.m / V;               // reduced length in load units
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-        const int64_t o = unit / a.split;
+        const int64_t o = a.split == 1 ? unit : div_nonneg(unit, a.split);
         const int sp = (int)(unit - o * a.split);
         const int64_t j0 = int64_t(sp) * a.rows_per_split;
         const int64_t j1 = j0 + a.rows_per_split < len ? j0 + a.rows_per_split : len;
@@ -931,11 +966,17 @@ bool launch_tile(const Launch &L, dim3 grid, hipStream_t st)
         RK_TILE(false, tune::kColumnsScalarLanes, B, true);
         return true;
     }
+    // one reduced dim and at most one kept dim after the run's: the plain form
+    const bool plain = a.seg_nd == 0 && a.segs == 1 && a.outer_nd <= 1 && (a.split == 1 || a.splits_per_seg == a.split);
+#define RK_COLS(CL)                                                                                         \
+    (plain ? launch_first(&k_dims_tile<In, Acc, Op, Map, true, CL, B, U, true, true>, grid, dim3(B), st, L, a) \
+           : launch_first(&k_dims_tile<In, Acc, Op, Map, true, CL, B, U, true>, grid, dim3(B), st, L, a))
     switch (L.lanes) {          // tile rows of 16 * lanes bytes
-    case 8: RK_TILE(true, 8, B, true); return true;
-    case 16: RK_TILE(true, 16, B, true); return true;
-    case 32: RK_TILE(true, 32, B, true); return true;
+    case 8: RK_COLS(8); return true;
+    case 16: RK_COLS(16); return true;
+    case 32: RK_COLS(32); return true;
     }
+#undef RK_COLS
 #undef RK_TILE
     return false;
 }

@@ -328,16 +328,18 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         d.rows_per_split = d.row_len;
         d.segs_per_split = d.segs;
         d.splits_per_seg = 1;
-        if (d.kernel == K_COLUMNS) {
-            const int64_t target = int64_t(num_cus) * tune::kColumnsBlocksPerCu;
+        const bool split_tiles = d.kernel == K_COLUMNS || (d.kernel == K_TILED && tune::kTiledBlocksPerCu > 0);
+        if (split_tiles) {
+            const bool cols = d.kernel == K_COLUMNS;
+            const int64_t target = int64_t(num_cus) * (cols ? tune::kColumnsBlocksPerCu : tune::kTiledBlocksPerCu);
+            const int64_t min_rows = cols ? tune::kColumnsMinRows : tune::kTiledMinRows;
             int64_t s = std::max<int64_t>(1, ceil_div(target, d.tiles));
-            s = std::min<int64_t>(s, std::max<int64_t>(1, m / tune::kColumnsMinRows));
+            s = std::min<int64_t>(s, std::max<int64_t>(1, m / min_rows));
             if (s <= d.segs) {
                 d.segs_per_split = ceil_div(d.segs, s);
                 d.split = int(ceil_div(d.segs, d.segs_per_split));
             } else {
-                int64_t per = std::min<int64_t>(ceil_div(s, d.segs),
-                                                std::max<int64_t>(1, d.row_len / tune::kColumnsMinRows));
+                int64_t per = std::min<int64_t>(ceil_div(s, d.segs), std::max<int64_t>(1, d.row_len / min_rows));
                 d.rows_per_split = ceil_div(d.row_len, per);
                 per = ceil_div(d.row_len, d.rows_per_split);
                 d.segs_per_split = 1;

@@ -66,6 +66,8 @@ constexpr int kColumnsScalarLanes = 64;               // columns tile without 16
 constexpr int kFillTilesPerCu = 1;        // rule 2: tiled while its tiles number fewer than CUs * this
 constexpr int kColumnsBlocksPerCu = 1;    // columns split target: CUs * this blocks
 constexpr int64_t kColumnsMinRows = 128;  // rows per split chunk, at least
+constexpr int kTiledBlocksPerCu = 0;      // tiled split target (0: the tiled kernel is not split)
+constexpr int64_t kTiledMinRows = 256;    //   ... rows per split chunk, at least
 constexpr int kRowWavesPerCu = 8;         // row kernel split target (3136x256x84 f32 dims=(1,3): 42.4 us;
                                           // 16, 32, 64 per CU: 46.5, 49.7, 48.0)
 constexpr int64_t kRowMinChunk = 2048;    // elements per row chunk, at least

@@ -520,10 +520,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         }
         return;
     }
-    const int64_t line = g / a.tiles_per_line;
+    // tiles, and so lines, number below 2^31: 32-bit arithmetic
+    const uint32_t line32 = uint32_t(g) / uint32_t(a.tiles_per_line);
+    const int64_t line = line32;
     const int64_t t = g - line * a.tiles_per_line;
-    const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
-    const int64_t ob = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
+    const S *x = static_cast<const S *>(a.x) + layout_offset32(a.kept_nd, a.kept_ext, a.kept_in, line32);
+    const int64_t ob = layout_offset32(a.kept_nd, a.kept_ext, a.kept_out, line32);
     // the wave's number, read as uniform so that its arithmetic is scalar
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t first = t * T + int64_t(w) * UC * CH + int64_t(lane_id()) * V;
@@ -604,8 +606,13 @@ __global__ __launch_bounds__(BLOCK) void k_scan_rowwave(ScanArgs a)
     const int64_t line = int64_t(blockIdx.x) * (BLOCK / 64) + wave;
     if (line >= a.lines)
         return;                                // whole wave; no block barrier below
-    const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
-    const int64_t ob = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
+    // lines number below 2^33 here (grid below 2^31, 4 waves a block): the
+    // 32-bit form whenever the count fits
+    const bool small = uint64_t(a.lines) <= 0xffffffffu;
+    const S *x = static_cast<const S *>(a.x) + (small ? layout_offset32(a.kept_nd, a.kept_ext, a.kept_in, uint32_t(line))
+                                                      : layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line));
+    const int64_t ob = small ? layout_offset32(a.kept_nd, a.kept_ext, a.kept_out, uint32_t(line))
+                             : layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
     Acc carry = from_bits<Acc>(a.init_bits);
     for (int64_t c0 = int64_t(lane_id()) * V; c0 - int64_t(lane_id()) * V < a.m; c0 += UC * CH) {
         typename C::Raw raw[UC];
