@@ -2,9 +2,9 @@
 launch that fails.
 
 PR #139 ("Finish whole-array reductions on the device", section
-"Compatibility") has init applied exactly once and the output never used
-for intermediate values; so a call that cannot finish must leave `out` as it
-was and say so, never store a fold of the partials it happened to see.  The
+"Compatibility") applies init once and keeps intermediate values out of the
+output; so a call that cannot finish must leave `out` as it was and say so,
+never store a fold of the partials it happened to see.  The
 waits are forced to give up from the host (a test hook makes them wait for a
 tag or flag no block sets, for a few polls), so every kernel still ends
 normally; the failed launches are refused before anything is enqueued.
