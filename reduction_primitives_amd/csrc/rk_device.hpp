@@ -766,8 +766,11 @@ __device__ __forceinline__ void advance_tag(int slot, uint32_t tag)
 // calls across the wrap of the tags.  One block of kFinalTagCopies threads.
 // In the unit's own namespace: it writes this unit's g_final, and a kernel of
 // one name in every unit would be launched through one host stub, the
-// linker's pick, and so always reach one unit's copy.
+// linker's pick, and so always reach one unit's copy.  A template, as is
+// every other use of g_final, so that the units that never instantiate one
+// (the scan units) hold no copy of the array.
 namespace RK_UNIT {
+template <int = 0>
 __global__ void k_set_final_tag(int slot, uint32_t e)
 {
     if (threadIdx.x < kFinalTagCopies)

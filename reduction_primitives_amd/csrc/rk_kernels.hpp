@@ -1148,7 +1148,9 @@ int run_acc(const Launch &L)
 // block has ended.  Synchronous (hipMemcpy to and from the tables).  In the
 // unit's own namespace: an inline function of one name in every unit is
 // merged by the linker into one copy, which would only see that unit's tables.
+// REPAIR: the unit holds whole-array tagged words (the scan units hold none).
 namespace RK_UNIT {
+template <bool REPAIR>
 inline int take_timeouts(int slot, uint64_t *count, bool repair)
 {
     uint32_t t[kTimeoutEntries];
@@ -1161,11 +1163,13 @@ inline int take_timeouts(int slot, uint64_t *count, bool repair)
         (t[kArriveSlots] && hipMemcpyToSymbol(HIP_SYMBOL(g_timeouts), &zero, 4, size_t(kArriveSlots) * 4,
                                               hipMemcpyHostToDevice) != hipSuccess))
         return ST_HIP;
-    if (repair && t[e] && e != kArriveSlots) {
-        static const uint64_t zeros[2 * kFinalCapacity] = {};
-        const size_t off = (size_t(e) * kFinalSlotWords + kFinalHeaderWords) * sizeof(uint64_t);
-        if (hipMemcpyToSymbol(HIP_SYMBOL(g_final), zeros, sizeof zeros, off, hipMemcpyHostToDevice) != hipSuccess)
-            return ST_HIP;
+    if constexpr (REPAIR) {
+        if (repair && t[e] && e != kArriveSlots) {
+            static const uint64_t zeros[2 * kFinalCapacity] = {};
+            const size_t off = (size_t(e) * kFinalSlotWords + kFinalHeaderWords) * sizeof(uint64_t);
+            if (hipMemcpyToSymbol(HIP_SYMBOL(g_final), zeros, sizeof zeros, off, hipMemcpyHostToDevice) != hipSuccess)
+                return ST_HIP;
+        }
     }
     *count += n;
     return ST_OK;
@@ -1177,12 +1181,12 @@ template <class In>
 int run_in(const Launch &L)
 {
     if (L.kernel == K_SET_TAG) {                // this translation unit's copy of the slot
-        hipLaunchKernelGGL(RK_UNIT::k_set_final_tag, dim3(1), dim3(kFinalTagCopies), 0,
+        hipLaunchKernelGGL(RK_UNIT::k_set_final_tag<>, dim3(1), dim3(kFinalTagCopies), 0,
                            static_cast<hipStream_t>(L.stream), L.all.arrive_slot, uint32_t(L.all.n));
         return hipGetLastError() == hipSuccess ? ST_OK : ST_HIP;
     }
     if (L.kernel == K_TAKE_TIMEOUTS)            // this translation unit's counts (the stream has drained)
-        return RK_UNIT::take_timeouts(L.all.arrive_slot, static_cast<uint64_t *>(L.all.ws), L.all.n != 0);
+        return RK_UNIT::take_timeouts<true>(L.all.arrive_slot, static_cast<uint64_t *>(L.all.ws), L.all.n != 0);
     if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
         if (L.acc == F32) return run_acc<In, float>(L);
         if (L.acc == F64) return run_acc<In, double>(L);

@@ -982,7 +982,7 @@ template <class In>
 int run_scan_in(const ScanLaunch &L)
 {
     if (L.kernel == SK_TAKE_TIMEOUTS)           // this translation unit's counts (the stream has drained)
-        return RK_UNIT::take_timeouts(L.args.slot, static_cast<uint64_t *>(L.args.ws), false);
+        return RK_UNIT::take_timeouts<false>(L.args.slot, static_cast<uint64_t *>(L.args.ws), false);
     if constexpr (std::is_same_v<In, float> || std::is_same_v<In, bf16_in> || std::is_same_v<In, f16_in>) {
         if (L.acc == F32) return run_scan_acc<In, float>(L);
         if (L.acc == F64) return run_scan_acc<In, double>(L);
