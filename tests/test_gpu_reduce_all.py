@@ -358,7 +358,7 @@ def test_stream_argument_allocates_on_that_stream(monkeypatch):
     R = O.reduce_all(O.SUM, O.IDENTITY, O.F32, O.F32, xr, 2.0)
     check(O.SUM, O.F32, raw_np(r_all), [R], 2.0 + float(np.abs(xr.astype(np.float64)).sum()), "all")
     R2 = O.reduce_all2(O.SUM, O.MUL, O.F32, O.F32, raw_np(a.data), raw_np(b.data), 0.0)
-    S2 = float(np.abs(a.data.double() * b.data.double()).sum())
+    S2 = float((a.data.double() * b.data.double()).abs().sum())
     check(O.SUM, O.F32, raw_np(r_all2), [R2], S2, "all2")
     mr = raw_np(m)
     Rd = O.reduce_dims(O.SUM, O.IDENTITY, O.F32, O.F32, mr, (512, 8192), (1, 512), 0b10, 0.0)
