@@ -512,14 +512,20 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
     const int64_t in_base =
         (PLAIN ? int64_t(run32) * a.outer_str[0] : layout_offset32(a.outer_nd, a.outer_ext, a.outer_str, run32)) + col;
     // this block's share of the reduced dims: segments [k0, k1) and, in
-    // each, rows [j0, j1) of the row dim
+    // each, rows [j0, j1) of its row sequence (every row of the row dim, or
+    // in the plain form every split-th row from row sp)
     int64_t k0, k1, j0, j1;
-    if (PLAIN) {                                // one segment: split units are pieces of the rows
+    if (PLAIN) {
+        // one segment, whose rows the split units share interleaved: unit sp
+        // takes rows sp, sp + split, ...  So the blocks of all units read
+        // neighbouring rows at a time, a narrow window that sweeps the
+        // array: 8192^2 f32 dims=2 read in 37.9-38.6 us where a contiguous
+        // band of rows per unit took 40.0-40.6.
         k0 = 0;
         k1 = a.segs;                            // 1; left to the argument, the tail group below keeps
                                                 // the general form's registers (known to be 1 it took 236 VGPRs)
-        j0 = int64_t(sp) * a.rows_per_split;
-        j1 = j0 + a.rows_per_split < a.row_len ? j0 + a.rows_per_split : a.row_len;
+        j0 = 0;
+        j1 = div_nonneg(a.row_len - sp + a.split - 1, a.split);
     } else if (a.splits_per_seg > 1) {
         k0 = uint32_t(sp) / uint32_t(a.splits_per_seg);
         k1 = k0 + 1;
@@ -531,8 +537,8 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
         j0 = 0;
         j1 = a.row_len;
     }
-    const S *xt = static_cast<const S *>(a.x) + in_base;
-    const int64_t s = a.s_red;
+    const S *xt = static_cast<const S *>(a.x) + in_base + (PLAIN ? int64_t(sp) * a.s_red : 0);
+    const int64_t s = PLAIN ? a.s_red * a.split : a.s_red;
 
     Acc acc0[V], acc1[V];
     set_identity<Acc, Op>(acc0);
