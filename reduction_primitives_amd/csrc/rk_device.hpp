@@ -702,17 +702,22 @@ __device__ __forceinline__ void publish_tagged(int slot, int b, Acc v, uint32_t 
 
 // Block 0: wait until all `grid` partials carry `tag`, then fold thread t's
 // partials t, t + BLOCK, ... in that order (every thread's result, before
-// the block reduction).  Called by every thread of block 0.  After
-// `spin_limit` polls without every tag it gives up and returns false in
-// `*ok` (the same in every thread): the fold is then incomplete.
+// the block reduction).  Called by every thread of block 0.  Each thread
+// polls its own words until they all carry the tag, and the block meets
+// once, at the end: a barrier per poll would hold every thread to the
+// slowest one's round trip (the 10^8 f32 sum measured 0.5 us faster so).
+// A thread that reaches `spin_limit` polls without every tag gives up, and
+// then the block returns false in `*ok` (the same in every thread): the
+// fold is incomplete.
 template <class Acc, class Op, int BLOCK>
 __device__ Acc collect_tagged(int slot, int grid, uint32_t tag, uint32_t spin_limit, bool *ok_out)
 {
     const uint64_t *w = &g_final[int64_t(slot) * kFinalSlotWords + kFinalHeaderWords];
     __shared__ int s_ready;
     Acc v = Op::template identity<Acc>();
+    bool ok = true;
     for (uint32_t spin = 0;; ++spin) {
-        bool ok = true;
+        ok = true;
         v = Op::template identity<Acc>();
         for (int k = threadIdx.x; k < grid; k += BLOCK) {
             if constexpr (sizeof(Acc) == 4) {
@@ -726,20 +731,17 @@ __device__ Acc collect_tagged(int slot, int grid, uint32_t tag, uint32_t spin_li
                 v = Op::apply(v, bitcast<Acc>((lo & 0xffffffffu) | (hi << 32)));
             }
         }
-        if (threadIdx.x == 0)
-            s_ready = 1;
-        __syncthreads();
-        if (!ok)
-            s_ready = 0;
-        __syncthreads();
-        const bool ready = s_ready != 0;
-        __syncthreads();
-        if (ready || spin >= spin_limit) {
-            *ok_out = ready;
+        if (ok || spin >= spin_limit)
             break;
-        }
         __builtin_amdgcn_s_sleep(1);
     }
+    if (threadIdx.x == 0)
+        s_ready = 1;
+    __syncthreads();
+    if (!ok)
+        s_ready = 0;
+    __syncthreads();
+    *ok_out = s_ready != 0;
     return v;
 }
 
