@@ -148,6 +148,7 @@ SELECTOR_CASES = [
     ((5, 6, 7), (1, 3), torch.float32, "generic", "two non-adjacent reduced dims"),
     ((33, 5, 9, 4), (2, 4), torch.float32, "thread", "4-d, two short reduced dims"),
     ((1000, 1), (1, 2), torch.float32, "all", "single output, contiguous"),
+    ((1000, 3000), 2, torch.float32, "columns", "ragged last tile, split units of uneven row counts"),
 ]
 
 
