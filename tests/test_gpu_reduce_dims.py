@@ -444,3 +444,47 @@ def test_workspace_reuse_for_split_dims():
         R = O.reduce_dims(O.SUM, O.IDENTITY, in_c, O.F32, xr, shape, CM(shape), mask, 0.0)
         S = magnitude(O.IDENTITY, in_c, O.F32, xr, 0.0, reduce=(xr, shape, CM(shape), mask))
         check(O.SUM, O.F32, raw_np(out), R, S, f"reuse {shape}")
+
+
+# ------------------------------------------------------------ dtype matrix
+# The dims kernels of every input dtype's translation unit: each accumulator
+# and output the dtype table allows for f16, f64 and int64 inputs (f32, bf16
+# and int32 inputs run through the cases above), on one layout per kernel.
+
+DIMS_COMBOS = [  # (input, accumulator, output)
+    (torch.float16, torch.float32, torch.float16),
+    (torch.float16, torch.float64, torch.float32),
+    (torch.float64, torch.float64, torch.float64),
+    (torch.float64, torch.float64, torch.float32),
+    (torch.int64, torch.int64, torch.int64),
+    (torch.int32, torch.int32, torch.int32),          # sums wrap in the 32-bit accumulator
+    (torch.float32, torch.float64, torch.float64),
+]
+
+DIMS_LAYOUTS = [  # (shape, reduced dims)
+    ((1000, 3000), 2),        # columns, plain
+    ((96, 1000, 3), 2),       # columns, middle dim
+    ((3000, 777), 1),         # row
+    ((2100, 300, 21), (1, 3)),  # row over 21 segments (4 KB rows and longer), several per split unit
+    ((3072, 256), 2),         # tiled
+    ((65536, 16), 2),         # thread per output
+    ((500, 9, 7), (1, 3)),    # generic
+]
+
+
+def _draw_dims(dtype, n, seed, out_dtype):
+    if dtype.is_floating_point:
+        x = W.normal(n, seed, dtype) if dtype != torch.float64 else W.normal(n, seed).double()
+        if out_dtype == torch.float16:
+            x = x * 0.25        # sums of up to 44,100 values of N(0, 1/16): a few hundred at most
+        return x
+    return W.randint(n, -2**20, 2**20, seed, dtype)
+
+
+@pytest.mark.parametrize("combo", DIMS_COMBOS, ids=lambda c: "-".join(str(t).split(".")[1] for t in c))
+@pytest.mark.parametrize("op", ["sum", "max"])
+def test_dims_dtype_matrix(combo, op):
+    in_dt, acc_dt, out_dt = combo
+    for i, (shape, dims) in enumerate(DIMS_LAYOUTS):
+        x = _draw_dims(in_dt, math.prod(shape), 9800 + 10 * i, out_dt)
+        dims_and_check(x, shape, CM(shape), dims, op=op, acc=acc_dt, out_dtype=out_dt)
