@@ -431,3 +431,39 @@ def test_beyond_2_31_elements():
     assert bool((last == k).all().item()) and int(cols[L - 1].item()) == 1
     del ones, cols
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------ dims scans, dtype matrix
+# The dims scan kernels of the f16, f64 and int64 units (and 32-bit integer
+# and float64 accumulators), one layout per kernel, every output compared.
+
+SCAN_DIMS_COMBOS = [  # (input, accumulator, output)
+    (torch.float16, torch.float32, torch.float16),
+    (torch.float64, torch.float64, torch.float64),
+    (torch.int64, torch.int64, torch.int64),
+    (torch.int32, torch.int32, torch.int32),          # sums wrap in the 32-bit accumulator
+    (torch.float32, torch.float64, torch.float64),
+]
+
+SCAN_DIMS_LAYOUTS = [  # (shape, dim)
+    ((3 * TILE + 100, 3), 1),   # tile, look-back along each line
+    ((3000, 40), 1),            # row-wave
+    ((40, 3000, 5), 2),         # columns, look-back across chunks
+    ((100, 300), 1),            # lines
+]
+
+
+@pytest.mark.parametrize("combo", SCAN_DIMS_COMBOS, ids=lambda c: "-".join(str(t).split(".")[1] for t in c))
+@pytest.mark.parametrize("op", ["sum", "max"])
+def test_scan_dims_dtype_matrix(combo, op):
+    in_t, acc_t, out_t = combo
+    for i, (shape, dim) in enumerate(SCAN_DIMS_LAYOUTS):
+        n = math.prod(shape)
+        if in_t.is_floating_point:
+            x = W.normal(n, 12300 + i, in_t) if in_t != torch.float64 else W.normal(n, 12300 + i).double()
+            if out_t == torch.float16:
+                x = x * 0.25            # prefix sums and their magnitudes stay below float16's 65,504
+        else:
+            x = W.randint(n, -2**20, 2**20, 12400 + i, in_t)
+        scan_and_check(x, shape, W.cm_strides(shape), dim, op=op, acc=acc_t, out_dtype=out_t,
+                       inclusive=bool(i % 2), init=None if op != "sum" else 1)
