@@ -517,10 +517,10 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
     int64_t k0, k1, j0, j1;
     if (PLAIN) {
         // one segment, whose rows the split units share interleaved: unit sp
-        // takes rows sp, sp + split, ...  So the blocks of all units read
-        // neighbouring rows at a time, a narrow window that sweeps the
-        // array: 8192^2 f32 dims=2 read in 37.9-38.6 us where a contiguous
-        // band of rows per unit took 40.0-40.6.
+        // takes rows sp, sp + split, ...  With a contiguous band of rows per
+        // unit, the units' concurrent streams sat a power of two apart (64 MB
+        // for 8192^2 f32), likely on the same memory channels and banks: that
+        // geometry read in 40.0-40.6 us, the interleaved one in 37.9-38.6.
         k0 = 0;
         k1 = a.segs;                            // 1; left to the argument, the tail group below keeps
                                                 // the general form's registers (known to be 1 it took 236 VGPRs)
