@@ -73,8 +73,8 @@ class Call:
         self.name, self.kind, self.bytes_alg, self.fn = name, kind, bytes_alg, fn
         self.timed, self.kernel = timed, kernel
 
-    def __call__(self):
-        rc = self.fn()
+    def __call__(self, k=0):
+        rc = self.fn(k)
         if rc != 0:
             raise RuntimeError(f"{self.name}: rk status {rc}")
 
@@ -91,7 +91,7 @@ def build_step(rk, torch, dev):
     x = [xf.data.to(dev) for _ in range(3)]
     p = [perm.data.to(dev) for _ in range(2)]
     y = [mf.data.to(dev) for _ in range(4)]
-    z = mi.data.to(dev)
+    z = [mi.data.to(dev) for _ in range(3)]
     torch.cuda.synchronize()
 
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -123,37 +123,39 @@ def build_step(rk, torch, dev):
     init_p = ctypes.byref(init15)
     # The three timed float32 sums come last, behind seven queued calls, so
     # their launch events never wait on an idle GPU; the host call, which
-    # drains the stream, closes the step.
+    # drains the stream, closes the step.  A call's argument k rotates it over
+    # the copies of its input (k = 0 in the step), so that calls issued back
+    # to back each read an input that two or more calls have not touched.
     calls = [
         Call("max_1e8_i32_perm", "all", nb + 4,
-             lambda: rk.rk_reduce_all(MAX, ID, I32, I32, I32, p[0].data_ptr(), N_WHOLE, None, OW,
+             lambda k=0: rk.rk_reduce_all(MAX, ID, I32, I32, I32, p[k % 2].data_ptr(), N_WHOLE, None, OW,
                                       o_max.data_ptr(), ws, st)),
         Call("min_1e8_i32_perm", "all", nb + 4,
-             lambda: rk.rk_reduce_all(MIN, ID, I32, I32, I32, p[1].data_ptr(), N_WHOLE, None, OW,
+             lambda k=0: rk.rk_reduce_all(MIN, ID, I32, I32, I32, p[(k + 1) % 2].data_ptr(), N_WHOLE, None, OW,
                                       o_min.data_ptr(), ws, st)),
         Call("sum_8192sq_f32_dims2", "dims", mb + SIDE * 4,
-             lambda: rk.rk_reduce_dims(SUM, ID, F32, F32, F32, y[0].data_ptr(), 2, shape, strides, 2,
+             lambda k=0: rk.rk_reduce_dims(SUM, ID, F32, F32, F32, y[k % 4].data_ptr(), 2, shape, strides, 2,
                                        None, OW, o_d2.data_ptr(), ws, st)),
         Call("sum_8192sq_f32_dims1", "dims", mb + SIDE * 4,
-             lambda: rk.rk_reduce_dims(SUM, ID, F32, F32, F32, y[1].data_ptr(), 2, shape, strides, 1,
+             lambda k=0: rk.rk_reduce_dims(SUM, ID, F32, F32, F32, y[(k + 1) % 4].data_ptr(), 2, shape, strides, 1,
                                        None, OW, o_d1.data_ptr(), ws, st)),
         Call("max_8192sq_f32_dims2", "dims", mb + SIDE * 4,
-             lambda: rk.rk_reduce_dims(MAX, ID, F32, F32, F32, y[2].data_ptr(), 2, shape, strides, 2,
+             lambda k=0: rk.rk_reduce_dims(MAX, ID, F32, F32, F32, y[(k + 2) % 4].data_ptr(), 2, shape, strides, 2,
                                        None, OW, o_mx.data_ptr(), ws, st)),
         Call("sumsq_8192sq_f32_all", "dims", mb + 4,
-             lambda: rk.rk_reduce_dims(SUM, SQ, F32, F32, F32, y[3].data_ptr(), 2, shape, strides, 3,
+             lambda k=0: rk.rk_reduce_dims(SUM, SQ, F32, F32, F32, y[(k + 3) % 4].data_ptr(), 2, shape, strides, 3,
                                        None, OW, o_sq.data_ptr(), ws, st)),
         Call("sum_8192sq_i32_dims1_i64", "dims", mb + SIDE * 8,
-             lambda: rk.rk_reduce_dims(SUM, ID, I32, I64, I64, z.data_ptr(), 2, shape, strides, 1,
+             lambda k=0: rk.rk_reduce_dims(SUM, ID, I32, I64, I64, z[k % 3].data_ptr(), 2, shape, strides, 1,
                                        None, OW, o_i.data_ptr(), ws, st)),
         Call("sum_1e8_f32_init1.5", "all", nb + 4,
-             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[1].data_ptr(), N_WHOLE, init_p, OW,
+             lambda k=0: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[(k + 1) % 3].data_ptr(), N_WHOLE, init_p, OW,
                                       o_scalar.data_ptr(), ws, st), True, DOMINANT),
         Call("sum_1e8_f32_fold", "all", nb + 8,
-             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[2].data_ptr(), N_WHOLE, None, FO,
+             lambda k=0: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[(k + 2) % 3].data_ptr(), N_WHOLE, None, FO,
                                       o_scalar.data_ptr(), ws, st), True, DOMINANT),
         Call("sum_1e8_f32_host", "all", nb + 4,
-             lambda: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[0].data_ptr(), N_WHOLE, None, HO,
+             lambda k=0: rk.rk_reduce_all(SUM, ID, F32, F32, F32, x[k % 3].data_ptr(), N_WHOLE, None, HO,
                                       ctypes.addressof(host_out), ws, st), True, DOMINANT),
     ]
     outs = dict(host=host_out, scalar=o_scalar, max=o_max, min=o_min, d2=o_d2, d1=o_d1, mx=o_mx,
@@ -275,12 +277,36 @@ def traffic_from_profile():
         return None
 
 
+PIPE_CALLS, PIPE_ROUNDS = 20, 5
+
+
+def pipelined(c, torch):
+    """A device-mode call issued PIPE_CALLS times back to back on one stream,
+    each on an input no call of the last two or more has read (the call's
+    rotation index), all queued behind GPU work; one event pair around the
+    sequence.  Per call: the sequence's time over PIPE_CALLS, launch gaps
+    between calls included.  Median and min over PIPE_ROUNDS sequences."""
+    ts = []
+    for _ in range(PIPE_ROUNDS):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        for k in range(PIPE_CALLS):
+            c(k)
+        e.record()
+        e.synchronize()
+        ts.append(b.elapsed_time(e) * 1e3 / PIPE_CALLS)
+    return ts
+
+
 def per_call_table(calls, torch, reps, rounds, dev):
     """Per call, the whole rk call timed cold (the Infinity Cache first filled
     with other, clean lines by reading a 1 GiB buffer) and warm (the same call
     again right after, back to back): `reps` samples of each in each of
     `rounds` rounds, the calls interleaved within a round.  Reported per call
-    and mode: the min and the median of the round with the lowest median."""
+    and mode: the min and the median of the round with the lowest median.
+    Device-mode calls also get a pipelined figure (see pipelined())."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     ts = {c.name: {m: [[] for _ in range(rounds)] for m in ("cold", "warm")} for c in calls}
 
@@ -316,9 +342,17 @@ def per_call_table(calls, torch, reps, rounds, dev):
             rows[mode] = dict(us_min=round(min(best), 2), us_median=round(statistics.median(best), 2),
                               GBps=round(c.bytes_alg / (min(best) * 1e-6) / 1e9, 1),
                               GBps_median=round(c.bytes_alg / (statistics.median(best) * 1e-6) / 1e9, 1))
+        pipe = ""
+        if not c.name.endswith("_host"):
+            pt = pipelined(c, torch)
+            med = statistics.median(pt)
+            rows["pipelined"] = dict(us_median=round(med, 2), us_min=round(min(pt), 2),
+                                     GBps_median=round(c.bytes_alg / (med * 1e-6) / 1e9, 1),
+                                     calls=PIPE_CALLS, rounds=PIPE_ROUNDS)
+            pipe = f"  pipelined {med:8.1f} us"
         table[c.name] = rows
         log(f"  {c.name:28s} warm {rows['warm']['us_min']:8.1f} / {rows['warm']['us_median']:8.1f} us"
-            f"  cold {rows['cold']['us_min']:8.1f} / {rows['cold']['us_median']:8.1f} us (min / median)")
+            f"  cold {rows['cold']['us_min']:8.1f} / {rows['cold']['us_median']:8.1f} us (min / median){pipe}")
     del flush
     return table
 
@@ -686,7 +720,9 @@ def main():
         "parity_vs_oracle": parity,
         "per_call": per_call,
         "per_call_method": (f"{args.per_call_reps} reps x {args.per_call_rounds} rounds, calls interleaved; "
-                            "min and median of the round with the lowest median" if per_call else None),
+                            "min and median of the round with the lowest median; pipelined: "
+                            f"{PIPE_CALLS} calls back to back on rotating inputs, one event pair, "
+                            f"median of {PIPE_ROUNDS} sequences" if per_call else None),
         "configs": configs,
     }
     del keep
