@@ -16,6 +16,7 @@ import torch
 import oracle as O
 from reduction_primitives_amd import workloads as W
 from tests import golden_cases
+from tests.layouts import random_view
 from tests.parity import check, code_of, magnitude, raw_np
 
 pytestmark = pytest.mark.gpu
@@ -488,3 +489,34 @@ def test_dims_dtype_matrix(combo, op):
     for i, (shape, dims) in enumerate(DIMS_LAYOUTS):
         x = _draw_dims(in_dt, math.prod(shape), 9800 + 10 * i, out_dt)
         dims_and_check(x, shape, CM(shape), dims, op=op, acc=acc_dt, out_dtype=out_dt)
+
+
+# ------------------------------------------------------------ seeded sweep
+# Views drawn from one seed per case (tests/layouts.py) with a random
+# non-empty set of reduced dims, mostly leaving some dims kept.  Whatever
+# kernel the planner takes, every output must match the oracle.
+
+SWEEP_CASES = 96
+
+
+def _random_view(seed):
+    shape, strides, offset, numel, rng = random_view(seed)
+    nd = len(shape)
+    k = nd if nd == 1 or rng.random() < 0.15 else int(rng.integers(1, nd))   # mostly some dims kept
+    dims = tuple(sorted(int(d) + 1 for d in rng.choice(nd, k, replace=False)))
+    return shape, strides, dims, offset, numel
+
+
+@pytest.mark.parametrize("case", range(SWEEP_CASES))
+def test_seeded_layout_sweep(case):
+    shape, strides, dims, offset, numel = _random_view(20_000 + case)
+    what = f"sweep case {case}: {shape} strides {strides} dims={dims} offset {offset}"
+    x = W.normal(numel, 21_000 + case)
+    dims_and_check(x, shape, strides, dims, init=0.5, offset=offset, what=what + " sum")
+    dims_and_check(x, shape, strides, dims, op="max", offset=offset, what=what + " max")
+    xi = W.randint(numel, -10**6, 10**6, 22_000 + case)
+    dims_and_check(xi, shape, strides, dims, acc=torch.int64, out_dtype=torch.int64, mode="fold",
+                   offset=offset, what=what + " int32->int64 fold")
+    xb = W.normal(numel, 23_000 + case, torch.bfloat16)
+    dims_and_check(xb, shape, strides, dims, map_="square", out_dtype=torch.float32, offset=offset,
+                   what=what + " bf16 square")

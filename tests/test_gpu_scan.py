@@ -23,6 +23,7 @@ import torch
 
 import oracle as O
 from reduction_primitives_amd import workloads as W
+from tests.layouts import innermost, random_view
 from tests.parity import code_of, raw_np
 
 pytestmark = pytest.mark.gpu
@@ -467,3 +468,31 @@ def test_scan_dims_dtype_matrix(combo, op):
             x = W.randint(n, -2**20, 2**20, 12400 + i, in_t)
         scan_and_check(x, shape, W.cm_strides(shape), dim, op=op, acc=acc_t, out_dtype=out_t,
                        inclusive=bool(i % 2), init=None if op != "sum" else 1)
+
+
+# ------------------------------------------------------------ seeded sweep
+# Views drawn from one seed per case (tests/layouts.py), scanned along a
+# random dim.  Whatever kernel the planner takes, every output must match
+# the oracle to the bar above.
+
+SCAN_SWEEP_CASES = 64
+
+
+@pytest.mark.parametrize("case", range(SCAN_SWEEP_CASES))
+def test_seeded_scan_sweep(case):
+    along_inner = case % 2 == 0                 # even cases: long contiguous lines (row-wave, tile)
+    shape, strides, offset, numel, rng = random_view(30_000 + case, long_inner=along_inner)
+    inner = innermost(strides)
+    if along_inner and inner is not None:
+        dim = inner + 1
+    else:
+        dim = int(rng.integers(1, len(shape) + 1))
+    what = f"scan sweep case {case}: {shape} strides {strides} dim={dim} offset {offset}"
+    x = W.normal(numel, 31_000 + case)
+    scan_and_check(x, shape, strides, dim, init=0.5, offset=offset, what=what + " sum")
+    scan_and_check(x, shape, strides, dim, op="max", inclusive=False, offset=offset, what=what + " max excl")
+    xi = W.randint(numel, -10**6, 10**6, 32_000 + case)
+    scan_and_check(xi, shape, strides, dim, acc=torch.int64, out_dtype=torch.int64, offset=offset,
+                   what=what + " int32->int64")
+    xb = W.normal(numel, 33_000 + case, torch.bfloat16)
+    scan_and_check(xb, shape, strides, dim, out_dtype=torch.float32, offset=offset, what=what + " bf16->f32")
