@@ -287,3 +287,33 @@ def test_beyond_2_31_elements():
     assert int(rk.reduce_all2(ones[:n], twos, "absdiff", acc=torch.int64, out_dtype=torch.int64).item()) == n
     del ones, twos
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ seeded sweep
+# Pairs drawn from one seed per case: an input type, each input at its own
+# offset of 0-7 elements (so every pair of 16-byte phases occurs), a length
+# log-uniform up to 2 million, a map, an op and a finishing mode.
+
+SWEEP2_TYPES = [  # (input, accumulator and output)
+    (torch.float32, torch.float32), (torch.bfloat16, torch.float32), (torch.float16, torch.float32),
+    (torch.float64, torch.float64), (torch.int32, torch.int64), (torch.int64, torch.int64),
+]
+
+
+@pytest.mark.parametrize("case", range(64))
+def test_seeded_pair_sweep(case):
+    rng = np.random.default_rng(40_000 + case)
+    in_t, acc_t = SWEEP2_TYPES[int(rng.integers(0, len(SWEEP2_TYPES)))]
+    oa, ob = int(rng.integers(0, 8)), int(rng.integers(0, 8))
+    n = int(round(np.exp(rng.uniform(0, np.log(2e6)))))
+    m = ["mul", "sqdiff", "absdiff"][int(rng.integers(0, 3))]
+    op = ["sum", "max", "min"][int(rng.integers(0, 3))]
+    mode = ["overwrite", "fold", "host"][int(rng.integers(0, 3))]
+    if in_t.is_floating_point:
+        a, b = W.normal(n + 8, 41_000 + case, in_t), W.normal(n + 8, 42_000 + case, in_t)
+    else:
+        a = W.randint(n + 8, -1000, 1000, 41_000 + case, in_t)
+        b = W.randint(n + 8, -1000, 1000, 42_000 + case, in_t)
+    run2(a, b, m, op=op, acc=acc_t, out_dtype=acc_t, mode=mode, init=0.5 if op == "sum" and in_t.is_floating_point
+         else None, off_a=oa, off_b=ob, n=n,
+         what=f"pair sweep case {case}: {in_t} {op}/{m}/{mode} n={n} offs=({oa},{ob})")
