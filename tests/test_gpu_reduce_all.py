@@ -429,3 +429,25 @@ def test_beyond_2_31_elements():
     assert bool((cols == k).all().item())
     del ones
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ seeded sweep
+# Calls drawn from one seed per case: a row of the dtype table, an op, a map,
+# a finishing mode, a start offset of 0-7 elements and a length log-uniform
+# up to 3 million (100,003 at most into float16, whose sums must stay finite).
+
+@pytest.mark.parametrize("case", range(64))
+def test_seeded_whole_sweep(case):
+    rng = np.random.default_rng(50_000 + case)
+    in_dt, acc_dt, out_dt = COMBOS[int(rng.integers(0, len(COMBOS)))]
+    op = ["sum", "max", "min"][int(rng.integers(0, 3))]
+    map_ = ["identity", "square", "abs"][int(rng.integers(0, 3))]
+    mode = ["overwrite", "fold", "host"][int(rng.integers(0, 3))]
+    offset = int(rng.integers(0, 8))
+    n = int(round(np.exp(rng.uniform(0, np.log(3e6)))))
+    if out_dt == torch.float16:
+        n = min(n, 100_003)
+    x = _draw(in_dt, n + offset, 51_000 + case, out_dt)
+    init = None if op != "sum" else (0.5 if in_dt.is_floating_point else 3)
+    run_and_check(x, op=op, map_=map_, acc=acc_dt, out_dtype=out_dt, mode=mode, init=init, offset=offset,
+                  what=f"whole sweep case {case}: {in_dt}->{acc_dt}->{out_dt} {op}/{map_}/{mode} n={n} offset {offset}")
