@@ -1014,11 +1014,13 @@ int run_typed(const Launch &L)
         split = L.dims.split;
         break;
     }
-    case K_ROW:
-        launch_first(&k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, tune::kRowUnroll>, grid, block, st, L,
-                     L.dims);
+    case K_ROW: {
+        constexpr int RU = sizeof(Acc) == 8 && sizeof(typename InTraits<In>::S) == 2 ? tune::kRowUnrollHalfToWide
+                                                                                    : tune::kRowUnroll;
+        launch_first(&k_dims_row<In, Acc, Op, Map, tune::kDimsBlock, RU>, grid, block, st, L, L.dims);
         split = L.dims.split;
         break;
+    }
     case K_GENERIC:
         if (L.vec > 1) {
             if (L.vec != InTraits<In>::vec)

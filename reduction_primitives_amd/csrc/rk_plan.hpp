@@ -53,7 +53,13 @@ constexpr int kPass2Block = 256;          // threads of the one-block second pas
 // dims
 constexpr int kDimsBlock = 256;           // row and generic kernels
 constexpr int kDimsUnroll = 8;            // loads in flight per thread (tile kernels)
-constexpr int kRowUnroll = 16;            // loads in flight per lane (row kernel)
+// Loads in flight per lane (row kernel).  8 takes the f32 kernel to 58 VGPRs,
+// so all 8 waves per SIMD are resident (16: 91, five); against 16 it measured
+// 0.6-0.9 us faster on 3136x256x84 dims=(1,3), 0.2-0.3 on 3072x2048 and 0.2
+// on 8192^2 dims=1.  2-byte inputs into 8-byte accumulators keep 16: with 8
+// the compiler takes their sums to 135-145 VGPRs, past the 128 of 4 waves.
+constexpr int kRowUnroll = 8;
+constexpr int kRowUnrollHalfToWide = 16;
 constexpr int kThreadBlock = 256;         // thread-per-output kernel
 constexpr int kTiledBlock = 1024;         // one-pass tiled kernel: 16 waves share a tile
 constexpr int kColumnsBlock = 256;        // split columns kernel
