@@ -291,8 +291,10 @@ const char *rk_status_string(int status);
 
 /* Kernels a call can take.  The dims selector (PR #176, "This PR" item 1)
  * chooses among THREAD, TILED and COLUMNS for a strided reduced dim with
- * contiguous runs of outputs; ROW serves a contiguous reduced dim, GENERIC
- * any other layout, and a single output takes the whole-array path. */
+ * contiguous runs of outputs (in the output's order, or else in storage
+ * order, each output then stored at its own place); ROW serves a contiguous
+ * reduced dim, GENERIC any other layout, and a single output takes the
+ * whole-array path. */
 typedef enum {
     RK_KERNEL_NONE = 0,         /* nothing to compute (no outputs) */
     RK_KERNEL_ALL = 1,          /* whole-array first pass (+ one-block second pass) */

@@ -907,6 +907,11 @@ int reduce_dims(int op, int map, int in_dtype, int acc_dtype, int out_dtype, con
         a.red_str[i] = d.red.str[i];
     }
     a.fin = make_finish(op, acc_dtype, out_dtype, mode, init, out);
+    a.omap.nd = d.out_map.nd;
+    for (int i = 0; i < 4; ++i) {
+        a.omap.ext[i] = i < d.out_map.nd ? d.out_map.ext[i] : 0;
+        a.omap.str[i] = i < d.out_map.nd ? d.out_map.str[i] : 0;
+    }
     a.arrive_slot = d.fused_ok ? arrive_slot(st) : -1;
     L.stream = st;
     L.ev_begin = t_ev_begin;

@@ -514,6 +514,23 @@ __device__ __forceinline__ void store_host_result(const Finish &f, Acc *ws, int 
     }
 }
 
+__device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b);
+
+// Where output o (in the kernel's numbering) sits in the output: o itself,
+// or, under an output map, its digits over m.ext times m.str.
+__device__ __forceinline__ int64_t out_index(const OutMap &m, int64_t o)
+{
+    if (m.nd == 0)
+        return o;
+    int64_t r = 0;
+    for (int k = 0; k + 1 < m.nd; ++k) {
+        const int64_t q = div_nonneg(o, m.ext[k]);
+        r += (o - q * m.ext[k]) * m.str[k];
+        o = q;
+    }
+    return r + o * m.str[m.nd - 1];
+}
+
 // The one finishing step of every last pass, for output o.
 //   OVERWRITE: out[o] = convert(op(init, v))
 //   FOLD:      out[o] = convert(op(widen(out[o]), v))

@@ -634,7 +634,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
                 if (a.split > 1)
                     ws[int64_t(sp) * a.n_out + o] = acc0[i];
                 else
-                    finish_store<Op>(a.fin, o, acc0[i]);
+                    finish_store<Op>(a.fin, out_index(a.omap, o), acc0[i]);
             }
         }
     } else {
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
         }
         if (a.split == 1) {
             if (mine)
-                finish_store<Op>(a.fin, o, v);
+                finish_store<Op>(a.fin, out_index(a.omap, o), v);
             return;
         }
         if (a.arrive_slot < 0) {                // a second launch folds the splits
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(BLOCK) void k_dims_tile(DimsArgs a)
         if (!last)
             return;
         if (mine)
-            finish_store<Op>(a.fin, o, fold_partials<Acc, Op>(ws, o, a.split, a.n_out));
+            finish_store<Op>(a.fin, out_index(a.omap, o), fold_partials<Acc, Op>(ws, o, a.split, a.n_out));
     }
 }
 
@@ -906,7 +906,8 @@ __global__ __launch_bounds__(BLOCK) void k_dims_generic(DimsArgs a)
 
 // Second pass of a split dims reduction: fold split partials per output.
 template <class Acc, class Op, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_split_finish(const Acc *ws, int64_t n_out, int split, Finish fin)
+__global__ __launch_bounds__(BLOCK) void k_split_finish(const Acc *ws, int64_t n_out, int split, Finish fin,
+                                                        OutMap omap)
 {
     const int64_t o = int64_t(blockIdx.x) * BLOCK + threadIdx.x;
     if (o >= n_out)
@@ -914,7 +915,7 @@ __global__ __launch_bounds__(BLOCK) void k_split_finish(const Acc *ws, int64_t n
     Acc v = ws[o];
     for (int k = 1; k < split; ++k)
         v = Op::apply(v, ws[int64_t(k) * n_out + o]);
-    finish_store<Op>(fin, o, v);
+    finish_store<Op>(fin, out_index(omap, o), v);
 }
 
 // ================================================================== launchers
@@ -1047,7 +1048,7 @@ int run_typed(const Launch &L)
         constexpr int B = 256;
         const unsigned g = (unsigned)((L.dims.n_out + B - 1) / B);
         hipLaunchKernelGGL((k_split_finish<Acc, Op, B>), dim3(g), dim3(B), 0, st,
-                           static_cast<const Acc *>(L.dims.ws), L.dims.n_out, split, L.dims.fin);
+                           static_cast<const Acc *>(L.dims.ws), L.dims.n_out, split, L.dims.fin, L.dims.omap);
     } else {
         return ST_OK;
     }

@@ -59,6 +59,17 @@ struct Finish {
                           // workspace: at host_seq_offset)
 };
 
+// Outputs numbered in storage order instead of the output's own (a tile
+// kernel over kept dims that only run contiguously in another order): output
+// o goes to sum_k digit_k(o) * str[k], o's digits taken over ext in order.
+// nd 0: output o is out[o].  Only the dims arguments carry one; the
+// whole-array arguments and their kernels' code stay as they are.
+struct OutMap {
+    int nd;
+    int64_t ext[4];
+    int64_t str[4];
+};
+
 struct AllArgs {
     const void *x;        // first element
     const void *y;        // two-input source: first element of the second input
@@ -106,6 +117,7 @@ struct DimsArgs {
     int64_t red_str[4];
     int arrive_slot;      // >= 0 with split > 1: the last block (or wave) of each output finishes
     Finish fin;
+    OutMap omap;          // tile kernels: where each output goes (nd 0: in order)
 };
 
 struct Launch {

@@ -3,6 +3,7 @@
 #include "rk_scan_plan.hpp"
 
 #include <algorithm>
+#include <cstdint>
 
 namespace rk {
 
@@ -163,6 +164,39 @@ static void push_dim(Layout &l, int64_t e, int64_t s)
     ++l.nd;
 }
 
+// Kept dims (output order, merged) that are contiguous in storage only in
+// another order: the order of increasing stride (broadcast dims last).  When
+// the first of them then has stride 1, `sorted` gets them in that order
+// (merged where chained) and `map` the unmerged dims in that order with each
+// one's stride in the output (the product of the extents before it in output
+// order); returns false otherwise and leaves both untouched.
+static bool storage_order_runs(const Layout &kept, Layout *sorted, Layout *map)
+{
+    int idx[kMaxDims];
+    for (int i = 0; i < kept.nd; ++i)
+        idx[i] = i;
+    auto key = [&](int i) { return kept.str[i] == 0 ? INT64_MAX : kept.str[i]; };
+    std::stable_sort(idx, idx + kept.nd, [&](int x, int y) { return key(x) < key(y); });
+    if (kept.nd < 2 || kept.str[idx[0]] != 1)
+        return false;
+    int64_t ostr[kMaxDims];
+    int64_t acc = 1;
+    for (int i = 0; i < kept.nd; ++i) {
+        ostr[i] = acc;
+        acc *= kept.ext[i];
+    }
+    Layout s, mp;
+    for (int k = 0; k < kept.nd; ++k) {
+        push_dim(s, kept.ext[idx[k]], kept.str[idx[k]]);
+        mp.ext[mp.nd] = kept.ext[idx[k]];
+        mp.str[mp.nd] = ostr[idx[k]];
+        ++mp.nd;
+    }
+    *sorted = s;
+    *map = mp;
+    return true;
+}
+
 int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64_t *shape,
               const int64_t *strides, uint32_t mask, int num_cus, DimsPlan *p)
 {
@@ -228,6 +262,10 @@ int plan_dims(int in_dtype, int acc_dtype, uintptr_t addr, int ndim, const int64
         } else if (d.kept.str[0] == 1) {
             // contiguous runs of outputs over any reduced dims (PR #176's
             // selector; several reduced dims become segments of rows)
+            d.kernel = select_strided_kernel(d.kept.ext[0], n_out, m, isz, num_cus);
+        } else if (storage_order_runs(d.kept, &d.kept, &d.out_map)) {
+            // the kept dims run contiguously in storage order (a permuted
+            // view): the same tile kernels, numbering outputs in that order
             d.kernel = select_strided_kernel(d.kept.ext[0], n_out, m, isz, num_cus);
         } else {
             d.kernel = K_GENERIC;

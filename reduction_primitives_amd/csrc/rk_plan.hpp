@@ -110,7 +110,12 @@ struct DimsPlan {
     int launches = 0;
     int64_t n_out = 0;      // outputs
     int64_t m = 0;          // elements folded into each output
-    Layout kept;            // normalised kept dims (output order)
+    Layout kept;            // normalised kept dims (output order; storage order under out_map)
+    // Tile kernels over kept dims that run contiguously only in storage
+    // order: `kept` is then in that order, and output k of that numbering is
+    // stored at sum_i digit_i(k) * out_map.str[i], k's digits taken over
+    // out_map.ext (the kept dims in storage order, unmerged).  nd 0: no map.
+    Layout out_map;
     Layout red;             // normalised reduced dims
     AllPlan all;            // K_ALL / K_ALL_STRIDED
     // tile kernels (THREAD / TILED / COLUMNS): outputs come in runs of

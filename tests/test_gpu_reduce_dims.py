@@ -265,6 +265,15 @@ GENERAL_CASES = [
     (1025 * 9 * 5, (1025, 9, 5), CM((1025, 9, 5)), (1, 3), "row",
      "rows of 4100 bytes: every row at its own 16-byte phase"),
     (2 * 300 * 40, (300, 40), (2, 600), 1, "generic", "strided gather along the reduced dim"),
+    # permuted views: the kept dims run contiguously only in storage order, so
+    # the tile kernels number outputs in that order and store each one at its
+    # place in the output
+    (7680000, (64, 3000, 40), (40, 2560, 1), 2, "columns", "permuted view, kept dims transposed in storage"),
+    (69300, (33, 700, 3), (3, 99, 1), 2, "columns", "permuted view, element loads"),
+    (102400, (64, 50, 32), (32, 2048, 1), 2, "tiled", "permuted view, short reduced dim"),
+    (1536000, (16, 300, 8, 40), (8, 5120, 1, 128), 2, "tiled", "permuted 4-d view, three kept dims in storage order"),
+    (60000, (100, 20, 30), (600, 1, 20), 1, "tiled", "permuted view, reduced dim outermost"),
+    (3465, (7, 5, 9, 11), (5, 1, 385, 35), 3, "thread", "permuted 4-d view, thread per output"),
 ]
 
 
