@@ -296,7 +296,8 @@ DIMS_CASES = [
     ((3000, 40), None, 1, "scan_rowwave", "contiguous lines shorter than a tile"),
     ((300, 5000), None, 1, "scan_rowwave", "many short contiguous lines"),
     ((300, 200), None, 2, "scan_columns", "strided scan dim"),
-    ((100, 300), None, 1, "scan_lines", "short contiguous lines"),
+    ((50, 300), None, 1, "scan_lines", "contiguous lines shorter than a wave's chunk"),
+    ((100, 300), None, 1, "scan_rowwave", "contiguous lines of one to four wave chunks"),
     ((64, 100, 8), None, 2, "scan_columns", "middle dim of a 3-d array"),
     ((64, 100, 8), None, 3, "scan_columns", "last dim of a 3-d array"),
     ((10, 100, 8), None, 2, "scan_lines", "runs of lines too narrow for tiles"),
@@ -450,7 +451,7 @@ SCAN_DIMS_LAYOUTS = [  # (shape, dim)
     ((3 * TILE + 100, 3), 1),   # tile, look-back along each line
     ((3000, 40), 1),            # row-wave
     ((40, 3000, 5), 2),         # columns, look-back across chunks
-    ((100, 300), 1),            # lines
+    ((50, 300), 1),             # lines
 ]
 
 
