@@ -605,8 +605,15 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         d.kernel = SK_LINES;
         d.block = tune::kScanBlock;
         d.vec = 1;
-        d.grid = std::min<int64_t>(ceil_div(d.lines, tune::kScanBlock),
-                                   int64_t(num_cus) * tune::kScanLinesBlocksPerCu);
+        if (scan_lines_packed(d.s_in, d.s_out, d.m)) {
+            // short contiguous lines: 64 / m whole lines to a wave
+            const int64_t waves = ceil_div(d.lines, 64 / d.m);
+            d.grid = std::min<int64_t>(ceil_div(waves, tune::kScanBlock / 64),
+                                       int64_t(num_cus) * tune::kScanPackedBlocksPerCu);
+        } else {
+            d.grid = std::min<int64_t>(ceil_div(d.lines, tune::kScanBlock),
+                                       int64_t(num_cus) * tune::kScanLinesBlocksPerCu);
+        }
     }
     *p = d;
     return ST_OK;

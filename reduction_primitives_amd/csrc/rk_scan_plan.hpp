@@ -50,7 +50,19 @@ constexpr int kScanColLanes = 32;         // lanes across a tile row with 16-byt
 constexpr int kScanColLanesScalar = 64;   //   ... with element loads
 constexpr int kScanColRows = 16;          // consecutive scan positions per thread (8: 125.7 us at 1024 threads)
 constexpr int64_t kScanColMinRun = 16;    // runs of lines narrower than this take the lines kernel
+constexpr int kScanPackedBlocksPerCu = 8; // lines kernel, packed form: grid cap
 }  // namespace tune
+
+// The lines kernel's packed form: lines contiguous along the scan dim in
+// input and output, from a quarter wave long up to a wave (and the row-wave
+// length), go 64 / m whole lines to a wave.  Against a thread per line (f32,
+// about 5 million elements): lines of 50 88.8 -> 36.3 us, of 24 47.2 -> 34.1;
+// lines of 10 stay with a thread each (27.8 against 30.6 packed), whose
+// neighbours share its cache lines.  One test for the planner and the launch.
+constexpr bool scan_lines_packed(int64_t s_in, int64_t s_out, int64_t m)
+{
+    return s_in == 1 && s_out == 1 && m >= 16 && m < 64 && m < tune::kScanWaveMinLen;
+}
 
 // Scans (prefix folds) along one dim: every line -- all indices fixed but
 // the scan dim's -- is scanned on its own.  Line l starts at input element

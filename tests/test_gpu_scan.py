@@ -296,7 +296,11 @@ DIMS_CASES = [
     ((3000, 40), None, 1, "scan_rowwave", "contiguous lines shorter than a tile"),
     ((300, 5000), None, 1, "scan_rowwave", "many short contiguous lines"),
     ((300, 200), None, 2, "scan_columns", "strided scan dim"),
-    ((50, 300), None, 1, "scan_lines", "contiguous lines shorter than a wave's chunk"),
+    ((50, 300), None, 1, "scan_lines", "contiguous lines shorter than a wave's chunk: packed into waves"),
+    ((10, 3000), None, 1, "scan_lines", "contiguous lines under a quarter wave: a thread each"),
+    ((50, 700), (1, 53), 1, "scan_lines", "packed lines with gaps between them"),
+    ((16, 30, 7), None, 1, "scan_lines", "packed lines at the offsets of two kept dims, four to a wave"),
+    ((63, 301), None, 1, "scan_lines", "packed lines one short of a wave, last group partial"),
     ((100, 300), None, 1, "scan_rowwave", "contiguous lines of one to four wave chunks"),
     ((64, 100, 8), None, 2, "scan_columns", "middle dim of a 3-d array"),
     ((64, 100, 8), None, 3, "scan_columns", "last dim of a 3-d array"),
