@@ -606,8 +606,9 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         d.block = tune::kScanBlock;
         d.vec = 1;
         if (scan_lines_packed(d.s_in, d.s_out, d.m)) {
-            // short contiguous lines: 64 / m whole lines to a wave
-            const int64_t waves = ceil_div(d.lines, 64 / d.m);
+            // short contiguous lines packed whole into waves
+            const int64_t lanes = ceil_div(d.m, int64_t(scan_packed_width(d.m)));
+            const int64_t waves = ceil_div(d.lines, 64 / lanes);
             d.grid = std::min<int64_t>(ceil_div(waves, tune::kScanBlock / 64),
                                        int64_t(num_cus) * tune::kScanPackedBlocksPerCu);
         } else {

@@ -887,59 +887,78 @@ __global__ __launch_bounds__(BLOCK) void k_scan_lines(ScanArgs a)
 }
 
 // Lines kernel, packed form, for lines contiguous along the scan dim in
-// input and output and shorter than a wave (scan_lines_packed): a wave takes
-// 64 / m whole lines, lane j holding element j % m of its line j / m (the
-// lanes past the last whole line idle), and scans each line at once with a
-// segmented wave scan: at distance d = 1, 2, 4, ... a lane folds in the value
-// d lanes below it when that lane holds an element of the same line.  Waves
-// stride over the groups of lines, U groups a round with their loads in
-// flight together (one a round waited on memory latency every group).
-template <class In, class Acc, class Op, int BLOCK, int U>
+// input and output and shorter than four waves (scan_lines_packed): a lane
+// holds E consecutive elements, a line takes L = ceil(m / E) lanes and a wave
+// 64 / L whole lines, lane j holding elements (j % L) * E, ... of its line
+// j / L (the lanes past the last whole line idle).  A lane scans its own E
+// elements, then the lines' lane totals go through a segmented wave scan: at
+// distance d = 1, 2, 4, ... a lane folds in the lane d below it when that
+// lane holds the same line.  An output is op(op(init, the lanes before), its
+// lane's running value).  Waves stride over the groups of lines, U groups a
+// round with their loads in flight together (one a round waited on memory
+// latency every group).
+template <class In, class Acc, class Op, int BLOCK, int U, int E>
 __global__ __launch_bounds__(BLOCK) void k_scan_packed(ScanArgs a)
 {
     using S = typename InTraits<In>::S;
     const int m = int(a.m);
-    const int per = 64 / m;
+    const int L = (m + E - 1) / E;
+    const int per = 64 / L;
     const int lane = lane_id();
-    const int g = lane / m;
-    const int p = lane - g * m;
+    const int g = lane / L;
+    const int q = lane - g * L;
     const Acc init = from_bits<Acc>(a.init_bits);
     const int64_t groups = (a.lines + per - 1) / per;
     const int64_t nw = int64_t(gridDim.x) * (BLOCK / 64);
-    // U groups a round, their loads all issued before the first scan
     for (int64_t w0 = int64_t(blockIdx.x) * (BLOCK / 64) + (threadIdx.x >> 6); w0 < groups; w0 += nw * U) {
-        Acc v[U];
+        S raw[U][E];
         int64_t ob[U];
         bool act[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t line = (w0 + u * nw) * per + g;
             act[u] = g < per && w0 + u * nw < groups && line < a.lines;
-            v[u] = Op::template identity<Acc>();
             ob[u] = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                raw[u][e] = S{};
             if (act[u]) {
                 const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
                 ob[u] = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
-                v[u] = InTraits<In>::template one<Acc>(load1(x + p));
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (q * E + e < m)
+                        raw[u][e] = load1(x + q * E + e);
             }
         }
         issue_barrier();
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            for (int d = 1; d < m; d <<= 1) {
-                const Acc t = __shfl_up(v[u], d, 64);
-                if (p >= d)
-                    v[u] = Op::apply(t, v[u]);
+            Acc l[E];
+            Acc t = Op::template identity<Acc>();
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (act[u] && q * E + e < m)
+                    t = Op::apply(t, InTraits<In>::template one<Acc>(raw[u][e]));
+                l[e] = t;
             }
-            Acc o[1];
-            if (a.inclusive) {
-                o[0] = Op::apply(init, v[u]);
-            } else {
-                const Acc t = __shfl_up(v[u], 1, 64);
-                o[0] = p == 0 ? init : Op::apply(init, t);
+            for (int d = 1; d < L; d <<= 1) {
+                const Acc y = __shfl_up(t, d, 64);
+                if (q >= d)
+                    t = Op::apply(y, t);
             }
-            if (act[u])
-                store_run<Acc, 1>(a.out, ob[u] + p, a.out_dtype, o);
+            const Acc before = __shfl_up(t, 1, 64);
+            const Acc base = q == 0 ? init : Op::apply(init, before);
+            if (!act[u])
+                continue;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (q * E + e < m) {
+                    Acc o[1];
+                    o[0] = a.inclusive ? Op::apply(base, l[e]) : e == 0 ? base : Op::apply(base, l[e - 1]);
+                    store_run<Acc, 1>(a.out, ob[u] + q * E + e, a.out_dtype, o);
+                }
+            }
         }
     }
 }
@@ -1004,9 +1023,13 @@ int run_scan_typed(const ScanLaunch &L)
             launch_first(&k_scan_rowwave<In, Acc, Op, B, U, 1>, grid, block, st, ev, L.args);
         break;
     case SK_LINES:
-        if (scan_lines_packed(L.args.s_in, L.args.s_out, L.args.m))
-            launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
-        else
+        if (scan_lines_packed(L.args.s_in, L.args.s_out, L.args.m)) {
+            switch (scan_packed_width(L.args.m)) {
+            case 1: launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll, 1>, grid, block, st, ev, L.args); break;
+            case 2: launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll, 2>, grid, block, st, ev, L.args); break;
+            default: launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll / 2, 4>, grid, block, st, ev, L.args); break;
+            }
+        } else
             launch_first(&k_scan_lines<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
         break;
     case SK_COLUMNS: {

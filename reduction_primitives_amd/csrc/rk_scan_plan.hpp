@@ -34,11 +34,11 @@ constexpr int kScanUnroll = 8;            // 16-byte chunks in flight per lane (
                                           // kernel with element loads)
 constexpr int kScanLinesUnroll = 8;       // elements in flight per thread (lines kernel)
 constexpr int kScanLinesBlocksPerCu = 8;  // lines kernel grid cap
-// Contiguous lines at least this long take a wave (or tiles): a wave's chunk.
-// Against 256 (f32 cumsum along dim 1, about 5 million elements): lines of 200
-// 119.3 -> 29.0 us, of 100 77.4 -> 50.5; shorter ones stay with a thread per
-// line (lines of 50: 88.8 against 104 us as waves, of 24: 47 against 178).
-constexpr int64_t kScanWaveMinLen = 64;
+// Contiguous lines at least this long take a wave each (or tiles); shorter
+// ones from 16 elements are packed whole into waves (scan_lines_packed).  f32
+// cumsum along dim 1, about 5 million elements: lines of 200 22.2 us packed,
+// 28.9 a wave each, 119.3 a thread each; lines of 100 28.9, 50.5 and 77.4.
+constexpr int64_t kScanWaveMinLen = 256;
 constexpr int64_t kScanTileFewLines = 4;  // fewer lines than CUs * this, each >= kScanTileMinLen: tiles
 constexpr int64_t kScanTileMinLen = 4096;
 constexpr int kScanSpinLimit = 1 << 24;   // look-back: sleeps per wait before giving up (about a second)
@@ -54,15 +54,18 @@ constexpr int kScanPackedBlocksPerCu = 8; // lines kernel, packed form: grid cap
 }  // namespace tune
 
 // The lines kernel's packed form: lines contiguous along the scan dim in
-// input and output, from a quarter wave long up to a wave (and the row-wave
-// length), go 64 / m whole lines to a wave.  Against a thread per line (f32,
-// about 5 million elements): lines of 50 88.8 -> 36.3 us, of 24 47.2 -> 34.1;
-// lines of 10 stay with a thread each (27.8 against 30.6 packed), whose
-// neighbours share its cache lines.  One test for the planner and the launch.
+// input and output, from a quarter wave long up to the row-wave length (at
+// most 4 waves), go whole to waves, each lane holding scan_packed_width(m)
+// consecutive elements.  Against a thread per line (f32, about 5 million
+// elements): lines of 50 88.8 -> 36.3 us, of 24 47.2 -> 34.1; lines of 10
+// stay with a thread each (27.8 against 30.6 packed), whose neighbours share
+// its cache lines.  One test for the planner and the launch.
 constexpr bool scan_lines_packed(int64_t s_in, int64_t s_out, int64_t m)
 {
-    return s_in == 1 && s_out == 1 && m >= 16 && m < 64 && m < tune::kScanWaveMinLen;
+    return s_in == 1 && s_out == 1 && m >= 16 && m < 256 && m < tune::kScanWaveMinLen;
 }
+// Elements a lane holds in the packed form: 1 below 64, 2 below 128, else 4.
+constexpr int scan_packed_width(int64_t m) { return m < 64 ? 1 : m < 128 ? 2 : 4; }
 
 // Scans (prefix folds) along one dim: every line -- all indices fixed but
 // the scan dim's -- is scanned on its own.  Line l starts at input element

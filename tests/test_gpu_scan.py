@@ -301,7 +301,9 @@ DIMS_CASES = [
     ((50, 700), (1, 53), 1, "scan_lines", "packed lines with gaps between them"),
     ((16, 30, 7), None, 1, "scan_lines", "packed lines at the offsets of two kept dims, four to a wave"),
     ((63, 301), None, 1, "scan_lines", "packed lines one short of a wave, last group partial"),
-    ((100, 300), None, 1, "scan_rowwave", "contiguous lines of one to four wave chunks"),
+    ((100, 300), None, 1, "scan_lines", "contiguous lines of 100: packed, two elements to a lane"),
+    ((201, 299), None, 1, "scan_lines", "contiguous lines of 201: packed, four elements to a lane"),
+    ((256, 300), None, 1, "scan_rowwave", "contiguous lines of four wave chunks: a wave each"),
     ((64, 100, 8), None, 2, "scan_columns", "middle dim of a 3-d array"),
     ((64, 100, 8), None, 3, "scan_columns", "last dim of a 3-d array"),
     ((10, 100, 8), None, 2, "scan_lines", "runs of lines too narrow for tiles"),
@@ -455,7 +457,8 @@ SCAN_DIMS_LAYOUTS = [  # (shape, dim)
     ((3 * TILE + 100, 3), 1),   # tile, look-back along each line
     ((3000, 40), 1),            # row-wave
     ((40, 3000, 5), 2),         # columns, look-back across chunks
-    ((50, 300), 1),             # lines
+    ((50, 300), 1),             # lines, packed one element to a lane
+    ((100, 301), 1),            # lines, packed two elements to a lane
 ]
 
 

@@ -398,8 +398,10 @@ def test_scan_plans():
     assert p.kernel == rk.RK_KERNEL_SCAN_LINES and p.workspace_bytes == 0        # runs of 10 lines
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [50, 300], [1, 50], 0, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_LINES                      # lines shorter than a wave's chunk
-    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [64, 300], [1, 64], 0, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE                    # a wave's chunk and longer
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [255, 300], [1, 255], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_LINES                      # packed, four elements to a lane
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [256, 300], [1, 256], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE                    # four wave chunks and longer
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 3, [0, 5, 5], [1, 1, 5], 1, 256)
     assert p.kernel == rk.RK_KERNEL_NONE and p.launches == 0
     with pytest.raises(rk.RkError):
