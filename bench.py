@@ -515,11 +515,20 @@ def configs_table(rk, torch, dev, reps):
     md = mf.data.to(dev)
     scan("8192x8192 f32 cumsum dims=1", md, mf.shape, mf.strides, 1)
     scan("8192x8192 f32 cumsum dims=2", md, mf.shape, mf.strides, 2)
+    # the same storage read as its transpose (a row-major matrix): input and
+    # output contiguous along different axes
+    rm = (mf.shape[1], 1)
+    scan("8192x8192 f32 row-major cumsum dims=2", md, mf.shape, rm, 2)
+    scan("8192x8192 f32 row-major cumsum dims=1", md, mf.shape, rm, 1)
     del md
-    for arr in W.general_layouts():
+    pv = W.permuted_kept()
+    scan("256x1024x256 f32 permuted cumsum dims=2", pv.data.to(dev), pv.shape, pv.view_strides, 2)
+    for arr in W.general_layouts() + [W.permuted_kept()]:
         xd = arr.data.to(dev)
         view(arr.name, xd, arr.shape, arr.view_strides, arr.dims)
         del xd
+    for arr in W.short_lines():
+        scan(arr.name, arr.data.to(dev), arr.shape, arr.view_strides, arr.dims[0])
     mf, mi = W.matrix_8192()
     md, mid = mf.data.to(dev), mi.data.to(dev)
     dims("8192x8192 f32 sum dims=2", mf, md, 2)

@@ -264,7 +264,8 @@ size_t rk_scan_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64
  * when that size is 0); a workspace must not be shared by calls that may run
  * at the same time.  stream: hipStream_t or NULL; asynchronous.  A line
  * contiguous along the scan dim and at least one tile long (or a strided scan
- * dim over runs of contiguous lines) is scanned in one pass with decoupled
+ * dim over runs of contiguous lines, or a view whose input and output are
+ * contiguous along different axes) is scanned in one pass with decoupled
  * look-back between tiles.  The tiles' counter and flags (along contiguous
  * lines: all of the per-tile state) live in the library's per-stream slot
  * when they fit one (4096 tiles along contiguous lines, 8192 for a strided
@@ -308,8 +309,12 @@ typedef enum {
     RK_KERNEL_SCAN_TILE = 9,    /* scan: tiles of contiguous lines, decoupled look-back (+ a clearing launch) */
     RK_KERNEL_SCAN_ROWWAVE = 10,/* scan: one wave per contiguous line shorter than a tile */
     RK_KERNEL_SCAN_LINES = 11,  /* scan: one thread per line along a strided scan dim */
-    RK_KERNEL_SCAN_COLUMNS = 12 /* scan: tiles of contiguous lines x scan positions, look-back along
+    RK_KERNEL_SCAN_COLUMNS = 12,/* scan: tiles of contiguous lines x scan positions, look-back along
                                    a strided scan dim (+ a clearing launch) */
+    RK_KERNEL_SCAN_TRANSPOSE = 13 /* scan: input and output contiguous along different axes (a
+                                   transposed or permuted view): tiles of lines x scan positions
+                                   staged through LDS, look-back along the scan dim (+ a clearing
+                                   launch) */
 } rk_kernel;
 
 typedef struct {

@@ -17,7 +17,8 @@ from ._native import (  # noqa: F401
     EXPORTS, KERNEL_NAMES, LIB_PATH, RK_BF16, RK_ERR_HIP, RK_ERR_INVALID_ARGUMENT, RK_ERR_TOO_LARGE,
     RK_ERR_UNSUPPORTED, RK_F16, RK_F32, RK_F64, RK_I32, RK_I64, RK_KERNEL_ALL,
     RK_KERNEL_ALL2, RK_KERNEL_ALL_STRIDED, RK_KERNEL_COLUMNS, RK_KERNEL_GENERIC, RK_KERNEL_NONE,
-    RK_KERNEL_ROW, RK_KERNEL_SCAN_COLUMNS, RK_KERNEL_SCAN_LINES, RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_TILE, RK_KERNEL_THREAD,
+    RK_KERNEL_ROW, RK_KERNEL_SCAN_COLUMNS, RK_KERNEL_SCAN_LINES, RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_TILE,
+    RK_KERNEL_SCAN_TRANSPOSE, RK_KERNEL_THREAD,
     RK_KERNEL_TILED, RK_MAP2_ABSDIFF, RK_MAP2_MUL, RK_MAP2_SQDIFF,
     RK_MAP_ABS, RK_MAP_IDENTITY, RK_MAP_SQUARE,
     RK_MODE_FOLD, RK_MODE_HOST, RK_MODE_OVERWRITE, RK_OK, RK_OP_MAX, RK_OP_MIN, RK_OP_SUM,

@@ -21,10 +21,10 @@ RK_F32, RK_BF16, RK_F16, RK_F64, RK_I32, RK_I64 = 0, 1, 2, 3, 4, 5
 RK_MODE_OVERWRITE, RK_MODE_FOLD, RK_MODE_HOST = 0, 1, 2
 (RK_KERNEL_NONE, RK_KERNEL_ALL, RK_KERNEL_ALL_STRIDED, RK_KERNEL_THREAD, RK_KERNEL_TILED,
  RK_KERNEL_COLUMNS, RK_KERNEL_ROW, RK_KERNEL_GENERIC, RK_KERNEL_ALL2, RK_KERNEL_SCAN_TILE,
- RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_LINES, RK_KERNEL_SCAN_COLUMNS) = range(13)
+ RK_KERNEL_SCAN_ROWWAVE, RK_KERNEL_SCAN_LINES, RK_KERNEL_SCAN_COLUMNS, RK_KERNEL_SCAN_TRANSPOSE) = range(14)
 KERNEL_NAMES = {0: "none", 1: "all", 2: "all_strided", 3: "thread", 4: "tiled", 5: "columns",
                 6: "row", 7: "generic", 8: "all2", 9: "scan_tile", 10: "scan_rowwave",
-                11: "scan_lines", 12: "scan_columns"}
+                11: "scan_lines", 12: "scan_columns", 13: "scan_transpose"}
 
 # every function include/rk.h declares
 EXPORTS = ("rk_workspace_size", "rk_reduce_all", "rk_reduce_all2", "rk_reduce_dims", "rk_status_string",

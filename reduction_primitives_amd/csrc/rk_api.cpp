@@ -950,8 +950,9 @@ int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, co
     info->kernel = d.kernel == SK_TILE ? RK_KERNEL_SCAN_TILE
                    : d.kernel == SK_ROWWAVE ? RK_KERNEL_SCAN_ROWWAVE
                    : d.kernel == SK_LINES ? RK_KERNEL_SCAN_LINES
-                   : d.kernel == SK_COLUMNS ? RK_KERNEL_SCAN_COLUMNS : RK_KERNEL_NONE;
-    const bool lookback = d.kernel == SK_TILE || d.kernel == SK_COLUMNS;
+                   : d.kernel == SK_COLUMNS ? RK_KERNEL_SCAN_COLUMNS
+                   : d.kernel == SK_TRANSPOSE ? RK_KERNEL_SCAN_TRANSPOSE : RK_KERNEL_NONE;
+    const bool lookback = d.kernel == SK_TILE || d.kernel == SK_COLUMNS || d.kernel == SK_TRANSPOSE;
     // a look-back scan clears its state with a launch of its own unless the
     // state fits a library slot
     const int64_t cap = d.kernel == SK_TILE ? kScanRecCapacity : kScanFlagCapacity;
@@ -959,7 +960,9 @@ int rk_plan_scan(int in_dtype, int acc_dtype, int out_dtype, const void *ptr, co
                      : lookback && !(d.tiles <= cap && g_fused_finish.load()) ? 2 : 1;
     info->grid = d.grid;
     info->block = d.block;
-    info->split = int(d.kernel == SK_COLUMNS ? d.chunks : d.tiles_per_line > 0 ? d.tiles_per_line : 1);
+    info->split = int(d.kernel == SK_COLUMNS || d.kernel == SK_TRANSPOSE ? d.chunks
+                      : d.tiles_per_line > 0                            ? d.tiles_per_line
+                                                                        : 1);
     info->vec = d.vec;
     info->tile_outputs = int(d.tile_elems);
     info->n_out = d.lines * d.m;
@@ -1019,6 +1022,7 @@ int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void 
     L.acc = acc_dtype;
     L.op = op;
     L.vec = d.vec;
+    L.tmode = d.tmode;
     L.grid = d.grid;
     L.block = d.block;
     ScanArgs &a = L.args;
@@ -1044,7 +1048,7 @@ int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void 
     a.init_bits = start_bits(op, acc_dtype, init);
     // look-back state in a library slot when the tiles' state fits one (no clearing launch)
     a.slot = (d.kernel == SK_TILE && d.tiles <= kScanRecCapacity) ||
-                     (d.kernel == SK_COLUMNS && d.tiles <= kScanFlagCapacity)
+                     ((d.kernel == SK_COLUMNS || d.kernel == SK_TRANSPOSE) && d.tiles <= kScanFlagCapacity)
                  ? arrive_slot(static_cast<hipStream_t>(stream))
                  : -1;
     const int64_t force = g_force_wait.load(std::memory_order_relaxed);

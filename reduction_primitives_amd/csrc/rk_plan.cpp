@@ -484,6 +484,68 @@ int64_t scan_tile_elems(int in_dtype, int block, int vl)
     return int64_t(block / 64) * scan_lane_chunks(unroll, 16 / isz, vl) * 64 * vl;
 }
 
+// The transposing kernel, when the input and the output are contiguous along
+// different axes that each span at least kScanTrMinRun elements: the scan
+// dim and a kept dim with output stride 1 (mode 0), a kept dim with input
+// stride 1 and another with output stride 1 (mode 1), or a kept dim with
+// input stride 1 and the scan dim (mode 2).  The kept dims are reordered to
+// (a, b, the rest), a missing axis taking extent 1.
+static bool plan_scan_transpose(ScanPlan &d, int isz, int asz)
+{
+    const Layout &k = d.kept_in;
+    int ia = -1, ib = -1;
+    for (int i = 0; i < k.nd; ++i) {
+        if (ia < 0 && k.str[i] == 1)
+            ia = i;
+        if (ib < 0 && d.kept_out[i] == 1)
+            ib = i;
+    }
+    const int64_t R = tune::kScanTrMinRun;
+    int mode = -1;
+    if (d.s_in == 1 && d.s_out != 1 && ib >= 0 && d.m >= R && k.ext[ib] >= R)
+        mode = 0;
+    else if (ia >= 0 && ib >= 0 && ia != ib && k.ext[ia] >= R && k.ext[ib] >= R)
+        mode = 1;
+    else if (ia >= 0 && d.s_out == 1 && d.s_in != 1 && d.m >= R && k.ext[ia] >= R)
+        mode = 2;
+    if (mode < 0)
+        return false;
+    const int da = mode == 0 ? -1 : ia, db = mode == 2 ? -1 : ib;
+    Layout t;
+    int64_t to[kMaxDims] = {0, 0, 0, 0};
+    auto put = [&](int i) {
+        t.ext[t.nd] = i < 0 ? 1 : k.ext[i];
+        t.str[t.nd] = i < 0 ? 0 : k.str[i];
+        to[t.nd] = i < 0 ? 0 : d.kept_out[i];
+        ++t.nd;
+    };
+    put(da);
+    put(db);
+    for (int i = 0; i < k.nd; ++i)
+        if (i != da && i != db)
+            put(i);
+    const int slot = std::max(isz, asz) > 4 ? 8 : 4;
+    const int64_t ta = scan_tr_ta(mode), tb = scan_tr_tb(mode), tp = scan_tr_tp(mode, slot);
+    const int64_t per_run = ceil_div(t.ext[0], ta) * ceil_div(t.ext[1], tb);
+    d.kernel = SK_TRANSPOSE;
+    d.tmode = mode;
+    d.kept_in = t;
+    for (int i = 0; i < kMaxDims; ++i)
+        d.kept_out[i] = to[i];
+    d.block = tune::kScanTrBlock;
+    d.vec = 1;
+    d.col_tiles_per_run = per_run;
+    d.col_tiles = d.lines / (t.ext[0] * t.ext[1]) * per_run;
+    d.chunks = ceil_div(d.m, tp);
+    d.tiles = d.col_tiles * d.chunks;
+    d.tile_elems = ta * tb * tp;
+    d.grid = d.tiles;
+    if (d.tiles > INT32_MAX)                    // refused by the caller; no state size to form
+        return true;
+    d.ws_bytes = round_up_256(size_t(scan_columns_state_bytes(d.tiles, ta * tb)));
+    return true;
+}
+
 int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uintptr_t out_addr, int ndim,
               const int64_t *shape, const int64_t *strides, int dim, int num_cus, ScanPlan *p)
 {
@@ -601,6 +663,9 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             }
         }
         d.ws_bytes = ws;
+    } else if (plan_scan_transpose(d, isz, asz)) {
+        if (d.tiles > INT32_MAX)                // tiles are numbered by a 32-bit counter
+            return ST_INVALID;
     } else {
         d.kernel = SK_LINES;
         d.block = tune::kScanBlock;

@@ -10,7 +10,7 @@
 // coalesced load), scans its own few elements, and a wave64 DPP scan of the
 // lane totals gives every lane its offset, so no element goes through LDS.
 //
-// Three kernels, chosen by plan_scan():
+// Kernels, chosen by plan_scan():
 //   k_scan_tile     lines contiguous along the scan dim and at least one
 //                   tile long (the whole array included): one pass, tiles in
 //                   the order of a counter, each tile's prefix from its
@@ -20,6 +20,9 @@
 //   k_scan_rowwave  shorter contiguous lines: one wave per line;
 //   k_scan_columns  a strided scan dim over runs of contiguous lines: tiles of
 //                   lines x scan positions, look-back along the scan dim;
+//   k_scan_transpose input and output contiguous along different axes (a
+//                   transposed or permuted view): tiles staged through LDS,
+//                   look-back along the scan dim;
 //   k_scan_lines    any other layout: one thread per line, walking it.
 #pragma once
 
@@ -963,6 +966,287 @@ __global__ __launch_bounds__(BLOCK) void k_scan_packed(ScanArgs a)
     }
 }
 
+// A value kept in an LDS slot at least as wide as it.
+template <class T, class Slot>
+__device__ __forceinline__ void slot_put(Slot &s, T v)
+{
+    static_assert(sizeof(T) <= sizeof(Slot), "slot too narrow");
+    __builtin_memcpy(&s, &v, sizeof(T));
+}
+template <class T, class Slot>
+__device__ __forceinline__ T slot_get(const Slot &s)
+{
+    T v;
+    __builtin_memcpy(&v, &s, sizeof(T));
+    return v;
+}
+
+// Transposing kernel, for layouts whose input and output are contiguous
+// along different axes (scan_tr_ta/tb/tp give a tile's extents for each
+// mode).  A tile is TA x TB lines -- kept dims 0 and 1 after the plan's
+// reordering, a and b -- by TP scan positions.  It is loaded with the
+// input's contiguous axis across the lanes into LDS; each thread then scans
+// its own lines along the positions there, its prefix per line from the
+// tiles before it along the scan dim by decoupled look-back (tiles numbered
+// chunk-major, as in the columns kernel; wave 0 polls a window of 64
+// predecessors' flags and every thread folds its own lines' values), and
+// writes the outputs back into the same slots; the tile is then stored with
+// the output's contiguous axis across the lanes.  Column c of LDS row p sits
+// at c ^ ((p + c / 32) % 32): a row, a column, and the b axis at a fixed a
+// each cover 32 banks.
+template <class In, class Acc, class Op, int MODE>
+__global__ __launch_bounds__(tune::kScanTrBlock) void k_scan_transpose(ScanArgs a)
+{
+    using S = typename InTraits<In>::S;
+    constexpr int BLOCK = tune::kScanTrBlock;
+    constexpr int SB = (sizeof(S) > sizeof(Acc) ? sizeof(S) : sizeof(Acc)) > 4 ? 8 : 4;
+    using Slot = std::conditional_t<SB == 8, uint64_t, uint32_t>;
+    constexpr int TA = scan_tr_ta(MODE), TB = scan_tr_tb(MODE), TL = TA * TB, TP = scan_tr_tp(MODE, SB);
+    constexpr int LPT = TL / BLOCK;            // lines per thread
+    constexpr int EPT = TL * TP / BLOCK;       // tile elements per thread
+    static_assert(TL % BLOCK == 0 && TL % 32 == 0 && BLOCK % TP == 0 && EPT % 16 == 0, "tile geometry");
+
+    __shared__ Slot tile[TL * TP];
+    __shared__ uint32_t s_id;
+    __shared__ int s_first;
+    const ScanState st(a.ws, a.tiles, a.slot, TL);
+    if (threadIdx.x == 0)
+        s_id = __hip_atomic_fetch_add(st.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t gu = s_id;
+    if (gu >= a.tiles) {                       // never: the counter starts at zero every call
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(st.timeout, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            record_timeout(a.slot);
+        }
+        return;
+    }
+    // chunk t along the scan dim, line tile ct = (run, tile along b, tile along a)
+    const uint32_t t32 = gu / (uint32_t)a.col_tiles;
+    const uint32_t ct32 = gu - t32 * (uint32_t)a.col_tiles;
+    const uint32_t run32 = ct32 / (uint32_t)a.col_tiles_per_run;
+    const uint32_t rem = ct32 - run32 * (uint32_t)a.col_tiles_per_run;
+    const uint32_t nta = (uint32_t)((a.kept_ext[0] + TA - 1) / TA);
+    const uint32_t tbi = rem / nta, tai = rem - tbi * nta;
+    const int64_t g = gu, t = t32, ct = ct32;
+    const int64_t a0 = int64_t(tai) * TA, b0 = int64_t(tbi) * TB, p0 = t * TP;
+    const int na = (int)(a.kept_ext[0] - a0 < TA ? a.kept_ext[0] - a0 : TA);
+    const int nb = (int)(a.kept_ext[1] - b0 < TB ? a.kept_ext[1] - b0 : TB);
+    const int np = (int)(a.m - p0 < TP ? a.m - p0 : TP);
+    const int64_t sb_in = a.kept_in[1], sa_out = a.kept_out[0];
+    const S *x = static_cast<const S *>(a.x) + layout_offset32(a.kept_nd - 2, a.kept_ext + 2, a.kept_in + 2, run32) +
+                 a0 * a.kept_in[0] + b0 * sb_in + p0 * a.s_in;
+    const int64_t ob = layout_offset32(a.kept_nd - 2, a.kept_ext + 2, a.kept_out + 2, run32) + a0 * sa_out +
+                       b0 * a.kept_out[1] + p0 * a.s_out;
+    auto at = [](int ia, int ib, int ip) {
+        const int c = ia + TA * ib;
+        return ip * TL + (c ^ ((ip + (c >> 5)) & 31));
+    };
+
+    // loads: element e of the tile with the input's contiguous axis fastest
+    // (p in mode 0, a otherwise; that axis has input stride 1).  Every lane
+    // loads, those past the view's edge the tile's first element (never
+    // used): loads under a branch each were issued one at a time.
+    S raw[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = int(threadIdx.x) + k * BLOCK;
+        const int ia = MODE == 0 ? 0 : e % TA;
+        const int ib = MODE == 0 ? e / TP : (e / TA) % TB;
+        const int ip = MODE == 0 ? e % TP : e / TL;
+        const int64_t off = MODE == 0 ? ip + ib * sb_in : ia + ib * sb_in + ip * a.s_in;
+        raw[k] = load1(x + (ia < na && ib < nb && ip < np ? off : 0));
+    }
+    issue_barrier();
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = int(threadIdx.x) + k * BLOCK;
+        const int ia = MODE == 0 ? 0 : e % TA;
+        const int ib = MODE == 0 ? e / TP : (e / TA) % TB;
+        const int ip = MODE == 0 ? e % TP : e / TL;
+        if (ia < na && ib < nb && ip < np)
+            slot_put<S>(tile[at(ia, ib, ip)], raw[k]);
+    }
+    __syncthreads();
+
+    // this thread's lines c = threadIdx.x + j * BLOCK, every position of them
+    // read from LDS at once (those past the view's edge hold no input and are
+    // left out of the totals; their outputs are never stored)
+    S vals[LPT][TP];
+    Acc tot[LPT];
+    bool act[LPT];
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+        const int c = int(threadIdx.x) + j * BLOCK, ia = c % TA, ib = c / TA;
+        act[j] = ia < na && ib < nb;
+#pragma unroll
+        for (int p = 0; p < TP; ++p)
+            vals[j][p] = slot_get<S>(tile[at(ia, ib, p)]);
+    }
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+        tot[j] = Op::template identity<Acc>();
+#pragma unroll
+        for (int p = 0; p < TP; ++p)
+            if (p < np)
+                tot[j] = Op::apply(tot[j], InTraits<In>::template one<Acc>(vals[j][p]));
+    }
+    // the tile's per-line values, packed as Acc: line c of tile g at g * TL + c
+    const int64_t slot = g * TL + threadIdx.x;
+    if (t > 0) {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j)
+            if (act[j])
+                store_partial(reinterpret_cast<Acc *>(st.aggs) + slot + j * BLOCK, tot[j]);
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(st.flag(g), kFlagAggregate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    Acc acc[LPT];
+    const Acc init = from_bits<Acc>(a.init_bits);
+#pragma unroll
+    for (int j = 0; j < LPT; ++j)
+        acc[j] = t == 0 ? init : Op::template identity<Acc>();
+    if (t > 0) {
+        int64_t top = t - 1;
+        for (;;) {
+            if (threadIdx.x < 64) {
+                const int64_t jt = top - int64_t(threadIdx.x);
+                uint64_t pm = 0;
+                for (uint32_t spin = 0;; ++spin) {
+                    const uint32_t f = jt >= 0 ? __hip_atomic_load(st.flag(jt * a.col_tiles + ct), __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT)
+                                               : kFlagPrefix;
+                    pm = __ballot(f == kFlagPrefix);
+                    const uint64_t zm = __ballot(f == 0);
+                    // done when every predecessor nearer than the first prefix has published
+                    const uint64_t need = pm ? (pm & (0 - pm)) - 1 : ~uint64_t(0);
+                    if ((zm & need) == 0 && !a.force_wait)
+                        break;
+                    if (spin >= a.spin_limit) {
+                        if (threadIdx.x == 0) {
+                            __hip_atomic_store(st.timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            record_timeout(a.slot);
+                        }
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (threadIdx.x == 0)
+                    s_first = pm ? __builtin_ctzll(pm) : 64;
+            }
+            __syncthreads();
+            const int first = s_first;
+            // the window's values, QB predecessors' loads in flight at a time
+            constexpr int QB = 8;
+            for (int q0 = 0; q0 <= first && q0 < 64 && top - q0 >= 0; q0 += QB) {
+                Acc v[QB][LPT];
+#pragma unroll
+                for (int u = 0; u < QB; ++u) {
+                    // unused slots load predecessor q0's values (in bounds, discarded)
+                    const int q = q0 + u;
+                    const bool use = q <= first && q < 64 && top - q >= 0;
+                    const int qq = use ? q : q0;
+                    const Acc *src = reinterpret_cast<const Acc *>(qq == first ? st.pres : st.aggs) +
+                                     ((top - qq) * a.col_tiles + ct) * TL + threadIdx.x;
+#pragma unroll
+                    for (int j = 0; j < LPT; ++j) {
+                        const Acc w = load_partial(src + j * BLOCK);
+                        v[u][j] = use && act[j] ? w : Op::template identity<Acc>();
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < QB; ++u)
+#pragma unroll
+                    for (int j = 0; j < LPT; ++j)
+                        acc[j] = Op::apply(v[u][j], acc[j]);
+            }
+            __syncthreads();                   // s_first is written again by the next window
+            if (first < 64)
+                break;
+            top -= 64;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < LPT; ++j)
+        if (act[j])
+            store_partial(reinterpret_cast<Acc *>(st.pres) + slot + j * BLOCK, Op::apply(acc[j], tot[j]));
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(st.flag(g), kFlagPrefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // outputs into this thread's own slots
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+        const int c = int(threadIdx.x) + j * BLOCK, ia = c % TA, ib = c / TA;
+        Acc run = acc[j];
+#pragma unroll
+        for (int p = 0; p < TP; ++p) {
+            const Acc e = InTraits<In>::template one<Acc>(vals[j][p]);
+            Acc o;
+            if (a.inclusive) {
+                run = Op::apply(run, e);
+                o = run;
+            } else {
+                o = run;
+                run = Op::apply(run, e);
+            }
+            slot_put<Acc>(tile[at(ia, ib, p)], o);
+        }
+    }
+    __syncthreads();
+
+    // stores: the output's contiguous axis fastest (p in mode 2, b otherwise;
+    // that axis has output stride 1), SBATCH slots read from LDS ahead of
+    // their stores, the output type fixed outside the loop
+    auto store_tile = [&](auto od) {
+        constexpr int OD = decltype(od)::value;
+        constexpr int SBATCH = 16;
+#pragma unroll
+        for (int k0 = 0; k0 < EPT; k0 += SBATCH) {
+            Acc o[SBATCH];
+#pragma unroll
+            for (int u = 0; u < SBATCH; ++u) {
+                const int e = int(threadIdx.x) + (k0 + u) * BLOCK;
+                const int ip = MODE == 2 ? e % TP : e / TL;
+                const int ia = MODE == 2 ? e / TP : (e / TB) % TA;
+                const int ib = MODE == 2 ? 0 : e % TB;
+                o[u] = slot_get<Acc>(tile[at(ia, ib, ip)]);
+            }
+#pragma unroll
+            for (int u = 0; u < SBATCH; ++u) {
+                const int e = int(threadIdx.x) + (k0 + u) * BLOCK;
+                const int ip = MODE == 2 ? e % TP : e / TL;
+                const int ia = MODE == 2 ? e / TP : (e / TB) % TA;
+                const int ib = MODE == 2 ? 0 : e % TB;
+                if (ia < na && ib < nb && ip < np) {
+                    const Acc w[1] = {o[u]};
+                    const int64_t off = MODE == 2 ? ip + ia * sa_out : ib + ia * sa_out + ip * a.s_out;
+                    store_run_as<OD, Acc, 1, true>(a.out, ob + off, w);
+                }
+            }
+        }
+    };
+    if constexpr (std::is_floating_point_v<Acc>) {
+        switch (a.out_dtype) {
+        case F32: store_tile(std::integral_constant<int, F32>{}); break;
+        case F64: store_tile(std::integral_constant<int, F64>{}); break;
+        case BF16: store_tile(std::integral_constant<int, BF16>{}); break;
+        case F16: store_tile(std::integral_constant<int, F16>{}); break;
+        default: break;
+        }
+    } else {
+        switch (a.out_dtype) {
+        case I32: store_tile(std::integral_constant<int, I32>{}); break;
+        case I64: store_tile(std::integral_constant<int, I64>{}); break;
+        default: break;
+        }
+    }
+    scan_release(st, a.ws, a.tiles);
+}
+
 // ---------------------------------------------------------------- launchers
 
 // Zero the first `words` 32-bit words of the workspace: the look-back
@@ -984,7 +1268,9 @@ int run_scan_typed(const ScanLaunch &L)
     constexpr int UT = tune::kScanTileUnroll;
     constexpr int UW = tune::kScanWaveUnroll;
     constexpr int BC = tune::kScanColBlock;
-    if (L.kernel == SK_COLUMNS ? L.block != BC : (L.block != B && !(L.kernel == SK_TILE && L.block == BT)))
+    if (L.kernel == SK_COLUMNS ? L.block != BC
+        : L.kernel == SK_TRANSPOSE ? L.block != tune::kScanTrBlock
+                                   : (L.block != B && !(L.kernel == SK_TILE && L.block == BT)))
         return ST_INVALID;
     // a ScanLaunch carries no Launch; launch_first only reads the events
     Launch ev;
@@ -1045,6 +1331,18 @@ int run_scan_typed(const ScanLaunch &L)
                          grid, block, st, ev, L.args);
         break;
     }
+    case SK_TRANSPOSE:
+        if (vl != 1)
+            return ST_INVALID;
+        if (L.args.slot < 0)
+            clear_state(L.args, 64 + scan_flag_lines(L.args.tiles) * 32, st);
+        switch (L.tmode) {
+        case 0: launch_first(&k_scan_transpose<In, Acc, Op, 0>, grid, block, st, ev, L.args); break;
+        case 1: launch_first(&k_scan_transpose<In, Acc, Op, 1>, grid, block, st, ev, L.args); break;
+        case 2: launch_first(&k_scan_transpose<In, Acc, Op, 2>, grid, block, st, ev, L.args); break;
+        default: return ST_INVALID;
+        }
+        break;
     default:
         return ST_INVALID;
     }

@@ -15,7 +15,7 @@
 namespace rk {
 
 // Scan kernels (rk_scan.hpp).
-enum ScanKernel { SK_NONE = 0, SK_TILE = 1, SK_ROWWAVE = 2, SK_LINES = 3, SK_COLUMNS = 4,
+enum ScanKernel { SK_NONE = 0, SK_TILE = 1, SK_ROWWAVE = 2, SK_LINES = 3, SK_COLUMNS = 4, SK_TRANSPOSE = 5,
                   SK_TAKE_TIMEOUTS = 100 };   // read and clear the count of waits that gave up (no scan)
 
 namespace tune {
@@ -51,6 +51,9 @@ constexpr int kScanColLanesScalar = 64;   //   ... with element loads
 constexpr int kScanColRows = 16;          // consecutive scan positions per thread (8: 125.7 us at 1024 threads)
 constexpr int64_t kScanColMinRun = 16;    // runs of lines narrower than this take the lines kernel
 constexpr int kScanPackedBlocksPerCu = 8; // lines kernel, packed form: grid cap
+constexpr int kScanTrBlock = 256;         // transposing scan: threads per block
+constexpr int kScanTrTileKB = 64;         //   ... and LDS per tile (two blocks to a CU)
+constexpr int64_t kScanTrMinRun = 16;     // its two contiguous axes span at least this many elements
 }  // namespace tune
 
 // The lines kernel's packed form: lines contiguous along the scan dim in
@@ -84,7 +87,8 @@ struct ScanArgs {
     int64_t s_in, s_out;  // scan-dim strides in elements
     int64_t tiles_per_line;   // tile kernel
     int64_t tiles;            // tile and columns kernels
-    int64_t col_tiles_per_run;    // columns kernel: tiles across one run of lines (kept dim 0)
+    int64_t col_tiles_per_run;    // columns kernel: tiles across one run of lines (kept dim 0);
+                                  // transposing kernel: across kept dims 0 and 1 (its a and b)
     int64_t col_tiles;            //   ... across all runs; tiles = col_tiles * chunks of the scan dim
     int inclusive;
     int out_dtype;
@@ -94,6 +98,24 @@ struct ScanArgs {
     uint32_t spin_limit;  // look-back: polls of one window before the wait gives up
     uint32_t force_wait;  // 0; nonzero only to make every look-back wait until it gives up (a test hook)
 };
+
+// Transposing scan (k_scan_transpose): the input is contiguous along one
+// axis of a line x position tile and the output along another, so a tile
+// goes through LDS between its loads and its stores.  Its axes: a, a kept dim
+// with input stride 1; b, a kept dim with output stride 1; p, the scan
+// positions.  Mode 0: the scan dim is the input's contiguous one (a row-major
+// matrix scanned along its rows, say), a tile is 256 b x 64 p; mode 1: a and
+// b are different kept dims (a permuted view), 32 a x 32 b x 16 p; mode 2:
+// the scan dim is the output's contiguous one, 256 a x 64 p.  Each side then
+// moves runs of 32 or more consecutive elements.  A tile holds 16384 slots of
+// 4 bytes (the larger of the input and accumulator elements), or half as
+// many positions of 8-byte slots: kScanTrTileKB = 64 KB of LDS.
+constexpr int scan_tr_ta(int mode) { return mode == 0 ? 1 : mode == 1 ? 32 : 256; }
+constexpr int scan_tr_tb(int mode) { return mode == 0 ? 256 : mode == 1 ? 32 : 1; }
+constexpr int scan_tr_tp(int mode, int slot_bytes)
+{
+    return (mode == 1 ? 16 : 64) * 4 / slot_bytes * tune::kScanTrTileKB / 64;
+}
 
 // Columns-scan state: a 256-byte header (as the tile scan's), the flags --
 // 32-bit words, the flag of tile g at word (g % lines) * 32 + g / lines,
@@ -126,6 +148,7 @@ struct ScanLaunch {
     int kernel;           // rk::ScanKernel
     int acc, op;
     int vec;              // elements per load (1: element loads)
+    int tmode;            // transposing kernel: its mode
     int64_t grid;
     int block;
     ScanArgs args;
@@ -156,8 +179,9 @@ struct ScanPlan {
     int64_t tile_elems = 0; // elements per tile (tile and columns kernels)
     int64_t tiles_per_line = 0;
     int64_t tiles = 0;
-    int64_t col_tiles_per_run = 0;   // columns kernel
+    int64_t col_tiles_per_run = 0;   // columns and transposing kernels
     int64_t col_tiles = 0;
+    int tmode = 0;                   // transposing kernel: its mode
     int64_t chunks = 0;
     int64_t grid = 0;
     int block = tune::kScanBlock;

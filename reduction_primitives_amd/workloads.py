@@ -172,3 +172,27 @@ def general_layouts() -> list:
     out.append(View("1024x2048x8x4 f32 dims=(2,4)", uniform(math.prod(shape), -1.0, 1.0, 7002),
                     shape, cm_strides(shape), (2, 4), "U[-1,1) seed 7002"))
     return out
+
+
+def permuted_kept() -> View:
+    """A view whose two kept dims are swapped against storage: (256, 1024,
+    256) with strides (256, 65536, 1), i.e. storage (256, 256, 1024) read with
+    dims 1 and 3 exchanged, reduced or scanned along dim 2 -- 67,108,864 float32 U[-1,1)
+    elements.  The outputs are contiguous only in storage order, a layout
+    PR #176's opening paragraphs leave to the one-thread or one-block per
+    output kernels."""
+    shape = (256, 1024, 256)
+    return View("256x1024x256 f32 permuted dims=2", uniform(math.prod(shape), -1.0, 1.0, 7003),
+                shape, (256, 65536, 1), (2,), "U[-1,1) seed 7003")
+
+
+def short_lines() -> list:
+    """Scans along dim 1 of contiguous lines shorter than 256 elements (PR
+    #202's table of time ratios has scans along dims=1 beside whole ones):
+    5,000,000 float32 U[-1,1) elements as lines of 50, 100 and 200."""
+    out = []
+    for m, seed in ((50, 7004), (100, 7005), (200, 7006)):
+        shape = (m, 5_000_000 // m)
+        out.append(View(f"{m}x{shape[1]} f32 cumsum dims=1", uniform(math.prod(shape), -1.0, 1.0, seed),
+                        shape, cm_strides(shape), (1,), f"U[-1,1) seed {seed}"))
+    return out

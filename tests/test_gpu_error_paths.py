@@ -93,6 +93,32 @@ def test_collection_that_gives_up_stores_nothing_and_is_reported():
     assert rk.rk_stream_timeouts(st) == 0
 
 
+def test_transposing_scan_give_up_is_reported():
+    """A transposing scan (a row-major matrix along its rows) whose
+    look-back waits all give up: the stream's count records it, and the next
+    call on the stream is exact."""
+    rk = _rk()
+    shape, strides = (300, 2000), (2000, 1)
+    x = W.randint(600_000, -1000, 1000, 9620)
+    xd = x.to(DEV)
+    plan = rk.plan_scan(torch.int32, shape, strides, 2, acc=torch.int64)
+    assert plan["kernel_name"] == "scan_transpose" and plan["split"] > 1
+    s = torch.cuda.Stream()
+    st = ctypes.c_void_p(s.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        rk.rk_stream_timeouts(st)
+        with forced_give_up():
+            rk.scan(xd, shape, strides, 2, acc=torch.int64, out_dtype=torch.int64)
+            assert rk.rk_stream_timeouts(st) >= 1
+        assert rk.rk_stream_timeouts(st) == 0
+        c = rk.scan(xd, shape, strides, 2, acc=torch.int64, out_dtype=torch.int64)
+    s.synchronize()
+    R = O.scan_dims(O.SUM, O.I32, O.I64, raw_np(x), shape, strides, 1, 0, True)
+    assert np.array_equal(raw_np(c), R)
+    assert rk.rk_stream_timeouts(st) == 0
+
+
 def test_host_copy_back_reports_a_give_up():
     """Host mode without the pinned result buffer (RK_HOST_COPY): the result
     is copied back from the workspace with the call's sequence word, so a

@@ -81,6 +81,11 @@ def _depth(plan, k):
         # look-back chain; in the tile the row groups before it, the prefix and
         # the thread's positions up to k
         return k // rows + (rpg + rg) + (rg + 1 + rpg) + 1
+    if name == "scan_transpose":
+        # a tile's aggregate folds its positions in order (at most 64); the
+        # look-back adds one term per tile before it (at least 8 positions
+        # each); in the tile the prefix, then the positions up to k
+        return k // 8 + 64 + 1 + 64 + 1
     return k + 1                                # lines: one thread walks the line
 
 
@@ -311,8 +316,16 @@ DIMS_CASES = [
     ((130, 2000), (1, 131), 2, "scan_columns", "padded rows: element loads"),
     ((700, 9, 3), None, 1, "scan_rowwave", "lines at the offsets of two kept dims"),
     ((33, 5, 9, 4), None, 4, "scan_columns", "4-d"),
-    ((256, 300), (300, 1), 1, "scan_lines", "transposed view: input lines strided"),
-    ((256, 300), (300, 1), 2, "scan_lines", "transposed view: output lines strided"),
+    ((256, 300), (300, 1), 1, "scan_transpose", "transposed view along its strided dim: scan dim contiguous in the output"),
+    ((256, 300), (300, 1), 2, "scan_transpose", "transposed view along its contiguous dim: lines contiguous in the output"),
+    ((512, 3000), (3000, 1), 2, "scan_transpose", "transposed view, long lines: look-back over windows of 64 tiles"),
+    ((1000, 19), (19, 1), 2, "scan_transpose", "transposed view, lines of 19: one ragged chunk"),
+    ((19, 1000), (1000, 1), 1, "scan_transpose", "transposed view, 19 lines: one ragged tile of lines"),
+    ((64, 3000, 40), (40, 2560, 1), 2, "scan_transpose", "permuted view: input and output contiguous along different kept dims"),
+    ((40, 7, 50), (350, 50, 1), 2, "scan_transpose", "permuted view, ragged tiles along both kept dims"),
+    ((100, 17, 33), (561, 33, 1), 2, "scan_transpose", "scan dim contiguous in the input, an outer kept dim"),
+    ((17, 33, 100), (3300, 100, 1), 1, "scan_transpose", "scan dim contiguous in the output, an outer kept dim"),
+    ((10, 300), (300, 1), 2, "scan_lines", "transposed view with lines too few for a tile: a thread each"),
 ]
 
 
@@ -375,7 +388,8 @@ def test_tile_state_paths(on):
     workspace header."""
     rk = _rk()
     cases = [((3 * TILE + 5,), (1,), 1), ((10**6 + 3,), (1,), 1), ((TILE,), (1,), 1),
-             ((300, 2000), (1, 300), 2), ((10**8,), (1,), 1), ((5000, 2), (1, 5000), 1)]
+             ((300, 2000), (1, 300), 2), ((10**8,), (1,), 1), ((5000, 2), (1, 5000), 1),
+             ((300, 2000), (2000, 1), 2), ((30, 4000, 40), (160000, 40, 1), 1)]
     with _fused(rk, on):
         for rep in range(2):
             for shape, strides, dim in cases:
@@ -453,12 +467,15 @@ SCAN_DIMS_COMBOS = [  # (input, accumulator, output)
     (torch.float32, torch.float64, torch.float64),
 ]
 
-SCAN_DIMS_LAYOUTS = [  # (shape, dim)
-    ((3 * TILE + 100, 3), 1),   # tile, look-back along each line
-    ((3000, 40), 1),            # row-wave
-    ((40, 3000, 5), 2),         # columns, look-back across chunks
-    ((50, 300), 1),             # lines, packed one element to a lane
-    ((100, 301), 1),            # lines, packed two elements to a lane
+SCAN_DIMS_LAYOUTS = [  # (shape, dim, strides or None)
+    ((3 * TILE + 100, 3), 1, None),            # tile, look-back along each line
+    ((3000, 40), 1, None),                     # row-wave
+    ((40, 3000, 5), 2, None),                  # columns, look-back across chunks
+    ((50, 300), 1, None),                      # lines, packed one element to a lane
+    ((100, 301), 1, None),                     # lines, packed two elements to a lane
+    ((300, 700), 2, (700, 1)),                 # transposing, scan dim contiguous in the input
+    ((300, 700), 1, (700, 1)),                 # transposing, scan dim contiguous in the output
+    ((40, 300, 50), 2, (300 * 50, 50, 1)),     # transposing, two kept dims
 ]
 
 
@@ -466,7 +483,7 @@ SCAN_DIMS_LAYOUTS = [  # (shape, dim)
 @pytest.mark.parametrize("op", ["sum", "max"])
 def test_scan_dims_dtype_matrix(combo, op):
     in_t, acc_t, out_t = combo
-    for i, (shape, dim) in enumerate(SCAN_DIMS_LAYOUTS):
+    for i, (shape, dim, strides) in enumerate(SCAN_DIMS_LAYOUTS):
         n = math.prod(shape)
         if in_t.is_floating_point:
             x = W.normal(n, 12300 + i, in_t) if in_t != torch.float64 else W.normal(n, 12300 + i).double()
@@ -474,7 +491,7 @@ def test_scan_dims_dtype_matrix(combo, op):
                 x = x * 0.25            # prefix sums and their magnitudes stay below float16's 65,504
         else:
             x = W.randint(n, -2**20, 2**20, 12400 + i, in_t)
-        scan_and_check(x, shape, W.cm_strides(shape), dim, op=op, acc=acc_t, out_dtype=out_t,
+        scan_and_check(x, shape, strides or W.cm_strides(shape), dim, op=op, acc=acc_t, out_dtype=out_t,
                        inclusive=bool(i % 2), init=None if op != "sum" else 1)
 
 
