@@ -52,7 +52,13 @@ constexpr int kScanColRows = 16;          // consecutive scan positions per thre
 constexpr int64_t kScanColMinRun = 16;    // runs of lines narrower than this take the lines kernel
 constexpr int kScanPackedBlocksPerCu = 8; // lines kernel, packed form: grid cap
 constexpr int kScanTrBlock = 256;         // transposing scan: threads per block
-constexpr int kScanTrTileKB = 64;         //   ... and LDS per tile (two blocks to a CU)
+// LDS per tile of the transposing scan when the scan dim is the output's
+// contiguous one (mode 2): 32 KB tiles fit four blocks to a CU (92 VGPRs),
+// 140-145 us against 155-172 at 64 KB on row-major 8192x8192 f32 along dim 1.
+// The other modes keep 64 KB: at 32 KB the scan dim contiguous in the input
+// took 174 us against 157 (three blocks to a CU, 135 VGPRs; 198 us at four,
+// with the registers held to 128), the permuted view 200 against 167.
+constexpr int kScanTrTileKBScanOut = 32;
 constexpr int64_t kScanTrMinRun = 16;     // its two contiguous axes span at least this many elements
 }  // namespace tune
 
@@ -106,15 +112,18 @@ struct ScanArgs {
 // positions.  Mode 0: the scan dim is the input's contiguous one (a row-major
 // matrix scanned along its rows, say), a tile is 256 b x 64 p; mode 1: a and
 // b are different kept dims (a permuted view), 32 a x 32 b x 16 p; mode 2:
-// the scan dim is the output's contiguous one, 256 a x 64 p.  Each side then
-// moves runs of 32 or more consecutive elements.  A tile holds 16384 slots of
-// 4 bytes (the larger of the input and accumulator elements), or half as
-// many positions of 8-byte slots: kScanTrTileKB = 64 KB of LDS.
+// the scan dim is the output's contiguous one, 256 a x 32 p.  Each side then
+// moves runs of 32 or more consecutive elements (16 for 8-byte slots in mode
+// 2).  A slot is the larger of the input and accumulator elements, 4 or 8
+// bytes; 8-byte slots halve the positions.  A tile takes 64 KB of LDS, 32 KB
+// in mode 2.
 constexpr int scan_tr_ta(int mode) { return mode == 0 ? 1 : mode == 1 ? 32 : 256; }
 constexpr int scan_tr_tb(int mode) { return mode == 0 ? 256 : mode == 1 ? 32 : 1; }
 constexpr int scan_tr_tp(int mode, int slot_bytes)
 {
-    return (mode == 1 ? 16 : 64) * 4 / slot_bytes * tune::kScanTrTileKB / 64;
+    return mode == 1 ? 16 * 4 / slot_bytes
+           : mode == 0 ? 64 * 4 / slot_bytes
+                       : 64 * 4 / slot_bytes * tune::kScanTrTileKBScanOut / 64;
 }
 
 // Columns-scan state: a 256-byte header (as the tile scan's), the flags --

@@ -404,7 +404,7 @@ def test_scan_plans():
     assert p.kernel == rk.RK_KERNEL_SCAN_ROWWAVE                    # four wave chunks and longer
     # input and output contiguous along different axes: the transposing tiles.
     # A row-major 512 x 3000 matrix along its rows (tiles of 256 lines x 64
-    # positions), along its columns (256 lines x 64), and a permuted view
+    # positions), along its columns (256 lines x 32), and a permuted view
     # whose kept dims are contiguous in input and output apart (32 x 32 lines
     # x 16 positions); 8-byte accumulators halve the positions.  The state
     # holds 16 bytes per line of a tile, as the columns kernel's.
@@ -415,7 +415,7 @@ def test_scan_plans():
     p = rk.rk_plan_scan(i32, i64, i64, 0, 0, 2, [512, 3000], [3000, 1], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TRANSPOSE and p.split == -(-3000 // 32) and p.tile_outputs == 256 * 32
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [512, 3000], [3000, 1], 0, 256)
-    assert p.kernel == rk.RK_KERNEL_SCAN_TRANSPOSE and p.split == 8 and p.grid == 8 * -(-3000 // 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TRANSPOSE and p.split == 16 and p.grid == 16 * -(-3000 // 256)
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 3, [64, 3000, 40], [40, 2560, 1], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TRANSPOSE and p.split == -(-3000 // 16) and p.grid == 4 * p.split
     assert p.tile_outputs == 32 * 32 * 16 and p.launches == 1
