@@ -435,10 +435,12 @@ def test_tile_state_on_many_streams():
 def test_beyond_2_31_elements():
     """A scan of more than 2^31 int32 ones into int64 (8.6 GB in, 17 GB out):
     more tiles than a library slot holds, so the workspace state and its
-    clearing launch; output k is k + 1 (sampled), and along dims=2 of a
-    (2^16, 32769) view the last line's outputs sit past 2^31 elements."""
+    clearing launch; output k is k + 1 (sampled).  Along dims=2 of a
+    (2^16, 32769) view the last line's outputs sit past 2^31 elements, and so
+    do those of the same ones read as a row-major (32769, 2^16) matrix
+    scanned along its rows (the transposing tiles)."""
     rk = _rk()
-    n = 2**31 + 3000
+    n = 2**31 + 70_000
     ones = torch.ones(n, dtype=torch.int32, device=DEV)
     plan = rk.plan_scan(torch.int32, (n,), (1,), 1, acc=torch.int64)
     assert plan["kernel_name"] == "scan_tile" and plan["launches"] == 2
@@ -451,7 +453,16 @@ def test_beyond_2_31_elements():
     assert rk.plan_scan(torch.int32, (L, k), (1, L), 2, acc=torch.int64)["kernel_name"] == "scan_columns"
     last = cols[(k - 1) * L:k * L]
     assert bool((last == k).all().item()) and int(cols[L - 1].item()) == 1
-    del ones, cols
+    del cols
+    assert k == 32769 and k * L > 2**31
+    assert rk.plan_scan(torch.int32, (k, L), (L, 1), 2, acc=torch.int64)["kernel_name"] == "scan_transpose"
+    rows = rk.scan(ones, (k, L), (L, 1), 2, acc=torch.int64, out_dtype=torch.int64)
+    # output (i, j) sits at i + k * j and holds j + 1
+    ij = [(0, 0), (k - 1, 0), (0, L - 1), (k - 1, L - 1), (12345, 40000), (k - 1, 32767), (k - 2, L - 2)]
+    idx = torch.tensor([i + k * j for i, j in ij], device=DEV)
+    assert rows[idx].cpu().tolist() == [j + 1 for _, j in ij]
+    assert bool((rows[k * (L - 1):] == L).all().item())
+    del ones, rows
     torch.cuda.empty_cache()
 
 
