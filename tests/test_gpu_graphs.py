@@ -50,9 +50,14 @@ def _replays(rk, fused):
     out_dot = torch.empty(1, dtype=torch.int64, device=DEV)
     out_dims = torch.empty(8192, dtype=torch.int64, device=DEV)
     out_scan = torch.empty(m, dtype=torch.int64, device=DEV)
+    out_tr = torch.empty(8192 * 512, dtype=torch.int64, device=DEV)
+    tr_shape, tr_strides = (512, 8192), (8192, 1)          # the matrix read row-major, scanned along its rows
     ws_all = rk.workspace_for(rk.rk_workspace_size(rk.RK_I32, rk.RK_I64, 1, [n], [1], 1), DEV)
     ws_dims = rk.workspace_for(rk.rk_workspace_size(rk.RK_I32, rk.RK_I64, 2, shape, strides, 0b10), DEV)
     ws_scan = rk.workspace_for(rk.rk_scan_workspace_size(rk.RK_I32, rk.RK_I64, 1, [m], [1], 0), DEV)
+    ws_tr = rk.workspace_for(rk.rk_scan_workspace_size(rk.RK_I32, rk.RK_I64, 2, tr_shape, tr_strides, 1), DEV)
+    plan_tr = rk.plan_scan(torch.int32, tr_shape, tr_strides, 2, acc=torch.int64)
+    assert plan_tr["kernel_name"] == "scan_transpose" and plan_tr["launches"] == (1 if fused else 2)
     assert rk.plan_dims(torch.int32, shape, strides, 2, acc=torch.int64)["split"] > 1
     plan = rk.plan_scan(torch.int32, (m,), (1,), 1, acc=torch.int64)
     assert plan["kernel_name"] == "scan_tile"
@@ -64,6 +69,7 @@ def _replays(rk, fused):
         rk.reduce_dims(mat, shape, strides, 2, acc=torch.int64, out_dtype=torch.int64, out=out_dims,
                        workspace=ws_dims)
         rk.scan(s, acc=torch.int64, out_dtype=torch.int64, out=out_scan, workspace=ws_scan)
+        rk.scan(mat, tr_shape, tr_strides, 2, acc=torch.int64, out_dtype=torch.int64, out=out_tr, workspace=ws_tr)
 
     def fill(seed):
         xs = W.randint(n, -1000, 1000, seed)
@@ -80,6 +86,8 @@ def _replays(rk, fused):
         want = ms.long().view(512, 8192).sum(dim=0).numpy()
         assert np.array_equal(raw_np(out_dims), want)
         assert np.array_equal(raw_np(out_scan), np.cumsum(ss.numpy().astype(np.int64)))
+        rows = np.cumsum(ms.numpy().astype(np.int64).reshape(512, 8192), axis=1)
+        assert np.array_equal(raw_np(out_tr), rows.T.reshape(-1))      # column-major (512, 8192) output
 
     data = fill(14000)
     torch.cuda.synchronize()
