@@ -935,30 +935,44 @@ __global__ __launch_bounds__(BLOCK) void k_scan_packed(ScanArgs a)
             }
         }
         issue_barrier();
+        Acc l[U][E], t[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            Acc l[E];
-            Acc t = Op::template identity<Acc>();
+            t[u] = Op::template identity<Acc>();
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 if (act[u] && q * E + e < m)
-                    t = Op::apply(t, InTraits<In>::template one<Acc>(raw[u][e]));
-                l[e] = t;
+                    t[u] = Op::apply(t[u], InTraits<In>::template one<Acc>(raw[u][e]));
+                l[u][e] = t[u];
             }
-            for (int d = 1; d < L; d <<= 1) {
-                const Acc y = __shfl_up(t, d, 64);
-                if (q >= d)
-                    t = Op::apply(y, t);
+        }
+        // each step's lane moves for all U groups at once, so their LDS
+        // round trips overlap (group by group they went one at a time)
+        for (int d = 1; d < L; d <<= 1) {
+            Acc y[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                y[u] = __shfl_up(t[u], d, 64);
+            if (q >= d) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    t[u] = Op::apply(y[u], t[u]);
             }
-            const Acc before = __shfl_up(t, 1, 64);
-            const Acc base = q == 0 ? init : Op::apply(init, before);
+        }
+        Acc before[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            before[u] = __shfl_up(t[u], 1, 64);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const Acc base = q == 0 ? init : Op::apply(init, before[u]);
             if (!act[u])
                 continue;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 if (q * E + e < m) {
                     Acc o[1];
-                    o[0] = a.inclusive ? Op::apply(base, l[e]) : e == 0 ? base : Op::apply(base, l[e - 1]);
+                    o[0] = a.inclusive ? Op::apply(base, l[u][e]) : e == 0 ? base : Op::apply(base, l[u][e - 1]);
                     store_run<Acc, 1>(a.out, ob[u] + q * E + e, a.out_dtype, o);
                 }
             }
