@@ -66,7 +66,8 @@ constexpr int64_t kScanTrMinRun = 16;     // its two contiguous axes span at lea
 // input and output, from a quarter wave long up to the row-wave length (at
 // most 4 waves), go whole to waves, each lane holding scan_packed_width(m)
 // consecutive elements.  Against a thread per line (f32, about 5 million
-// elements): lines of 50 88.8 -> 36.3 us, of 24 47.2 -> 34.1; lines of 10
+// elements, before its lane moves were issued for all groups at once): lines
+// of 50 88.8 -> 36.3 us, of 24 47.2 -> 34.1; lines of 10
 // stay with a thread each (27.8 against 30.6 packed), whose neighbours share
 // its cache lines.  One test for the planner and the launch.
 constexpr bool scan_lines_packed(int64_t s_in, int64_t s_out, int64_t m)
