@@ -900,7 +900,10 @@ __global__ __launch_bounds__(BLOCK) void k_scan_lines(ScanArgs a)
 // lane's running value).  Waves stride over the groups of lines, U groups a
 // round with their loads in flight together (one a round waited on memory
 // latency every group).
-template <class In, class Acc, class Op, int BLOCK, int U, int E>
+//
+// L32: the line count fits 32 bits, so a line's offsets take 32-bit
+// divisions (the 64-bit ones sat on every group's path to its loads).
+template <class In, class Acc, class Op, int BLOCK, int U, int E, bool L32>
 __global__ __launch_bounds__(BLOCK) void k_scan_packed(ScanArgs a)
 {
     using S = typename InTraits<In>::S;
@@ -926,8 +929,11 @@ __global__ __launch_bounds__(BLOCK) void k_scan_packed(ScanArgs a)
             for (int e = 0; e < E; ++e)
                 raw[u][e] = S{};
             if (act[u]) {
-                const S *x = static_cast<const S *>(a.x) + layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line);
-                ob[u] = layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
+                const S *x = static_cast<const S *>(a.x) +
+                             (L32 ? layout_offset32(a.kept_nd, a.kept_ext, a.kept_in, uint32_t(line))
+                                  : layout_offset(a.kept_nd, a.kept_ext, a.kept_in, line));
+                ob[u] = L32 ? layout_offset32(a.kept_nd, a.kept_ext, a.kept_out, uint32_t(line))
+                            : layout_offset(a.kept_nd, a.kept_ext, a.kept_out, line);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     if (q * E + e < m)
@@ -1324,11 +1330,17 @@ int run_scan_typed(const ScanLaunch &L)
         break;
     case SK_LINES:
         if (scan_lines_packed(L.args.s_in, L.args.s_out, L.args.m)) {
+            constexpr int UL = tune::kScanPackedUnroll;
+            const bool l32 = L.args.lines <= int64_t(UINT32_MAX);
+#define RK_PACKED(UK, EK)                                                                                    \
+    (l32 ? launch_first(&k_scan_packed<In, Acc, Op, B, UK, EK, true>, grid, block, st, ev, L.args)             \
+         : launch_first(&k_scan_packed<In, Acc, Op, B, UK, EK, false>, grid, block, st, ev, L.args))
             switch (scan_packed_width(L.args.m)) {
-            case 1: launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll, 1>, grid, block, st, ev, L.args); break;
-            case 2: launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll, 2>, grid, block, st, ev, L.args); break;
-            default: launch_first(&k_scan_packed<In, Acc, Op, B, tune::kScanLinesUnroll / 2, 4>, grid, block, st, ev, L.args); break;
+            case 1: RK_PACKED(UL, 1); break;
+            case 2: RK_PACKED(UL, 2); break;
+            default: RK_PACKED(UL / 2, 4); break;
             }
+#undef RK_PACKED
         } else
             launch_first(&k_scan_lines<In, Acc, Op, B, tune::kScanLinesUnroll>, grid, block, st, ev, L.args);
         break;
