@@ -502,7 +502,7 @@ static bool plan_scan_transpose(ScanPlan &d, int isz, int asz)
     }
     const int64_t R = tune::kScanTrMinRun;
     int mode = -1;
-    if (d.s_in == 1 && d.s_out != 1 && ib >= 0 && d.m >= R && k.ext[ib] >= R)
+    if (d.s_in == 1 && d.s_out != 1 && ib >= 0 && d.m >= R && k.ext[ib] >= tune::kScanTrMinLines)
         mode = 0;
     else if (ia >= 0 && ib >= 0 && ia != ib && k.ext[ia] >= R && k.ext[ib] >= R)
         mode = 1;
@@ -666,6 +666,28 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
     } else if (plan_scan_transpose(d, isz, asz)) {
         if (d.tiles > INT32_MAX)                // tiles are numbered by a 32-bit counter
             return ST_INVALID;
+    } else if (d.s_in == 1 && d.m >= tune::kScanWaveMinLen) {
+        // lines contiguous in the input only, too few for the transposing
+        // tiles (a few rows of a row-major matrix along their rows): the tile
+        // kernel along each line, its outputs stored one by one
+        d.kernel = SK_TILE;
+        d.ostr = true;
+        bool vec_ok = in_addr % 16 == 0 && d.m % v == 0;
+        for (int i = 0; i < k.nd; ++i)
+            vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0;
+        d.vec = vec_ok ? v : 1;
+        d.block = tune::kScanTileBlock;
+        d.tile_elems = scan_tile_elems(in_dtype, tune::kScanTileBlock, d.vec);
+        if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus || d.vec == 1) {
+            d.block = tune::kScanBlock;
+            d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock, d.vec);
+        }
+        d.tiles_per_line = ceil_div(d.m, d.tile_elems);
+        d.tiles = d.lines * d.tiles_per_line;
+        if (d.tiles > INT32_MAX)
+            return ST_INVALID;
+        d.grid = d.tiles;
+        d.ws_bytes = round_up_256(size_t(scan_tile_state_bytes(d.tiles)));
     } else {
         d.kernel = SK_LINES;
         d.block = tune::kScanBlock;

@@ -12,7 +12,9 @@
 //
 // Kernels, chosen by plan_scan():
 //   k_scan_tile     lines contiguous along the scan dim and at least one
-//                   tile long (the whole array included): one pass, tiles in
+//                   tile long (the whole array included; also lines contiguous
+//                   in the input only, too few for the transposing tiles,
+//                   their outputs stored one by one): one pass, tiles in
 //                   the order of a counter, each tile's prefix from its
 //                   predecessors by decoupled look-back (Merrill and Garland,
 //                   "Single-pass Parallel Prefix Scan with Decoupled
@@ -497,7 +499,10 @@ __global__ __launch_bounds__(BLOCK) void k_scan_clear(uint32_t *w, int64_t words
 
 // Tile kernel: a tile is NW waves x UC chunks of consecutive elements of one
 // line; tiles are numbered by a counter in the order blocks start.
-template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = false>
+// OSTR: the outputs of a line are s_out apart (the scan dim is contiguous in
+// the input only: a few rows of a row-major matrix along their rows), each
+// stored on its own.
+template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = false, bool OSTR = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_tile(ScanArgs a)
 {
     using C = Chunk<In, Acc, Op, VL>;
@@ -586,8 +591,17 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         C::decode(raw[k], k < nk, e);
         chunk_scan<Acc, Op, V>(e, lane_excl, total);
         chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl), a.inclusive != 0, o);
-        if (k < nk)
-            store_run<Acc, V, NTS>(a.out, ob + first + k * CH, a.out_dtype, o);
+        if (k < nk) {
+            if constexpr (OSTR) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const Acc w[1] = {o[i]};
+                    store_run<Acc, 1>(a.out, ob + (first + k * CH + i) * a.s_out, a.out_dtype, w);
+                }
+            } else {
+                store_run<Acc, V, NTS>(a.out, ob + first + k * CH, a.out_dtype, o);
+            }
+        }
         carry = Op::apply(carry, total);
     }
     tile_release(st, a.ws, a.tiles);
@@ -1308,7 +1322,14 @@ int run_scan_typed(const ScanLaunch &L)
         if (L.args.slot < 0)
             clear_state(L.args, scan_tile_state_bytes(L.args.tiles) / 4, st);
 #define RK_SCAN_TILE(BK, UK, VLN) launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true>, grid, block, st, ev, L.args)
-        if (L.block == BT) {
+#define RK_SCAN_TILE_OSTR(BK, UK, VLN)                                                                       \
+    launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true, true>, grid, block, st, ev, L.args)
+        if (L.ostr) {                            // strided outputs: the input's vector or element loads
+            if (L.block == BT && vl == VV) RK_SCAN_TILE_OSTR(BT, UT, VV);
+            else if (L.block == B && vl == VV) RK_SCAN_TILE_OSTR(B, U, VV);
+            else if (L.block == B && vl == 1) RK_SCAN_TILE_OSTR(B, U, 1);
+            else return ST_INVALID;
+        } else if (L.block == BT) {
             if (vl == VV) RK_SCAN_TILE(BT, UT, VV);
             else if (vl == VW) RK_SCAN_TILE(BT, UT, VW);
             else return ST_INVALID;             // element loads take the small tiles
@@ -1318,6 +1339,7 @@ int run_scan_typed(const ScanLaunch &L)
             else RK_SCAN_TILE(B, U, 1);
         }
 #undef RK_SCAN_TILE
+#undef RK_SCAN_TILE_OSTR
         break;
     }
     case SK_ROWWAVE:

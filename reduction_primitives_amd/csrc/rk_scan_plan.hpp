@@ -62,6 +62,11 @@ constexpr int kScanTrBlock = 256;         // transposing scan: threads per block
 // with the registers held to 128), the permuted view 200 against 167.
 constexpr int kScanTrTileKBScanOut = 32;
 constexpr int64_t kScanTrMinRun = 16;     // its two contiguous axes span at least this many elements
+// With the scan dim contiguous in the input, the transposing tiles need this
+// many lines; fewer take the tile kernel with outputs stored one by one.
+// 8 Mi f32 as L row-major rows along their rows, us transposing / tile: L = 16
+// 357 / 103, 32 194 / 122, 64 113 / 118, 128 70 / 116, 256 46 / 60.
+constexpr int64_t kScanTrMinLines = 64;
 }  // namespace tune
 
 // The lines kernel's packed form: lines contiguous along the scan dim in
@@ -161,6 +166,7 @@ struct ScanLaunch {
     int acc, op;
     int vec;              // elements per load (1: element loads)
     int tmode;            // transposing kernel: its mode
+    int ostr;             // tile kernel: outputs s_out apart along the scan dim
     int64_t grid;
     int block;
     ScanArgs args;
@@ -194,6 +200,7 @@ struct ScanPlan {
     int64_t col_tiles_per_run = 0;   // columns and transposing kernels
     int64_t col_tiles = 0;
     int tmode = 0;                   // transposing kernel: its mode
+    bool ostr = false;               // tile kernel: outputs s_out apart along the scan dim
     int64_t chunks = 0;
     int64_t grid = 0;
     int block = tune::kScanBlock;

@@ -325,7 +325,11 @@ DIMS_CASES = [
     ((40, 7, 50), (350, 50, 1), 2, "scan_transpose", "permuted view, ragged tiles along both kept dims"),
     ((100, 17, 33), (561, 33, 1), 2, "scan_transpose", "scan dim contiguous in the input, an outer kept dim"),
     ((17, 33, 100), (3300, 100, 1), 1, "scan_transpose", "scan dim contiguous in the output, an outer kept dim"),
-    ((10, 300), (300, 1), 2, "scan_lines", "transposed view with lines too few for a tile: a thread each"),
+    ((10, 300), (300, 1), 2, "scan_tile", "ten row-major rows along their rows: tiles, outputs stored one by one"),
+    ((8, 100_000), (100_000, 1), 2, "scan_tile", "few long row-major rows: look-back along each, strided outputs"),
+    ((5, 10_001), (10_001, 1), 2, "scan_tile", "few rows of odd length: element loads, strided outputs"),
+    ((2, 3, 20_000), (60_000, 20_000, 1), 3, "scan_tile", "row-major 3-d along its last dim: two kept dims, strided outputs"),
+    ((8, 200), (200, 1), 2, "scan_lines", "few short row-major rows: a thread each"),
 ]
 
 

@@ -419,8 +419,16 @@ def test_scan_plans():
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 3, [64, 3000, 40], [40, 2560, 1], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TRANSPOSE and p.split == -(-3000 // 16) and p.grid == 4 * p.split
     assert p.tile_outputs == 32 * 32 * 16 and p.launches == 1
-    # too few lines, or too short a contiguous run, for such tiles: a thread per line
-    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10, 300], [300, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_LINES
+    # too few lines for such tiles, the scan dim contiguous in the input: the
+    # tile kernel along each line (outputs stored one by one), 256-thread
+    # tiles while the large ones number fewer than the CUs
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8, 10**6], [10**6, 1], 1, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 256 and p.vec == 4 and p.split == -(-10**6 // small)
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [5, 10001], [10001, 1], 1, 256).vec == 1
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [63, 500000], [500000, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_TILE
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [64, 500000], [500000, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_TRANSPOSE
+    # shorter than a wave's chunk, or too short a contiguous run: a thread per line
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10, 200], [200, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_LINES
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [300, 10], [10, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_LINES
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 3, [0, 5, 5], [1, 1, 5], 1, 256)
     assert p.kernel == rk.RK_KERNEL_NONE and p.launches == 0
