@@ -1023,7 +1023,7 @@ int rk_scan_dims(int op, int in_dtype, int acc_dtype, int out_dtype, const void 
     L.op = op;
     L.vec = d.vec;
     L.tmode = d.tmode;
-    L.ostr = d.ostr ? 1 : 0;
+    L.tstr = d.tstr;
     L.grid = d.grid;
     L.block = d.block;
     ScanArgs &a = L.args;

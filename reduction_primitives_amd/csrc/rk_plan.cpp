@@ -506,7 +506,7 @@ static bool plan_scan_transpose(ScanPlan &d, int isz, int asz)
         mode = 0;
     else if (ia >= 0 && ib >= 0 && ia != ib && k.ext[ia] >= R && k.ext[ib] >= R)
         mode = 1;
-    else if (ia >= 0 && d.s_out == 1 && d.s_in != 1 && d.m >= R && k.ext[ia] >= R)
+    else if (ia >= 0 && d.s_out == 1 && d.s_in != 1 && d.m >= R && k.ext[ia] >= tune::kScanTrMinLines)
         mode = 2;
     if (mode < 0)
         return false;
@@ -671,7 +671,7 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         // tiles (a few rows of a row-major matrix along their rows): the tile
         // kernel along each line, its outputs stored one by one
         d.kernel = SK_TILE;
-        d.ostr = true;
+        d.tstr = 1;
         bool vec_ok = in_addr % 16 == 0 && d.m % v == 0;
         for (int i = 0; i < k.nd; ++i)
             vec_ok = vec_ok && (k.str[i] * isz) % 16 == 0;
@@ -682,6 +682,21 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
             d.block = tune::kScanBlock;
             d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock, d.vec);
         }
+        d.tiles_per_line = ceil_div(d.m, d.tile_elems);
+        d.tiles = d.lines * d.tiles_per_line;
+        if (d.tiles > INT32_MAX)
+            return ST_INVALID;
+        d.grid = d.tiles;
+        d.ws_bytes = round_up_256(size_t(scan_tile_state_bytes(d.tiles)));
+    } else if (d.s_out == 1 && d.m >= tune::kScanWaveMinLen) {
+        // the mirror: lines contiguous in the output only, too few for the
+        // transposing tiles (a few columns of a row-major matrix along its
+        // columns): the tile kernel, element loads s_in apart
+        d.kernel = SK_TILE;
+        d.tstr = 2;
+        d.vec = 1;
+        d.block = tune::kScanBlock;
+        d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock, 1);
         d.tiles_per_line = ceil_div(d.m, d.tile_elems);
         d.tiles = d.lines * d.tiles_per_line;
         if (d.tiles > INT32_MAX)

@@ -13,8 +13,8 @@
 // Kernels, chosen by plan_scan():
 //   k_scan_tile     lines contiguous along the scan dim and at least one
 //                   tile long (the whole array included; also lines contiguous
-//                   in the input only, too few for the transposing tiles,
-//                   their outputs stored one by one): one pass, tiles in
+//                   on one side only, too few for the transposing tiles, the
+//                   other side's elements moved one by one): one pass, tiles in
 //                   the order of a counter, each tile's prefix from its
 //                   predecessors by decoupled look-back (Merrill and Garland,
 //                   "Single-pass Parallel Prefix Scan with Decoupled
@@ -499,12 +499,14 @@ __global__ __launch_bounds__(BLOCK) void k_scan_clear(uint32_t *w, int64_t words
 
 // Tile kernel: a tile is NW waves x UC chunks of consecutive elements of one
 // line; tiles are numbered by a counter in the order blocks start.
-// OSTR: the outputs of a line are s_out apart (the scan dim is contiguous in
+// STR = 1: the outputs of a line are s_out apart (the scan dim contiguous in
 // the input only: a few rows of a row-major matrix along their rows), each
-// stored on its own.
-template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = false, bool OSTR = false>
+// stored on its own.  STR = 2: the inputs are s_in apart (the scan dim
+// contiguous in the output only), loaded one element a lane.
+template <class In, class Acc, class Op, int BLOCK, int U, int VL, bool NTS = false, int STR = 0>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void k_scan_tile(ScanArgs a)
 {
+    static_assert(STR != 2 || VL == 1, "strided inputs take element loads");
     using C = Chunk<In, Acc, Op, VL>;
     using S = typename C::S;
     constexpr int V = C::V;
@@ -545,8 +547,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int k = 0; k < UC; ++k) {
         raw[k] = typename C::Raw{};
-        if (k < nk)
-            raw[k] = C::load(x, first + k * CH, a.m);
+        if (k < nk) {
+            if constexpr (STR == 2)
+                raw[k] = load1(x + (first + k * CH) * a.s_in);
+            else
+                raw[k] = C::load(x, first + k * CH, a.m);
+        }
     }
     issue_barrier();
 
@@ -592,7 +598,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
         chunk_scan<Acc, Op, V>(e, lane_excl, total);
         chunk_outputs<Acc, Op, V>(e, Op::apply(carry, lane_excl), a.inclusive != 0, o);
         if (k < nk) {
-            if constexpr (OSTR) {
+            if constexpr (STR == 1) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) {
                     const Acc w[1] = {o[i]};
@@ -1322,12 +1328,15 @@ int run_scan_typed(const ScanLaunch &L)
         if (L.args.slot < 0)
             clear_state(L.args, scan_tile_state_bytes(L.args.tiles) / 4, st);
 #define RK_SCAN_TILE(BK, UK, VLN) launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true>, grid, block, st, ev, L.args)
-#define RK_SCAN_TILE_OSTR(BK, UK, VLN)                                                                       \
-    launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true, true>, grid, block, st, ev, L.args)
-        if (L.ostr) {                            // strided outputs: the input's vector or element loads
-            if (L.block == BT && vl == VV) RK_SCAN_TILE_OSTR(BT, UT, VV);
-            else if (L.block == B && vl == VV) RK_SCAN_TILE_OSTR(B, U, VV);
-            else if (L.block == B && vl == 1) RK_SCAN_TILE_OSTR(B, U, 1);
+#define RK_SCAN_TILE_STR(BK, UK, VLN, SK)                                                                     \
+    launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true, SK>, grid, block, st, ev, L.args)
+        if (L.tstr == 1) {                       // strided outputs: the input's vector or element loads
+            if (L.block == BT && vl == VV) RK_SCAN_TILE_STR(BT, UT, VV, 1);
+            else if (L.block == B && vl == VV) RK_SCAN_TILE_STR(B, U, VV, 1);
+            else if (L.block == B && vl == 1) RK_SCAN_TILE_STR(B, U, 1, 1);
+            else return ST_INVALID;
+        } else if (L.tstr == 2) {                // strided inputs: element loads, small tiles
+            if (L.block == B && vl == 1) RK_SCAN_TILE_STR(B, U, 1, 2);
             else return ST_INVALID;
         } else if (L.block == BT) {
             if (vl == VV) RK_SCAN_TILE(BT, UT, VV);
@@ -1339,7 +1348,7 @@ int run_scan_typed(const ScanLaunch &L)
             else RK_SCAN_TILE(B, U, 1);
         }
 #undef RK_SCAN_TILE
-#undef RK_SCAN_TILE_OSTR
+#undef RK_SCAN_TILE_STR
         break;
     }
     case SK_ROWWAVE:

@@ -62,8 +62,9 @@ constexpr int kScanTrBlock = 256;         // transposing scan: threads per block
 // with the registers held to 128), the permuted view 200 against 167.
 constexpr int kScanTrTileKBScanOut = 32;
 constexpr int64_t kScanTrMinRun = 16;     // its two contiguous axes span at least this many elements
-// With the scan dim contiguous in the input, the transposing tiles need this
-// many lines; fewer take the tile kernel with outputs stored one by one.
+// With the scan dim contiguous on one side, the transposing tiles need this
+// many lines; fewer take the tile kernel, the other side's elements moved one
+// by one.
 // 8 Mi f32 as L row-major rows along their rows, us transposing / tile: L = 16
 // 357 / 103, 32 194 / 122, 64 113 / 118, 128 70 / 116, 256 46 / 60.
 constexpr int64_t kScanTrMinLines = 64;
@@ -166,7 +167,7 @@ struct ScanLaunch {
     int acc, op;
     int vec;              // elements per load (1: element loads)
     int tmode;            // transposing kernel: its mode
-    int ostr;             // tile kernel: outputs s_out apart along the scan dim
+    int tstr;             // tile kernel: 1 outputs s_out apart, 2 inputs s_in apart
     int64_t grid;
     int block;
     ScanArgs args;
@@ -200,7 +201,7 @@ struct ScanPlan {
     int64_t col_tiles_per_run = 0;   // columns and transposing kernels
     int64_t col_tiles = 0;
     int tmode = 0;                   // transposing kernel: its mode
-    bool ostr = false;               // tile kernel: outputs s_out apart along the scan dim
+    int tstr = 0;                    // tile kernel: 1 outputs s_out apart, 2 inputs s_in apart
     int64_t chunks = 0;
     int64_t grid = 0;
     int block = tune::kScanBlock;

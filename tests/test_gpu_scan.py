@@ -330,6 +330,9 @@ DIMS_CASES = [
     ((5, 10_001), (10_001, 1), 2, "scan_tile", "few rows of odd length: element loads, strided outputs"),
     ((2, 3, 20_000), (60_000, 20_000, 1), 3, "scan_tile", "row-major 3-d along its last dim: two kept dims, strided outputs"),
     ((8, 200), (200, 1), 2, "scan_lines", "few short row-major rows: a thread each"),
+    ((100_000, 8), (8, 1), 1, "scan_tile", "few row-major columns along their columns: element loads s_in apart"),
+    ((10_001, 5), (5, 1), 1, "scan_tile", "few columns of odd length, strided inputs"),
+    ((20_000, 3, 2), (6, 2, 1), 1, "scan_tile", "row-major 3-d along its first dim: two kept dims, strided inputs"),
 ]
 
 
@@ -393,7 +396,7 @@ def test_tile_state_paths(on):
     rk = _rk()
     cases = [((3 * TILE + 5,), (1,), 1), ((10**6 + 3,), (1,), 1), ((TILE,), (1,), 1),
              ((300, 2000), (1, 300), 2), ((10**8,), (1,), 1), ((5000, 2), (1, 5000), 1),
-             ((300, 2000), (2000, 1), 2), ((30, 4000, 40), (160000, 40, 1), 1)]
+             ((300, 2000), (2000, 1), 2), ((30, 2000, 64), (128000, 64, 1), 1), ((5000, 6), (6, 1), 1)]
     with _fused(rk, on):
         for rep in range(2):
             for shape, strides, dim in cases:

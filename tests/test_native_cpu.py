@@ -427,6 +427,12 @@ def test_scan_plans():
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [5, 10001], [10001, 1], 1, 256).vec == 1
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [63, 500000], [500000, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_TILE
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [64, 500000], [500000, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_TRANSPOSE
+    # the mirror, the scan dim contiguous in the output only: element loads
+    # s_in apart, 256-thread tiles; the transposing tiles from 64 lines
+    p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10**6, 8], [8, 1], 0, 256)
+    assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 256 and p.vec == 1 and p.split == -(-10**6 // small)
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [500000, 63], [63, 1], 0, 256).kernel == rk.RK_KERNEL_SCAN_TILE
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [500000, 64], [64, 1], 0, 256).kernel == rk.RK_KERNEL_SCAN_TRANSPOSE
     # shorter than a wave's chunk, or too short a contiguous run: a thread per line
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [10, 200], [200, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_LINES
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [300, 10], [10, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_LINES
