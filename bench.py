@@ -520,6 +520,9 @@ def configs_table(rk, torch, dev, reps):
     rm = (mf.shape[1], 1)
     scan("8192x8192 f32 row-major cumsum dims=2", md, mf.shape, rm, 2)
     scan("8192x8192 f32 row-major cumsum dims=1", md, mf.shape, rm, 1)
+    # few lines contiguous on one side only: 8 row-major rows along their rows, and the mirror
+    scan("8x1000000 f32 row-major cumsum dims=2", md, (8, 10**6), (10**6, 1), 2)
+    scan("1000000x8 f32 row-major cumsum dims=1", md, (10**6, 8), (8, 1), 1)
     del md
     pv = W.permuted_kept()
     scan("256x1024x256 f32 permuted cumsum dims=2", pv.data.to(dev), pv.shape, pv.view_strides, 2)
