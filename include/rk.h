@@ -263,10 +263,11 @@ size_t rk_scan_workspace_size(int in_dtype, int acc_dtype, int ndim, const int64
  * pointer to >= rk_scan_workspace_size bytes, aligned to 8 (NULL allowed
  * when that size is 0); a workspace must not be shared by calls that may run
  * at the same time.  stream: hipStream_t or NULL; asynchronous.  A line
- * contiguous along the scan dim and at least one tile long (or a strided scan
- * dim over runs of contiguous lines, or a view whose input and output are
- * contiguous along different axes) is scanned in one pass with decoupled
- * look-back between tiles.  The tiles' counter and flags (along contiguous
+ * contiguous along the scan dim and at least one tile long (or contiguous on
+ * one side only, input or output, the other side's elements then moved one
+ * by one; or a strided scan dim over runs of contiguous lines; or a view
+ * whose input and output are contiguous along different axes) is scanned in
+ * one pass with decoupled look-back between tiles.  The tiles' counter and flags (along contiguous
  * lines: all of the per-tile state) live in the library's per-stream slot
  * when they fit one (4096 tiles along contiguous lines, 8192 for a strided
  * scan dim; the last block of the call zeroes them again), otherwise in the
@@ -306,7 +307,8 @@ typedef enum {
     RK_KERNEL_ROW = 6,          /* one wave per output over a contiguous reduced dim */
     RK_KERNEL_GENERIC = 7,      /* one block per output, any layout */
     RK_KERNEL_ALL2 = 8,         /* whole-array passes over a two-input source (rk_reduce_all2) */
-    RK_KERNEL_SCAN_TILE = 9,    /* scan: tiles of contiguous lines, decoupled look-back (+ a clearing launch) */
+    RK_KERNEL_SCAN_TILE = 9,    /* scan: tiles of lines contiguous along the scan dim (in input and output,
+                                   or on one side for a few lines), decoupled look-back (+ a clearing launch) */
     RK_KERNEL_SCAN_ROWWAVE = 10,/* scan: one wave per contiguous line shorter than a tile */
     RK_KERNEL_SCAN_LINES = 11,  /* scan: one thread per line along a strided scan dim */
     RK_KERNEL_SCAN_COLUMNS = 12,/* scan: tiles of contiguous lines x scan positions, look-back along
