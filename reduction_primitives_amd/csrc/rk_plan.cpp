@@ -678,7 +678,8 @@ int plan_scan(int in_dtype, int acc_dtype, int out_dtype, uintptr_t in_addr, uin
         d.vec = vec_ok ? v : 1;
         d.block = tune::kScanTileBlock;
         d.tile_elems = scan_tile_elems(in_dtype, tune::kScanTileBlock, d.vec);
-        if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus || d.vec == 1) {
+        // large tiles only while a lane's vector of accumulators stays within 32 bytes
+        if (d.lines * ceil_div(d.m, d.tile_elems) < num_cus || d.vec == 1 || v * asz > 32) {
             d.block = tune::kScanBlock;
             d.tile_elems = scan_tile_elems(in_dtype, tune::kScanBlock, d.vec);
         }

@@ -1331,10 +1331,17 @@ int run_scan_typed(const ScanLaunch &L)
 #define RK_SCAN_TILE_STR(BK, UK, VLN, SK)                                                                     \
     launch_first(&k_scan_tile<In, Acc, Op, BK, UK, VLN, true, SK>, grid, block, st, ev, L.args)
         if (L.tstr == 1) {                       // strided outputs: the input's vector or element loads
-            if (L.block == BT && vl == VV) RK_SCAN_TILE_STR(BT, UT, VV, 1);
-            else if (L.block == B && vl == VV) RK_SCAN_TILE_STR(B, U, VV, 1);
+            // large tiles only while a lane's vector of accumulators stays within 32 bytes
+            // (bf16 or f16 into f64 went to scratch memory there)
+            constexpr bool large_ok = VV * sizeof(Acc) <= 32;
+            if (L.block == B && vl == VV) RK_SCAN_TILE_STR(B, U, VV, 1);
             else if (L.block == B && vl == 1) RK_SCAN_TILE_STR(B, U, 1, 1);
-            else return ST_INVALID;
+            else if (L.block == BT && vl == VV) {
+                if constexpr (large_ok) RK_SCAN_TILE_STR(BT, UT, VV, 1);
+                else return ST_INVALID;
+            } else {
+                return ST_INVALID;
+            }
         } else if (L.tstr == 2) {                // strided inputs: element loads, small tiles
             if (L.block == B && vl == 1) RK_SCAN_TILE_STR(B, U, 1, 2);
             else return ST_INVALID;

@@ -327,6 +327,7 @@ DIMS_CASES = [
     ((17, 33, 100), (3300, 100, 1), 1, "scan_transpose", "scan dim contiguous in the output, an outer kept dim"),
     ((10, 300), (300, 1), 2, "scan_tile", "ten row-major rows along their rows: tiles, outputs stored one by one"),
     ((8, 100_000), (100_000, 1), 2, "scan_tile", "few long row-major rows: look-back along each, strided outputs"),
+    ((40, 500_000), (500_000, 1), 2, "scan_tile", "40 long row-major rows: large tiles, strided outputs"),
     ((5, 10_001), (10_001, 1), 2, "scan_tile", "few rows of odd length: element loads, strided outputs"),
     ((2, 3, 20_000), (60_000, 20_000, 1), 3, "scan_tile", "row-major 3-d along its last dim: two kept dims, strided outputs"),
     ((8, 200), (200, 1), 2, "scan_lines", "few short row-major rows: a thread each"),
@@ -479,6 +480,7 @@ def test_beyond_2_31_elements():
 
 SCAN_DIMS_COMBOS = [  # (input, accumulator, output)
     (torch.float16, torch.float32, torch.float16),
+    (torch.bfloat16, torch.float64, torch.float64),
     (torch.float64, torch.float64, torch.float64),
     (torch.int64, torch.int64, torch.int64),
     (torch.int32, torch.int32, torch.int32),          # sums wrap in the 32-bit accumulator
@@ -494,6 +496,8 @@ SCAN_DIMS_LAYOUTS = [  # (shape, dim, strides or None)
     ((300, 700), 2, (700, 1)),                 # transposing, scan dim contiguous in the input
     ((300, 700), 1, (700, 1)),                 # transposing, scan dim contiguous in the output
     ((40, 300, 50), 2, (300 * 50, 50, 1)),     # transposing, two kept dims
+    ((8, 20_000), 2, (20_000, 1)),             # tiles along few row-major rows, strided outputs
+    ((20_000, 8), 1, (8, 1)),                  # tiles along few row-major columns, strided inputs
 ]
 
 

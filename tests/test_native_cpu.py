@@ -425,6 +425,9 @@ def test_scan_plans():
     p = rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [8, 10**6], [10**6, 1], 1, 256)
     assert p.kernel == rk.RK_KERNEL_SCAN_TILE and p.block == 256 and p.vec == 4 and p.split == -(-10**6 // small)
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [5, 10001], [10001, 1], 1, 256).vec == 1
+    assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [40, 500000], [500000, 1], 1, 256).block == 1024
+    # bf16 into f64: 256-thread tiles (eight f64 a lane in the large ones went to scratch memory)
+    assert rk.rk_plan_scan(bf16, f64, f64, 0, 0, 2, [40, 500000], [500000, 1], 1, 256).block == 256
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [63, 500000], [500000, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_TILE
     assert rk.rk_plan_scan(f32, f32, f32, 0, 0, 2, [64, 500000], [500000, 1], 1, 256).kernel == rk.RK_KERNEL_SCAN_TRANSPOSE
     # the mirror, the scan dim contiguous in the output only: element loads
